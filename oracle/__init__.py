@@ -1,0 +1,133 @@
+"""DMS oracle -- TEST INFRASTRUCTURE ONLY.
+
+Plain CPU statement of DMS decode / prefill attention (see dms_oracle.c for the
+rule and its sources).  Only ``tests/``, ``__graft_entry__.smoke()`` and the
+CPU-baseline leg of ``bench.py`` may import this package; the GPU library never
+does, and this package imports nothing from it.
+
+Everything here is argument marshalling around dms_oracle.c, plus the byte
+accounting of a live set (live count x 2 tensors x head_dim x 2 bytes), which is
+the definition of the "KV bytes" a compact store holds.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+import threading
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "dms_oracle.c")
+_SO = os.path.join(_HERE, "libdms_oracle.so")
+_lock = threading.Lock()
+_handle = None
+
+
+def build(force: bool = False, src: str = _SRC, so: str = _SO) -> str:
+    """Compile the oracle (gcc -O2 -fopenmp) into a shared library."""
+    if force or not os.path.exists(so) or os.path.getmtime(so) < os.path.getmtime(src):
+        tmp = so + ".tmp%d" % os.getpid()
+        subprocess.check_call(["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-std=c11",
+                               src, "-o", tmp, "-lm"])
+        os.replace(tmp, so)
+    return so
+
+
+def load(so: str) -> ctypes.CDLL:
+    """Load an oracle library and declare its entry points."""
+    lib = ctypes.CDLL(so)
+    vp, i32, i64, dbl = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_double
+    lib.dms_oracle_marks.argtypes = [vp, i64, vp]
+    lib.dms_oracle_marks.restype = None
+    lib.dms_oracle_live_positions.argtypes = [i64, i64, vp, i64, vp]
+    lib.dms_oracle_live_positions.restype = i64
+    lib.dms_oracle_attend.argtypes = [i32, i32, i32, i64, dbl, i64, vp, vp, i64, vp, vp, vp, vp]
+    lib.dms_oracle_attend.restype = ctypes.c_int
+    return lib
+
+
+def _lib():
+    global _handle
+    with _lock:
+        if _handle is None:
+            build()
+            _handle = load(_SO)
+    return _handle
+
+
+class Oracle:
+    """The oracle's entry points bound to one compiled library (the default one,
+    or a differently compiled copy that a test wants to exercise)."""
+
+    def __init__(self, lib: ctypes.CDLL):
+        self.lib = lib
+
+    def marks(self, logits: np.ndarray) -> np.ndarray:
+        lg = np.ascontiguousarray(logits, np.float32)
+        out = np.empty(lg.shape, np.uint8)
+        self.lib.dms_oracle_marks(lg.ctypes.data, lg.size, out.ctypes.data)
+        return out
+
+    def live_positions(self, t: int, window: int, marks_col: np.ndarray) -> np.ndarray:
+        """Live set of one head at query position t; marks_col[s] is the mark of s."""
+        m = np.ascontiguousarray(marks_col, np.uint8)
+        if t >= m.shape[0]:
+            raise ValueError("t beyond the marks given")
+        out = np.empty(t + 1, np.int32)
+        n = self.lib.dms_oracle_live_positions(t, window, m.ctypes.data, 1, out.ctypes.data)
+        return out[:n].copy()
+
+    def live_count(self, t: int, window: int, marks_col: np.ndarray) -> int:
+        m = np.ascontiguousarray(marks_col, np.uint8)
+        return int(self.lib.dms_oracle_live_positions(t, window, m.ctypes.data, 1, None))
+
+    def attend(self, q: np.ndarray, query_pos, k: np.ndarray, v: np.ndarray,
+               marks: np.ndarray, window: int, scale: float = 0.0) -> np.ndarray:
+        """q [nq][Hq][D], k/v [T][Hkv][D] bf16 bits (uint16); marks [T][Hkv].
+        Returns out [nq][Hq][D] float64."""
+        q = np.ascontiguousarray(q, np.uint16)
+        k = np.ascontiguousarray(k, np.uint16)
+        v = np.ascontiguousarray(v, np.uint16)
+        marks = np.ascontiguousarray(marks, np.uint8)
+        qp = np.ascontiguousarray(np.asarray(query_pos, np.int64).reshape(-1))
+        nq, hq, d = q.shape
+        nk, hkv, d2 = k.shape
+        if d2 != d or v.shape != k.shape or marks.shape != (nk, hkv) or qp.shape[0] != nq:
+            raise ValueError("shape mismatch")
+        if hq % hkv:
+            raise ValueError("n_q_heads must be a multiple of n_kv_heads")
+        out = np.empty((nq, hq, d), np.float64)
+        rc = self.lib.dms_oracle_attend(hq, hkv, d, int(window), float(scale), nq, qp.ctypes.data,
+                                        q.ctypes.data, nk, k.ctypes.data, v.ctypes.data,
+                                        marks.ctypes.data, out.ctypes.data)
+        if rc != 0:
+            raise ValueError("query position outside the keys given")
+        return out
+
+
+def default() -> Oracle:
+    return Oracle(_lib())
+
+
+def marks(logits):
+    return default().marks(logits)
+
+
+def live_positions(t, window, marks_col):
+    return default().live_positions(t, window, marks_col)
+
+
+def live_count(t, window, marks_col):
+    return default().live_count(t, window, marks_col)
+
+
+def attend(q, query_pos, k, v, marks_, window, scale=0.0):
+    return default().attend(q, query_pos, k, v, marks_, window, scale)
+
+
+def kv_bytes_live(live_counts, head_dim: int) -> int:
+    """Bytes a compact store needs for the given live counts: K and V rows of
+    head_dim bf16 values each."""
+    return int(np.sum(np.asarray(live_counts, np.int64))) * 2 * head_dim * 2

@@ -1,0 +1,140 @@
+/*
+ * DMS ORACLE -- TEST INFRASTRUCTURE ONLY.
+ *
+ * A plain, slow CPU statement of what DMS decode / prefill attention computes.
+ * Only the tests, the smoke check and the benchmark's CPU-baseline leg may load
+ * this file.  It shares no code, header, table or helper with the GPU library;
+ * it never looks at a compact store: it keeps the full, uncompressed K/V of
+ * every token and decides per (query, key) whether the key is visible.
+ *
+ * Sources (the method is described in prose only):
+ *  [MV] "NVIDIA veroeffentlicht Qwen3-8B-DMS-8x mit innovativer
+ *       Speicherkompression fuer verbesserte Inferenzzeiten" (mindverse news
+ *       page), section "Dynamic Memory Sparsification (DMS): Eine innovative
+ *       Loesung": eviction is learned per head; the policy spans the range from
+ *       a sliding window over the most recent 512 tokens to full attention; a
+ *       token marked for eviction is kept for a while after it is marked
+ *       (delayed eviction).
+ *  [ST] "Nvidia DMS: szhatie pamyati LLM v 8 raz" (stiva.ai blog), sections
+ *       "Dynamic Memory Sparsification: ..." (one keep/evict signal per token)
+ *       and "Klyuchevoe izobretenie: delayed eviction" (a marked token stays
+ *       readable for some hundreds of further steps, then is removed).
+ *  [FD] "FastDMS: vLLM BF16/FP8 ... 6.4x KV cache" (molayo1419.me), quality
+ *       method paragraph: the eviction-disabled reference is the same engine
+ *       with a 1M-token window, i.e. the whole KV cache is kept.
+ *
+ * Readings taken where the pages leave a step open:
+ *  - a token's keep/evict decision is taken from its own logit when it is
+ *    appended; it is marked iff logit > 0 (a logit of exactly 0 is not marked);
+ *  - the delay window w counts query steps: a marked token at position s is
+ *    visible to the queries t = s, s+1, ..., s+w-1 and to no later one
+ *    (t < s + w); an unmarked token is visible to every t >= s;
+ *  - a query always sees its own token (the causal diagonal);
+ *  - scores are scale * <q, k> with scale = 1/sqrt(head_dim) unless given;
+ *  - grouped-query attention maps q head hq to kv head hq / (Hq / Hkv).
+ *
+ * Arithmetic: inputs are bf16 bit patterns; every product, sum, exp and divide
+ * is done in double.  Softmax subtracts the maximum visible score before exp.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+static double bf16_bits_to_double(uint16_t b) {
+    uint32_t u = (uint32_t)b << 16;
+    float f;
+    memcpy(&f, &u, 4);
+    return (double)f;
+}
+
+/* Eviction marks: m = (logit > 0), one byte per logit ([ST] keep/evict signal). */
+void dms_oracle_marks(const float* logits, int64_t n, uint8_t* marks) {
+    for (int64_t i = 0; i < n; ++i) marks[i] = logits[i] > 0.0f ? 1 : 0;
+}
+
+/* The visibility rule ([MV], [ST]): key position s is visible to query position
+ * t iff s <= t and (s is not marked, or t < s + w). */
+static int visible(int64_t t, int64_t s, int marked, int64_t window) {
+    if (s > t) return 0;
+    if (!marked) return 1;
+    return t < s + window;
+}
+
+/* Live set of one head at query position t: every s <= t visible to t, in
+ * ascending order.  marks are read as marks[s * stride].  Writes the positions
+ * to out (when out is not NULL) and returns how many there are. */
+int64_t dms_oracle_live_positions(int64_t t, int64_t window, const uint8_t* marks,
+                                  int64_t stride, int32_t* out) {
+    int64_t n = 0;
+    for (int64_t s = 0; s <= t; ++s) {
+        if (visible(t, s, marks[s * stride], window)) {
+            if (out) out[n] = (int32_t)s;
+            ++n;
+        }
+    }
+    return n;
+}
+
+/* Masked attention over the full K/V of one (sequence, layer).
+ *
+ *   q     [n_queries][n_q_heads][head_dim]   bf16 bits, row i is the query at
+ *                                            position query_pos[i]
+ *   k, v  [n_keys][n_kv_heads][head_dim]     bf16 bits, row s = position s
+ *   marks [n_keys][n_kv_heads]               0/1
+ *   out   [n_queries][n_q_heads][head_dim]   double
+ *
+ * For each query t and q head hq (kv head h = hq / group):
+ *   z_s = scale * sum_d q[t,hq,d] * k[s,h,d]           for visible s
+ *   out = sum_s exp(z_s - max z) v[s,h,:] / sum_s exp(z_s - max z)
+ * Returns 0, or -1 when a query position is outside [0, n_keys). */
+int dms_oracle_attend(int32_t n_q_heads, int32_t n_kv_heads, int32_t head_dim,
+                      int64_t window, double scale, int64_t n_queries,
+                      const int64_t* query_pos, const uint16_t* q, int64_t n_keys,
+                      const uint16_t* k, const uint16_t* v, const uint8_t* marks,
+                      double* out) {
+    const int32_t group = n_q_heads / n_kv_heads;
+    for (int64_t i = 0; i < n_queries; ++i)
+        if (query_pos[i] < 0 || query_pos[i] >= n_keys) return -1;
+    if (scale == 0.0) scale = 1.0 / sqrt((double)head_dim);
+
+#pragma omp parallel
+    {
+        double* z = (double*)malloc(sizeof(double) * (size_t)n_keys);
+        double* qd = (double*)malloc(sizeof(double) * (size_t)head_dim);
+#pragma omp for schedule(dynamic, 1) collapse(2)
+        for (int64_t i = 0; i < n_queries; ++i) {
+            for (int32_t hq = 0; hq < n_q_heads; ++hq) {
+                const int64_t t = query_pos[i];
+                const int32_t h = hq / group;
+                const uint16_t* qrow = q + (i * n_q_heads + hq) * (int64_t)head_dim;
+                for (int32_t d = 0; d < head_dim; ++d) qd[d] = bf16_bits_to_double(qrow[d]);
+
+                double zmax = -INFINITY;
+                for (int64_t s = 0; s <= t; ++s) {
+                    if (!visible(t, s, marks[s * n_kv_heads + h], window)) continue;
+                    const uint16_t* krow = k + (s * n_kv_heads + h) * (int64_t)head_dim;
+                    double dot = 0.0;
+                    for (int32_t d = 0; d < head_dim; ++d) dot += qd[d] * bf16_bits_to_double(krow[d]);
+                    z[s] = scale * dot;
+                    if (z[s] > zmax) zmax = z[s];
+                }
+
+                double* o = out + (i * n_q_heads + hq) * (int64_t)head_dim;
+                for (int32_t d = 0; d < head_dim; ++d) o[d] = 0.0;
+                double denom = 0.0;
+                for (int64_t s = 0; s <= t; ++s) {
+                    if (!visible(t, s, marks[s * n_kv_heads + h], window)) continue;
+                    const double wgt = exp(z[s] - zmax);
+                    const uint16_t* vrow = v + (s * n_kv_heads + h) * (int64_t)head_dim;
+                    denom += wgt;
+                    for (int32_t d = 0; d < head_dim; ++d) o[d] += wgt * bf16_bits_to_double(vrow[d]);
+                }
+                for (int32_t d = 0; d < head_dim; ++d) o[d] /= denom;
+            }
+        }
+        free(qd);
+        free(z);
+    }
+    return 0;
+}
