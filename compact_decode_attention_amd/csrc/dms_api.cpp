@@ -1,0 +1,419 @@
+// Host side of the DMS C ABI (include/dms.h): configuration checks, arena
+// layout, per-(sequence, layer) bookkeeping, kernel launches and stats.
+#include "dms.h"
+
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "dms_internal.h"
+
+namespace {
+
+thread_local std::string g_err;
+
+dms_status fail(dms_status s, const std::string& msg) {
+    g_err = msg;
+    return s;
+}
+
+dms_status hip_fail(hipError_t e, const char* what) {
+    return fail(DMS_E_HIP, std::string(what) + ": " + hipGetErrorString(e));
+}
+
+constexpr size_t kAlign = 256;
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+enum Section { S_K, S_V, S_POS, S_STACK, S_HSTATE, S_PTABLE, S_RING, S_PART, S_PREFIX, S_INV, S_CTL, S_N };
+
+struct Layout {
+    size_t off[S_N + 1];
+    int64_t heads;
+    int32_t pages_per_head, ring_len, max_items, max_call_heads;
+};
+
+bool make_layout(const dms_pool_config* c, Layout* L, std::string* why) {
+    auto bad = [&](const char* m) { *why = m; return false; };
+    if (!c) return bad("config is NULL");
+    if (c->n_layers < 1) return bad("n_layers must be >= 1");
+    if (c->n_kv_heads < 1) return bad("n_kv_heads must be >= 1");
+    if (c->n_q_heads < c->n_kv_heads || c->n_q_heads % c->n_kv_heads) return bad("n_q_heads must be a multiple of n_kv_heads");
+    const int g = c->n_q_heads / c->n_kv_heads;
+    if (g != 1 && g != 2 && g != 4 && g != 8) return bad("n_q_heads / n_kv_heads must be 1, 2, 4 or 8");
+    if (c->head_dim != 64 && c->head_dim != 128) return bad("head_dim must be 64 or 128");
+    if (c->window < 1) return bad("window must be >= 1");
+    if (c->max_seqs < 1) return bad("max_seqs must be >= 1");
+    if (c->max_positions < 1 || c->max_positions > (1 << 30)) return bad("max_positions must be in [1, 2^30]");
+    if (c->page_slots != 0 && c->page_slots != DMS_PAGE_SLOTS) return bad("page_slots must be 0 or 64");
+    if (c->max_pages < 1 || c->max_pages > (int64_t)INT32_MAX) return bad("max_pages must be in [1, 2^31)");
+    if (!(c->softmax_scale >= 0.f) || !std::isfinite(c->softmax_scale)) return bad("softmax_scale must be finite and >= 0");
+    for (int i = 0; i < 4; ++i)
+        if (c->reserved[i] != 0) return bad("reserved fields must be 0");
+    const int64_t heads = (int64_t)c->max_seqs * c->n_layers * c->n_kv_heads;
+    if (heads > (int64_t)INT32_MAX / 4) return bad("max_seqs * n_layers * n_kv_heads too large");
+    if ((int64_t)c->n_layers * c->n_kv_heads > dms::kMaxCallHeads) return bad("n_layers * n_kv_heads too large");
+    const int64_t D = c->head_dim;
+    L->heads = heads;
+    L->pages_per_head = (c->max_positions + dms::kPage - 1) / dms::kPage;
+    L->ring_len = c->window < c->max_positions ? c->window : 0;
+    L->max_call_heads = (int32_t)std::min<int64_t>(heads, dms::kMaxCallHeads);
+    const int64_t items = c->max_pages * dms::kPage / dms::kChunk + L->max_call_heads + 1;
+    if (items > INT32_MAX) return bad("max_pages too large");
+    L->max_items = (int32_t)items;
+    size_t sz[S_N];
+    sz[S_K] = (size_t)c->max_pages * dms::kPage * D * 2;
+    sz[S_V] = sz[S_K];
+    sz[S_POS] = (size_t)c->max_pages * dms::kPage * 4;
+    sz[S_STACK] = (size_t)c->max_pages * 4;
+    sz[S_HSTATE] = (size_t)heads * 16;
+    sz[S_PTABLE] = (size_t)heads * L->pages_per_head * 4;
+    sz[S_RING] = (size_t)heads * L->ring_len * 4;
+    sz[S_PART] = (size_t)L->max_items * g * (D + 2) * 4;
+    sz[S_PREFIX] = (size_t)(L->max_call_heads + 1) * 4;
+    sz[S_INV] = (size_t)c->n_kv_heads * c->max_positions * 4;
+    sz[S_CTL] = 64 * 4;
+    size_t o = 0;
+    for (int i = 0; i < S_N; ++i) {
+        L->off[i] = o;
+        o = align_up(o + sz[i]);
+    }
+    L->off[S_N] = o;
+    return true;
+}
+
+// SplitMix64 step, used only to shuffle the initial page order on request.
+uint64_t mix64(uint64_t& s) {
+    uint64_t z = (s += 0x9E3779B97F4A7C15ULL);
+    z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ULL;
+    z = (z ^ (z >> 27)) * 0x94D049BB133111EBULL;
+    return z ^ (z >> 31);
+}
+
+}  // namespace
+
+struct dms_pool {
+    dms_pool_config cfg;
+    bool timing = false;
+    std::vector<hipEvent_t> events;  // triples recorded by decode launches while timing
+    Layout layout;
+    dms::PoolDev dev;
+    char* arena;
+    std::vector<int32_t> pos;  // [max_seqs][n_layers]: next position, -1 = empty
+    int cu_count;
+    int32_t& position(int seq, int layer) { return pos[(size_t)seq * cfg.n_layers + layer]; }
+};
+
+extern "C" {
+
+const char* dms_last_error(void) { return g_err.c_str(); }
+
+size_t dms_pool_bytes(const dms_pool_config* cfg) {
+    Layout L;
+    std::string why;
+    if (!make_layout(cfg, &L, &why)) {
+        g_err = why;
+        return 0;
+    }
+    g_err.clear();
+    return L.off[S_N];
+}
+
+dms_status dms_pool_create(const dms_pool_config* cfg, void* arena, size_t arena_bytes, void* stream,
+                           dms_pool** out) {
+    if (!out) return fail(DMS_E_INVAL, "out is NULL");
+    *out = nullptr;
+    Layout L;
+    std::string why;
+    if (!make_layout(cfg, &L, &why)) return fail(DMS_E_INVAL, why);
+    if (!arena) return fail(DMS_E_INVAL, "arena is NULL");
+    if (reinterpret_cast<uintptr_t>(arena) % kAlign) return fail(DMS_E_INVAL, "arena must be 256-byte aligned");
+    if (arena_bytes < L.off[S_N]) return fail(DMS_E_NOMEM, "arena smaller than dms_pool_bytes()");
+    hipStream_t s = static_cast<hipStream_t>(stream);
+
+    dms_pool* p = new dms_pool();
+    p->cfg = *cfg;
+    if (p->cfg.page_slots == 0) p->cfg.page_slots = DMS_PAGE_SLOTS;
+    p->layout = L;
+    p->arena = static_cast<char*>(arena);
+    p->pos.assign((size_t)cfg->max_seqs * cfg->n_layers, -1);
+    p->cu_count = dms::device_cu_count();
+    char* a = p->arena;
+    dms::PoolDev& d = p->dev;
+    d.kpages = reinterpret_cast<uint16_t*>(a + L.off[S_K]);
+    d.vpages = reinterpret_cast<uint16_t*>(a + L.off[S_V]);
+    d.slot_pos = reinterpret_cast<int32_t*>(a + L.off[S_POS]);
+    d.stack = reinterpret_cast<int32_t*>(a + L.off[S_STACK]);
+    d.hstate = reinterpret_cast<int32_t*>(a + L.off[S_HSTATE]);
+    d.ptable = reinterpret_cast<int32_t*>(a + L.off[S_PTABLE]);
+    d.ring = reinterpret_cast<int32_t*>(a + L.off[S_RING]);
+    d.partials = reinterpret_cast<float*>(a + L.off[S_PART]);
+    d.prefix = reinterpret_cast<int32_t*>(a + L.off[S_PREFIX]);
+    d.inv = reinterpret_cast<int32_t*>(a + L.off[S_INV]);
+    d.ctl = reinterpret_cast<int32_t*>(a + L.off[S_CTL]);
+    d.max_pages = cfg->max_pages;
+    d.n_layers = cfg->n_layers;
+    d.n_q_heads = cfg->n_q_heads;
+    d.n_kv_heads = cfg->n_kv_heads;
+    d.head_dim = cfg->head_dim;
+    d.window = cfg->window;
+    d.ring_len = L.ring_len;
+    d.pages_per_head = L.pages_per_head;
+    d.max_positions = cfg->max_positions;
+    d.max_items = L.max_items;
+    const double scale = cfg->softmax_scale > 0.f ? (double)cfg->softmax_scale : 1.0 / std::sqrt((double)cfg->head_dim);
+    d.scale_log2 = (float)(scale * 1.4426950408889634);
+
+    // free stack: pops take stack[top-1] first, so store the hand-out order reversed
+    std::vector<int32_t> order((size_t)cfg->max_pages);
+    for (int64_t i = 0; i < cfg->max_pages; ++i) order[i] = (int32_t)i;
+    if (cfg->page_order_seed) {
+        uint64_t st = cfg->page_order_seed;
+        for (int64_t i = cfg->max_pages - 1; i > 0; --i) std::swap(order[i], order[mix64(st) % (uint64_t)(i + 1)]);
+    }
+    std::reverse(order.begin(), order.end());
+    int32_t ctl[64] = {0};
+    ctl[dms::kCtlTop] = (int32_t)cfg->max_pages;
+
+    hipError_t e = hipMemsetAsync(arena, 0, L.off[S_N], s);
+    if (e == hipSuccess) e = hipMemcpyAsync(d.stack, order.data(), order.size() * 4, hipMemcpyHostToDevice, s);
+    if (e == hipSuccess) e = hipMemcpyAsync(d.ctl, ctl, sizeof(ctl), hipMemcpyHostToDevice, s);
+    if (e == hipSuccess) e = hipStreamSynchronize(s);
+    if (e != hipSuccess) {
+        delete p;
+        return hip_fail(e, "pool initialisation");
+    }
+    *out = p;
+    g_err.clear();
+    return DMS_OK;
+}
+
+dms_status dms_pool_destroy(dms_pool* pool) {
+    if (!pool) return fail(DMS_E_INVAL, "pool is NULL");
+    hipError_t e = hipDeviceSynchronize();
+    for (hipEvent_t ev : pool->events) hipEventDestroy(ev);
+    delete pool;
+    if (e != hipSuccess) return hip_fail(e, "synchronise");
+    g_err.clear();
+    return DMS_OK;
+}
+
+dms_status dms_prefill(dms_pool* pool, int32_t seq, int32_t layer, int32_t n_tokens, const void* q, const void* k,
+                       const void* v, const float* logits, void* out, void* stream) {
+    if (!pool) return fail(DMS_E_INVAL, "pool is NULL");
+    const dms_pool_config& c = pool->cfg;
+    if (seq < 0 || seq >= c.max_seqs) return fail(DMS_E_INVAL, "seq out of range");
+    if (layer < 0 || layer >= c.n_layers) return fail(DMS_E_INVAL, "layer out of range");
+    if (n_tokens < 1 || n_tokens > c.max_positions) return fail(DMS_E_INVAL, "n_tokens must be in [1, max_positions]");
+    if (!k || !v || !logits) return fail(DMS_E_INVAL, "k, v and logits must not be NULL");
+    if (out && !q) return fail(DMS_E_INVAL, "q must not be NULL when out is given");
+    if (pool->position(seq, layer) >= 0) return fail(DMS_E_STATE, "this (seq, layer) already holds tokens");
+    dms::PrefillArgs a;
+    a.pool = pool->dev;
+    a.q = static_cast<const uint16_t*>(q);
+    a.k = static_cast<const uint16_t*>(k);
+    a.v = static_cast<const uint16_t*>(v);
+    a.logits = logits;
+    a.out = static_cast<uint16_t*>(out);
+    a.seq = seq;
+    a.layer = layer;
+    a.n_tokens = n_tokens;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    hipError_t e = dms::launch_prefill_compact(a, s);
+    if (e != hipSuccess) return hip_fail(e, "prefill compaction launch");
+    if (out) {
+        e = dms::launch_prefill_attend(a, s);
+        if (e != hipSuccess) return hip_fail(e, "prefill attention launch");
+    }
+    pool->position(seq, layer) = n_tokens;
+    g_err.clear();
+    return DMS_OK;
+}
+
+dms_status dms_decode_step(dms_pool* pool, int32_t n_seqs, const int32_t* seq_ids, int32_t layer0, int32_t n_layers,
+                           const void* q, const void* k, const void* v, const float* logits, void* out,
+                           void* stream) {
+    if (!pool) return fail(DMS_E_INVAL, "pool is NULL");
+    const dms_pool_config& c = pool->cfg;
+    if (n_seqs < 1 || n_seqs > c.max_seqs) return fail(DMS_E_INVAL, "n_seqs must be in [1, max_seqs]");
+    if (!seq_ids) return fail(DMS_E_INVAL, "seq_ids is NULL");
+    if (layer0 < 0 || n_layers < 1 || layer0 + n_layers > c.n_layers) return fail(DMS_E_INVAL, "layer range out of bounds");
+    if (!q || !k || !v || !logits || !out) return fail(DMS_E_INVAL, "q, k, v, logits and out must not be NULL");
+    std::vector<char> seen((size_t)c.max_seqs, 0);
+    for (int i = 0; i < n_seqs; ++i) {
+        const int s = seq_ids[i];
+        if (s < 0 || s >= c.max_seqs) return fail(DMS_E_INVAL, "seq id out of range");
+        if (seen[s]) return fail(DMS_E_INVAL, "seq ids must be distinct");
+        seen[s] = 1;
+        for (int l = layer0; l < layer0 + n_layers; ++l) {
+            const int p = pool->position(s, l);
+            if (p < 0) return fail(DMS_E_STATE, "decode on a (seq, layer) that was not prefilled");
+            if (p >= c.max_positions) return fail(DMS_E_STATE, "sequence reached max_positions");
+        }
+    }
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    const int hkv = c.n_kv_heads;
+    const int per_launch = std::max(1, std::min(dms::kMaxCallSeqs, dms::kMaxCallHeads / (n_layers * hkv)));
+    for (int sb = 0; sb < n_seqs; sb += per_launch) {
+        dms::DecodeArgs a;
+        a.pool = pool->dev;
+        a.q = static_cast<const uint16_t*>(q);
+        a.k = static_cast<const uint16_t*>(k);
+        a.v = static_cast<const uint16_t*>(v);
+        a.logits = logits;
+        a.out = static_cast<uint16_t*>(out);
+        a.n_seqs_total = n_seqs;
+        a.seq_base = sb;
+        a.n_seqs = std::min(per_launch, n_seqs - sb);
+        a.layer0 = layer0;
+        a.n_layers = n_layers;
+        a.n_call_heads = a.n_layers * a.n_seqs * hkv;
+        int64_t bound = 0;  // split-K items: n_live <= position, ceil(n_live / chunk) per head
+        for (int i = 0; i < a.n_seqs; ++i) {
+            a.seq_ids[i] = seq_ids[sb + i];
+            for (int l = layer0; l < layer0 + n_layers; ++l)
+                bound += (int64_t)hkv * ((pool->position(a.seq_ids[i], l) + dms::kChunk - 1) / dms::kChunk);
+        }
+        const int grid = (int)std::max<int64_t>(1, std::min<int64_t>(bound, (int64_t)pool->cu_count * 4));
+        hipEvent_t* ev = nullptr;
+        if (pool->timing) {
+            const size_t base = pool->events.size();
+            pool->events.resize(base + 3, nullptr);
+            for (size_t i = base; i < base + 3; ++i) {
+                hipError_t ce = hipEventCreate(&pool->events[i]);
+                if (ce != hipSuccess) return hip_fail(ce, "timing event");
+            }
+            ev = &pool->events[base];
+        }
+        hipError_t e = dms::launch_decode(a, grid, st, ev);
+        if (e != hipSuccess) return hip_fail(e, "decode launch");
+    }
+    for (int i = 0; i < n_seqs; ++i)
+        for (int l = layer0; l < layer0 + n_layers; ++l) pool->position(seq_ids[i], l) += 1;
+    g_err.clear();
+    return DMS_OK;
+}
+
+dms_status dms_query_stats(dms_pool* pool, int32_t seq, dms_stats* out, int32_t* live_per_layer_head) {
+    if (!pool || !out) return fail(DMS_E_INVAL, "pool and out must not be NULL");
+    const dms_pool_config& c = pool->cfg;
+    if (seq < -1 || seq >= c.max_seqs) return fail(DMS_E_INVAL, "seq out of range");
+    if (live_per_layer_head && seq < 0) return fail(DMS_E_INVAL, "live_per_layer_head needs seq >= 0");
+    hipError_t e = hipDeviceSynchronize();
+    if (e != hipSuccess) return hip_fail(e, "synchronise");
+    const int64_t per_seq = (int64_t)c.n_layers * c.n_kv_heads;
+    const int s0 = seq < 0 ? 0 : seq, s1 = seq < 0 ? c.max_seqs : seq + 1;
+    std::vector<int32_t> hs((size_t)(s1 - s0) * per_seq * 4);
+    int32_t ctl[64];
+    e = hipMemcpy(hs.data(), pool->dev.hstate + (size_t)s0 * per_seq * 4, hs.size() * 4, hipMemcpyDeviceToHost);
+    if (e == hipSuccess) e = hipMemcpy(ctl, pool->dev.ctl, sizeof(ctl), hipMemcpyDeviceToHost);
+    if (e != hipSuccess) return hip_fail(e, "read pool state");
+    const int64_t D = c.head_dim;
+    std::memset(out, 0, sizeof(*out));
+    int64_t dense_tokens = 0;
+    for (int s = s0; s < s1; ++s) {
+        for (int l = 0; l < c.n_layers; ++l) {
+            int32_t& hp = pool->position(s, l);
+            const int32_t* h0 = &hs[(((size_t)(s - s0) * c.n_layers + l) * c.n_kv_heads) * 4];
+            if (hp >= 0) hp = h0[2];  // device counters are authoritative (graph replays bypass the host)
+            if (hp > 0) dense_tokens += (int64_t)hp * c.n_kv_heads;
+            for (int h = 0; h < c.n_kv_heads; ++h) {
+                const int32_t* x = h0 + h * 4;
+                out->live_slots += x[0];
+                out->pages_used += x[1];
+                if (live_per_layer_head) live_per_layer_head[l * c.n_kv_heads + h] = x[0];
+            }
+        }
+    }
+    out->kv_bytes_live = out->live_slots * 2 * D * 2;
+    out->kv_bytes_allocated = out->pages_used * dms::kPage * 2 * D * 2;
+    out->kv_bytes_dense_equiv = dense_tokens * 2 * D * 2;
+    out->pages_free = ctl[dms::kCtlTop];
+    out->workspace_bytes = (int64_t)(pool->layout.off[S_N] - pool->layout.off[S_POS]);
+    out->position = seq >= 0 ? pool->position(seq, 0) : -1;
+    out->device_error = ctl[dms::kCtlError] ? DMS_E_CAPACITY : DMS_OK;
+    if (ctl[dms::kCtlError]) return fail(DMS_E_CAPACITY, "the shared page pool ran out on the device");
+    g_err.clear();
+    return DMS_OK;
+}
+
+dms_status dms_export_live(dms_pool* pool, int32_t seq, int32_t layer, int32_t kv_head, int32_t* positions,
+                           int32_t cap, int32_t* n) {
+    if (!pool || !n) return fail(DMS_E_INVAL, "pool and n must not be NULL");
+    const dms_pool_config& c = pool->cfg;
+    if (seq < 0 || seq >= c.max_seqs || layer < 0 || layer >= c.n_layers || kv_head < 0 || kv_head >= c.n_kv_heads)
+        return fail(DMS_E_INVAL, "(seq, layer, kv_head) out of range");
+    hipError_t e = hipDeviceSynchronize();
+    if (e != hipSuccess) return hip_fail(e, "synchronise");
+    const int64_t gh = ((int64_t)seq * c.n_layers + layer) * c.n_kv_heads + kv_head;
+    int32_t hs[4];
+    e = hipMemcpy(hs, pool->dev.hstate + gh * 4, sizeof(hs), hipMemcpyDeviceToHost);
+    if (e != hipSuccess) return hip_fail(e, "read head state");
+    const int live = hs[0], np = hs[1];
+    *n = live;
+    if (live > cap || (live > 0 && !positions)) return fail(DMS_E_INVAL, "positions array too small");
+    std::vector<int32_t> pages((size_t)np);
+    if (np > 0) {
+        e = hipMemcpy(pages.data(), pool->dev.ptable + gh * pool->layout.pages_per_head, (size_t)np * 4,
+                      hipMemcpyDeviceToHost);
+        if (e != hipSuccess) return hip_fail(e, "read page table");
+    }
+    std::vector<int32_t> buf(dms::kPage);
+    int got = 0;
+    for (int j = 0; j < np && got < live; ++j) {
+        e = hipMemcpy(buf.data(), pool->dev.slot_pos + (size_t)pages[j] * dms::kPage, dms::kPage * 4,
+                      hipMemcpyDeviceToHost);
+        if (e != hipSuccess) return hip_fail(e, "read slot positions");
+        const int take = std::min(dms::kPage, live - got);
+        std::memcpy(positions + got, buf.data(), (size_t)take * 4);
+        got += take;
+    }
+    std::sort(positions, positions + live);
+    g_err.clear();
+    return DMS_OK;
+}
+
+dms_status dms_seq_release(dms_pool* pool, int32_t seq, void* stream) {
+    if (!pool) return fail(DMS_E_INVAL, "pool is NULL");
+    if (seq < 0 || seq >= pool->cfg.max_seqs) return fail(DMS_E_INVAL, "seq out of range");
+    hipError_t e = dms::launch_seq_release(pool->dev, seq, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "release launch");
+    for (int l = 0; l < pool->cfg.n_layers; ++l) pool->position(seq, l) = -1;
+    g_err.clear();
+    return DMS_OK;
+}
+
+dms_status dms_timing_enable(dms_pool* pool, int32_t enable) {
+    if (!pool) return fail(DMS_E_INVAL, "pool is NULL");
+    pool->timing = enable != 0;
+    g_err.clear();
+    return DMS_OK;
+}
+
+dms_status dms_timing_read(dms_pool* pool, double* attend_ms, double* merge_ms, int64_t* launches) {
+    if (!pool || !attend_ms || !merge_ms || !launches) return fail(DMS_E_INVAL, "NULL argument");
+    hipError_t e = hipDeviceSynchronize();
+    if (e != hipSuccess) return hip_fail(e, "synchronise");
+    double a = 0, m = 0;
+    const size_t n = pool->events.size() / 3;
+    for (size_t i = 0; i < n; ++i) {
+        float t0 = 0, t1 = 0;
+        e = hipEventElapsedTime(&t0, pool->events[3 * i], pool->events[3 * i + 1]);
+        if (e == hipSuccess) e = hipEventElapsedTime(&t1, pool->events[3 * i + 1], pool->events[3 * i + 2]);
+        if (e != hipSuccess) return hip_fail(e, "event elapsed time");
+        a += t0;
+        m += t1;
+    }
+    for (hipEvent_t ev : pool->events) hipEventDestroy(ev);
+    pool->events.clear();
+    *attend_ms = a;
+    *merge_ms = m;
+    *launches = (int64_t)n;
+    g_err.clear();
+    return DMS_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,87 @@
+// Internal layout of a DMS pool and the kernel launchers (not part of the ABI).
+//
+// Arena layout (every section 256-byte aligned):
+//   kpages   bf16 [max_pages][head_dim/8][64][8]   K, 16-byte dim chunks, key-major:
+//                                                  chunk c of 64 consecutive slots is
+//                                                  1 KB contiguous (lane = slot loads)
+//   vpages   bf16 [max_pages][8][head_dim][8]      V, 8-slot blocks, dim-major: the
+//                                                  16 bytes at (block, d) are 8
+//                                                  consecutive slots of dim d
+//   slot_pos int32 [max_pages][64]                 position held by each slot
+//   stack    int32 [max_pages]                     free pages, stack[0 .. top)
+//   hstate   int32 [heads][4]                      {n_live, n_pages, position, 0}
+//   ptable   int32 [heads][pages_per_head]         page of slots 64j .. 64j+63
+//   ring     int32 [heads][ring_len]               entry of position s at s % w:
+//                                                  (slot << 1) | mark, -1 = none
+//   partials f32   [max_items][G*(head_dim+2)]     split-K partials {m[G], l[G], acc[G][D]}
+//   prefix   int32 [max_call_heads + 1]            split-K item offsets of the last call
+//   inv      int32 [n_kv_heads][max_positions]     prefill scratch: slot -> position
+//   ctl      int32 [64]                            {stack top, sticky error, ...}
+// heads = max_seqs * n_layers * n_kv_heads, head id = (seq * n_layers + layer) * n_kv_heads + h.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace dms {
+
+constexpr int kPage = 64;          // slots per page
+constexpr int kChunkPages = 4;     // pages per split-K work item (one per wave)
+constexpr int kChunk = kPage * kChunkPages;
+constexpr int kMaxCallSeqs = 256;  // sequences per kernel launch (larger calls are split)
+constexpr int kMaxCallHeads = 16384;
+constexpr int kCtlTop = 0;
+constexpr int kCtlError = 1;
+
+struct PoolDev {
+    uint16_t* kpages;
+    uint16_t* vpages;
+    int32_t* slot_pos;
+    int32_t* stack;
+    int32_t* hstate;
+    int32_t* ptable;
+    int32_t* ring;
+    float* partials;
+    int32_t* prefix;
+    int32_t* inv;
+    int32_t* ctl;
+    int64_t max_pages;
+    int32_t n_layers, n_q_heads, n_kv_heads, head_dim;
+    int32_t window, ring_len, pages_per_head, max_positions;
+    int32_t max_items;
+    float scale_log2;  // softmax scale * log2(e): scores are kept in base-2 units
+};
+
+struct DecodeArgs {
+    PoolDev pool;
+    const uint16_t* q;
+    const uint16_t* k;
+    const uint16_t* v;
+    const float* logits;
+    uint16_t* out;
+    int32_t n_seqs_total;  // sequences of the whole call (row stride of the inputs)
+    int32_t seq_base;      // first sequence of this launch within the call
+    int32_t n_seqs;        // sequences in this launch
+    int32_t layer0, n_layers;
+    int32_t n_call_heads;  // n_layers * n_seqs * n_kv_heads
+    int32_t seq_ids[kMaxCallSeqs];
+};
+
+struct PrefillArgs {
+    PoolDev pool;
+    const uint16_t* q;
+    const uint16_t* k;
+    const uint16_t* v;
+    const float* logits;
+    uint16_t* out;
+    int32_t seq, layer, n_tokens;
+};
+
+// ev (optional): three events recorded before the attention kernel, between the
+// two kernels and after the merge kernel
+hipError_t launch_decode(const DecodeArgs& a, int grid, hipStream_t s, hipEvent_t* ev);
+hipError_t launch_prefill_compact(const PrefillArgs& a, hipStream_t s);
+hipError_t launch_prefill_attend(const PrefillArgs& a, hipStream_t s);
+hipError_t launch_seq_release(const PoolDev& p, int32_t seq, hipStream_t s);
+int device_cu_count();
+
+}  // namespace dms

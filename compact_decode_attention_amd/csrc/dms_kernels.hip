@@ -1,0 +1,620 @@
+// DMS compact-store kernels for CDNA4 (gfx950): decode (split-K flash-decode
+// over the live slots + merge + eviction/append), prefill compaction, and
+// sequence release.
+//
+// What a decode step computes for one (sequence, layer, kv head) at position t
+// (DMS delayed eviction: "NVIDIA veroeffentlicht Qwen3-8B-DMS-8x ..." news page,
+// section "Dynamic Memory Sparsification (DMS): Eine innovative Loesung"; stiva.ai
+// "Nvidia DMS ...", section on delayed eviction; compact store with reclaimed
+// slots: the FastDMS announcement on molayo1419.me):
+//   live set before the step  V(t-1), stored in slots 0 .. n_old-1 of the head
+//   the token at t-w leaves if it was marked; its slot e is reused by token t,
+//   otherwise token t takes slot n_old (a new page every 64 slots)
+//   out[g] = softmax over V(t) = V(t-1) \ {t-w if marked} + {t}
+//
+// Kernels of one decode call:
+//   decode_attend  -- persistent grid; every block derives the split-K work list
+//                     (4 pages per item, one page per wave) from the live counts,
+//                     then each wave computes a partial softmax over one page:
+//                     QK^T with lane = slot (v_dot2_f32_bf16 over 16-byte K chunks
+//                     loaded 1 KB-coalesced from the key-major K page), the page
+//                     max and sum by wavefront reductions, and PV with lane = dim
+//                     (v_dot2 over key pairs of the dim-major V page).  The block
+//                     folds its 4 waves into one partial per item.
+//   decode_merge   -- one wave per head: log-sum-exp merge of the partials plus
+//                     the new token, bf16 output; then mark, expiry, slot reuse or
+//                     page allocation, K/V append and the head's counters.
+// The attend kernel only reads pool state; all writes happen in the merge kernel,
+// after every reader of this step has finished (kernel boundary).
+#include "dms_internal.h"
+
+#include <math.h>
+
+namespace dms {
+namespace {
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
+
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);  // keep NaN a NaN
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return (uint16_t)(u >> 16);
+}
+
+// a.lo*b.lo + a.hi*b.hi + c, bf16 pairs, fp32 accumulate
+__device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a),
+                                           __builtin_bit_cast(bf16x2_t, b), c, false);
+}
+
+// Wavefront reductions on DPP (no LDS): butterflies inside each 16-lane row,
+// then row_bcast:15 / row_bcast:31 fold the four rows into lane 63, which is
+// read back as a wave-uniform value.
+template <int CTRL, int ROW_MASK = 0xf>
+__device__ __forceinline__ float dpp_f(float old, float x) {
+    return __builtin_amdgcn_update_dpp(old, x, CTRL, ROW_MASK, 0xf, false);
+}
+
+// readlane on the bit pattern (the builtin takes an int; a float argument would
+// be converted by value)
+__device__ __forceinline__ float readlane_f(float x, int lane) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), lane));
+}
+
+__device__ __forceinline__ float wave_max(float x) {
+    x = fmaxf(x, dpp_f<0xB1>(x, x));        // quad_perm [1,0,3,2]
+    x = fmaxf(x, dpp_f<0x4E>(x, x));        // quad_perm [2,3,0,1]
+    x = fmaxf(x, dpp_f<0x141>(x, x));       // row_half_mirror
+    x = fmaxf(x, dpp_f<0x140>(x, x));       // row_mirror
+    x = fmaxf(x, dpp_f<0x142, 0xa>(x, x));  // row_bcast:15 into rows 1, 3
+    x = fmaxf(x, dpp_f<0x143, 0xc>(x, x));  // row_bcast:31 into rows 2, 3
+    return readlane_f(x, 63);
+}
+
+__device__ __forceinline__ float wave_sum(float x) {
+    x += dpp_f<0xB1>(0.f, x);
+    x += dpp_f<0x4E>(0.f, x);
+    x += dpp_f<0x141>(0.f, x);
+    x += dpp_f<0x140>(0.f, x);
+    x += dpp_f<0x142, 0xa>(0.f, x);
+    x += dpp_f<0x143, 0xc>(0.f, x);
+    return readlane_f(x, 63);
+}
+
+// Scheduling fence for register values: an empty volatile asm that reads and
+// writes x.  Volatile asm keeps its place among memory operations, so the
+// arithmetic producing x stays ahead of the loads issued after this point.
+__device__ __forceinline__ void pin(float& x) { asm volatile("" : "+v"(x)); }
+
+// Raw buffer resource over [base, base + bytes): loads beyond it return 0.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, int bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, bytes, 0x00020000);
+}
+
+__device__ __forceinline__ uint4 buffer_load16(__amdgpu_buffer_rsrc_t r, int voff, int soff) {
+    const auto v = __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0);
+    return make_uint4(v[0], v[1], v[2], v[3]);
+}
+
+__device__ __forceinline__ int wave_incl_scan(int x, int lane) {
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        int y = __shfl_up(x, o, 64);
+        if (lane >= o) x += y;
+    }
+    return x;
+}
+
+// Exclusive scan of one int per thread over a block of NT threads (NT % 64 == 0).
+template <int NT>
+__device__ int block_excl_scan(int x, int* total, int* s_wave) {
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    constexpr int NW = NT / 64;
+    int incl = wave_incl_scan(x, lane);
+    if (lane == 63) s_wave[wave] = incl;
+    __syncthreads();
+    if (wave == 0) {
+        int v = lane < NW ? s_wave[lane] : 0;
+        int vi = wave_incl_scan(v, lane);
+        if (lane < NW) s_wave[NW + lane] = vi - v;  // exclusive wave offsets
+        if (lane == NW - 1) s_wave[2 * NW] = vi;
+    }
+    __syncthreads();
+    int r = s_wave[NW + wave] + incl - x;
+    *total = s_wave[2 * NW];
+    __syncthreads();
+    return r;
+}
+
+// Intra-wave LDS hand-off: order this wave's LDS writes before its later reads.
+__device__ __forceinline__ void wave_lds_sync() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+struct CallHead {
+    int gh;   // global head id
+    int row;  // input row (layer-in-call, sequence-in-call)
+    int h;    // kv head
+};
+
+__device__ __forceinline__ CallHead call_head(const DecodeArgs& a, int ch) {
+    const int hkv = a.pool.n_kv_heads;
+    const int per_layer = a.n_seqs * hkv;
+    const int li = ch / per_layer;
+    const int rem = ch - li * per_layer;
+    const int si = rem / hkv;
+    const int h = rem - si * hkv;
+    CallHead c;
+    c.h = h;
+    c.gh = ((a.seq_ids[si] * a.pool.n_layers) + a.layer0 + li) * hkv + h;
+    c.row = li * a.n_seqs_total + a.seq_base + si;
+    return c;
+}
+
+// Slot of the token that expires at step t (position t-w, if it was marked), or -1.
+__device__ __forceinline__ int expiring_slot(const PoolDev& P, int gh, int t) {
+    if (P.ring_len <= 0 || t < P.window) return -1;
+    const int r = P.ring[(size_t)gh * P.ring_len + (t % P.window)];
+    return (r >= 0 && (r & 1)) ? (r >> 1) : -1;
+}
+
+// ---------------------------------------------------------------------------
+// decode: split-K attention over the live slots
+// ---------------------------------------------------------------------------
+template <int D, int G>
+__global__ __launch_bounds__(256, 4) void decode_attend_kernel(DecodeArgs a) {
+    constexpr int NC = D / 8;   // 16-byte K chunks per slot
+    constexpr int VJ = D / 64;  // dims per lane in PV
+    constexpr int NW = 4;       // waves per block = pages per item
+    extern __shared__ int32_t s_prefix[];  // [n_call_heads + 1]
+    __shared__ uint32_t s_q[G][D / 2];
+    __shared__ uint16_t s_p[NW][G][kPage];
+    __shared__ float s_m[NW][G], s_l[NW][G];
+    __shared__ float s_acc[NW][G][D];
+    __shared__ int s_scan[2 * NW + 1];
+
+    const PoolDev& P = a.pool;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
+    const int H = a.n_call_heads;
+
+    // ---- work list: ceil(n_live / kChunk) items per head, exclusive prefix in LDS
+    const int per = (H + 255) / 256;
+    const int h0 = min(tid * per, H), h1 = min(h0 + per, H);
+    int local = 0;
+    for (int ch = h0; ch < h1; ++ch) {
+        const int n = P.hstate[(size_t)call_head(a, ch).gh * 4];
+        const int c = (n + kChunk - 1) / kChunk;
+        s_prefix[ch] = c;
+        local += c;
+    }
+    int total;
+    int off = block_excl_scan<256>(local, &total, s_scan);
+    for (int ch = h0; ch < h1; ++ch) {
+        const int c = s_prefix[ch];
+        s_prefix[ch] = off;
+        off += c;
+    }
+    if (tid == 0) s_prefix[H] = total;
+    __syncthreads();
+    if (blockIdx.x == 0)
+        for (int i = tid; i <= H; i += 256) P.prefix[i] = s_prefix[i];
+
+    for (int item = blockIdx.x; item < total; item += gridDim.x) {
+        int lo = 0, hi = H;  // s_prefix[lo] <= item < s_prefix[hi]
+        while (hi - lo > 1) {
+            const int mid = (lo + hi) >> 1;
+            if (s_prefix[mid] <= item) lo = mid; else hi = mid;
+        }
+        // the search result is the same in every lane; say so, so that head state,
+        // page ids and buffer resources live in scalar registers
+        lo = __builtin_amdgcn_readfirstlane(lo);
+        const int chunk = item - __builtin_amdgcn_readfirstlane(s_prefix[lo]);
+        const CallHead c = call_head(a, lo);
+        const int32_t* hs = P.hstate + (size_t)c.gh * 4;
+        const int n_old = hs[0];
+        const int t = hs[2];
+        const int e = expiring_slot(P, c.gh, t);
+
+        const uint32_t* qsrc =
+            reinterpret_cast<const uint32_t*>(a.q + ((size_t)c.row * P.n_q_heads + c.h * G) * D);
+        for (int i = tid; i < G * D / 2; i += 256) s_q[i / (D / 2)][i % (D / 2)] = qsrc[i];
+        __syncthreads();
+
+        const int pi = chunk * NW + wave;
+        const int base = pi * kPage;
+        float m[G], l[G], acc[G][VJ];
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+            m[g] = -INFINITY;
+            l[g] = 0.f;
+#pragma unroll
+            for (int j = 0; j < VJ; ++j) acc[g][j] = 0.f;
+        }
+        if (base < n_old) {
+            const int page = P.ptable[(size_t)c.gh * P.pages_per_head + pi];
+            const __amdgpu_buffer_rsrc_t kr = buffer_rsrc(P.kpages + (size_t)page * (kPage * D), kPage * D * 2);
+            const __amdgpu_buffer_rsrc_t vr = buffer_rsrc(P.vpages + (size_t)page * (kPage * D), kPage * D * 2);
+            // K chunk cc of slot `lane`: 64 lanes read 1 KB contiguous
+            uint4 kc[NC];
+#pragma unroll
+            for (int cc = 0; cc < NC; ++cc) kc[cc] = buffer_load16(kr, lane * 16, cc * kPage * 16);
+
+            // QK^T, lane = slot.  q is read from LDS (same address in every lane:
+            // a broadcast), one chunk ahead of its use; each q head is one chain
+            // of dot products over the 16-byte K chunks held in registers.
+            float z[G];
+#pragma unroll
+            for (int g = 0; g < G; ++g) {
+                float zg = 0.f;
+                uint4 qn = *reinterpret_cast<const uint4*>(&s_q[g][0]);
+#pragma unroll
+                for (int cc = 0; cc < NC; ++cc) {
+                    const uint4 qv = qn;
+                    if (cc + 1 < NC) qn = *reinterpret_cast<const uint4*>(&s_q[g][(cc + 1) * 4]);
+                    zg = dot2(qv.x, kc[cc].x, zg);
+                    zg = dot2(qv.y, kc[cc].y, zg);
+                    zg = dot2(qv.z, kc[cc].z, zg);
+                    zg = dot2(qv.w, kc[cc].w, zg);
+                    pin(zg);
+                }
+                z[g] = zg;
+            }
+            // V loads go out after QK (K registers are free again); other waves
+            // keep the memory pipe busy meanwhile.
+            uint4 vc[8][VJ];
+#pragma unroll
+            for (int b = 0; b < 8; ++b)
+#pragma unroll
+                for (int j = 0; j < VJ; ++j) vc[b][j] = buffer_load16(vr, lane * 16, (b * D + j * 64) * 16);
+            const int slot = base + lane;
+            const bool valid = slot < n_old && slot != e;
+#pragma unroll
+            for (int g = 0; g < G; ++g) {
+                // additive mask: a select here lets the compiler sink the whole QK
+                // product into a branch behind every load of the page
+                const float zz = fmaf(z[g], P.scale_log2, valid ? 0.f : -INFINITY);
+                const float pm = wave_max(zz);
+                float p = 0.f;
+                if (pm != -INFINITY) p = exp2f(zz - pm);
+                const uint16_t pb = f32_to_bf16(p);
+                s_p[wave][g][lane] = pb;
+                m[g] = pm;
+                l[g] = wave_sum(bf16_to_f32(pb));
+            }
+            wave_lds_sync();
+            // PV, lane = dim: each 16-byte V unit holds 8 consecutive slots of one
+            // dim, i.e. 4 key pairs, matched by 4 bf16 pairs of p (broadcast reads).
+            uint4 pn[G];
+#pragma unroll
+            for (int g = 0; g < G; ++g) pn[g] = *reinterpret_cast<const uint4*>(&s_p[wave][g][0]);
+#pragma unroll
+            for (int b = 0; b < 8; ++b) {
+                uint4 pp[G];
+#pragma unroll
+                for (int g = 0; g < G; ++g) pp[g] = pn[g];
+                if (b + 1 < 8) {
+#pragma unroll
+                    for (int g = 0; g < G; ++g) pn[g] = *reinterpret_cast<const uint4*>(&s_p[wave][g][(b + 1) * 8]);
+                }
+#pragma unroll
+                for (int g = 0; g < G; ++g) {
+#pragma unroll
+                    for (int j = 0; j < VJ; ++j) {
+                        acc[g][j] = dot2(pp[g].x, vc[b][j].x, acc[g][j]);
+                        acc[g][j] = dot2(pp[g].y, vc[b][j].y, acc[g][j]);
+                        acc[g][j] = dot2(pp[g].z, vc[b][j].z, acc[g][j]);
+                        acc[g][j] = dot2(pp[g].w, vc[b][j].w, acc[g][j]);
+                        pin(acc[g][j]);
+                    }
+                }
+            }
+        }
+        if (lane == 0) {
+#pragma unroll
+            for (int g = 0; g < G; ++g) {
+                s_m[wave][g] = m[g];
+                s_l[wave][g] = l[g];
+            }
+        }
+#pragma unroll
+        for (int g = 0; g < G; ++g)
+#pragma unroll
+            for (int j = 0; j < VJ; ++j) s_acc[wave][g][j * 64 + lane] = acc[g][j];
+        __syncthreads();
+
+        float* part = P.partials + (size_t)item * (G * (D + 2));
+        for (int i = tid; i < G * D; i += 256) {
+            const int g = i / D, d = i - g * D;
+            float M = s_m[0][g];
+#pragma unroll
+            for (int w = 1; w < NW; ++w) M = fmaxf(M, s_m[w][g]);
+            float o = 0.f, L = 0.f;
+            if (M != -INFINITY) {
+#pragma unroll
+                for (int w = 0; w < NW; ++w) {
+                    const float sc = exp2f(s_m[w][g] - M);
+                    o += sc * s_acc[w][g][d];
+                    L += sc * s_l[w][g];
+                }
+            }
+            part[2 * G + g * D + d] = o;
+            if (d == 0) {
+                part[g] = M;
+                part[G + g] = L;
+            }
+        }
+        __syncthreads();
+    }
+}
+
+// ---------------------------------------------------------------------------
+// decode: merge partials + new token, then evict / append
+// ---------------------------------------------------------------------------
+template <int D, int G>
+__global__ __launch_bounds__(64) void decode_merge_kernel(DecodeArgs a) {
+    constexpr int VJ = D / 64;
+    const PoolDev& P = a.pool;
+    const int lane = threadIdx.x;
+    const CallHead c = call_head(a, blockIdx.x);
+    int32_t* hs = P.hstate + (size_t)c.gh * 4;
+    const int n_old = hs[0];
+    const int n_pages = hs[1];
+    const int t = hs[2];
+    const int i0 = P.prefix[blockIdx.x], i1 = P.prefix[blockIdx.x + 1];
+
+    const uint16_t* qg = a.q + ((size_t)c.row * P.n_q_heads + c.h * G) * D;
+    const uint16_t* kn = a.k + ((size_t)c.row * P.n_kv_heads + c.h) * D;
+    const uint16_t* vn = a.v + ((size_t)c.row * P.n_kv_heads + c.h) * D;
+    float kf[VJ], vf[VJ];
+#pragma unroll
+    for (int j = 0; j < VJ; ++j) {
+        kf[j] = bf16_to_f32(kn[j * 64 + lane]);
+        vf[j] = bf16_to_f32(vn[j * 64 + lane]);
+    }
+    uint16_t* og = a.out + ((size_t)c.row * P.n_q_heads + c.h * G) * D;
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+        float dp = 0.f;
+#pragma unroll
+        for (int j = 0; j < VJ; ++j) dp = fmaf(bf16_to_f32(qg[g * D + j * 64 + lane]), kf[j], dp);
+        const float zn = wave_sum(dp) * P.scale_log2;
+        float M = zn;
+        for (int i = i0; i < i1; ++i) M = fmaxf(M, P.partials[(size_t)i * (G * (D + 2)) + g]);
+        const float sn = exp2f(zn - M);
+        float L = sn;
+        float o[VJ];
+#pragma unroll
+        for (int j = 0; j < VJ; ++j) o[j] = sn * vf[j];
+        for (int i = i0; i < i1; ++i) {
+            const float* part = P.partials + (size_t)i * (G * (D + 2));
+            const float sc = exp2f(part[g] - M);
+            L = fmaf(sc, part[G + g], L);
+#pragma unroll
+            for (int j = 0; j < VJ; ++j) o[j] = fmaf(sc, part[2 * G + g * D + j * 64 + lane], o[j]);
+        }
+        const float inv = 1.f / L;
+#pragma unroll
+        for (int j = 0; j < VJ; ++j) og[g * D + j * 64 + lane] = f32_to_bf16(o[j] * inv);
+    }
+
+    // ---- eviction decision, expiry, slot reuse / allocation, append
+    const int mark = a.logits[(size_t)c.row * P.n_kv_heads + c.h] > 0.f ? 1 : 0;
+    const int e = expiring_slot(P, c.gh, t);
+    int slot, n_new, np = n_pages, page;
+    if (e >= 0) {
+        slot = e;
+        n_new = n_old;
+        page = P.ptable[(size_t)c.gh * P.pages_per_head + slot / kPage];
+    } else {
+        slot = n_old;
+        n_new = n_old + 1;
+        if ((slot % kPage) == 0) {
+            int pg = -1;
+            if (lane == 0) {
+                const int old = atomicSub(&P.ctl[kCtlTop], 1);
+                if (old < 1) {
+                    atomicAdd(&P.ctl[kCtlTop], 1);
+                    atomicOr(&P.ctl[kCtlError], 1);
+                } else {
+                    pg = P.stack[old - 1];
+                }
+            }
+            page = __shfl(pg, 0, 64);
+            if (page < 0) return;  // pool exhausted: the sticky flag is set, the token is dropped
+            if (lane == 0) P.ptable[(size_t)c.gh * P.pages_per_head + slot / kPage] = page;
+            np = slot / kPage + 1;
+        } else {
+            page = P.ptable[(size_t)c.gh * P.pages_per_head + slot / kPage];
+        }
+    }
+    const int j = slot % kPage;
+    uint16_t* kp = P.kpages + (size_t)page * (kPage * D);
+    uint16_t* vp = P.vpages + (size_t)page * (kPage * D);
+    if (lane < D / 8)
+        *reinterpret_cast<uint4*>(kp + ((size_t)lane * kPage + j) * 8) =
+            *reinterpret_cast<const uint4*>(kn + lane * 8);
+#pragma unroll
+    for (int jj = 0; jj < VJ; ++jj) vp[((size_t)(j / 8) * D + jj * 64 + lane) * 8 + (j % 8)] = vn[jj * 64 + lane];
+    if (lane == 0) {
+        P.slot_pos[(size_t)page * kPage + j] = t;
+        if (P.ring_len > 0) P.ring[(size_t)c.gh * P.ring_len + (t % P.window)] = (slot << 1) | mark;
+        hs[0] = n_new;
+        hs[1] = np;
+        hs[2] = t + 1;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// prefill: marks, live set of the last position, page allocation, ring
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(1024) void prefill_scan_kernel(PrefillArgs a) {
+    const PoolDev& P = a.pool;
+    __shared__ int s_scan[2 * 16 + 1];
+    __shared__ int s_base;
+    const int tid = threadIdx.x;
+    const int h = blockIdx.x;
+    const int hkv = P.n_kv_heads;
+    const int gh = (a.seq * P.n_layers + a.layer) * hkv + h;
+    const int T = a.n_tokens, w = P.window;
+    const int per = (T + 1023) / 1024;
+    const int s0 = min(tid * per, T), s1 = min(s0 + per, T);
+    // live at the last position T-1: unmarked, or inside the window (s >= T - w)
+    int cnt = 0;
+    for (int s = s0; s < s1; ++s) cnt += (s >= T - w || !(a.logits[(size_t)s * hkv + h] > 0.f)) ? 1 : 0;
+    int n;
+    int off = block_excl_scan<1024>(cnt, &n, s_scan);
+    int32_t* inv = P.inv + (size_t)h * P.max_positions;
+    for (int s = s0; s < s1; ++s)
+        if (s >= T - w || !(a.logits[(size_t)s * hkv + h] > 0.f)) inv[off++] = s;
+    const int np = (n + kPage - 1) / kPage;
+    if (tid == 0) {
+        const int old = atomicSub(&P.ctl[kCtlTop], np);
+        if (old < np) {
+            atomicAdd(&P.ctl[kCtlTop], np);
+            atomicOr(&P.ctl[kCtlError], 1);
+            s_base = -1;
+        } else {
+            s_base = old;
+        }
+    }
+    __syncthreads();
+    int32_t* hs = P.hstate + (size_t)gh * 4;
+    if (s_base < 0) {
+        if (tid == 0) { hs[0] = 0; hs[1] = 0; hs[2] = T; hs[3] = 0; }
+        return;
+    }
+    for (int j = tid; j < np; j += 1024)
+        P.ptable[(size_t)gh * P.pages_per_head + j] = P.stack[s_base - 1 - j];
+    if (tid == 0) { hs[0] = n; hs[1] = np; hs[2] = T; hs[3] = 0; }
+    // ring entry idx holds the newest position s < T with s % w == idx (all of
+    // them lie in the window, so their slots are the last ones: n - T + s)
+    for (int idx = tid; idx < P.ring_len; idx += 1024) {
+        int entry = -1;
+        if (idx <= T - 1) {
+            const int s = idx + w * ((T - 1 - idx) / w);
+            const int mark = a.logits[(size_t)s * hkv + h] > 0.f ? 1 : 0;
+            entry = ((n - T + s) << 1) | mark;
+        }
+        P.ring[(size_t)gh * P.ring_len + idx] = entry;
+    }
+}
+
+// Gather the live rows into the head's pages: one block per destination page.
+template <int D>
+__global__ __launch_bounds__(256) void prefill_compact_kernel(PrefillArgs a) {
+    constexpr int NC = D / 8;
+    const PoolDev& P = a.pool;
+    __shared__ int s_src[kPage];
+    __shared__ uint16_t s_v[kPage][D + 8];
+    const int tid = threadIdx.x;
+    const int pj = blockIdx.x, h = blockIdx.y;
+    const int hkv = P.n_kv_heads;
+    const int gh = (a.seq * P.n_layers + a.layer) * hkv + h;
+    const int n = P.hstate[(size_t)gh * 4];
+    if (pj * kPage >= n) return;
+    const int page = P.ptable[(size_t)gh * P.pages_per_head + pj];
+    const int cnt = min(kPage, n - pj * kPage);
+    if (tid < kPage) s_src[tid] = tid < cnt ? P.inv[(size_t)h * P.max_positions + pj * kPage + tid] : -1;
+    __syncthreads();
+    uint16_t* kp = P.kpages + (size_t)page * (kPage * D);
+    uint16_t* vp = P.vpages + (size_t)page * (kPage * D);
+    const uint4 zero = make_uint4(0, 0, 0, 0);
+    for (int u = tid; u < NC * kPage; u += 256) {
+        const int cc = u / kPage, j = u - cc * kPage;
+        const int s = s_src[j];
+        const uint4 val = s >= 0 ? *reinterpret_cast<const uint4*>(a.k + ((size_t)s * hkv + h) * D + cc * 8) : zero;
+        *reinterpret_cast<uint4*>(kp + ((size_t)cc * kPage + j) * 8) = val;
+    }
+    for (int u = tid; u < kPage * NC; u += 256) {
+        const int j = u / NC, cc = u - j * NC;
+        const int s = s_src[j];
+        const uint4 val = s >= 0 ? *reinterpret_cast<const uint4*>(a.v + ((size_t)s * hkv + h) * D + cc * 8) : zero;
+        *reinterpret_cast<uint4*>(&s_v[j][cc * 8]) = val;
+    }
+    __syncthreads();
+    for (int u = tid; u < 8 * D; u += 256) {
+        const int b = u / D, d = u - b * D;
+        uint32_t w4[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            w4[i] = (uint32_t)s_v[8 * b + 2 * i][d] | ((uint32_t)s_v[8 * b + 2 * i + 1][d] << 16);
+        *reinterpret_cast<uint4*>(vp + ((size_t)b * D + d) * 8) = make_uint4(w4[0], w4[1], w4[2], w4[3]);
+    }
+    if (tid < kPage) P.slot_pos[(size_t)page * kPage + tid] = s_src[tid];
+}
+
+__global__ __launch_bounds__(64) void seq_release_kernel(PoolDev P, int seq) {
+    const int gh = seq * P.n_layers * P.n_kv_heads + blockIdx.x;
+    int32_t* hs = P.hstate + (size_t)gh * 4;
+    const int np = hs[1];
+    int base = 0;
+    if (threadIdx.x == 0 && np > 0) base = atomicAdd(&P.ctl[kCtlTop], np);
+    base = __shfl(base, 0, 64);
+    for (int j = threadIdx.x; j < np; j += 64) P.stack[base + j] = P.ptable[(size_t)gh * P.pages_per_head + j];
+    if (threadIdx.x == 0) { hs[0] = 0; hs[1] = 0; hs[2] = 0; hs[3] = 0; }
+}
+
+template <int D, int G>
+hipError_t launch_decode_t(const DecodeArgs& a, int grid, hipStream_t s, hipEvent_t* ev) {
+    const size_t shm = (size_t)(a.n_call_heads + 1) * sizeof(int32_t);
+    hipError_t err;
+    if (ev && (err = hipEventRecord(ev[0], s)) != hipSuccess) return err;
+    hipLaunchKernelGGL((decode_attend_kernel<D, G>), dim3(grid), dim3(256), shm, s, a);
+    if ((err = hipGetLastError()) != hipSuccess) return err;
+    if (ev && (err = hipEventRecord(ev[1], s)) != hipSuccess) return err;
+    hipLaunchKernelGGL((decode_merge_kernel<D, G>), dim3(a.n_call_heads), dim3(64), 0, s, a);
+    if ((err = hipGetLastError()) != hipSuccess) return err;
+    if (ev && (err = hipEventRecord(ev[2], s)) != hipSuccess) return err;
+    return hipSuccess;
+}
+
+template <int D>
+hipError_t launch_decode_d(const DecodeArgs& a, int grid, hipStream_t s, hipEvent_t* ev) {
+    switch (a.pool.n_q_heads / a.pool.n_kv_heads) {
+        case 1: return launch_decode_t<D, 1>(a, grid, s, ev);
+        case 2: return launch_decode_t<D, 2>(a, grid, s, ev);
+        case 4: return launch_decode_t<D, 4>(a, grid, s, ev);
+        case 8: return launch_decode_t<D, 8>(a, grid, s, ev);
+    }
+    return hipErrorInvalidValue;
+}
+
+}  // namespace
+
+hipError_t launch_decode(const DecodeArgs& a, int grid, hipStream_t s, hipEvent_t* ev) {
+    if (a.pool.head_dim == 128) return launch_decode_d<128>(a, grid, s, ev);
+    if (a.pool.head_dim == 64) return launch_decode_d<64>(a, grid, s, ev);
+    return hipErrorInvalidValue;
+}
+
+hipError_t launch_prefill_compact(const PrefillArgs& a, hipStream_t s) {
+    hipLaunchKernelGGL(prefill_scan_kernel, dim3(a.pool.n_kv_heads), dim3(1024), 0, s, a);
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+    const dim3 grid((a.n_tokens + kPage - 1) / kPage, a.pool.n_kv_heads);
+    if (a.pool.head_dim == 128)
+        hipLaunchKernelGGL(prefill_compact_kernel<128>, grid, dim3(256), 0, s, a);
+    else
+        hipLaunchKernelGGL(prefill_compact_kernel<64>, grid, dim3(256), 0, s, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_seq_release(const PoolDev& p, int32_t seq, hipStream_t s) {
+    hipLaunchKernelGGL(seq_release_kernel, dim3(p.n_layers * p.n_kv_heads), dim3(64), 0, s, p, seq);
+    return hipGetLastError();
+}
+
+int device_cu_count() {
+    int dev = 0, n = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return 256;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) return 256;
+    return n;
+}
+
+}  // namespace dms

@@ -1,0 +1,181 @@
+/*
+ * dms.h -- C ABI of the DMS compact-KV decode library for MI355X (gfx950).
+ *
+ * Dynamic Memory Sparsification (DMS) lets every attention head decide, per
+ * token, whether to keep that token's key/value or to evict it; an evicted
+ * token stays readable for a delay window of w further steps and is then
+ * dropped (delayed eviction).  Sources: "NVIDIA veroeffentlicht
+ * Qwen3-8B-DMS-8x ..." (mindverse news page), section "Dynamic Memory
+ * Sparsification (DMS): Eine innovative Loesung"; "Nvidia DMS: szhatie pamyati
+ * LLM v 8 raz" (stiva.ai), sections on the keep/evict signal and on delayed
+ * eviction.  The FastDMS announcement ("FastDMS: vLLM BF16/FP8 ... 6.4x KV
+ * cache", molayo1419.me) describes the compact store this library keeps: the
+ * slots of evicted tokens are physically reclaimed, so token counts vary per
+ * layer and per head and the saving shows up in real device memory (its
+ * memory table and its "What's the catch?" table, PagedAttention row).
+ *
+ * Visibility rule (the plain reading of those pages, stated once here):
+ *   token s is marked for eviction iff its logit is > 0 (strictly);
+ *   token s is visible to the query at position t iff s <= t and
+ *   (s is unmarked or t < s + w).
+ * So a marked token is seen by the w queries s .. s+w-1, its own included.
+ * A window w >= max_positions never expires anything (the FastDMS quality
+ * method's "eviction disabled" reference is a 1M-token window).
+ *
+ * Conventions shared by every entry point
+ *  - All tensor arguments are device pointers owned by the caller; they must
+ *    stay valid until the work enqueued on `stream` has finished.  bf16 values
+ *    are passed as their 16-bit patterns.  Rows are contiguous, 16-byte aligned.
+ *  - `stream` is a hipStream_t (NULL = the legacy default stream).  Calls
+ *    enqueue kernels and return without waiting, except dms_pool_create,
+ *    dms_pool_destroy, dms_query_stats and dms_export_live, which synchronise.
+ *  - Errors found on the host are returned at once and nothing is enqueued.
+ *    A device-side failure (the shared page pool running out) sets a sticky
+ *    flag that the next synchronising call returns as DMS_E_CAPACITY.
+ *  - Error text for the last failing call on the calling thread:
+ *    dms_last_error().  No C++ exception crosses this interface.
+ *  - A pool is not thread-safe; use it from one host thread and order all of
+ *    its work on one stream (or synchronise between streams).
+ *  - The library never allocates device memory: the caller hands over one
+ *    arena of dms_pool_bytes() bytes and keeps ownership of it.
+ */
+#ifndef DMS_H_
+#define DMS_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int32_t dms_status;
+enum {
+    DMS_OK = 0,
+    DMS_E_INVAL = -1,     /* bad argument, shape or pointer */
+    DMS_E_NOMEM = -2,     /* arena smaller than dms_pool_bytes() */
+    DMS_E_CAPACITY = -3,  /* the shared page pool ran out (device-side, sticky) */
+    DMS_E_STATE = -4,     /* call not valid in the pool's current state */
+    DMS_E_HIP = -5        /* a HIP runtime call failed */
+};
+
+/* Slots per page of the compact store.  Fixed: one page is one 64-lane
+ * wavefront's worth of keys. */
+#define DMS_PAGE_SLOTS 64
+
+typedef struct dms_pool dms_pool; /* opaque; owned by the library */
+
+typedef struct {
+    int32_t n_layers;      /* >= 1 */
+    int32_t n_q_heads;     /* multiple of n_kv_heads; n_q_heads / n_kv_heads in {1,2,4,8} */
+    int32_t n_kv_heads;    /* >= 1 */
+    int32_t head_dim;      /* 64 or 128 */
+    int32_t window;        /* delay window w >= 1 */
+    int32_t max_seqs;      /* sequences sharing the pool's one page allocator */
+    int32_t max_positions; /* most tokens (prompt + generated) one sequence may hold */
+    int32_t page_slots;    /* 0 or DMS_PAGE_SLOTS */
+    int64_t max_pages;     /* pages in the shared pool; each page holds 64 slots of K and V */
+    float softmax_scale;   /* 0 => 1/sqrt(head_dim) */
+    uint32_t page_order_seed; /* 0: pages are handed out in ascending order; otherwise
+                                 in a seeded shuffled order (physical placement must
+                                 not change any result) */
+    int32_t reserved[4];   /* must be 0 */
+} dms_pool_config;
+
+/* Bytes of device memory (the arena) a pool with this configuration needs, or 0
+ * if the configuration is invalid (dms_last_error() says why). */
+size_t dms_pool_bytes(const dms_pool_config* cfg);
+
+/* Create a pool inside the caller's arena (device memory, >= dms_pool_bytes()
+ * bytes, 256-byte aligned).  Clears the arena and fills the page free list on
+ * `stream`, then synchronises.  The arena stays owned by the caller and must
+ * outlive the pool. */
+dms_status dms_pool_create(const dms_pool_config* cfg, void* arena, size_t arena_bytes,
+                           void* stream, dms_pool** out);
+
+/* Synchronise the device and free the host-side handle (not the arena). */
+dms_status dms_pool_destroy(dms_pool* pool);
+
+/* Prefill: the first n_tokens tokens (positions 0 .. n_tokens-1) of one
+ * (sequence, layer).  Marks every token from its logit, stores exactly the
+ * tokens visible to the last position n_tokens-1 in the compact store (unmarked
+ * tokens older than the window, plus the last min(n_tokens, w) tokens) in
+ * position order, and records the marks of the window so that decode can
+ * expire them on time.  When out is not NULL it also writes the masked causal
+ * attention output of every position (query t sees the keys visible to t).
+ *   q      bf16 [n_tokens][n_q_heads][head_dim]  (may be NULL when out is NULL)
+ *   k, v   bf16 [n_tokens][n_kv_heads][head_dim]
+ *   logits fp32 [n_tokens][n_kv_heads]
+ *   out    bf16 [n_tokens][n_q_heads][head_dim] or NULL
+ * q and k arrive after any positional encoding.  Returns DMS_E_STATE if this
+ * (seq, layer) already holds tokens (release the sequence first). */
+dms_status dms_prefill(dms_pool* pool, int32_t seq, int32_t layer, int32_t n_tokens,
+                       const void* q, const void* k, const void* v, const float* logits,
+                       void* out, void* stream);
+
+/* One decode step for n_seqs sequences over layers layer0 .. layer0+n_layers-1.
+ * For every (layer, sequence, kv head), in this order: mark the new token from
+ * its logit; expire the token whose delay window has just run out (position
+ * t-w, if it was marked) and put its slot on the free list; take a slot for the
+ * new token from the free list or the end of the store (a fresh page from the
+ * shared pool when needed); write the new K/V; and attend the head's query
+ * group over every live token, the new one included.
+ *   seq_ids host int32 [n_seqs], distinct, each already prefilled on every
+ *           layer of the call
+ *   q       bf16 [n_layers][n_seqs][n_q_heads][head_dim]
+ *   k, v    bf16 [n_layers][n_seqs][n_kv_heads][head_dim]
+ *   logits  fp32 [n_layers][n_seqs][n_kv_heads]
+ *   out     bf16 [n_layers][n_seqs][n_q_heads][head_dim]
+ * Each (seq, layer) keeps its own position counter; the new token's position
+ * is that counter.  A model calls this once per layer (n_layers = 1); a caller
+ * whose layers have independent inputs may step several layers in one call. */
+dms_status dms_decode_step(dms_pool* pool, int32_t n_seqs, const int32_t* seq_ids,
+                           int32_t layer0, int32_t n_layers, const void* q, const void* k,
+                           const void* v, const float* logits, void* out, void* stream);
+
+typedef struct {
+    int64_t live_slots;           /* tokens held, summed over the queried layers and kv heads */
+    int64_t kv_bytes_live;        /* live_slots * 2 (K,V) * head_dim * 2 bytes */
+    int64_t kv_bytes_allocated;   /* pages held * 64 slots * 2 * head_dim * 2 bytes */
+    int64_t kv_bytes_dense_equiv; /* what a store keeping every token would hold */
+    int64_t pages_used;           /* pages held by the queried sequence(s) */
+    int64_t pages_free;           /* free pages in the whole pool */
+    int64_t workspace_bytes;      /* arena bytes outside the K/V pages (tables, split-K partials) */
+    int32_t position;             /* seq >= 0: the next position of layer 0; -1 if not prefilled */
+    int32_t device_error;         /* sticky device status: DMS_OK or DMS_E_CAPACITY */
+} dms_stats;
+
+/* Synchronise and report the store's size for one sequence (seq >= 0) or for
+ * all sequences (seq = -1).  live_per_layer_head, when not NULL, is a host
+ * array [n_layers][n_kv_heads] (seq >= 0 only) that receives the live counts.
+ * Returns DMS_E_CAPACITY (after filling *out) if the sticky device flag is set. */
+dms_status dms_query_stats(dms_pool* pool, int32_t seq, dms_stats* out,
+                           int32_t* live_per_layer_head);
+
+/* Synchronise and list the positions of the tokens one (seq, layer, kv_head)
+ * holds, ascending, into the host array positions[cap]; *n receives the count
+ * (DMS_E_INVAL if it exceeds cap). */
+dms_status dms_export_live(dms_pool* pool, int32_t seq, int32_t layer, int32_t kv_head,
+                           int32_t* positions, int32_t cap, int32_t* n);
+
+/* Return every page of a sequence to the shared pool and forget its tokens on
+ * all layers (enqueued on `stream`).  The sequence may then be prefilled again. */
+dms_status dms_seq_release(dms_pool* pool, int32_t seq, void* stream);
+
+/* Kernel timing for measurement.  While enabled, every decode launch records
+ * HIP events on its stream around its attention kernel and around its merge /
+ * append kernel.  dms_timing_read synchronises, adds up the elapsed times of all
+ * launches recorded since the last read (milliseconds) and how many there were,
+ * and releases the events.  Disabled by default; enabling adds an event record
+ * between kernels. */
+dms_status dms_timing_enable(dms_pool* pool, int32_t enable);
+dms_status dms_timing_read(dms_pool* pool, double* attend_ms, double* merge_ms, int64_t* launches);
+
+/* Text of the last error on the calling thread ("" if none). */
+const char* dms_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DMS_H_ */

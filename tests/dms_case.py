@@ -1,0 +1,196 @@
+"""Drives the GPU library through the C ABI on seeded inputs and checks it
+against the oracle: outputs within tolerance, live sets and counts exactly.
+
+Tolerance: |gpu - ref| <= ATOL + RTOL * |ref| elementwise, with ATOL = 2e-3 and
+RTOL = 1e-2 (bf16 K/V/Q inputs, fp32 accumulation, bf16 output; the reference
+is the oracle in fp64 on the same bf16 inputs).
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass, field
+from typing import Callable, List, Optional
+
+import numpy as np
+
+import oracle
+import synth
+
+ATOL = 2e-3
+RTOL = 1e-2
+
+
+def bf16_bits_to_f64(bits: np.ndarray) -> np.ndarray:
+    return synth.bf16_to_f32(bits).astype(np.float64)
+
+
+def assert_close(gpu_bits: np.ndarray, ref: np.ndarray, what: str = ""):
+    got = bf16_bits_to_f64(gpu_bits)
+    err = np.abs(got - ref)
+    bound = ATOL + RTOL * np.abs(ref)
+    bad = err > bound
+    if bad.any():
+        i = np.unravel_index(np.argmax(err - bound), err.shape)
+        raise AssertionError("%s: %d of %d outside |d| <= %g + %g|ref| (worst at %s: gpu %r ref %r)"
+                             % (what, int(bad.sum()), bad.size, ATOL, RTOL, i, got[i], ref[i]))
+    return float(err.max()), float((err / np.maximum(np.abs(ref), 1e-30)).max())
+
+
+@dataclass
+class SeqData:
+    """Full per-(seq, layer) inputs for positions 0 .. total-1 (bf16 bits / f32)."""
+    q: np.ndarray
+    k: np.ndarray
+    v: np.ndarray
+    logits: np.ndarray
+
+
+@dataclass
+class Case:
+    n_layers: int
+    n_q_heads: int
+    n_kv_heads: int
+    head_dim: int
+    window: int
+    ctx_lens: List[int]
+    steps: int
+    seed: int = 1234
+    logits_fn: Optional[Callable] = None   # (seq, layer, positions[n]) -> float32 [n][Hkv]
+    keep_mu: float = -1.2                  # logit = -(mu + N(0,1)) when logits_fn is None
+    page_order_seed: int = 0
+    max_pages: Optional[int] = None
+    max_positions: Optional[int] = None
+    zero_q: bool = False
+    data: dict = field(default_factory=dict)
+
+    @property
+    def n_seqs(self):
+        return len(self.ctx_lens)
+
+    def total(self, s):
+        return self.ctx_lens[s] + self.steps
+
+    def gen(self):
+        H, Hq, D = self.n_kv_heads, self.n_q_heads, self.head_dim
+        for s in range(self.n_seqs):
+            T = self.total(s)
+            for l in range(self.n_layers):
+                sid = lambda tag: synth.stream_id(tag, s, l)
+                q = synth.normal_bf16(self.seed, sid(synth.TAG_Q), 0, T * Hq * D).reshape(T, Hq, D)
+                if self.zero_q:
+                    q[:] = 0
+                k = synth.normal_bf16(self.seed, sid(synth.TAG_K), 0, T * H * D).reshape(T, H, D)
+                v = synth.normal_bf16(self.seed, sid(synth.TAG_V), 0, T * H * D).reshape(T, H, D)
+                if self.logits_fn is not None:
+                    lg = np.asarray(self.logits_fn(s, l, np.arange(T)), np.float32).reshape(T, H)
+                else:
+                    z = synth.normal_f32(self.seed, sid(synth.TAG_SCORE), 0, T * H).reshape(T, H)
+                    lg = (-(self.keep_mu + z.astype(np.float64))).astype(np.float32)
+                self.data[(s, l)] = SeqData(q, k, v, lg)
+        return self
+
+    def pool_kwargs(self):
+        maxpos = self.max_positions or max(self.total(s) for s in range(self.n_seqs))
+        if self.max_pages is None:
+            per_head = (maxpos + 63) // 64
+            max_pages = per_head * self.n_layers * self.n_kv_heads * self.n_seqs
+        else:
+            max_pages = self.max_pages
+        return dict(n_layers=self.n_layers, n_q_heads=self.n_q_heads, n_kv_heads=self.n_kv_heads,
+                    head_dim=self.head_dim, window=self.window, max_seqs=self.n_seqs,
+                    max_positions=maxpos, max_pages=max_pages, page_order_seed=self.page_order_seed)
+
+    # ---- oracle side
+    def marks(self, s, l):
+        return oracle.marks(self.data[(s, l)].logits)
+
+    def oracle_out(self, s, l, t):
+        d = self.data[(s, l)]
+        m = self.marks(s, l)
+        return oracle.attend(d.q[t:t + 1], [t], d.k[:t + 1], d.v[:t + 1], m[:t + 1], self.window)[0]
+
+    def oracle_live(self, s, l, h, t):
+        return oracle.live_positions(t, self.window, self.marks(s, l)[:t + 1, h])
+
+
+def to_dev(arr, torch, dtype):
+    a = np.ascontiguousarray(arr)
+    if dtype == torch.bfloat16:
+        return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to("cuda")
+    return torch.from_numpy(a).to("cuda")
+
+
+def from_dev_bf16(t) -> np.ndarray:
+    import torch
+    return t.view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+class Runner:
+    """Runs a Case on the GPU through the binding's Pool."""
+
+    def __init__(self, case: Case):
+        import torch
+        import compact_decode_attention_amd as dms
+        self.torch = torch
+        self.dms = dms
+        self.case = case
+        self.pool = dms.Pool(**case.pool_kwargs())
+
+    def prefill_all(self):
+        c, torch = self.case, self.torch
+        for s in range(c.n_seqs):
+            T = c.ctx_lens[s]
+            for l in range(c.n_layers):
+                d = c.data[(s, l)]
+                self.pool.prefill(s, l, to_dev(d.k[:T], torch, torch.bfloat16),
+                                  to_dev(d.v[:T], torch, torch.bfloat16),
+                                  to_dev(d.logits[:T], torch, torch.float32))
+
+    def step_inputs(self, i, seqs, layers):
+        """Inputs of decode step i for the given seqs and layers, [layers][seqs]..."""
+        c, torch = self.case, self.torch
+        q = np.stack([np.stack([c.data[(s, l)].q[c.ctx_lens[s] + i] for s in seqs]) for l in layers])
+        k = np.stack([np.stack([c.data[(s, l)].k[c.ctx_lens[s] + i] for s in seqs]) for l in layers])
+        v = np.stack([np.stack([c.data[(s, l)].v[c.ctx_lens[s] + i] for s in seqs]) for l in layers])
+        lg = np.stack([np.stack([c.data[(s, l)].logits[c.ctx_lens[s] + i] for s in seqs]) for l in layers])
+        return (to_dev(q, torch, torch.bfloat16), to_dev(k, torch, torch.bfloat16),
+                to_dev(v, torch, torch.bfloat16), to_dev(lg, torch, torch.float32))
+
+    def decode(self, i, seqs=None, layer0=0, n_layers=None):
+        c, torch = self.case, self.torch
+        seqs = list(range(c.n_seqs)) if seqs is None else list(seqs)
+        n_layers = c.n_layers - layer0 if n_layers is None else n_layers
+        layers = list(range(layer0, layer0 + n_layers))
+        q, k, v, lg = self.step_inputs(i, seqs, layers)
+        out = torch.empty((n_layers, len(seqs), c.n_q_heads, c.head_dim), dtype=torch.bfloat16, device="cuda")
+        self.pool.decode_step(seqs, layer0, q, k, v, lg, out)
+        return from_dev_bf16(out)
+
+    def check_live(self, t_of_seq):
+        """Every (seq, layer, kv head): exported positions == oracle live set."""
+        c = self.case
+        st, _ = self.pool.stats()
+        for s in range(c.n_seqs):
+            t = t_of_seq[s]
+            _, live = self.pool.stats(s, per_head=True)
+            for l in range(c.n_layers):
+                for h in range(c.n_kv_heads):
+                    got = self.pool.export_live(s, l, h)
+                    ref = c.oracle_live(s, l, h, t)
+                    assert np.array_equal(got, ref), ("live set", s, l, h, t, len(got), len(ref))
+                    assert live[l, h] == len(ref)
+        return st
+
+    def check_outputs(self, out, i, seqs=None, layer0=0):
+        c = self.case
+        seqs = list(range(c.n_seqs)) if seqs is None else list(seqs)
+        worst = (0.0, 0.0)
+        for li in range(out.shape[0]):
+            for si, s in enumerate(seqs):
+                t = c.ctx_lens[s] + i
+                ref = c.oracle_out(s, layer0 + li, t)
+                e = assert_close(out[li, si], ref, "seq %d layer %d t %d" % (s, layer0 + li, t))
+                worst = (max(worst[0], e[0]), max(worst[1], e[1]))
+        return worst
+
+    def close(self):
+        self.pool.close()

@@ -1,0 +1,202 @@
+"""GPU parity of the decode path (through the C ABI) against the oracle:
+outputs within tolerance at every step, live sets and counts exactly."""
+import numpy as np
+import pytest
+
+from dms_case import Case, Runner
+
+pytestmark = pytest.mark.gpu
+
+
+def run_case(case, check_live_every=1, layer_batched=True):
+    case.gen()
+    r = Runner(case)
+    try:
+        r.prefill_all()
+        r.check_live([case.ctx_lens[s] - 1 for s in range(case.n_seqs)])
+        worst = (0.0, 0.0)
+        for i in range(case.steps):
+            if layer_batched:
+                out = r.decode(i)
+            else:
+                out = np.concatenate([r.decode(i, layer0=l, n_layers=1) for l in range(case.n_layers)])
+            e = r.check_outputs(out, i)
+            worst = (max(worst[0], e[0]), max(worst[1], e[1]))
+            if check_live_every and (i % check_live_every == 0 or i == case.steps - 1):
+                r.check_live([case.ctx_lens[s] + i for s in range(case.n_seqs)])
+        return r, worst
+    except Exception:
+        r.close()
+        raise
+
+
+def test_tiny_d64_ctx1024_end_to_end():
+    """One layer, 32 q / 8 kv heads, D=64, 1024-token prompt, 16 steps, w=256,
+    keep score N(-1.2, 1) (about 1/8 kept)."""
+    case = Case(n_layers=1, n_q_heads=32, n_kv_heads=8, head_dim=64, window=256,
+                ctx_lens=[1024], steps=16, seed=20261203)
+    r, worst = run_case(case)
+    st, _ = r.pool.stats(0)
+    assert st.position == 1024 + 16
+    assert st.device_error == 0
+    r.close()
+    print("worst abs %.3g rel %.3g" % worst)
+
+
+def test_page_order_does_not_change_results():
+    outs = []
+    for seed in (0, 987654321):
+        case = Case(n_layers=2, n_q_heads=8, n_kv_heads=2, head_dim=128, window=40,
+                    ctx_lens=[300, 170], steps=70, seed=5, page_order_seed=seed)
+        case.gen()
+        r = Runner(case)
+        r.prefill_all()
+        o = [r.decode(i) for i in range(case.steps)]
+        r.close()
+        outs.append(np.stack(o))
+    assert np.array_equal(outs[0], outs[1])
+
+
+@pytest.mark.parametrize("marks", ["all", "none", "random"])
+@pytest.mark.parametrize("window", [1, 2, 64, 1 << 20])
+def test_windows_and_mark_extremes(marks, window):
+    H = 2
+    if marks == "all":
+        fn = lambda s, l, p: np.ones((len(p), H), np.float32)
+    elif marks == "none":
+        fn = lambda s, l, p: -np.ones((len(p), H), np.float32)
+    else:
+        fn = None
+    case = Case(n_layers=1, n_q_heads=8, n_kv_heads=H, head_dim=64, window=window,
+                ctx_lens=[63, 64, 65, 1], steps=70, seed=11, logits_fn=fn, keep_mu=0.0,
+                max_positions=200)
+    r, _ = run_case(case, check_live_every=7)
+    r.close()
+
+
+@pytest.mark.parametrize("head_dim", [64, 128])
+@pytest.mark.parametrize("group", [1, 2, 4, 8])
+def test_group_sizes(head_dim, group):
+    case = Case(n_layers=1, n_q_heads=2 * group, n_kv_heads=2, head_dim=head_dim, window=24,
+                ctx_lens=[200, 77], steps=30, seed=group * 100 + head_dim)
+    r, _ = run_case(case, check_live_every=10)
+    r.close()
+
+
+def test_per_layer_calls_match_layer_batched():
+    res = []
+    for batched in (True, False):
+        case = Case(n_layers=3, n_q_heads=16, n_kv_heads=4, head_dim=128, window=32,
+                    ctx_lens=[129, 500, 64], steps=20, seed=77)
+        case.gen()
+        r = Runner(case)
+        r.prefill_all()
+        outs = []
+        for i in range(case.steps):
+            if batched:
+                outs.append(r.decode(i))
+            else:
+                outs.append(np.concatenate([r.decode(i, layer0=l, n_layers=1) for l in range(3)]))
+        r.check_live([case.ctx_lens[s] + case.steps - 1 for s in range(3)])
+        r.close()
+        res.append(np.stack(outs))
+    assert np.array_equal(res[0], res[1])
+
+
+def test_subset_of_sequences_per_call():
+    """Sequences stepped by separate calls keep their own positions."""
+    case = Case(n_layers=1, n_q_heads=8, n_kv_heads=2, head_dim=64, window=16,
+                ctx_lens=[40, 90, 17], steps=12, seed=3)
+    case.gen()
+    r = Runner(case)
+    r.prefill_all()
+    for i in range(case.steps):
+        o1 = r.decode(i, seqs=[2, 0])
+        r.check_outputs(o1, i, seqs=[2, 0])
+        o2 = r.decode(i, seqs=[1])
+        r.check_outputs(o2, i, seqs=[1])
+    r.check_live([case.ctx_lens[s] + case.steps - 1 for s in range(3)])
+    r.close()
+
+
+def test_zero_query_gives_mean_of_live_values():
+    case = Case(n_layers=1, n_q_heads=4, n_kv_heads=1, head_dim=128, window=10,
+                ctx_lens=[150], steps=20, seed=9, zero_q=True)
+    r, _ = run_case(case, check_live_every=5)
+    r.close()
+
+
+def test_release_and_reprefill_conserves_pages():
+    case = Case(n_layers=2, n_q_heads=8, n_kv_heads=2, head_dim=64, window=8,
+                ctx_lens=[300, 200], steps=10, seed=21)
+    case.gen()
+    r = Runner(case)
+    st0, _ = r.pool.stats()
+    total_pages = st0.pages_free
+    r.prefill_all()
+    for i in range(case.steps):
+        r.decode(i)
+    st1, _ = r.pool.stats()
+    assert st1.pages_used + st1.pages_free == total_pages
+    r.pool.release(0)
+    st2, _ = r.pool.stats()
+    assert st2.pages_used + st2.pages_free == total_pages
+    s0, _ = r.pool.stats(0)
+    assert s0.live_slots == 0 and s0.position == -1
+    # prefill seq 0 again and keep decoding both
+    import compact_decode_attention_amd as dms
+    case.steps_done = case.steps
+    T = case.ctx_lens[0]
+    for l in range(2):
+        d = case.data[(0, l)]
+        from dms_case import to_dev
+        t = r.torch
+        r.pool.prefill(0, l, to_dev(d.k[:T], t, t.bfloat16), to_dev(d.v[:T], t, t.bfloat16),
+                       to_dev(d.logits[:T], t, t.float32))
+    r.check_live([T - 1, case.ctx_lens[1] + case.steps - 1])
+    st3, _ = r.pool.stats()
+    assert st3.pages_used + st3.pages_free == total_pages
+    r.close()
+
+
+def test_capacity_exhaustion_is_reported():
+    import compact_decode_attention_amd as dms
+    case = Case(n_layers=1, n_q_heads=4, n_kv_heads=1, head_dim=64, window=4,
+                ctx_lens=[64], steps=3, seed=1, max_pages=1,
+                logits_fn=lambda s, l, p: -np.ones((len(p), 1), np.float32))
+    case.gen()
+    r = Runner(case)
+    r.prefill_all()            # 64 live tokens: exactly one page
+    r.decode(0)                # token 64 needs a second page: none left
+    with pytest.raises(dms.DMSError) as ei:
+        r.pool.stats()
+    assert ei.value.status == dms.DMS_E_CAPACITY
+    st, _ = r.pool.stats(raise_on_error=False)
+    assert st.device_error == dms.DMS_E_CAPACITY
+    r.close()
+
+
+def test_host_side_errors():
+    import compact_decode_attention_amd as dms
+    case = Case(n_layers=2, n_q_heads=4, n_kv_heads=1, head_dim=64, window=4,
+                ctx_lens=[10], steps=2, seed=1)
+    case.gen()
+    r = Runner(case)
+    with pytest.raises(dms.DMSError) as ei:
+        r.decode(0)            # not prefilled
+    assert ei.value.status == dms.DMS_E_STATE
+    r.prefill_all()
+    from dms_case import to_dev
+    t = r.torch
+    d = case.data[(0, 0)]
+    with pytest.raises(dms.DMSError) as ei:
+        r.pool.prefill(0, 0, to_dev(d.k[:10], t, t.bfloat16), to_dev(d.v[:10], t, t.bfloat16),
+                       to_dev(d.logits[:10], t, t.float32))
+    assert ei.value.status == dms.DMS_E_STATE
+    with pytest.raises(dms.DMSError) as ei:
+        dms.dms_decode_step(r.pool.handle, [0, 0], 0, 1, 1, 1, 1, 1, 1, 0)
+    assert ei.value.status == dms.DMS_E_INVAL
+    with pytest.raises(dms.DMSError) as ei:
+        dms.dms_decode_step(r.pool.handle, [0], 1, 2, 1, 1, 1, 1, 1, 0)
+    assert ei.value.status == dms.DMS_E_INVAL
+    r.close()
