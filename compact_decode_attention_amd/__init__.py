@@ -197,7 +197,7 @@ def dms_timing_enable(pool: int, enable: bool):
 
 
 def dms_timing_read(pool: int):
-    """(attention-kernel ms, merge-kernel ms, launches) since the last read."""
+    """(attention-kernel ms, merge-kernel ms, launches) summed since the last read."""
     a, m, n = ctypes.c_double(), ctypes.c_double(), ctypes.c_int64()
     _check(lib().dms_timing_read(ctypes.c_void_p(pool), ctypes.byref(a), ctypes.byref(m), ctypes.byref(n)))
     return a.value, m.value, n.value

@@ -69,7 +69,7 @@ bool make_layout(const dms_pool_config* c, Layout* L, std::string* why) {
     sz[S_V] = sz[S_K];
     sz[S_POS] = (size_t)c->max_pages * dms::kPage * 4;
     sz[S_STACK] = (size_t)c->max_pages * 4;
-    sz[S_HSTATE] = (size_t)heads * 16;
+    sz[S_HSTATE] = (size_t)heads * dms::kHS * 4;
     sz[S_PTABLE] = (size_t)heads * L->pages_per_head * 4;
     sz[S_RING] = (size_t)heads * L->ring_len * 4;
     sz[S_PART] = (size_t)L->max_items * g * (D + 2) * 4;
@@ -178,8 +178,11 @@ dms_status dms_pool_create(const dms_pool_config* cfg, void* arena, size_t arena
     int32_t ctl[64] = {0};
     ctl[dms::kCtlTop] = (int32_t)cfg->max_pages;
 
+    std::vector<int32_t> rec((size_t)L.heads * dms::kHS, 0);  // empty heads: no expiring slot
+    for (int64_t h = 0; h < L.heads; ++h) rec[(size_t)h * dms::kHS + dms::kHsExp] = -1;
     hipError_t e = hipMemsetAsync(arena, 0, L.off[S_N], s);
     if (e == hipSuccess) e = hipMemcpyAsync(d.stack, order.data(), order.size() * 4, hipMemcpyHostToDevice, s);
+    if (e == hipSuccess) e = hipMemcpyAsync(d.hstate, rec.data(), rec.size() * 4, hipMemcpyHostToDevice, s);
     if (e == hipSuccess) e = hipMemcpyAsync(d.ctl, ctl, sizeof(ctl), hipMemcpyHostToDevice, s);
     if (e == hipSuccess) e = hipStreamSynchronize(s);
     if (e != hipSuccess) {
@@ -275,9 +278,10 @@ dms_status dms_decode_step(dms_pool* pool, int32_t n_seqs, const int32_t* seq_id
         for (int i = 0; i < a.n_seqs; ++i) {
             a.seq_ids[i] = seq_ids[sb + i];
             for (int l = layer0; l < layer0 + n_layers; ++l)
-                bound += (int64_t)hkv * ((pool->position(a.seq_ids[i], l) + dms::kChunk - 1) / dms::kChunk);
+                bound += (int64_t)hkv * std::max(1, (pool->position(a.seq_ids[i], l) + dms::kChunk - 1) / dms::kChunk);
         }
-        const int grid = (int)std::max<int64_t>(1, std::min<int64_t>(bound, (int64_t)pool->cu_count * 4));
+        const int per_cu = std::min(dms::kGridPerCU, dms::decode_blocks_per_cu(a));
+        const int grid = (int)std::max<int64_t>(1, std::min<int64_t>(bound, (int64_t)pool->cu_count * per_cu));
         hipEvent_t* ev = nullptr;
         if (pool->timing) {
             const size_t base = pool->events.size();
@@ -306,9 +310,9 @@ dms_status dms_query_stats(dms_pool* pool, int32_t seq, dms_stats* out, int32_t*
     if (e != hipSuccess) return hip_fail(e, "synchronise");
     const int64_t per_seq = (int64_t)c.n_layers * c.n_kv_heads;
     const int s0 = seq < 0 ? 0 : seq, s1 = seq < 0 ? c.max_seqs : seq + 1;
-    std::vector<int32_t> hs((size_t)(s1 - s0) * per_seq * 4);
+    std::vector<int32_t> hs((size_t)(s1 - s0) * per_seq * dms::kHS);
     int32_t ctl[64];
-    e = hipMemcpy(hs.data(), pool->dev.hstate + (size_t)s0 * per_seq * 4, hs.size() * 4, hipMemcpyDeviceToHost);
+    e = hipMemcpy(hs.data(), pool->dev.hstate + (size_t)s0 * per_seq * dms::kHS, hs.size() * 4, hipMemcpyDeviceToHost);
     if (e == hipSuccess) e = hipMemcpy(ctl, pool->dev.ctl, sizeof(ctl), hipMemcpyDeviceToHost);
     if (e != hipSuccess) return hip_fail(e, "read pool state");
     const int64_t D = c.head_dim;
@@ -317,14 +321,14 @@ dms_status dms_query_stats(dms_pool* pool, int32_t seq, dms_stats* out, int32_t*
     for (int s = s0; s < s1; ++s) {
         for (int l = 0; l < c.n_layers; ++l) {
             int32_t& hp = pool->position(s, l);
-            const int32_t* h0 = &hs[(((size_t)(s - s0) * c.n_layers + l) * c.n_kv_heads) * 4];
-            if (hp >= 0) hp = h0[2];  // device counters are authoritative (graph replays bypass the host)
+            const int32_t* h0 = &hs[(((size_t)(s - s0) * c.n_layers + l) * c.n_kv_heads) * dms::kHS];
+            if (hp >= 0) hp = h0[dms::kHsPos];  // device counters are authoritative (graph replays bypass the host)
             if (hp > 0) dense_tokens += (int64_t)hp * c.n_kv_heads;
             for (int h = 0; h < c.n_kv_heads; ++h) {
-                const int32_t* x = h0 + h * 4;
-                out->live_slots += x[0];
-                out->pages_used += x[1];
-                if (live_per_layer_head) live_per_layer_head[l * c.n_kv_heads + h] = x[0];
+                const int32_t* x = h0 + h * dms::kHS;
+                out->live_slots += x[dms::kHsLive];
+                out->pages_used += x[dms::kHsPages];
+                if (live_per_layer_head) live_per_layer_head[l * c.n_kv_heads + h] = x[dms::kHsLive];
             }
         }
     }
@@ -349,10 +353,10 @@ dms_status dms_export_live(dms_pool* pool, int32_t seq, int32_t layer, int32_t k
     hipError_t e = hipDeviceSynchronize();
     if (e != hipSuccess) return hip_fail(e, "synchronise");
     const int64_t gh = ((int64_t)seq * c.n_layers + layer) * c.n_kv_heads + kv_head;
-    int32_t hs[4];
-    e = hipMemcpy(hs, pool->dev.hstate + gh * 4, sizeof(hs), hipMemcpyDeviceToHost);
+    int32_t hs[dms::kHS];
+    e = hipMemcpy(hs, pool->dev.hstate + gh * dms::kHS, sizeof(hs), hipMemcpyDeviceToHost);
     if (e != hipSuccess) return hip_fail(e, "read head state");
-    const int live = hs[0], np = hs[1];
+    const int live = hs[dms::kHsLive], np = hs[dms::kHsPages];
     *n = live;
     if (live > cap || (live > 0 && !positions)) return fail(DMS_E_INVAL, "positions array too small");
     std::vector<int32_t> pages((size_t)np);
@@ -397,20 +401,20 @@ dms_status dms_timing_read(dms_pool* pool, double* attend_ms, double* merge_ms, 
     if (!pool || !attend_ms || !merge_ms || !launches) return fail(DMS_E_INVAL, "NULL argument");
     hipError_t e = hipDeviceSynchronize();
     if (e != hipSuccess) return hip_fail(e, "synchronise");
-    double a = 0, m = 0;
+    double ta = 0, tm = 0;
     const size_t n = pool->events.size() / 3;
     for (size_t i = 0; i < n; ++i) {
         float t0 = 0, t1 = 0;
         e = hipEventElapsedTime(&t0, pool->events[3 * i], pool->events[3 * i + 1]);
         if (e == hipSuccess) e = hipEventElapsedTime(&t1, pool->events[3 * i + 1], pool->events[3 * i + 2]);
         if (e != hipSuccess) return hip_fail(e, "event elapsed time");
-        a += t0;
-        m += t1;
+        ta += t0;
+        tm += t1;
     }
     for (hipEvent_t ev : pool->events) hipEventDestroy(ev);
     pool->events.clear();
-    *attend_ms = a;
-    *merge_ms = m;
+    *attend_ms = ta;
+    *merge_ms = tm;
     *launches = (int64_t)n;
     g_err.clear();
     return DMS_OK;

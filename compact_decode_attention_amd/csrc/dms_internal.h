@@ -9,14 +9,14 @@
 //                                                  consecutive slots of dim d
 //   slot_pos int32 [max_pages][64]                 position held by each slot
 //   stack    int32 [max_pages]                     free pages, stack[0 .. top)
-//   hstate   int32 [heads][4]                      {n_live, n_pages, position, 0}
+//   hstate   int32 [heads][8]                      per-head record (kHs* below)
 //   ptable   int32 [heads][pages_per_head]         page of slots 64j .. 64j+63
 //   ring     int32 [heads][ring_len]               entry of position s at s % w:
 //                                                  (slot << 1) | mark, -1 = none
 //   partials f32   [max_items][G*(head_dim+2)]     split-K partials {m[G], l[G], acc[G][D]}
-//   prefix   int32 [max_call_heads + 1]            split-K item offsets of the last call
+//   prefix   int32 [max_call_heads + 1]            first split-K item of each head (last launch)
 //   inv      int32 [n_kv_heads][max_positions]     prefill scratch: slot -> position
-//   ctl      int32 [64]                            {stack top, sticky error, ...}
+//   ctl      int32 [64]                            pool counters (kCtl* below)
 // heads = max_seqs * n_layers * n_kv_heads, head id = (seq * n_layers + layer) * n_kv_heads + h.
 #pragma once
 #include <hip/hip_runtime.h>
@@ -24,13 +24,36 @@
 
 namespace dms {
 
+// Split-K work item of the decode kernel: a block of 4 waves, each wave taking
+// kPagesPerWave pages of one head.  kGridPerCU blocks per compute unit form the
+// persistent grid.  (Tuning constants; overridable at build time.)
+#ifndef DMS_PAGES_PER_WAVE
+#define DMS_PAGES_PER_WAVE 1
+#endif
+#ifndef DMS_GRID_PER_CU
+#define DMS_GRID_PER_CU 4
+#endif
 constexpr int kPage = 64;          // slots per page
-constexpr int kChunkPages = 4;     // pages per split-K work item (one per wave)
+constexpr int kPagesPerWave = DMS_PAGES_PER_WAVE;
+constexpr int kChunkPages = 4 * kPagesPerWave;
 constexpr int kChunk = kPage * kChunkPages;
+constexpr int kGridPerCU = DMS_GRID_PER_CU;
 constexpr int kMaxCallSeqs = 256;  // sequences per kernel launch (larger calls are split)
-constexpr int kMaxCallHeads = 16384;
-constexpr int kCtlTop = 0;
-constexpr int kCtlError = 1;
+constexpr int kMaxCallHeads = 4096;  // heads per launch (the work list lives in LDS)
+
+// ctl words
+constexpr int kCtlTop = 0;    // free pages on the stack
+constexpr int kCtlError = 1;  // sticky: nonzero once the page pool ran out
+
+// Per-head record, 8 int32:
+//   [0] n_live       tokens held, in slots 0 .. n_live-1
+//   [1] n_pages      pages in the head's page table
+//   [2] position     position of the next token
+//   [3] e_next       slot of the token that expires when `position` is appended
+//                    (position - w, if it was marked), or -1
+//   [4..7]           unused
+constexpr int kHS = 8;
+constexpr int kHsLive = 0, kHsPages = 1, kHsPos = 2, kHsExp = 3;
 
 struct PoolDev {
     uint16_t* kpages;
@@ -76,9 +99,11 @@ struct PrefillArgs {
     int32_t seq, layer, n_tokens;
 };
 
-// ev (optional): three events recorded before the attention kernel, between the
-// two kernels and after the merge kernel
+// ev (optional): two events recorded before the first and after the last
+// kernel of the decode launch
 hipError_t launch_decode(const DecodeArgs& a, int grid, hipStream_t s, hipEvent_t* ev);
+// blocks of the attention kernel one compute unit holds at once for this call
+int decode_blocks_per_cu(const DecodeArgs& a);
 hipError_t launch_prefill_compact(const PrefillArgs& a, hipStream_t s);
 hipError_t launch_prefill_attend(const PrefillArgs& a, hipStream_t s);
 hipError_t launch_seq_release(const PoolDev& p, int32_t seq, hipStream_t s);

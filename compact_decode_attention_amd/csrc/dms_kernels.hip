@@ -1,5 +1,5 @@
 // DMS compact-store kernels for CDNA4 (gfx950): decode (split-K flash-decode
-// over the live slots + merge + eviction/append), prefill compaction, and
+// over the live slots, then merge and eviction/append), prefill compaction, and
 // sequence release.
 //
 // What a decode step computes for one (sequence, layer, kv head) at position t
@@ -12,20 +12,20 @@
 //   otherwise token t takes slot n_old (a new page every 64 slots)
 //   out[g] = softmax over V(t) = V(t-1) \ {t-w if marked} + {t}
 //
-// Kernels of one decode call:
+// Kernels of one decode launch:
 //   decode_attend  -- persistent grid; every block derives the split-K work list
-//                     (4 pages per item, one page per wave) from the live counts,
-//                     then each wave computes a partial softmax over one page:
-//                     QK^T with lane = slot (v_dot2_f32_bf16 over 16-byte K chunks
-//                     loaded 1 KB-coalesced from the key-major K page), the page
-//                     max and sum by wavefront reductions, and PV with lane = dim
-//                     (v_dot2 over key pairs of the dim-major V page).  The block
-//                     folds its 4 waves into one partial per item.
-//   decode_merge   -- one wave per head: log-sum-exp merge of the partials plus
-//                     the new token, bf16 output; then mark, expiry, slot reuse or
-//                     page allocation, K/V append and the head's counters.
-// The attend kernel only reads pool state; all writes happen in the merge kernel,
-// after every reader of this step has finished (kernel boundary).
+//                     (ceil(n_old / 256) items per head, 4 pages per item, one
+//                     page per wave) from the head records, then each wave folds
+//                     one page into a running softmax: QK^T with lane = slot
+//                     (v_dot2_f32_bf16 over 16-byte K chunks loaded 1 KB-coalesced
+//                     from the key-major K page), page max and sum by DPP
+//                     wavefront reductions, PV with lane = dim (v_dot2 over key
+//                     pairs of the dim-major V page).  A block folds its 4 waves
+//                     into one partial per item.  This kernel only reads the pool.
+//   decode_merge   -- per head: log-sum-exp merge of the partials with the new
+//                     token (bf16 output), and, in separate blocks, mark, expiry,
+//                     slot reuse or page allocation, K/V append and the record.
+// The kernel boundary orders every read of this step before every write.
 #include "dms_internal.h"
 
 #include <math.h>
@@ -88,6 +88,14 @@ __device__ __forceinline__ float wave_sum(float x) {
 // writes x.  Volatile asm keeps its place among memory operations, so the
 // arithmetic producing x stays ahead of the loads issued after this point.
 __device__ __forceinline__ void pin(float& x) { asm volatile("" : "+v"(x)); }
+
+// An opaque copy of x: values computed from it inside a loop cannot be hoisted
+// out of the loop (a persistent loop would otherwise keep every per-thread
+// address alive in registers across all its iterations).
+__device__ __forceinline__ int launder(int x) {
+    asm volatile("" : "+v"(x));
+    return x;
+}
 
 // Raw buffer resource over [base, base + bytes): loads beyond it return 0.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, int bytes) {
@@ -156,22 +164,141 @@ __device__ __forceinline__ CallHead call_head(const DecodeArgs& a, int ch) {
     return c;
 }
 
-// Slot of the token that expires at step t (position t-w, if it was marked), or -1.
-__device__ __forceinline__ int expiring_slot(const PoolDev& P, int gh, int t) {
-    if (P.ring_len <= 0 || t < P.window) return -1;
-    const int r = P.ring[(size_t)gh * P.ring_len + (t % P.window)];
+// Slot of the token at position s if it is marked (ring entry of s), else -1.
+__device__ __forceinline__ int marked_slot_at(const PoolDev& P, int gh, int s) {
+    if (P.ring_len <= 0 || s < 0) return -1;
+    const int r = P.ring[(size_t)gh * P.ring_len + (s % P.window)];
     return (r >= 0 && (r & 1)) ? (r >> 1) : -1;
 }
 
 // ---------------------------------------------------------------------------
-// decode: split-K attention over the live slots
+// decode, kernel 1: split-K attention over the live slots
 // ---------------------------------------------------------------------------
+
+// K chunk cc of slot `lane` of one page: 64 lanes read 1 KB contiguous.  An
+// empty page (live = false) gets a zero-size resource: its loads return 0 and
+// move no data.
+template <int D>
+__device__ __forceinline__ void load_k_page(const PoolDev& P, int page, bool live, int lane, uint4 (&kc)[D / 8]) {
+    const __amdgpu_buffer_rsrc_t kr =
+        buffer_rsrc(P.kpages + (size_t)page * (kPage * D), live ? kPage * D * 2 : 0);
+#pragma unroll
+    for (int cc = 0; cc < D / 8; ++cc) kc[cc] = buffer_load16(kr, lane * 16, cc * kPage * 16);
+}
+
+// One page (64 slots) of one head, K already in registers, folded into a wave's
+// running softmax state (m: running max in base-2 units, l: running sum, acc:
+// running P.V for the dims this lane owns).  Slots at or beyond n_old and the
+// expiring slot e are masked; a page wholly beyond n_old changes nothing and
+// reads no memory.
 template <int D, int G>
-__global__ __launch_bounds__(256, 4) void decode_attend_kernel(DecodeArgs a) {
+__device__ __forceinline__ void attend_page(const PoolDev& P, int page, int base, int n_old, int e,
+                                            const uint4 (&kc)[D / 8], const uint32_t (*s_q)[D / 2],
+                                            uint16_t (*s_p)[kPage], int lane, float (&m)[G], float (&l)[G],
+                                            float (&acc)[G][D / 64]) {
     constexpr int NC = D / 8;   // 16-byte K chunks per slot
     constexpr int VJ = D / 64;  // dims per lane in PV
-    constexpr int NW = 4;       // waves per block = pages per item
-    extern __shared__ int32_t s_prefix[];  // [n_call_heads + 1]
+    // QK^T, lane = slot.  q is read from LDS (same address in every lane: a
+    // broadcast), one chunk ahead of its use; each q head is one chain of dot
+    // products over the 16-byte K chunks held in registers.
+    float z[G];
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+        float zg = 0.f;
+        uint4 qn = *reinterpret_cast<const uint4*>(&s_q[g][0]);
+#pragma unroll
+        for (int cc = 0; cc < NC; ++cc) {
+            const uint4 qv = qn;
+            if (cc + 1 < NC) qn = *reinterpret_cast<const uint4*>(&s_q[g][(cc + 1) * 4]);
+            zg = dot2(qv.x, kc[cc].x, zg);
+            zg = dot2(qv.y, kc[cc].y, zg);
+            zg = dot2(qv.z, kc[cc].z, zg);
+            zg = dot2(qv.w, kc[cc].w, zg);
+            pin(zg);
+        }
+        z[g] = zg;
+    }
+    // V loads go out after QK (K registers are free again); other waves keep the
+    // memory pipe busy meanwhile.
+    const __amdgpu_buffer_rsrc_t vr =
+        buffer_rsrc(P.vpages + (size_t)page * (kPage * D), base < n_old ? kPage * D * 2 : 0);
+    uint4 vc[8][VJ];
+#pragma unroll
+    for (int b = 0; b < 8; ++b)
+#pragma unroll
+        for (int j = 0; j < VJ; ++j) vc[b][j] = buffer_load16(vr, lane * 16, (b * D + j * 64) * 16);
+    const int slot = base + lane;
+    const bool valid = slot < n_old && slot != e;
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+        // additive mask: a select here lets the compiler sink the whole QK
+        // product into a branch behind every load of the page
+        const float zz = fmaf(z[g], P.scale_log2, valid ? 0.f : -INFINITY);
+        const float mn = fmaxf(m[g], wave_max(zz));
+        float p = 0.f, alpha = 1.f;
+        if (mn != -INFINITY) {
+            p = exp2f(zz - mn);
+            alpha = exp2f(m[g] - mn);
+        }
+        const uint16_t pb = f32_to_bf16(p);
+        s_p[g][lane] = pb;
+        l[g] = l[g] * alpha + wave_sum(bf16_to_f32(pb));
+        m[g] = mn;
+#pragma unroll
+        for (int j = 0; j < VJ; ++j) acc[g][j] *= alpha;
+    }
+    wave_lds_sync();
+    // PV, lane = dim: each 16-byte V unit holds 8 consecutive slots of one dim,
+    // i.e. 4 key pairs, matched by 4 bf16 pairs of p (broadcast reads).
+    uint4 pn[G];
+#pragma unroll
+    for (int g = 0; g < G; ++g) pn[g] = *reinterpret_cast<const uint4*>(&s_p[g][0]);
+#pragma unroll
+    for (int b = 0; b < 8; ++b) {
+        uint4 pp[G];
+#pragma unroll
+        for (int g = 0; g < G; ++g) pp[g] = pn[g];
+        if (b + 1 < 8) {
+#pragma unroll
+            for (int g = 0; g < G; ++g) pn[g] = *reinterpret_cast<const uint4*>(&s_p[g][(b + 1) * 8]);
+        }
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+#pragma unroll
+            for (int j = 0; j < VJ; ++j) {
+                acc[g][j] = dot2(pp[g].x, vc[b][j].x, acc[g][j]);
+                acc[g][j] = dot2(pp[g].y, vc[b][j].y, acc[g][j]);
+                acc[g][j] = dot2(pp[g].z, vc[b][j].z, acc[g][j]);
+                acc[g][j] = dot2(pp[g].w, vc[b][j].w, acc[g][j]);
+                pin(acc[g][j]);
+            }
+        }
+    }
+    wave_lds_sync();  // s_p is rewritten by this wave's next page
+}
+
+// Head of work item `item`: the largest head index whose first item is <= item.
+__device__ __forceinline__ int item_head(const int32_t* s_prefix, int H, int item) {
+    int lo = 0, hi = H;  // s_prefix[lo] <= item < s_prefix[hi]
+    while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (s_prefix[mid] <= item) lo = mid; else hi = mid;
+    }
+    // the same in every lane; say so, so that head state, page ids and buffer
+    // resources live in scalar registers
+    return __builtin_amdgcn_readfirstlane(lo);
+}
+
+template <int D, int G>
+__global__ __launch_bounds__(256, 4) void decode_attend_kernel(DecodeArgs a) {
+    constexpr int VJ = D / 64;  // dims per lane in PV
+    constexpr int NW = 4;       // waves per block
+    constexpr int QW = (G * D / 2 + 255) / 256;  // q dwords staged per thread
+    const int H = a.n_call_heads;
+    extern __shared__ int32_t s_dyn[];
+    int32_t* s_prefix = s_dyn;          // [H + 1] first item of each head
+    int32_t* s_nold = s_dyn + H + 1;    // [H] live count before this step
+    int32_t* s_exp = s_nold + H;        // [H] slot expiring at this step, or -1
     __shared__ uint32_t s_q[G][D / 2];
     __shared__ uint16_t s_p[NW][G][kPage];
     __shared__ float s_m[NW][G], s_l[NW][G];
@@ -181,14 +308,16 @@ __global__ __launch_bounds__(256, 4) void decode_attend_kernel(DecodeArgs a) {
     const PoolDev& P = a.pool;
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
-    const int H = a.n_call_heads;
 
-    // ---- work list: ceil(n_live / kChunk) items per head, exclusive prefix in LDS
+    // ---- work list: ceil(n_old / kChunk) items per head
     const int per = (H + 255) / 256;
     const int h0 = min(tid * per, H), h1 = min(h0 + per, H);
     int local = 0;
     for (int ch = h0; ch < h1; ++ch) {
-        const int n = P.hstate[(size_t)call_head(a, ch).gh * 4];
+        const int32_t* hs = P.hstate + (size_t)call_head(a, ch).gh * kHS;
+        const int n = hs[kHsLive];
+        s_nold[ch] = n;
+        s_exp[ch] = hs[kHsExp];
         const int c = (n + kChunk - 1) / kChunk;
         s_prefix[ch] = c;
         local += c;
@@ -205,29 +334,42 @@ __global__ __launch_bounds__(256, 4) void decode_attend_kernel(DecodeArgs a) {
     if (blockIdx.x == 0)
         for (int i = tid; i <= H; i += 256) P.prefix[i] = s_prefix[i];
 
-    for (int item = blockIdx.x; item < total; item += gridDim.x) {
-        int lo = 0, hi = H;  // s_prefix[lo] <= item < s_prefix[hi]
-        while (hi - lo > 1) {
-            const int mid = (lo + hi) >> 1;
-            if (s_prefix[mid] <= item) lo = mid; else hi = mid;
-        }
-        // the search result is the same in every lane; say so, so that head state,
-        // page ids and buffer resources live in scalar registers
-        lo = __builtin_amdgcn_readfirstlane(lo);
-        const int chunk = item - __builtin_amdgcn_readfirstlane(s_prefix[lo]);
-        const CallHead c = call_head(a, lo);
-        const int32_t* hs = P.hstate + (size_t)c.gh * 4;
-        const int n_old = hs[0];
-        const int t = hs[2];
-        const int e = expiring_slot(P, c.gh, t);
+    // page id of this wave's first page of an item (0 when the page is empty)
+    auto first_page = [&](int item) -> int {
+        if (item >= total) return 0;
+        const int hd = item_head(s_prefix, H, item);
+        const int pi = (item - __builtin_amdgcn_readfirstlane(s_prefix[hd])) * kChunkPages + wave;
+        if (pi * kPage >= __builtin_amdgcn_readfirstlane(s_nold[hd])) return 0;
+        return P.ptable[(size_t)call_head(a, hd).gh * P.pages_per_head + pi];
+    };
+    int page_next = first_page(blockIdx.x);
 
+    for (int item = blockIdx.x; item < total; item += gridDim.x) {
+        const int tid = launder(threadIdx.x), lane = tid & 63;
+        const int hd = item_head(s_prefix, H, item);
+        const int chunk = item - __builtin_amdgcn_readfirstlane(s_prefix[hd]);
+        const CallHead c = call_head(a, hd);
+        const int n_old = __builtin_amdgcn_readfirstlane(s_nold[hd]);
+        const int e = __builtin_amdgcn_readfirstlane(s_exp[hd]);
+        const int pi0 = chunk * kChunkPages + wave;
+        const int page0 = page_next;
+        page_next = first_page(item + gridDim.x);  // lands while this item runs
+
+        // q loads first, then this wave's first K page, then the q hand-off
         const uint32_t* qsrc =
             reinterpret_cast<const uint32_t*>(a.q + ((size_t)c.row * P.n_q_heads + c.h * G) * D);
-        for (int i = tid; i < G * D / 2; i += 256) s_q[i / (D / 2)][i % (D / 2)] = qsrc[i];
+        uint32_t qv[QW];
+#pragma unroll
+        for (int r = 0; r < QW; ++r) qv[r] = tid + r * 256 < G * D / 2 ? qsrc[tid + r * 256] : 0u;
+        uint4 kc[D / 8];
+        load_k_page<D>(P, page0, pi0 * kPage < n_old, lane, kc);
+#pragma unroll
+        for (int r = 0; r < QW; ++r) {
+            const int i = tid + r * 256;
+            if (i < G * D / 2) s_q[i / (D / 2)][i % (D / 2)] = qv[r];
+        }
         __syncthreads();
 
-        const int pi = chunk * NW + wave;
-        const int base = pi * kPage;
         float m[G], l[G], acc[G][VJ];
 #pragma unroll
         for (int g = 0; g < G; ++g) {
@@ -236,84 +378,17 @@ __global__ __launch_bounds__(256, 4) void decode_attend_kernel(DecodeArgs a) {
 #pragma unroll
             for (int j = 0; j < VJ; ++j) acc[g][j] = 0.f;
         }
-        if (base < n_old) {
-            const int page = P.ptable[(size_t)c.gh * P.pages_per_head + pi];
-            const __amdgpu_buffer_rsrc_t kr = buffer_rsrc(P.kpages + (size_t)page * (kPage * D), kPage * D * 2);
-            const __amdgpu_buffer_rsrc_t vr = buffer_rsrc(P.vpages + (size_t)page * (kPage * D), kPage * D * 2);
-            // K chunk cc of slot `lane`: 64 lanes read 1 KB contiguous
-            uint4 kc[NC];
+        // wave w takes pages w, w+4, ... of the item (empty ones are no-ops)
 #pragma unroll
-            for (int cc = 0; cc < NC; ++cc) kc[cc] = buffer_load16(kr, lane * 16, cc * kPage * 16);
-
-            // QK^T, lane = slot.  q is read from LDS (same address in every lane:
-            // a broadcast), one chunk ahead of its use; each q head is one chain
-            // of dot products over the 16-byte K chunks held in registers.
-            float z[G];
-#pragma unroll
-            for (int g = 0; g < G; ++g) {
-                float zg = 0.f;
-                uint4 qn = *reinterpret_cast<const uint4*>(&s_q[g][0]);
-#pragma unroll
-                for (int cc = 0; cc < NC; ++cc) {
-                    const uint4 qv = qn;
-                    if (cc + 1 < NC) qn = *reinterpret_cast<const uint4*>(&s_q[g][(cc + 1) * 4]);
-                    zg = dot2(qv.x, kc[cc].x, zg);
-                    zg = dot2(qv.y, kc[cc].y, zg);
-                    zg = dot2(qv.z, kc[cc].z, zg);
-                    zg = dot2(qv.w, kc[cc].w, zg);
-                    pin(zg);
-                }
-                z[g] = zg;
+        for (int k = 0; k < kPagesPerWave; ++k) {
+            const int pi = pi0 + k * NW;
+            const int base = pi * kPage;
+            int page = page0;
+            if (k > 0) {
+                page = base < n_old ? P.ptable[(size_t)c.gh * P.pages_per_head + pi] : 0;
+                load_k_page<D>(P, page, base < n_old, lane, kc);
             }
-            // V loads go out after QK (K registers are free again); other waves
-            // keep the memory pipe busy meanwhile.
-            uint4 vc[8][VJ];
-#pragma unroll
-            for (int b = 0; b < 8; ++b)
-#pragma unroll
-                for (int j = 0; j < VJ; ++j) vc[b][j] = buffer_load16(vr, lane * 16, (b * D + j * 64) * 16);
-            const int slot = base + lane;
-            const bool valid = slot < n_old && slot != e;
-#pragma unroll
-            for (int g = 0; g < G; ++g) {
-                // additive mask: a select here lets the compiler sink the whole QK
-                // product into a branch behind every load of the page
-                const float zz = fmaf(z[g], P.scale_log2, valid ? 0.f : -INFINITY);
-                const float pm = wave_max(zz);
-                float p = 0.f;
-                if (pm != -INFINITY) p = exp2f(zz - pm);
-                const uint16_t pb = f32_to_bf16(p);
-                s_p[wave][g][lane] = pb;
-                m[g] = pm;
-                l[g] = wave_sum(bf16_to_f32(pb));
-            }
-            wave_lds_sync();
-            // PV, lane = dim: each 16-byte V unit holds 8 consecutive slots of one
-            // dim, i.e. 4 key pairs, matched by 4 bf16 pairs of p (broadcast reads).
-            uint4 pn[G];
-#pragma unroll
-            for (int g = 0; g < G; ++g) pn[g] = *reinterpret_cast<const uint4*>(&s_p[wave][g][0]);
-#pragma unroll
-            for (int b = 0; b < 8; ++b) {
-                uint4 pp[G];
-#pragma unroll
-                for (int g = 0; g < G; ++g) pp[g] = pn[g];
-                if (b + 1 < 8) {
-#pragma unroll
-                    for (int g = 0; g < G; ++g) pn[g] = *reinterpret_cast<const uint4*>(&s_p[wave][g][(b + 1) * 8]);
-                }
-#pragma unroll
-                for (int g = 0; g < G; ++g) {
-#pragma unroll
-                    for (int j = 0; j < VJ; ++j) {
-                        acc[g][j] = dot2(pp[g].x, vc[b][j].x, acc[g][j]);
-                        acc[g][j] = dot2(pp[g].y, vc[b][j].y, acc[g][j]);
-                        acc[g][j] = dot2(pp[g].z, vc[b][j].z, acc[g][j]);
-                        acc[g][j] = dot2(pp[g].w, vc[b][j].w, acc[g][j]);
-                        pin(acc[g][j]);
-                    }
-                }
-            }
+            attend_page<D, G>(P, page, base, n_old, e, kc, s_q, s_p[wave], lane, m, l, acc);
         }
         if (lane == 0) {
 #pragma unroll
@@ -354,58 +429,136 @@ __global__ __launch_bounds__(256, 4) void decode_attend_kernel(DecodeArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// decode: merge partials + new token, then evict / append
+// decode, kernel 2: merge (blocks 0 .. H-1) and evict / append (blocks H .. 2H-1).
+// The two halves touch disjoint data: the merge reads the partials and the
+// inputs, the append writes the pool and the head records.  Each issues its
+// independent loads together, so a head costs two round trips to memory.
 // ---------------------------------------------------------------------------
-template <int D, int G>
-__global__ __launch_bounds__(64) void decode_merge_kernel(DecodeArgs a) {
-    constexpr int VJ = D / 64;
-    const PoolDev& P = a.pool;
-    const int lane = threadIdx.x;
-    const CallHead c = call_head(a, blockIdx.x);
-    int32_t* hs = P.hstate + (size_t)c.gh * 4;
-    const int n_old = hs[0];
-    const int n_pages = hs[1];
-    const int t = hs[2];
-    const int i0 = P.prefix[blockIdx.x], i1 = P.prefix[blockIdx.x + 1];
 
+// Log-sum-exp merge of a head's partials with the new token; bf16 output of the
+// head's G q heads.  256 threads; each owns NPAIR (q head, dim) outputs and keeps
+// a running max and sum over chunks of 16 partials.
+template <int D, int G>
+__device__ void merge_head(const DecodeArgs& a, int ch) {
+    const PoolDev& P = a.pool;
+    constexpr int NPAIR = (G * D + 255) / 256;
+    constexpr int PSTR = G * (D + 2);  // floats per partial
+    constexpr int CH = 16;
+    __shared__ float s_zn[G];
+    __shared__ float s_mc[CH][G], s_lc[CH][G];
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const CallHead c = call_head(a, ch);
+    const int i0 = P.prefix[ch];
+    const int n = P.prefix[ch + 1] - i0;
+    const float* part0 = P.partials + (size_t)i0 * PSTR;
     const uint16_t* qg = a.q + ((size_t)c.row * P.n_q_heads + c.h * G) * D;
     const uint16_t* kn = a.k + ((size_t)c.row * P.n_kv_heads + c.h) * D;
     const uint16_t* vn = a.v + ((size_t)c.row * P.n_kv_heads + c.h) * D;
-    float kf[VJ], vf[VJ];
+
+    float vnew[NPAIR];
 #pragma unroll
-    for (int j = 0; j < VJ; ++j) {
-        kf[j] = bf16_to_f32(kn[j * 64 + lane]);
-        vf[j] = bf16_to_f32(vn[j * 64 + lane]);
+    for (int r = 0; r < NPAIR; ++r) {
+        const int p = tid + r * 256;
+        vnew[r] = p < G * D ? bf16_to_f32(vn[p % D]) : 0.f;
     }
-    uint16_t* og = a.out + ((size_t)c.row * P.n_q_heads + c.h * G) * D;
-#pragma unroll
-    for (int g = 0; g < G; ++g) {
+    // new-token score of each q head (one wave per q head)
+    for (int g = wave; g < G; g += 4) {
         float dp = 0.f;
 #pragma unroll
-        for (int j = 0; j < VJ; ++j) dp = fmaf(bf16_to_f32(qg[g * D + j * 64 + lane]), kf[j], dp);
+        for (int j = 0; j < D / 64; ++j)
+            dp = fmaf(bf16_to_f32(qg[g * D + j * 64 + lane]), bf16_to_f32(kn[j * 64 + lane]), dp);
         const float zn = wave_sum(dp) * P.scale_log2;
-        float M = zn;
-        for (int i = i0; i < i1; ++i) M = fmaxf(M, P.partials[(size_t)i * (G * (D + 2)) + g]);
-        const float sn = exp2f(zn - M);
-        float L = sn;
-        float o[VJ];
-#pragma unroll
-        for (int j = 0; j < VJ; ++j) o[j] = sn * vf[j];
-        for (int i = i0; i < i1; ++i) {
-            const float* part = P.partials + (size_t)i * (G * (D + 2));
-            const float sc = exp2f(part[g] - M);
-            L = fmaf(sc, part[G + g], L);
-#pragma unroll
-            for (int j = 0; j < VJ; ++j) o[j] = fmaf(sc, part[2 * G + g * D + j * 64 + lane], o[j]);
-        }
-        const float inv = 1.f / L;
-#pragma unroll
-        for (int j = 0; j < VJ; ++j) og[g * D + j * 64 + lane] = f32_to_bf16(o[j] * inv);
+        if (lane == 0) s_zn[g] = zn;
     }
 
-    // ---- eviction decision, expiry, slot reuse / allocation, append
+    float M[NPAIR], L[NPAIR], o[NPAIR];
+#pragma unroll
+    for (int r = 0; r < NPAIR; ++r) {
+        M[r] = -INFINITY;
+        L[r] = 0.f;
+        o[r] = 0.f;
+    }
+    for (int ib = 0; ib < n; ib += CH) {
+        const int cnt = min(CH, n - ib);
+        if (tid < cnt * G) {
+            const int i = tid / G, g = tid - i * G;
+            s_mc[i][g] = part0[(size_t)(ib + i) * PSTR + g];
+            s_lc[i][g] = part0[(size_t)(ib + i) * PSTR + G + g];
+        }
+        float x[NPAIR][CH];
+#pragma unroll
+        for (int r = 0; r < NPAIR; ++r) {
+            const int p = tid + r * 256;
+#pragma unroll
+            for (int u = 0; u < CH; ++u)
+                x[r][u] = (u < cnt && p < G * D) ? part0[(size_t)(ib + u) * PSTR + 2 * G + p] : 0.f;
+        }
+        __syncthreads();
+#pragma unroll
+        for (int r = 0; r < NPAIR; ++r) {
+            const int g = min((tid + r * 256) / D, G - 1);
+            float cm = -INFINITY;
+            for (int u = 0; u < cnt; ++u) cm = fmaxf(cm, s_mc[u][g]);
+            const float mn = fmaxf(M[r], cm);
+            if (mn != -INFINITY) {
+                const float sc = exp2f(M[r] - mn);
+                o[r] *= sc;
+                L[r] *= sc;
+#pragma unroll
+                for (int u = 0; u < CH; ++u) {
+                    if (u < cnt) {
+                        const float w = exp2f(s_mc[u][g] - mn);
+                        o[r] = fmaf(w, x[r][u], o[r]);
+                        L[r] = fmaf(w, s_lc[u][g], L[r]);
+                    }
+                }
+                M[r] = mn;
+            }
+        }
+        __syncthreads();
+    }
+    __syncthreads();  // s_zn
+    uint16_t* og = a.out + ((size_t)c.row * P.n_q_heads + c.h * G) * D;
+#pragma unroll
+    for (int r = 0; r < NPAIR; ++r) {
+        const int p = tid + r * 256;
+        if (p < G * D) {
+            const float zn = s_zn[p / D];
+            const float mn = fmaxf(M[r], zn);
+            const float sc = exp2f(M[r] - mn), sn = exp2f(zn - mn);
+            og[p] = f32_to_bf16((o[r] * sc + sn * vnew[r]) / (L[r] * sc + sn));
+        }
+    }
+}
+
+// Mark the new token, expire position t-w if it was marked (its slot e is
+// reused), otherwise take slot n_old (a page from the shared pool when a new
+// page starts), write K/V, and advance the head record.  One wave.
+template <int D>
+__device__ void append_head(const DecodeArgs& a, int ch) {
+    constexpr int VJ = D / 64;
+    const PoolDev& P = a.pool;
+    const int lane = threadIdx.x & 63;
+    const CallHead c = call_head(a, ch);
+    int32_t* hs = P.hstate + (size_t)c.gh * kHS;
+    const int n_old = hs[kHsLive];
+    const int n_pages = hs[kHsPages];
+    const int t = hs[kHsPos];
+    const int e = hs[kHsExp];
+    const uint16_t* kn = a.k + ((size_t)c.row * P.n_kv_heads + c.h) * D;
+    const uint16_t* vn = a.v + ((size_t)c.row * P.n_kv_heads + c.h) * D;
+    uint4 kchunk = make_uint4(0, 0, 0, 0);
+    if (lane < D / 8) kchunk = *reinterpret_cast<const uint4*>(kn + lane * 8);
+    uint16_t vv[VJ];
+#pragma unroll
+    for (int jj = 0; jj < VJ; ++jj) vv[jj] = vn[jj * 64 + lane];
     const int mark = a.logits[(size_t)c.row * P.n_kv_heads + c.h] > 0.f ? 1 : 0;
-    const int e = expiring_slot(P, c.gh, t);
+    // the entry of position t+1-w (expires at the next step); for w = 1 that is
+    // the token written now
+    const int sx = t + 1 - P.window;
+    const int ring_next = (P.ring_len > 0 && sx >= 0 && P.window > 1)
+                              ? P.ring[(size_t)c.gh * P.ring_len + (sx % P.window)] : -1;
     int slot, n_new, np = n_pages, page;
     if (e >= 0) {
         slot = e;
@@ -436,17 +589,31 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(DecodeArgs a) {
     const int j = slot % kPage;
     uint16_t* kp = P.kpages + (size_t)page * (kPage * D);
     uint16_t* vp = P.vpages + (size_t)page * (kPage * D);
-    if (lane < D / 8)
-        *reinterpret_cast<uint4*>(kp + ((size_t)lane * kPage + j) * 8) =
-            *reinterpret_cast<const uint4*>(kn + lane * 8);
+    if (lane < D / 8) *reinterpret_cast<uint4*>(kp + ((size_t)lane * kPage + j) * 8) = kchunk;
 #pragma unroll
-    for (int jj = 0; jj < VJ; ++jj) vp[((size_t)(j / 8) * D + jj * 64 + lane) * 8 + (j % 8)] = vn[jj * 64 + lane];
+    for (int jj = 0; jj < VJ; ++jj) vp[((size_t)(j / 8) * D + jj * 64 + lane) * 8 + (j % 8)] = vv[jj];
     if (lane == 0) {
         P.slot_pos[(size_t)page * kPage + j] = t;
         if (P.ring_len > 0) P.ring[(size_t)c.gh * P.ring_len + (t % P.window)] = (slot << 1) | mark;
-        hs[0] = n_new;
-        hs[1] = np;
-        hs[2] = t + 1;
+        int e_next = -1;
+        if (P.ring_len > 0 && sx >= 0) {
+            if (P.window == 1) e_next = mark ? slot : -1;
+            else if (ring_next >= 0 && (ring_next & 1)) e_next = ring_next >> 1;
+        }
+        hs[kHsLive] = n_new;
+        hs[kHsPages] = np;
+        hs[kHsPos] = t + 1;
+        hs[kHsExp] = e_next;
+    }
+}
+
+template <int D, int G>
+__global__ __launch_bounds__(256) void decode_merge_kernel(DecodeArgs a) {
+    const int H = a.n_call_heads;
+    if ((int)blockIdx.x < H) {
+        merge_head<D, G>(a, blockIdx.x);
+    } else if (threadIdx.x < 64) {
+        append_head<D>(a, blockIdx.x - H);
     }
 }
 
@@ -484,14 +651,25 @@ __global__ __launch_bounds__(1024) void prefill_scan_kernel(PrefillArgs a) {
         }
     }
     __syncthreads();
-    int32_t* hs = P.hstate + (size_t)gh * 4;
+    int32_t* hs = P.hstate + (size_t)gh * kHS;
     if (s_base < 0) {
-        if (tid == 0) { hs[0] = 0; hs[1] = 0; hs[2] = T; hs[3] = 0; }
+        if (tid == 0)
+            for (int i = 0; i < kHS; ++i) hs[i] = i == kHsPos ? T : (i == kHsExp ? -1 : 0);
         return;
     }
     for (int j = tid; j < np; j += 1024)
         P.ptable[(size_t)gh * P.pages_per_head + j] = P.stack[s_base - 1 - j];
-    if (tid == 0) { hs[0] = n; hs[1] = np; hs[2] = T; hs[3] = 0; }
+    if (tid == 0) {
+        // the token expiring when position T is appended: T - w, if marked; it
+        // lies in the window, so its slot is n - T + (T - w)
+        int e = -1;
+        if (P.ring_len > 0 && T >= w && a.logits[(size_t)(T - w) * hkv + h] > 0.f) e = n - w;
+        for (int i = 0; i < kHS; ++i) hs[i] = 0;
+        hs[kHsLive] = n;
+        hs[kHsPages] = np;
+        hs[kHsPos] = T;
+        hs[kHsExp] = e;
+    }
     // ring entry idx holds the newest position s < T with s % w == idx (all of
     // them lie in the window, so their slots are the last ones: n - T + s)
     for (int idx = tid; idx < P.ring_len; idx += 1024) {
@@ -516,7 +694,7 @@ __global__ __launch_bounds__(256) void prefill_compact_kernel(PrefillArgs a) {
     const int pj = blockIdx.x, h = blockIdx.y;
     const int hkv = P.n_kv_heads;
     const int gh = (a.seq * P.n_layers + a.layer) * hkv + h;
-    const int n = P.hstate[(size_t)gh * 4];
+    const int n = P.hstate[(size_t)gh * kHS + kHsLive];
     if (pj * kPage >= n) return;
     const int page = P.ptable[(size_t)gh * P.pages_per_head + pj];
     const int cnt = min(kPage, n - pj * kPage);
@@ -551,27 +729,37 @@ __global__ __launch_bounds__(256) void prefill_compact_kernel(PrefillArgs a) {
 
 __global__ __launch_bounds__(64) void seq_release_kernel(PoolDev P, int seq) {
     const int gh = seq * P.n_layers * P.n_kv_heads + blockIdx.x;
-    int32_t* hs = P.hstate + (size_t)gh * 4;
-    const int np = hs[1];
+    int32_t* hs = P.hstate + (size_t)gh * kHS;
+    const int np = hs[kHsPages];
     int base = 0;
     if (threadIdx.x == 0 && np > 0) base = atomicAdd(&P.ctl[kCtlTop], np);
     base = __shfl(base, 0, 64);
     for (int j = threadIdx.x; j < np; j += 64) P.stack[base + j] = P.ptable[(size_t)gh * P.pages_per_head + j];
-    if (threadIdx.x == 0) { hs[0] = 0; hs[1] = 0; hs[2] = 0; hs[3] = 0; }
+    if (threadIdx.x == 0)
+        for (int i = 0; i < kHS; ++i) hs[i] = i == kHsExp ? -1 : 0;
 }
+
+size_t decode_shm(const DecodeArgs& a) { return (size_t)(3 * a.n_call_heads + 1) * sizeof(int32_t); }
 
 template <int D, int G>
 hipError_t launch_decode_t(const DecodeArgs& a, int grid, hipStream_t s, hipEvent_t* ev) {
-    const size_t shm = (size_t)(a.n_call_heads + 1) * sizeof(int32_t);
     hipError_t err;
     if (ev && (err = hipEventRecord(ev[0], s)) != hipSuccess) return err;
-    hipLaunchKernelGGL((decode_attend_kernel<D, G>), dim3(grid), dim3(256), shm, s, a);
+    hipLaunchKernelGGL((decode_attend_kernel<D, G>), dim3(grid), dim3(256), decode_shm(a), s, a);
     if ((err = hipGetLastError()) != hipSuccess) return err;
     if (ev && (err = hipEventRecord(ev[1], s)) != hipSuccess) return err;
-    hipLaunchKernelGGL((decode_merge_kernel<D, G>), dim3(a.n_call_heads), dim3(64), 0, s, a);
+    hipLaunchKernelGGL((decode_merge_kernel<D, G>), dim3(2 * a.n_call_heads), dim3(256), 0, s, a);
     if ((err = hipGetLastError()) != hipSuccess) return err;
     if (ev && (err = hipEventRecord(ev[2], s)) != hipSuccess) return err;
     return hipSuccess;
+}
+
+template <int D, int G>
+int blocks_per_cu_t(const DecodeArgs& a) {
+    int n = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_attend_kernel<D, G>, 256, decode_shm(a)) != hipSuccess)
+        return 1;
+    return n > 0 ? n : 1;
 }
 
 template <int D>
@@ -585,12 +773,27 @@ hipError_t launch_decode_d(const DecodeArgs& a, int grid, hipStream_t s, hipEven
     return hipErrorInvalidValue;
 }
 
+template <int D>
+int blocks_per_cu_d(const DecodeArgs& a) {
+    switch (a.pool.n_q_heads / a.pool.n_kv_heads) {
+        case 1: return blocks_per_cu_t<D, 1>(a);
+        case 2: return blocks_per_cu_t<D, 2>(a);
+        case 4: return blocks_per_cu_t<D, 4>(a);
+        case 8: return blocks_per_cu_t<D, 8>(a);
+    }
+    return 1;
+}
+
 }  // namespace
 
 hipError_t launch_decode(const DecodeArgs& a, int grid, hipStream_t s, hipEvent_t* ev) {
     if (a.pool.head_dim == 128) return launch_decode_d<128>(a, grid, s, ev);
     if (a.pool.head_dim == 64) return launch_decode_d<64>(a, grid, s, ev);
     return hipErrorInvalidValue;
+}
+
+int decode_blocks_per_cu(const DecodeArgs& a) {
+    return a.pool.head_dim == 128 ? blocks_per_cu_d<128>(a) : blocks_per_cu_d<64>(a);
 }
 
 hipError_t launch_prefill_compact(const PrefillArgs& a, hipStream_t s) {

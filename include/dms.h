@@ -163,11 +163,11 @@ dms_status dms_export_live(dms_pool* pool, int32_t seq, int32_t layer, int32_t k
 dms_status dms_seq_release(dms_pool* pool, int32_t seq, void* stream);
 
 /* Kernel timing for measurement.  While enabled, every decode launch records
- * HIP events on its stream around its attention kernel and around its merge /
- * append kernel.  dms_timing_read synchronises, adds up the elapsed times of all
- * launches recorded since the last read (milliseconds) and how many there were,
- * and releases the events.  Disabled by default; enabling adds an event record
- * between kernels. */
+ * HIP events on its stream before its attention kernel, between that kernel and
+ * its merge / append kernel, and after the latter.  dms_timing_read
+ * synchronises, adds up the elapsed times of all launches recorded since the
+ * last read (milliseconds) and how many there were, and releases the events.
+ * Disabled by default; enabling adds three event records per launch. */
 dms_status dms_timing_enable(dms_pool* pool, int32_t enable);
 dms_status dms_timing_read(dms_pool* pool, double* attend_ms, double* merge_ms, int64_t* launches);
 

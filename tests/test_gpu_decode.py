@@ -200,3 +200,12 @@ def test_host_side_errors():
         dms.dms_decode_step(r.pool.handle, [0], 1, 2, 1, 1, 1, 1, 1, 0)
     assert ei.value.status == dms.DMS_E_INVAL
     r.close()
+
+
+def test_many_items_per_head_across_blocks():
+    """Long live sets (many split-K items per head, merged by whichever block
+    finishes last) on several layers and sequences, every step checked."""
+    case = Case(n_layers=4, n_q_heads=16, n_kv_heads=4, head_dim=128, window=100,
+                ctx_lens=[3000, 5000, 1500], steps=12, seed=31, keep_mu=0.5)
+    r, _ = run_case(case, check_live_every=6)
+    r.close()
