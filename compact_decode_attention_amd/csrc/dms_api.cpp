@@ -28,7 +28,7 @@ dms_status hip_fail(hipError_t e, const char* what) {
 constexpr size_t kAlign = 256;
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
-enum Section { S_K, S_V, S_POS, S_STACK, S_HSTATE, S_PTABLE, S_RING, S_PART, S_PREFIX, S_INV, S_CTL, S_N };
+enum Section { S_K, S_V, S_POS, S_STACK, S_HSTATE, S_PTABLE, S_RING, S_PART, S_PREFIX, S_INV, S_PCNT, S_VT, S_CTL, S_N };
 
 struct Layout {
     size_t off[S_N + 1];
@@ -75,6 +75,8 @@ bool make_layout(const dms_pool_config* c, Layout* L, std::string* why) {
     sz[S_PART] = (size_t)L->max_items * g * (D + 2) * 4;
     sz[S_PREFIX] = (size_t)(L->max_call_heads + 1) * 4;
     sz[S_INV] = (size_t)c->n_kv_heads * c->max_positions * 4;
+    sz[S_PCNT] = sz[S_INV];
+    sz[S_VT] = (size_t)c->n_kv_heads * ((c->max_positions + 31) / 32 * 32) * D * 2;
     sz[S_CTL] = 64 * 4;
     size_t o = 0;
     for (int i = 0; i < S_N; ++i) {
@@ -153,6 +155,8 @@ dms_status dms_pool_create(const dms_pool_config* cfg, void* arena, size_t arena
     d.partials = reinterpret_cast<float*>(a + L.off[S_PART]);
     d.prefix = reinterpret_cast<int32_t*>(a + L.off[S_PREFIX]);
     d.inv = reinterpret_cast<int32_t*>(a + L.off[S_INV]);
+    d.pcnt = reinterpret_cast<int32_t*>(a + L.off[S_PCNT]);
+    d.vt = reinterpret_cast<uint16_t*>(a + L.off[S_VT]);
     d.ctl = reinterpret_cast<int32_t*>(a + L.off[S_CTL]);
     d.max_pages = cfg->max_pages;
     d.n_layers = cfg->n_layers;
@@ -163,6 +167,7 @@ dms_status dms_pool_create(const dms_pool_config* cfg, void* arena, size_t arena
     d.ring_len = L.ring_len;
     d.pages_per_head = L.pages_per_head;
     d.max_positions = cfg->max_positions;
+    d.max_pos32 = (cfg->max_positions + 31) / 32 * 32;
     d.max_items = L.max_items;
     const double scale = cfg->softmax_scale > 0.f ? (double)cfg->softmax_scale : 1.0 / std::sqrt((double)cfg->head_dim);
     d.scale_log2 = (float)(scale * 1.4426950408889634);

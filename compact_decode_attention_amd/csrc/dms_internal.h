@@ -16,6 +16,11 @@
 //   partials f32   [max_items][G*(head_dim+2)]     split-K partials {m[G], l[G], acc[G][D]}
 //   prefix   int32 [max_call_heads + 1]            first split-K item of each head (last launch)
 //   inv      int32 [n_kv_heads][max_positions]     prefill scratch: slot -> position
+//   pcnt     int32 [n_kv_heads][max_positions]     prefill scratch: live tokens in [0, s]
+//   vt       bf16 [n_kv_heads][max_pos32/8][head_dim][8]
+//                                                  prefill scratch: the prompt's V with 8
+//                                                  consecutive tokens per 16 bytes
+//                                                  (max_pos32 = max_positions rounded up to 32)
 //   ctl      int32 [64]                            pool counters (kCtl* below)
 // heads = max_seqs * n_layers * n_kv_heads, head id = (seq * n_layers + layer) * n_kv_heads + h.
 #pragma once
@@ -66,10 +71,12 @@ struct PoolDev {
     float* partials;
     int32_t* prefix;
     int32_t* inv;
+    int32_t* pcnt;
+    uint16_t* vt;
     int32_t* ctl;
     int64_t max_pages;
     int32_t n_layers, n_q_heads, n_kv_heads, head_dim;
-    int32_t window, ring_len, pages_per_head, max_positions;
+    int32_t window, ring_len, pages_per_head, max_positions, max_pos32;
     int32_t max_items;
     float scale_log2;  // softmax scale * log2(e): scores are kept in base-2 units
 };

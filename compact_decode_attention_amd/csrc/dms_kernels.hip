@@ -194,7 +194,7 @@ __device__ __forceinline__ void load_k_page(const PoolDev& P, int page, bool liv
 template <int D, int G>
 __device__ __forceinline__ void attend_page(const PoolDev& P, int page, int base, int n_old, int e,
                                             const uint4 (&kc)[D / 8], const uint32_t (*s_q)[D / 2],
-                                            uint16_t (*s_p)[kPage], int lane, float (&m)[G], float (&l)[G],
+                                            uint16_t (*s_p)[G][kPage], int lane, float (&m)[G], float (&l)[G],
                                             float (&acc)[G][D / 64]) {
     constexpr int NC = D / 8;   // 16-byte K chunks per slot
     constexpr int VJ = D / 64;  // dims per lane in PV
@@ -240,37 +240,44 @@ __device__ __forceinline__ void attend_page(const PoolDev& P, int page, int base
             p = exp2f(zz - mn);
             alpha = exp2f(m[g] - mn);
         }
-        const uint16_t pb = f32_to_bf16(p);
-        s_p[g][lane] = pb;
-        l[g] = l[g] * alpha + wave_sum(bf16_to_f32(pb));
+        // P enters the PV dot products as two bf16 parts, hi = bf16(p) and
+        // lo = bf16(p - hi): about 16 significant bits, fp32 accumulation
+        const uint16_t ph = f32_to_bf16(p);
+        s_p[0][g][lane] = ph;
+        s_p[1][g][lane] = f32_to_bf16(p - bf16_to_f32(ph));
+        l[g] = l[g] * alpha + wave_sum(p);
         m[g] = mn;
 #pragma unroll
         for (int j = 0; j < VJ; ++j) acc[g][j] *= alpha;
     }
     wave_lds_sync();
     // PV, lane = dim: each 16-byte V unit holds 8 consecutive slots of one dim,
-    // i.e. 4 key pairs, matched by 4 bf16 pairs of p (broadcast reads).
-    uint4 pn[G];
+    // i.e. 4 key pairs, matched by 4 bf16 pairs of p (broadcast reads), once for
+    // the high and once for the low part of p.
 #pragma unroll
-    for (int g = 0; g < G; ++g) pn[g] = *reinterpret_cast<const uint4*>(&s_p[g][0]);
+    for (int part = 0; part < 2; ++part) {
+        uint4 pn[G];
 #pragma unroll
-    for (int b = 0; b < 8; ++b) {
-        uint4 pp[G];
+        for (int g = 0; g < G; ++g) pn[g] = *reinterpret_cast<const uint4*>(&s_p[part][g][0]);
 #pragma unroll
-        for (int g = 0; g < G; ++g) pp[g] = pn[g];
-        if (b + 1 < 8) {
+        for (int b = 0; b < 8; ++b) {
+            uint4 pp[G];
 #pragma unroll
-            for (int g = 0; g < G; ++g) pn[g] = *reinterpret_cast<const uint4*>(&s_p[g][(b + 1) * 8]);
-        }
+            for (int g = 0; g < G; ++g) pp[g] = pn[g];
+            if (b + 1 < 8) {
 #pragma unroll
-        for (int g = 0; g < G; ++g) {
+                for (int g = 0; g < G; ++g) pn[g] = *reinterpret_cast<const uint4*>(&s_p[part][g][(b + 1) * 8]);
+            }
 #pragma unroll
-            for (int j = 0; j < VJ; ++j) {
-                acc[g][j] = dot2(pp[g].x, vc[b][j].x, acc[g][j]);
-                acc[g][j] = dot2(pp[g].y, vc[b][j].y, acc[g][j]);
-                acc[g][j] = dot2(pp[g].z, vc[b][j].z, acc[g][j]);
-                acc[g][j] = dot2(pp[g].w, vc[b][j].w, acc[g][j]);
-                pin(acc[g][j]);
+            for (int g = 0; g < G; ++g) {
+#pragma unroll
+                for (int j = 0; j < VJ; ++j) {
+                    acc[g][j] = dot2(pp[g].x, vc[b][j].x, acc[g][j]);
+                    acc[g][j] = dot2(pp[g].y, vc[b][j].y, acc[g][j]);
+                    acc[g][j] = dot2(pp[g].z, vc[b][j].z, acc[g][j]);
+                    acc[g][j] = dot2(pp[g].w, vc[b][j].w, acc[g][j]);
+                    pin(acc[g][j]);
+                }
             }
         }
     }
@@ -300,7 +307,7 @@ __global__ __launch_bounds__(256, 4) void decode_attend_kernel(DecodeArgs a) {
     int32_t* s_nold = s_dyn + H + 1;    // [H] live count before this step
     int32_t* s_exp = s_nold + H;        // [H] slot expiring at this step, or -1
     __shared__ uint32_t s_q[G][D / 2];
-    __shared__ uint16_t s_p[NW][G][kPage];
+    __shared__ uint16_t s_p[NW][2][G][kPage];  // per wave: p high and low parts
     __shared__ float s_m[NW][G], s_l[NW][G];
     __shared__ float s_acc[NW][G][D];
     __shared__ int s_scan[2 * NW + 1];
@@ -637,8 +644,11 @@ __global__ __launch_bounds__(1024) void prefill_scan_kernel(PrefillArgs a) {
     int n;
     int off = block_excl_scan<1024>(cnt, &n, s_scan);
     int32_t* inv = P.inv + (size_t)h * P.max_positions;
-    for (int s = s0; s < s1; ++s)
+    int32_t* pcnt = P.pcnt + (size_t)h * P.max_positions;
+    for (int s = s0; s < s1; ++s) {
         if (s >= T - w || !(a.logits[(size_t)s * hkv + h] > 0.f)) inv[off++] = s;
+        pcnt[s] = off;  // live tokens in [0, s]
+    }
     const int np = (n + kPage - 1) / kPage;
     if (tid == 0) {
         const int old = atomicSub(&P.ctl[kCtlTop], np);

@@ -1,0 +1,108 @@
+"""GPU parity of dms_prefill with output (masked causal attention on MFMA plus
+compaction) against the oracle: every query row within tolerance, live sets
+after the prefill exact, and decode continuing correctly from the compacted
+store."""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from dms_case import assert_close
+
+pytestmark = pytest.mark.gpu
+
+
+def bf(a, torch):
+    return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16)
+
+
+def make_inputs(T, Hq, Hkv, D, seed, marks):
+    q = synth.normal_bf16(seed, synth.stream_id(synth.TAG_Q), 0, T * Hq * D).reshape(T, Hq, D)
+    k = synth.normal_bf16(seed, synth.stream_id(synth.TAG_K), 0, T * Hkv * D).reshape(T, Hkv, D)
+    v = synth.normal_bf16(seed, synth.stream_id(synth.TAG_V), 0, T * Hkv * D).reshape(T, Hkv, D)
+    if marks == "all":
+        lg = np.ones((T, Hkv), np.float32)
+    elif marks == "none":
+        lg = -np.ones((T, Hkv), np.float32)
+    else:
+        z = synth.normal_f32(seed, synth.stream_id(synth.TAG_SCORE), 0, T * Hkv).reshape(T, Hkv)
+        lg = (-(-0.3 + z.astype(np.float64))).astype(np.float32)
+    return q, k, v, lg
+
+
+def run_prefill(T, w, marks, G=4, D=128, Hkv=2, seed=5, extra_positions=0, decode_steps=0):
+    import torch
+    import compact_decode_attention_amd as dms
+    Hq = G * Hkv
+    total = T + decode_steps
+    q, k, v, lg = make_inputs(total, Hq, Hkv, D, seed, marks)
+    maxpos = total + extra_positions
+    pool = dms.Pool(n_layers=1, n_q_heads=Hq, n_kv_heads=Hkv, head_dim=D, window=w, max_seqs=1,
+                    max_positions=maxpos, max_pages=Hkv * ((maxpos + 63) // 64))
+    dev = "cuda"
+    out = torch.empty((T, Hq, D), dtype=torch.bfloat16, device=dev)
+    pool.prefill(0, 0, bf(k[:T], torch).to(dev), bf(v[:T], torch).to(dev), torch.from_numpy(lg[:T]).to(dev),
+                 q=bf(q[:T], torch).to(dev), out=out)
+    got = out.view(torch.int16).cpu().numpy().view(np.uint16)
+    mk = oracle.marks(lg)
+    ref = oracle.attend(q[:T], np.arange(T), k[:T], v[:T], mk[:T], w)
+    assert_close(got, ref, "prefill T=%d w=%d marks=%s G=%d D=%d" % (T, w, marks, G, D))
+    for h in range(Hkv):
+        assert np.array_equal(pool.export_live(0, 0, h), oracle.live_positions(T - 1, w, mk[:T, h]))
+    for i in range(decode_steps):
+        t = T + i
+        o = torch.empty((1, 1, Hq, D), dtype=torch.bfloat16, device=dev)
+        pool.decode_step([0], 0, bf(q[t], torch).to(dev).view(1, 1, Hq, D), bf(k[t], torch).to(dev).view(1, 1, Hkv, D),
+                         bf(v[t], torch).to(dev).view(1, 1, Hkv, D), torch.from_numpy(lg[t]).to(dev).view(1, 1, Hkv), o)
+        r = oracle.attend(q[t:t + 1], [t], k[:t + 1], v[:t + 1], mk[:t + 1], w)[0]
+        assert_close(o.view(torch.int16).cpu().numpy().view(np.uint16)[0, 0], r, "decode after prefill t=%d" % t)
+    pool.close()
+
+
+@pytest.mark.parametrize("marks", ["random", "all", "none"])
+@pytest.mark.parametrize("w", [1, 16, 64])
+@pytest.mark.parametrize("T", [1, 31, 33, 130, 700])
+def test_prefill_shapes(T, w, marks):
+    run_prefill(T, w, marks)
+
+
+@pytest.mark.parametrize("T", [64, 500])
+def test_prefill_eviction_disabled(T):
+    """Window beyond every position: plain causal attention."""
+    run_prefill(T, 1 << 20, "random")
+
+
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("G", [1, 2, 4, 8])
+def test_prefill_group_sizes(G, D):
+    run_prefill(300, 40, "random", G=G, D=D, seed=G * 10 + D)
+
+
+def test_prefill_then_decode():
+    run_prefill(257, 32, "random", decode_steps=40, seed=9)
+
+
+def test_prefill_32k_sampled_rows():
+    """Qwen3-8B-shaped prefill of one layer: 32768 tokens, 32 q / 8 kv heads,
+    D=128, w=512, keep score N(-1.2, 1); sampled query rows vs the oracle."""
+    import torch
+    import compact_decode_attention_amd as dms
+    wl = synth.WORKLOADS["qwen3-8b_prefill32k"]
+    inp = synth.SynthInputs(wl)
+    T, Hq, Hkv, D, w = wl.ctx_len, wl.n_q_heads, wl.n_kv_heads, wl.head_dim, wl.window
+    q, k, v, lg = inp.q(0, 0, 0, T), inp.k(0, 0, 0, T), inp.v(0, 0, 0, T), inp.logits(0, 0, 0, T)
+    pool = dms.Pool(n_layers=1, n_q_heads=Hq, n_kv_heads=Hkv, head_dim=D, window=w, max_seqs=1,
+                    max_positions=T, max_pages=Hkv * (T // 64))
+    out = torch.empty((T, Hq, D), dtype=torch.bfloat16, device="cuda")
+    pool.prefill(0, 0, bf(k, torch).cuda(), bf(v, torch).cuda(), torch.from_numpy(lg).cuda(),
+                 q=bf(q, torch).cuda(), out=out)
+    got = out.view(torch.int16).cpu().numpy().view(np.uint16)
+    rng = np.random.default_rng(0)
+    rows = sorted(set([0, 1, 31, 32, 511, 512, 513, 1000, T - 33, T - 32, T - 1] +
+                      rng.integers(0, T, 24).tolist()))
+    mk = oracle.marks(lg)
+    ref = oracle.attend(q[rows], np.array(rows), k, v, mk, w)
+    assert_close(got[rows], ref, "prefill 32k rows")
+    for h in range(Hkv):
+        assert np.array_equal(pool.export_live(0, 0, h), oracle.live_positions(T - 1, w, mk[:, h]))
+    pool.close()
