@@ -1,18 +1,22 @@
 #!/usr/bin/env python
-"""DMS compact decode benchmark on one MI355X.
+"""DMS compact decode (and prefill) benchmark on one MI355X.
 
-Workload (default): Qwen3-8B-shaped decode -- 36 layers, 32 q / 8 kv heads,
-head_dim 128, bf16 K/V/Q ~ N(0,1), batch 1, an 8192-token prompt compacted by
-prefill, then 128 decode steps (positions 8192..8319), delay window w = 512,
-per-(layer, kv head) keep-score mean ~ U(-2, 0) (keep rates ~2%-50%).  All inputs
-are seeded synthetic data (synth/), resident in HBM before timing starts.
+Decode workload (the headline): Qwen3-8B-shaped decode -- 36 layers, 32 q / 8 kv
+heads, head_dim 128, bf16 K/V/Q ~ N(0,1), batch 1, an 8192-token prompt
+compacted by prefill, then 128 decode steps (positions 8192..8319), delay window
+w = 512, per-(layer, kv head) keep-score mean ~ U(-2, 0) (keep rates ~2%-50%).
+All inputs are seeded synthetic data (synth/), resident in HBM before timing.
 
 A step is one token through the whole DMS decode path of every layer: eviction
 decision, expiry, slot reclaim, K/V append and split-K attention with merge.
 `value` is decode tokens per second with one dms_decode_step call per token that
 covers all 36 layers (their inputs are independent in this synthetic workload).
-Two model-faithful modes are timed beside it and reported under "modes": one
-call per layer (36 calls per token) and a HIP graph of those 36 calls.
+Two model-faithful modes are timed beside it ("modes"): one call per layer (36
+calls per token) and a HIP graph of those 36 calls.
+
+Prefill leg ("prefill"): Qwen3-8B-shaped DMS prefill of one 32768-token prompt
+(32 q / 8 kv heads, D=128, w=512, keep score N(-1.2,1)), one layer's inputs
+prefilled into 36 layer slots: masked causal attention on MFMA plus compaction.
 
 Prints one JSON line.  --gpus N with N > 1 exits: this build runs on one GPU.
 """
@@ -32,6 +36,7 @@ sys.path.insert(0, ROOT)
 import synth  # noqa: E402
 
 HBM_PEAK_GBPS = 8000.0
+MFMA_BF16_PEAK_TFLOPS = 2500.0
 METRIC = "DMS compact decode tok/s + achieved HBM GB/s (% peak), Qwen3-8B shape, 8K ctx"
 
 
@@ -39,81 +44,57 @@ def log(*a):
     print("[bench]", *a, file=sys.stderr, flush=True)
 
 
-def live_count_series(logits_hd, ctx, steps, window):
-    """Live tokens per head after each decode step t = ctx .. ctx+steps-1, from the
-    logits (byte accounting only): #{s <= t-w : logit_s <= 0} + min(t+1, w)."""
-    unmarked = (logits_hd <= 0).astype(np.int64)            # [T_total]
-    csum = np.concatenate([[0], np.cumsum(unmarked)])        # csum[i] = #unmarked in [0, i)
-    out = np.empty(steps, np.int64)
-    for i in range(steps):
-        t = ctx + i
-        out[i] = csum[max(t - window + 1, 0)] + min(t + 1, window)
-    return out
+def live_counts(logits_hd, t_values, window):
+    """Live tokens of one head at each query position t (byte / flop accounting):
+    #{s <= t-w : logit_s <= 0} + min(t+1, w)."""
+    unmarked = (logits_hd <= 0).astype(np.int64)
+    csum = np.concatenate([[0], np.cumsum(unmarked)])  # csum[i] = #unmarked in [0, i)
+    t = np.asarray(t_values, np.int64)
+    return csum[np.maximum(t - window + 1, 0)] + np.minimum(t + 1, window)
 
 
-def main():
-    ap = argparse.ArgumentParser()
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=128, help="timed decode steps (tokens)")
-    ap.add_argument("--warmup", type=int, default=8)
-    ap.add_argument("--workload", default="qwen3-8b_ctx8192")
-    ap.add_argument("--modes", default="batched,per_layer,graph")
-    ap.add_argument("--cpu-baseline-steps", type=int, default=32,
-                    help="decode steps of the oracle sample (all layers); 0 disables")
-    ap.add_argument("--no-timing-pass", action="store_true")
-    args = ap.parse_args()
+def bf16_tensor(a, torch):
+    return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16)
 
-    if args.gpus != 1:
-        print("bench.py runs on one GPU only (this build has no multi-GPU path); got --gpus %d"
-              % args.gpus, file=sys.stderr)
-        sys.exit(2)
 
-    import torch
-    import compact_decode_attention_amd as dms
-
+# ---------------------------------------------------------------------------
+# decode
+# ---------------------------------------------------------------------------
+def bench_decode(args, torch, dms):
     wl = synth.WORKLOADS[args.workload]
-    if wl.prefill_only:
-        raise SystemExit("workload %s is a prefill workload" % wl.name)
+    if wl.prefill_only or wl.n_seqs != 1:
+        raise SystemExit("decode workload must be a single-sequence decode workload")
     inp = synth.SynthInputs(wl)
     L, Hq, H, D, w = wl.n_layers, wl.n_q_heads, wl.n_kv_heads, wl.head_dim, wl.window
-    B = wl.n_seqs
-    if B != 1:
-        raise SystemExit("batched workloads are timed by bench_batched (not in this script yet)")
     ctx = int(inp.ctx_lens()[0])
     K, W = args.steps, args.warmup
     if K > wl.gen_len:
         raise SystemExit("--steps beyond the workload's %d generated tokens" % wl.gen_len)
-    total = ctx + max(K, W)
+    S_all = max(K, W)
+    total = ctx + S_all
     dev = torch.device("cuda:0")
 
-    # ---- inputs (host generation, then resident on the device)
     t0 = time.time()
-    bf = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16)
-    pk, pv, plg = [], [], []
-    host_k, host_v, host_lg = [], [], []
+    pk, pv, plg, host_k, host_v, host_lg = [], [], [], [], [], []
     for l in range(L):
-        k = inp.k(0, l, 0, total)
-        v = inp.v(0, l, 0, total)
-        lg = inp.logits(0, l, 0, total)
+        k, v, lg = inp.k(0, l, 0, total), inp.v(0, l, 0, total), inp.logits(0, l, 0, total)
         host_k.append(k)
         host_v.append(v)
         host_lg.append(lg)
-        pk.append(bf(k[:ctx]).to(dev))
-        pv.append(bf(v[:ctx]).to(dev))
+        pk.append(bf16_tensor(k[:ctx], torch).to(dev))
+        pv.append(bf16_tensor(v[:ctx], torch).to(dev))
         plg.append(torch.from_numpy(lg[:ctx]).to(dev))
-    steps_all = max(K, W)
-    q_host = np.stack([inp.q(0, l, ctx, steps_all) for l in range(L)], axis=1)       # [S][L][Hq][D]
-    dq = bf(q_host).to(dev).view(steps_all, L, 1, Hq, D)
-    dk = bf(np.stack([hk[ctx:ctx + steps_all] for hk in host_k], axis=1)).to(dev).view(steps_all, L, 1, H, D)
-    dv = bf(np.stack([hv[ctx:ctx + steps_all] for hv in host_v], axis=1)).to(dev).view(steps_all, L, 1, H, D)
-    dl = torch.from_numpy(np.stack([hl[ctx:ctx + steps_all] for hl in host_lg], axis=1)).to(dev).view(steps_all, L, 1, H)
-    dout = torch.empty((steps_all, L, 1, Hq, D), dtype=torch.bfloat16, device=dev)
+    q_host = np.stack([inp.q(0, l, ctx, S_all) for l in range(L)], axis=1)  # [S][L][Hq][D]
+    dq = bf16_tensor(q_host, torch).to(dev).view(S_all, L, 1, Hq, D)
+    dk = bf16_tensor(np.stack([x[ctx:total] for x in host_k], axis=1), torch).to(dev).view(S_all, L, 1, H, D)
+    dv = bf16_tensor(np.stack([x[ctx:total] for x in host_v], axis=1), torch).to(dev).view(S_all, L, 1, H, D)
+    dl = torch.from_numpy(np.stack([x[ctx:total] for x in host_lg], axis=1)).to(dev).view(S_all, L, 1, H)
+    dout = torch.empty((S_all, L, 1, Hq, D), dtype=torch.bfloat16, device=dev)
     torch.cuda.synchronize()
-    log("inputs ready in %.1fs (ctx %d, %d layers)" % (time.time() - t0, ctx, L))
+    log("decode inputs ready in %.1fs (ctx %d, %d layers)" % (time.time() - t0, ctx, L))
 
-    max_pages = L * H * ((total + 63) // 64)
     pool = dms.Pool(n_layers=L, n_q_heads=Hq, n_kv_heads=H, head_dim=D, window=w, max_seqs=1,
-                    max_positions=total, max_pages=max_pages, device=dev)
+                    max_positions=total, max_pages=L * H * ((total + 63) // 64), device=dev)
     stream = torch.cuda.current_stream(dev)
 
     def reset():
@@ -131,12 +112,11 @@ def main():
                              dout[i, l:l + 1])
 
     # graph mode: static buffers, 36 captured per-layer calls, inputs copied in per step
-    sq = torch.empty_like(dq[0]); sk = torch.empty_like(dk[0]); sv = torch.empty_like(dv[0])
-    sl = torch.empty_like(dl[0]); so = torch.empty_like(dout[0])
-    graph = None
+    sq, sk, sv = torch.empty_like(dq[0]), torch.empty_like(dk[0]), torch.empty_like(dv[0])
+    sl, so = torch.empty_like(dl[0]), torch.empty_like(dout[0])
+    graph = [None]
 
     def capture_graph():
-        nonlocal graph
         g = torch.cuda.CUDAGraph()
         side = torch.cuda.Stream(device=dev)
         side.wait_stream(stream)
@@ -145,138 +125,214 @@ def main():
                 for l in range(L):
                     pool.decode_step([0], l, sq[l:l + 1], sk[l:l + 1], sv[l:l + 1], sl[l:l + 1], so[l:l + 1])
         stream.wait_stream(side)
-        graph = g
+        graph[0] = g
 
     def run_graph(i):
         sq.copy_(dq[i]); sk.copy_(dk[i]); sv.copy_(dv[i]); sl.copy_(dl[i])
-        graph.replay()
+        graph[0].replay()
         dout[i].copy_(so)
 
     runners = {"batched": run_batched, "per_layer": run_per_layer, "graph": run_graph}
     modes = [m for m in args.modes.split(",") if m]
-    results = {}
+    results, outs = {}, {}
     for mode in modes:
         fn = runners[mode]
         reset()
         if mode == "graph":
-            # capturing advances nothing on the device (no launch runs); positions
-            # live on the device, so each replay steps every layer once
-            capture_graph()
+            capture_graph()  # nothing runs during capture; positions live on the device
             reset()
         for i in range(W):
             fn(i)
-        torch.cuda.synchronize()
         reset()
+        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize()
-        ev0 = torch.cuda.Event(enable_timing=True)
-        ev1 = torch.cuda.Event(enable_timing=True)
         ev0.record(stream)
-        tw0 = time.perf_counter()
         for i in range(K):
             fn(i)
         ev1.record(stream)
         torch.cuda.synchronize()
-        wall = time.perf_counter() - tw0
         ms = ev0.elapsed_time(ev1)
-        st, live = pool.stats(0, per_head=True)
-        results[mode] = {"ms_total": ms, "ms_per_step": ms / K, "tok_per_s": K * B / (ms / 1e3),
-                         "wall_s": wall, "live_slots_end": int(st.live_slots)}
-        if mode == "batched":
-            out_batched = dout[:K].clone()
-        log("%s: %.4f ms/step, %.1f tok/s" % (mode, ms / K, K / (ms / 1e3)))
+        st, _ = pool.stats(0)
+        results[mode] = {"ms_per_step": ms / K, "tok_per_s": K / (ms / 1e3), "live_slots_end": int(st.live_slots)}
+        outs[mode] = dout[:K].clone()
+        log("decode %s: %.4f ms/step, %.1f tok/s" % (mode, ms / K, K / (ms / 1e3)))
+    same = all(torch.equal(outs[m], outs[modes[0]]) for m in modes)
 
-    # consistency: every mode produced the same bf16 outputs as the batched mode
-    # (re-run batched last so dout holds its outputs)
-    if "batched" in results and len(results) > 1:
-        results["outputs_identical_across_modes"] = True  # verified in tests; see parity suite
-
-    # ---- byte accounting
-    live_series = np.stack([np.stack([live_count_series(host_lg[l][:, h], ctx, K, w) for h in range(H)])
-                            for l in range(L)])  # [L][H][K]
+    # byte accounting from the logits: live slots read per step (the new token
+    # comes from the inputs), q, out, k/v append, logits
+    live = np.stack([np.stack([live_counts(host_lg[l][:, h], np.arange(ctx, ctx + K), w) for h in range(H)])
+                     for l in range(L)])  # [L][H][K]
     st, live_end = pool.stats(0, per_head=True)
-    if not np.array_equal(live_series[:, :, -1], live_end):
-        log("WARNING: live counts differ from the expected series")
-    kv_read = int(np.sum(live_series - 1)) * 2 * D * 2          # live slots minus the new token, K+V
+    assert np.array_equal(live[:, :, -1], live_end), "live counts differ from the logits"
+    kv_read = int(np.sum(live - 1)) * 2 * D * 2
     q_bytes = K * L * Hq * D * 2
-    step_bytes_total = kv_read + q_bytes + K * L * (Hq * D * 2 + H * 2 * D * 2 * 2 + H * 4)
-    # the attention kernel reads the live K/V (all but the new token) and q
-    attend_bytes_per_launch = (kv_read + q_bytes) / K
+    step_bytes = kv_read + q_bytes + K * L * (Hq * D * 2 + H * 2 * D * 2 * 2 + H * 4)
+    attend_bytes = (kv_read + q_bytes) / K  # per launch of the attention kernel
 
     roofline = None
-    if not args.no_timing_pass and "batched" in results:
+    if not args.no_timing_pass:
         reset()
         dms.dms_timing_enable(pool.handle, True)
-        ev0 = torch.cuda.Event(enable_timing=True)
-        ev1 = torch.cuda.Event(enable_timing=True)
-        ev0.record(stream)
         for i in range(K):
             run_batched(i)
-        ev1.record(stream)
-        torch.cuda.synchronize()
-        att_ms, mer_ms, n = dms.dms_timing_read(pool.handle)
+        tm = dms.dms_timing_read(pool.handle)
         dms.dms_timing_enable(pool.handle, False)
-        avg_att, avg_mer = att_ms / n, mer_ms / n
-        achieved = attend_bytes_per_launch / (avg_att / 1e3) / 1e9
+        n = tm.decode_launches
+        avg_att, avg_mer = tm.decode_attend_ms / n, tm.decode_merge_ms / n
+        achieved = attend_bytes / (avg_att / 1e3) / 1e9
         roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                     "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None,
-                    "kernel": "decode_attend_kernel<128,4>",
-                    "avg_launch_us": round(avg_att * 1e3, 2),
-                    "bytes_per_launch": int(attend_bytes_per_launch),
-                    "merge_kernel_avg_launch_us": round(avg_mer * 1e3, 2),
-                    "launches": int(n), "timed_ms_with_events": round(ev0.elapsed_time(ev1), 4)}
-        log("attend kernel: %.2f us/launch, %.1f GB/s (%.1f%% of peak); merge kernel %.2f us"
+                    "kernel": "decode_attend_kernel<128,4>", "avg_launch_us": round(avg_att * 1e3, 2),
+                    "bytes_per_launch": int(attend_bytes), "launches": int(n),
+                    "merge_kernel_avg_launch_us": round(avg_mer * 1e3, 2)}
+        log("decode attend kernel: %.2f us/launch, %.1f GB/s (%.1f%% of peak); merge kernel %.2f us"
             % (avg_att * 1e3, achieved, 100 * achieved / HBM_PEAK_GBPS, avg_mer * 1e3))
 
-    # ---- CPU baseline: the oracle on a bounded sample (first S steps, all layers)
     cpu = None
     S = min(args.cpu_baseline_steps, K)
     if S > 0:
-        import oracle
+        import oracle  # the CPU baseline is the oracle, timed as it stands
         cores = int(os.environ.get("OMP_NUM_THREADS", len(os.sched_getaffinity(0))))
         marks = [oracle.marks(host_lg[l]) for l in range(L)]
         tc = time.perf_counter()
         for i in range(S):
             t = ctx + i
             for l in range(L):
-                oracle.attend(q_host[i, l][None], [t], host_k[l][:t + 1], host_v[l][:t + 1],
-                              marks[l][:t + 1], w)
+                oracle.attend(q_host[i, l][None], [t], host_k[l][:t + 1], host_v[l][:t + 1], marks[l][:t + 1], w)
         cpu_s = time.perf_counter() - tc
         cpu = {"value": round(S / cpu_s, 3), "unit": "tok/s", "cores": cores, "kind": "oracle",
-               "sample": "first %d of the %d decode steps, all %d layers, 32 q heads each (full "
-                         "uncompressed K/V with the visibility mask), %.1f s" % (S, K, L, cpu_s)}
+               "sample": "%s: the first %d of the %d decode steps, all %d layers x %d q heads, masked "
+                         "attention over the full uncompressed K/V; %.1f s" % (wl.name, S, K, L, Hq, cpu_s)}
         log("cpu oracle: %.2f tok/s on %d threads" % (S / cpu_s, cores))
 
-    main_mode = "batched" if "batched" in results else modes[0]
-    ms_step = results[main_mode]["ms_per_step"]
-    value = results[main_mode]["tok_per_s"]
+    main = "batched" if "batched" in results else modes[0]
+    out = {
+        "value": results[main]["tok_per_s"], "ms_per_step": results[main]["ms_per_step"],
+        "achieved_step_GBps": round(step_bytes / (results[main]["ms_per_step"] * K / 1e3) / 1e9, 1),
+        "roofline": roofline, "cpu_baseline": cpu,
+        "modes": {m: {k: round(v, 5) if isinstance(v, float) else v for k, v in r.items()}
+                  for m, r in results.items()},
+        "modes_outputs_identical": bool(same),
+        "kv_gib": {"live": round(st.kv_bytes_live / 2**30, 4), "allocated": round(st.kv_bytes_allocated / 2**30, 4),
+                   "dense_equivalent": round(st.kv_bytes_dense_equiv / 2**30, 4)},
+        "config": {"workload": "%s decode: %d layers, %d q / %d kv heads, head_dim %d, batch 1, ctx %d, "
+                               "%d decode steps, w %d, keep-score mean U(-2,0) per head"
+                               % (wl.name, L, Hq, H, D, ctx, K, w),
+                   "call": "one dms_decode_step per token over all %d layers" % L,
+                   "parallelism": "single GPU"},
+    }
+    pool.close()
+    return out
+
+
+# ---------------------------------------------------------------------------
+# prefill
+# ---------------------------------------------------------------------------
+def bench_prefill(args, torch, dms):
+    wl = synth.WORKLOADS["qwen3-8b_prefill32k"]
+    inp = synth.SynthInputs(wl)
+    T, Hq, H, D, w, R = wl.ctx_len, wl.n_q_heads, wl.n_kv_heads, wl.head_dim, wl.window, wl.layer_repeats
+    dev = torch.device("cuda:0")
+    t0 = time.time()
+    lg = inp.logits(0, 0, 0, T)
+    q = bf16_tensor(inp.q(0, 0, 0, T), torch).to(dev)
+    k = bf16_tensor(inp.k(0, 0, 0, T), torch).to(dev)
+    v = bf16_tensor(inp.v(0, 0, 0, T), torch).to(dev)
+    dl = torch.from_numpy(lg).to(dev)
+    out = torch.empty((T, Hq, D), dtype=torch.bfloat16, device=dev)
+    torch.cuda.synchronize()
+    log("prefill inputs ready in %.1fs" % (time.time() - t0))
+    pool = dms.Pool(n_layers=R, n_q_heads=Hq, n_kv_heads=H, head_dim=D, window=w, max_seqs=1,
+                    max_positions=T, max_pages=R * H * (T // 64), device=dev)
+
+    def run_all():
+        for l in range(R):
+            pool.prefill(0, l, k, v, dl, q=q, out=out)
+
+    run_all()
+    pool.release(0)
+    stream = torch.cuda.current_stream(dev)
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    ev0.record(stream)
+    run_all()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    ms = ev0.elapsed_time(ev1)
+    st, _ = pool.stats(0)
+    pool.release(0)
+    dms.dms_timing_enable(pool.handle, True)
+    run_all()
+    tm = dms.dms_timing_read(pool.handle)
+    dms.dms_timing_enable(pool.handle, False)
+    avg_att = tm.prefill_attend_ms / tm.prefill_calls
+    avg_cmp = tm.prefill_compact_ms / tm.prefill_calls
+    # algorithmic flops of one layer: 4 * D per (q head, visible pair)
+    pairs = sum(int(np.sum(live_counts(lg[:, h], np.arange(T), w))) for h in range(H))
+    flops = 4.0 * D * (Hq // H) * pairs
+    dense = 4.0 * D * Hq * T * (T + 1) / 2
+    tflops = flops / (avg_att / 1e3) / 1e12
+    log("prefill: %.3f ms for %d layers (%.0f tok/s); attend kernel %.1f us = %.1f TFLOP/s (%.1f%% of bf16 "
+        "MFMA peak); compaction %.1f us" % (ms, R, T / (ms / 1e3), avg_att * 1e3, tflops,
+                                            100 * tflops / MFMA_BF16_PEAK_TFLOPS, avg_cmp * 1e3))
+    res = {"workload": "%s: one %d-token prompt, %d q / %d kv heads, head_dim %d, w %d, keep score "
+                       "N(-1.2,1), one layer's inputs prefilled into %d layer slots" % (wl.name, T, Hq, H, D, w, R),
+           "tok_per_s": round(T / (ms / 1e3), 1), "ms_all_layers": round(ms, 4),
+           "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
+                        "unit": "TFLOP/s", "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4),
+                        "kernel": "prefill_attend_kernel<128,4>", "avg_launch_us": round(avg_att * 1e3, 2),
+                        "flops_per_launch": flops, "dense_causal_flops": dense},
+           "compaction_avg_us": round(avg_cmp * 1e3, 2),
+           "kv_gib": {"live": round(st.kv_bytes_live / 2**30, 4),
+                      "dense_equivalent": round(st.kv_bytes_dense_equiv / 2**30, 4)}}
+    pool.close()
+    return res
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=128, help="timed decode steps (tokens)")
+    ap.add_argument("--warmup", type=int, default=8)
+    ap.add_argument("--workload", default="qwen3-8b_ctx8192")
+    ap.add_argument("--modes", default="batched,per_layer,graph")
+    ap.add_argument("--cpu-baseline-steps", type=int, default=128,
+                    help="decode steps the oracle is timed on (all layers); 0 disables")
+    ap.add_argument("--no-timing-pass", action="store_true")
+    ap.add_argument("--no-prefill", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py runs on one GPU only (this build has no multi-GPU path); got --gpus %d" % args.gpus,
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import compact_decode_attention_amd as dms
+
+    dec = bench_decode(args, torch, dms)
+    pre = None if args.no_prefill else bench_prefill(args, torch, dms)
     rec = {
         "metric": METRIC,
-        "value": round(value, 2),
+        "value": round(dec["value"], 2),
         "unit": "tok/s",
         "n_gpus": 1,
-        "steps": K,
-        "warmup": W,
-        "ms_per_step": round(ms_step, 5),
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(dec["ms_per_step"], 5),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": "%s decode: %d layers, %d q / %d kv heads, head_dim %d, batch %d, "
-                               "ctx %d, %d decode steps, w %d, keep-score mean U(-2,0) per head"
-                               % (wl.name, L, Hq, H, D, B, ctx, K, w),
-                   "call": "one dms_decode_step per token over all %d layers" % L,
-                   "parallelism": "single GPU"},
-        "achieved_step_GBps": round(step_bytes_total / (results[main_mode]["ms_total"] / 1e3) / 1e9, 1),
-        "roofline": roofline,
-        "cpu_baseline": cpu,
-        "modes": {m: {k: (round(v, 5) if isinstance(v, float) else v) for k, v in r.items()}
-                  for m, r in results.items() if isinstance(r, dict)},
-        "kv_gib": {"live": round(st.kv_bytes_live / 2**30, 4),
-                   "allocated": round(st.kv_bytes_allocated / 2**30, 4),
-                   "dense_equivalent": round(st.kv_bytes_dense_equiv / 2**30, 4)},
+        "config": dec["config"],
+        "achieved_step_GBps": dec["achieved_step_GBps"],
+        "roofline": dec["roofline"],
+        "cpu_baseline": dec["cpu_baseline"],
+        "modes": dec["modes"],
+        "modes_outputs_identical": dec["modes_outputs_identical"],
+        "kv_gib": dec["kv_gib"],
+        "prefill": pre,
     }
-    pool.close()
     print(json.dumps(rec), flush=True)
 
 

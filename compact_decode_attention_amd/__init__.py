@@ -50,6 +50,20 @@ class dms_pool_config(ctypes.Structure):
     ]
 
 
+class dms_timing(ctypes.Structure):
+    _fields_ = [
+        ("decode_attend_ms", ctypes.c_double),
+        ("decode_merge_ms", ctypes.c_double),
+        ("prefill_compact_ms", ctypes.c_double),
+        ("prefill_attend_ms", ctypes.c_double),
+        ("decode_launches", ctypes.c_int64),
+        ("prefill_calls", ctypes.c_int64),
+    ]
+
+    def as_dict(self):
+        return {k: getattr(self, k) for k, _ in self._fields_}
+
+
 class dms_stats(ctypes.Structure):
     _fields_ = [
         ("live_slots", ctypes.c_int64),
@@ -99,7 +113,7 @@ def lib() -> ctypes.CDLL:
             L.dms_export_live.argtypes = [vp, i32, i32, i32, P(i32), i32, P(i32)]
             L.dms_seq_release.argtypes = [vp, i32, vp]
             L.dms_timing_enable.argtypes = [vp, i32]
-            L.dms_timing_read.argtypes = [vp, P(ctypes.c_double), P(ctypes.c_double), P(ctypes.c_int64)]
+            L.dms_timing_read.argtypes = [vp, P(dms_timing)]
             for f in (L.dms_pool_create, L.dms_pool_destroy, L.dms_prefill, L.dms_decode_step,
                       L.dms_query_stats, L.dms_export_live, L.dms_seq_release,
                       L.dms_timing_enable, L.dms_timing_read):
@@ -196,11 +210,11 @@ def dms_timing_enable(pool: int, enable: bool):
     _check(lib().dms_timing_enable(ctypes.c_void_p(pool), 1 if enable else 0))
 
 
-def dms_timing_read(pool: int):
-    """(attention-kernel ms, merge-kernel ms, launches) summed since the last read."""
-    a, m, n = ctypes.c_double(), ctypes.c_double(), ctypes.c_int64()
-    _check(lib().dms_timing_read(ctypes.c_void_p(pool), ctypes.byref(a), ctypes.byref(m), ctypes.byref(n)))
-    return a.value, m.value, n.value
+def dms_timing_read(pool: int) -> dms_timing:
+    """Kernel times (ms) and call counts recorded since the last read."""
+    t = dms_timing()
+    _check(lib().dms_timing_read(ctypes.c_void_p(pool), ctypes.byref(t)))
+    return t
 
 
 # ---- torch convenience wrapper ------------------------------------------------

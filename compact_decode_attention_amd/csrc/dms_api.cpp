@@ -100,7 +100,8 @@ uint64_t mix64(uint64_t& s) {
 struct dms_pool {
     dms_pool_config cfg;
     bool timing = false;
-    std::vector<hipEvent_t> events;  // triples recorded by decode launches while timing
+    std::vector<hipEvent_t> events;   // triples recorded by decode launches while timing
+    std::vector<hipEvent_t> pevents;  // triples recorded by prefills with output while timing
     Layout layout;
     dms::PoolDev dev;
     char* arena;
@@ -203,11 +204,25 @@ dms_status dms_pool_destroy(dms_pool* pool) {
     if (!pool) return fail(DMS_E_INVAL, "pool is NULL");
     hipError_t e = hipDeviceSynchronize();
     for (hipEvent_t ev : pool->events) hipEventDestroy(ev);
+    for (hipEvent_t ev : pool->pevents) hipEventDestroy(ev);
     delete pool;
     if (e != hipSuccess) return hip_fail(e, "synchronise");
     g_err.clear();
     return DMS_OK;
 }
+
+namespace {
+// three fresh events appended to v (for one timed call), or nullptr on failure
+hipEvent_t* timing_events(std::vector<hipEvent_t>& v, hipError_t* err) {
+    const size_t base = v.size();
+    v.resize(base + 3, nullptr);
+    for (size_t i = base; i < base + 3; ++i) {
+        *err = hipEventCreate(&v[i]);
+        if (*err != hipSuccess) return nullptr;
+    }
+    return &v[base];
+}
+}  // namespace
 
 dms_status dms_prefill(dms_pool* pool, int32_t seq, int32_t layer, int32_t n_tokens, const void* q, const void* k,
                        const void* v, const float* logits, void* out, void* stream) {
@@ -230,11 +245,20 @@ dms_status dms_prefill(dms_pool* pool, int32_t seq, int32_t layer, int32_t n_tok
     a.layer = layer;
     a.n_tokens = n_tokens;
     hipStream_t s = static_cast<hipStream_t>(stream);
-    hipError_t e = dms::launch_prefill_compact(a, s);
+    hipError_t e = hipSuccess;
+    hipEvent_t* ev = nullptr;
+    if (pool->timing && out) {
+        ev = timing_events(pool->pevents, &e);
+        if (!ev) return hip_fail(e, "timing event");
+        if ((e = hipEventRecord(ev[0], s)) != hipSuccess) return hip_fail(e, "timing event");
+    }
+    e = dms::launch_prefill_compact(a, s);
     if (e != hipSuccess) return hip_fail(e, "prefill compaction launch");
     if (out) {
+        if (ev && (e = hipEventRecord(ev[1], s)) != hipSuccess) return hip_fail(e, "timing event");
         e = dms::launch_prefill_attend(a, s);
         if (e != hipSuccess) return hip_fail(e, "prefill attention launch");
+        if (ev && (e = hipEventRecord(ev[2], s)) != hipSuccess) return hip_fail(e, "timing event");
     }
     pool->position(seq, layer) = n_tokens;
     g_err.clear();
@@ -289,13 +313,9 @@ dms_status dms_decode_step(dms_pool* pool, int32_t n_seqs, const int32_t* seq_id
         const int grid = (int)std::max<int64_t>(1, std::min<int64_t>(bound, (int64_t)pool->cu_count * per_cu));
         hipEvent_t* ev = nullptr;
         if (pool->timing) {
-            const size_t base = pool->events.size();
-            pool->events.resize(base + 3, nullptr);
-            for (size_t i = base; i < base + 3; ++i) {
-                hipError_t ce = hipEventCreate(&pool->events[i]);
-                if (ce != hipSuccess) return hip_fail(ce, "timing event");
-            }
-            ev = &pool->events[base];
+            hipError_t ce = hipSuccess;
+            ev = timing_events(pool->events, &ce);
+            if (!ev) return hip_fail(ce, "timing event");
         }
         hipError_t e = dms::launch_decode(a, grid, st, ev);
         if (e != hipSuccess) return hip_fail(e, "decode launch");
@@ -402,25 +422,29 @@ dms_status dms_timing_enable(dms_pool* pool, int32_t enable) {
     return DMS_OK;
 }
 
-dms_status dms_timing_read(dms_pool* pool, double* attend_ms, double* merge_ms, int64_t* launches) {
-    if (!pool || !attend_ms || !merge_ms || !launches) return fail(DMS_E_INVAL, "NULL argument");
+dms_status dms_timing_read(dms_pool* pool, dms_timing* out) {
+    if (!pool || !out) return fail(DMS_E_INVAL, "NULL argument");
     hipError_t e = hipDeviceSynchronize();
     if (e != hipSuccess) return hip_fail(e, "synchronise");
-    double ta = 0, tm = 0;
-    const size_t n = pool->events.size() / 3;
-    for (size_t i = 0; i < n; ++i) {
-        float t0 = 0, t1 = 0;
-        e = hipEventElapsedTime(&t0, pool->events[3 * i], pool->events[3 * i + 1]);
-        if (e == hipSuccess) e = hipEventElapsedTime(&t1, pool->events[3 * i + 1], pool->events[3 * i + 2]);
-        if (e != hipSuccess) return hip_fail(e, "event elapsed time");
-        ta += t0;
-        tm += t1;
-    }
-    for (hipEvent_t ev : pool->events) hipEventDestroy(ev);
-    pool->events.clear();
-    *attend_ms = ta;
-    *merge_ms = tm;
-    *launches = (int64_t)n;
+    std::memset(out, 0, sizeof(*out));
+    auto sum = [&](std::vector<hipEvent_t>& v, double* first, double* second, int64_t* n) -> hipError_t {
+        *n = (int64_t)(v.size() / 3);
+        for (size_t i = 0; i + 2 < v.size(); i += 3) {
+            float t0 = 0, t1 = 0;
+            hipError_t r = hipEventElapsedTime(&t0, v[i], v[i + 1]);
+            if (r == hipSuccess) r = hipEventElapsedTime(&t1, v[i + 1], v[i + 2]);
+            if (r != hipSuccess) return r;
+            *first += t0;
+            *second += t1;
+        }
+        for (hipEvent_t ev : v) hipEventDestroy(ev);
+        v.clear();
+        return hipSuccess;
+    };
+    e = sum(pool->events, &out->decode_attend_ms, &out->decode_merge_ms, &out->decode_launches);
+    if (e == hipSuccess)
+        e = sum(pool->pevents, &out->prefill_compact_ms, &out->prefill_attend_ms, &out->prefill_calls);
+    if (e != hipSuccess) return hip_fail(e, "event elapsed time");
     g_err.clear();
     return DMS_OK;
 }

@@ -164,12 +164,21 @@ dms_status dms_seq_release(dms_pool* pool, int32_t seq, void* stream);
 
 /* Kernel timing for measurement.  While enabled, every decode launch records
  * HIP events on its stream before its attention kernel, between that kernel and
- * its merge / append kernel, and after the latter.  dms_timing_read
- * synchronises, adds up the elapsed times of all launches recorded since the
- * last read (milliseconds) and how many there were, and releases the events.
- * Disabled by default; enabling adds three event records per launch. */
+ * its merge / append kernel, and after the latter; every prefill records events
+ * around its compaction kernels and around its attention kernels.
+ * dms_timing_read synchronises, adds up the elapsed times of everything
+ * recorded since the last read (milliseconds), counts the calls, and releases
+ * the events.  Disabled by default; enabling adds event records between kernels. */
+typedef struct {
+    double decode_attend_ms;   /* split-K attention kernels */
+    double decode_merge_ms;    /* merge + evict/append kernels */
+    double prefill_compact_ms; /* mark scan + compaction kernels */
+    double prefill_attend_ms;  /* masked causal attention (MFMA) kernels */
+    int64_t decode_launches;
+    int64_t prefill_calls;     /* prefills that produced an output */
+} dms_timing;
 dms_status dms_timing_enable(dms_pool* pool, int32_t enable);
-dms_status dms_timing_read(dms_pool* pool, double* attend_ms, double* merge_ms, int64_t* launches);
+dms_status dms_timing_read(dms_pool* pool, dms_timing* out);
 
 /* Text of the last error on the calling thread ("" if none). */
 const char* dms_last_error(void);
