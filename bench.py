@@ -23,9 +23,11 @@ Prints one JSON line.  --gpus N with N > 1 exits: this build runs on one GPU.
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
 import sys
+import re
 import time
 
 import numpy as np
@@ -42,6 +44,56 @@ METRIC = "DMS compact decode tok/s + achieved HBM GB/s (% peak), Qwen3-8B shape,
 
 def log(*a):
     print("[bench]", *a, file=sys.stderr, flush=True)
+
+
+# Kernel sources whose HBM traffic the committed counter summary describes; the
+# figure is reported only while these files are unchanged.
+TRAFFIC_SOURCES = ["compact_decode_attention_amd/csrc/dms_kernels.hip",
+                   "compact_decode_attention_amd/csrc/dms_internal.h"]
+TRAFFIC_SUMMARY = "profiles/decode_attend_qwen3-8b_hbm_traffic.md"
+
+
+def sources_sha256(paths):
+    h = hashlib.sha256()
+    for p in paths:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def measured_traffic():
+    """HBM bytes per launch of the decode attention kernel from the committed
+    rocprofv3 FETCH_SIZE / WRITE_SIZE summary (each scaled by the same counter's
+    reading for a plain copy of known size), or None when the summary is missing
+    or was taken on other kernel sources."""
+    path = os.path.join(ROOT, TRAFFIC_SUMMARY)
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    with open(path) as f:
+        for line in f:
+            m = re.match(r"^- (\w+): (\S+)\s*$", line)
+            if m:
+                kv[m.group(1)] = m.group(2)
+    if kv.get("source_sha256") != sources_sha256(TRAFFIC_SOURCES):
+        return None
+    try:
+        return int(kv["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def copy_calibration(torch, mib):
+    """A plain device-to-device copy of known size, three times, so a counter
+    run over this process can scale FETCH_SIZE / WRITE_SIZE to bytes."""
+    n = mib << 20
+    src = torch.empty(n, dtype=torch.uint8, device="cuda:0").fill_(1)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    log("copy calibration: 3 copies of %d bytes" % n)
+    del src, dst
 
 
 def live_counts(logits_hd, t_values, window):
@@ -181,7 +233,7 @@ def bench_decode(args, torch, dms):
         avg_att, avg_mer = tm.decode_attend_ms / n, tm.decode_merge_ms / n
         achieved = attend_bytes / (avg_att / 1e3) / 1e9
         roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                    "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None,
+                    "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": measured_traffic(),
                     "kernel": "decode_attend_kernel<128,4>", "avg_launch_us": round(avg_att * 1e3, 2),
                     "bytes_per_launch": int(attend_bytes), "launches": int(n),
                     "merge_kernel_avg_launch_us": round(avg_mer * 1e3, 2)}
@@ -300,6 +352,8 @@ def main():
                     help="decode steps the oracle is timed on (all layers); 0 disables")
     ap.add_argument("--no-timing-pass", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="first run a plain copy of this many MiB (for counter scaling)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py runs on one GPU only (this build has no multi-GPU path); got --gpus %d" % args.gpus,
@@ -309,6 +363,8 @@ def main():
     import torch
     import compact_decode_attention_amd as dms
 
+    if args.copy_calibration_mib > 0:
+        copy_calibration(torch, args.copy_calibration_mib)
     dec = bench_decode(args, torch, dms)
     pre = None if args.no_prefill else bench_prefill(args, torch, dms)
     rec = {
