@@ -208,7 +208,9 @@ def bench_decode(args, torch, dms):
         results[mode] = {"ms_per_step": ms / K, "tok_per_s": K / (ms / 1e3), "live_slots_end": int(st.live_slots)}
         outs[mode] = dout[:K].clone()
         log("decode %s: %.4f ms/step, %.1f tok/s" % (mode, ms / K, K / (ms / 1e3)))
-    same = all(torch.equal(outs[m], outs[modes[0]]) for m in modes)
+    # the modes cut the page axis at different points (split-K rounding may
+    # differ in the last bits): report the largest difference to the first mode
+    diff = {m: float((outs[m].float() - outs[modes[0]].float()).abs().max()) for m in modes[1:]}
 
     # byte accounting from the logits: live slots read per step (the new token
     # comes from the inputs), q, out, k/v append, logits
@@ -264,7 +266,7 @@ def bench_decode(args, torch, dms):
         "roofline": roofline, "cpu_baseline": cpu,
         "modes": {m: {k: round(v, 5) if isinstance(v, float) else v for k, v in r.items()}
                   for m, r in results.items()},
-        "modes_outputs_identical": bool(same),
+        "modes_max_abs_diff": diff,
         "kv_gib": {"live": round(st.kv_bytes_live / 2**30, 4), "allocated": round(st.kv_bytes_allocated / 2**30, 4),
                    "dense_equivalent": round(st.kv_bytes_dense_equiv / 2**30, 4)},
         "config": {"workload": "%s decode: %d layers, %d q / %d kv heads, head_dim %d, batch 1, ctx %d, "
@@ -385,7 +387,7 @@ def main():
         "roofline": dec["roofline"],
         "cpu_baseline": dec["cpu_baseline"],
         "modes": dec["modes"],
-        "modes_outputs_identical": dec["modes_outputs_identical"],
+        "modes_max_abs_diff": dec["modes_max_abs_diff"],
         "kv_gib": dec["kv_gib"],
         "prefill": pre,
     }

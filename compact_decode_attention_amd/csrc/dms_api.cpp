@@ -61,9 +61,8 @@ bool make_layout(const dms_pool_config* c, Layout* L, std::string* why) {
     L->pages_per_head = (c->max_positions + dms::kPage - 1) / dms::kPage;
     L->ring_len = c->window < c->max_positions ? c->window : 0;
     L->max_call_heads = (int32_t)std::min<int64_t>(heads, dms::kMaxCallHeads);
-    const int64_t items = c->max_pages * dms::kPage / dms::kChunk + L->max_call_heads + 1;
-    if (items > INT32_MAX) return bad("max_pages too large");
-    L->max_items = (int32_t)items;
+    // partial slots: one per (attention wave, call head) pair that can occur
+    L->max_items = dms::kMaxAttendBlocks * dms::kAttendWaves + L->max_call_heads;
     size_t sz[S_N];
     sz[S_K] = (size_t)c->max_pages * dms::kPage * D * 2;
     sz[S_V] = sz[S_K];
@@ -107,6 +106,7 @@ struct dms_pool {
     char* arena;
     std::vector<int32_t> pos;  // [max_seqs][n_layers]: next position, -1 = empty
     int cu_count;
+    int attend_per_cu;  // attention blocks per compute unit (checked once, for the largest call)
     int32_t& position(int seq, int layer) { return pos[(size_t)seq * cfg.n_layers + layer]; }
 };
 
@@ -194,6 +194,16 @@ dms_status dms_pool_create(const dms_pool_config* cfg, void* arena, size_t arena
     if (e != hipSuccess) {
         delete p;
         return hip_fail(e, "pool initialisation");
+    }
+    {
+        dms::DecodeArgs probe{};
+        probe.pool = d;
+        probe.n_call_heads = L.max_call_heads;
+        p->attend_per_cu = std::min(dms::kAttendBlocksPerCU, dms::decode_blocks_per_cu(probe));
+        if (p->attend_per_cu < 1) {
+            delete p;
+            return fail(DMS_E_INVAL, "the decode kernel does not fit a compute unit with this configuration");
+        }
     }
     *out = p;
     g_err.clear();
@@ -303,21 +313,22 @@ dms_status dms_decode_step(dms_pool* pool, int32_t n_seqs, const int32_t* seq_id
         a.layer0 = layer0;
         a.n_layers = n_layers;
         a.n_call_heads = a.n_layers * a.n_seqs * hkv;
-        int64_t bound = 0;  // split-K items: n_live <= position, ceil(n_live / chunk) per head
+        int64_t bound = 0;  // pages of the call: n_live <= position, ceil(n_live / 64) per head
         for (int i = 0; i < a.n_seqs; ++i) {
             a.seq_ids[i] = seq_ids[sb + i];
             for (int l = layer0; l < layer0 + n_layers; ++l)
-                bound += (int64_t)hkv * std::max(1, (pool->position(a.seq_ids[i], l) + dms::kChunk - 1) / dms::kChunk);
+                bound += (int64_t)hkv * ((pool->position(a.seq_ids[i], l) + dms::kPage - 1) / dms::kPage);
         }
-        const int per_cu = std::min(dms::kGridPerCU, dms::decode_blocks_per_cu(a));
-        const int grid = (int)std::max<int64_t>(1, std::min<int64_t>(bound, (int64_t)pool->cu_count * per_cu));
+        int64_t grid = std::min<int64_t>((int64_t)pool->cu_count * pool->attend_per_cu, dms::kMaxAttendBlocks);
+        grid = std::max<int64_t>(1, std::min<int64_t>(grid, (bound + dms::kAttendWaves - 1) / dms::kAttendWaves));
+        a.n_waves = (int32_t)grid * dms::kAttendWaves;
         hipEvent_t* ev = nullptr;
         if (pool->timing) {
             hipError_t ce = hipSuccess;
             ev = timing_events(pool->events, &ce);
             if (!ev) return hip_fail(ce, "timing event");
         }
-        hipError_t e = dms::launch_decode(a, grid, st, ev);
+        hipError_t e = dms::launch_decode(a, (int)grid, st, ev);
         if (e != hipSuccess) return hip_fail(e, "decode launch");
     }
     for (int i = 0; i < n_seqs; ++i)

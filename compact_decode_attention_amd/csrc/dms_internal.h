@@ -13,8 +13,10 @@
 //   ptable   int32 [heads][pages_per_head]         page of slots 64j .. 64j+63
 //   ring     int32 [heads][ring_len]               entry of position s at s % w:
 //                                                  (slot << 1) | mark, -1 = none
-//   partials f32   [max_items][G*(head_dim+2)]     split-K partials {m[G], l[G], acc[G][D]}
-//   prefix   int32 [max_call_heads + 1]            first split-K item of each head (last launch)
+//   partials f32   [max_items][G*(head_dim+2)]     split-K partials {m[G], l[G], acc[G][D]},
+//                                                  slot w + ch for wave w and call head ch
+//   prefix   int32 [max_call_heads + 1]            first page of each call head on the page
+//                                                  axis of the last decode launch
 //   inv      int32 [n_kv_heads][max_positions]     prefill scratch: slot -> position
 //   pcnt     int32 [n_kv_heads][max_positions]     prefill scratch: live tokens in [0, s]
 //   vt       bf16 [n_kv_heads][max_pos32/8][head_dim][8]
@@ -29,22 +31,22 @@
 
 namespace dms {
 
-// Split-K work item of the decode kernel: a block of 4 waves, each wave taking
-// kPagesPerWave pages of one head.  kGridPerCU blocks per compute unit form the
-// persistent grid.  (Tuning constants; overridable at build time.)
-#ifndef DMS_PAGES_PER_WAVE
-#define DMS_PAGES_PER_WAVE 1
+// Decode attention: blocks of kAttendWaves waves (one per SIMD), at most
+// kAttendBlocksPerCU per compute unit and kMaxAttendBlocks per launch; the
+// partials hold one slot per (wave, call head) pair that can occur.
+// (Tuning constants; overridable at build time.)
+#ifndef DMS_ATTEND_WAVES
+#define DMS_ATTEND_WAVES 4
 #endif
-#ifndef DMS_GRID_PER_CU
-#define DMS_GRID_PER_CU 4
+#ifndef DMS_ATTEND_BLOCKS_PER_CU
+#define DMS_ATTEND_BLOCKS_PER_CU 1
 #endif
 constexpr int kPage = 64;          // slots per page
-constexpr int kPagesPerWave = DMS_PAGES_PER_WAVE;
-constexpr int kChunkPages = 4 * kPagesPerWave;
-constexpr int kChunk = kPage * kChunkPages;
-constexpr int kGridPerCU = DMS_GRID_PER_CU;
+constexpr int kAttendWaves = DMS_ATTEND_WAVES;
+constexpr int kAttendBlocksPerCU = DMS_ATTEND_BLOCKS_PER_CU;
+constexpr int kMaxAttendBlocks = 4096 / kAttendWaves;
 constexpr int kMaxCallSeqs = 256;  // sequences per kernel launch (larger calls are split)
-constexpr int kMaxCallHeads = 4096;  // heads per launch (the work list lives in LDS)
+constexpr int kMaxCallHeads = 4032;  // heads per launch (4 ints of plan per head in LDS, < 64 KB)
 
 // ctl words
 constexpr int kCtlTop = 0;    // free pages on the stack
@@ -93,6 +95,7 @@ struct DecodeArgs {
     int32_t n_seqs;        // sequences in this launch
     int32_t layer0, n_layers;
     int32_t n_call_heads;  // n_layers * n_seqs * n_kv_heads
+    int32_t n_waves;       // waves of the attention kernel's grid
     int32_t seq_ids[kMaxCallSeqs];
 };
 
@@ -109,7 +112,7 @@ struct PrefillArgs {
 // ev (optional): two events recorded before the first and after the last
 // kernel of the decode launch
 hipError_t launch_decode(const DecodeArgs& a, int grid, hipStream_t s, hipEvent_t* ev);
-// blocks of the attention kernel one compute unit holds at once for this call
+// blocks of the attention kernel one compute unit holds at once for this call (0: does not fit)
 int decode_blocks_per_cu(const DecodeArgs& a);
 hipError_t launch_prefill_compact(const PrefillArgs& a, hipStream_t s);
 hipError_t launch_prefill_attend(const PrefillArgs& a, hipStream_t s);

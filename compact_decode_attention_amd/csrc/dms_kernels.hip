@@ -13,15 +13,16 @@
 //   out[g] = softmax over V(t) = V(t-1) \ {t-w if marked} + {t}
 //
 // Kernels of one decode launch:
-//   decode_attend  -- persistent grid; every block derives the split-K work list
-//                     (ceil(n_old / 256) items per head, 4 pages per item, one
-//                     page per wave) from the head records, then each wave folds
-//                     one page into a running softmax: QK^T with lane = slot
-//                     (v_dot2_f32_bf16 over 16-byte K chunks loaded 1 KB-coalesced
-//                     from the key-major K page), page max and sum by DPP
-//                     wavefront reductions, PV with lane = dim (v_dot2 over key
-//                     pairs of the dim-major V page).  A block folds its 4 waves
-//                     into one partial per item.  This kernel only reads the pool.
+//   decode_attend  -- one block per compute unit; every block derives the page
+//                     axis of the call (ceil(n_old / 64) pages per head, heads in
+//                     call order) from the head records, then each wave folds an
+//                     equal run of consecutive pages into a running softmax:
+//                     QK^T with lane = slot (v_dot2_f32_bf16 over 16-byte K chunks
+//                     loaded 1 KB-coalesced from the key-major K page), page max
+//                     and sum by DPP wavefront reductions, PV with lane = dim
+//                     (v_dot2 over key pairs of the dim-major V page), the next
+//                     page's K and V in flight meanwhile.  One partial per (wave,
+//                     head) pair.  This kernel only reads the pool.
 //   decode_merge   -- per head: log-sum-exp merge of the partials with the new
 //                     token (bf16 output), and, in separate blocks, mark, expiry,
 //                     slot reuse or page allocation, K/V append and the record.
@@ -173,87 +174,116 @@ __device__ __forceinline__ int marked_slot_at(const PoolDev& P, int gh, int s) {
 
 // ---------------------------------------------------------------------------
 // decode, kernel 1: split-K attention over the live slots
+//
+// Work split.  The pages of the call's heads, concatenated in call-head order,
+// form one axis: head ch owns pages pp[ch] .. pp[ch+1]-1, pp being the exclusive
+// prefix of ceil(n_old / 64).  Its P pages are cut into W = min(waves, P) equal
+// runs; wave w takes pages [w*P/W, (w+1)*P/W) and folds them into a running
+// softmax, writing one partial per head its run touches, at partial slot w + ch
+// (distinct for all (w, ch) pairs that occur, and contiguous per head).  Waves
+// never wait for each other after the plan is built.
+//
+// Pipeline of one wave: K and V of page k+1 are requested while page k is being
+// computed (K right after QK^T has consumed the K registers, V right after P.V
+// has consumed the V registers), so each wave keeps 16-32 KB of loads in flight.
 // ---------------------------------------------------------------------------
 
-// K chunk cc of slot `lane` of one page: 64 lanes read 1 KB contiguous.  An
-// empty page (live = false) gets a zero-size resource: its loads return 0 and
-// move no data.
+// K chunks of one page (lane = slot; chunk cc of the page's 64 slots is 1 KB
+// contiguous).  A dead request gets a zero-size resource: no memory traffic.
 template <int D>
-__device__ __forceinline__ void load_k_page(const PoolDev& P, int page, bool live, int lane, uint4 (&kc)[D / 8]) {
-    const __amdgpu_buffer_rsrc_t kr =
-        buffer_rsrc(P.kpages + (size_t)page * (kPage * D), live ? kPage * D * 2 : 0);
+__device__ __forceinline__ void issue_k(const PoolDev& P, int page, bool live, int lane, uint4 (&kc)[D / 8]) {
+    const __amdgpu_buffer_rsrc_t r = buffer_rsrc(P.kpages + (size_t)page * (kPage * D), live ? kPage * D * 2 : 0);
 #pragma unroll
-    for (int cc = 0; cc < D / 8; ++cc) kc[cc] = buffer_load16(kr, lane * 16, cc * kPage * 16);
+    for (int cc = 0; cc < D / 8; ++cc) kc[cc] = buffer_load16(r, lane * 16, cc * kPage * 16);
 }
 
-// One page (64 slots) of one head, K already in registers, folded into a wave's
-// running softmax state (m: running max in base-2 units, l: running sum, acc:
-// running P.V for the dims this lane owns).  Slots at or beyond n_old and the
-// expiring slot e are masked; a page wholly beyond n_old changes nothing and
-// reads no memory.
-template <int D, int G>
-__device__ __forceinline__ void attend_page(const PoolDev& P, int page, int base, int n_old, int e,
-                                            const uint4 (&kc)[D / 8], const uint32_t (*s_q)[D / 2],
-                                            uint16_t (*s_p)[G][kPage], int lane, float (&m)[G], float (&l)[G],
-                                            float (&acc)[G][D / 64]) {
-    constexpr int NC = D / 8;   // 16-byte K chunks per slot
-    constexpr int VJ = D / 64;  // dims per lane in PV
-    // QK^T, lane = slot.  q is read from LDS (same address in every lane: a
-    // broadcast), one chunk ahead of its use; each q head is one chain of dot
-    // products over the 16-byte K chunks held in registers.
-    float z[G];
-#pragma unroll
-    for (int g = 0; g < G; ++g) {
-        float zg = 0.f;
-        uint4 qn = *reinterpret_cast<const uint4*>(&s_q[g][0]);
-#pragma unroll
-        for (int cc = 0; cc < NC; ++cc) {
-            const uint4 qv = qn;
-            if (cc + 1 < NC) qn = *reinterpret_cast<const uint4*>(&s_q[g][(cc + 1) * 4]);
-            zg = dot2(qv.x, kc[cc].x, zg);
-            zg = dot2(qv.y, kc[cc].y, zg);
-            zg = dot2(qv.z, kc[cc].z, zg);
-            zg = dot2(qv.w, kc[cc].w, zg);
-            pin(zg);
-        }
-        z[g] = zg;
-    }
-    // V loads go out after QK (K registers are free again); other waves keep the
-    // memory pipe busy meanwhile.
-    const __amdgpu_buffer_rsrc_t vr =
-        buffer_rsrc(P.vpages + (size_t)page * (kPage * D), base < n_old ? kPage * D * 2 : 0);
-    uint4 vc[8][VJ];
+// V units of one page (lane = dim: unit (b, j) holds slots 8b .. 8b+7 of dim j*64 + lane).
+template <int D>
+__device__ __forceinline__ void issue_v(const PoolDev& P, int page, bool live, int lane, uint4 (&vc)[8][D / 64]) {
+    const __amdgpu_buffer_rsrc_t r = buffer_rsrc(P.vpages + (size_t)page * (kPage * D), live ? kPage * D * 2 : 0);
 #pragma unroll
     for (int b = 0; b < 8; ++b)
 #pragma unroll
-        for (int j = 0; j < VJ; ++j) vc[b][j] = buffer_load16(vr, lane * 16, (b * D + j * 64) * 16);
-    const int slot = base + lane;
-    const bool valid = slot < n_old && slot != e;
+        for (int j = 0; j < D / 64; ++j) vc[b][j] = buffer_load16(r, lane * 16, (b * D + j * 64) * 16);
+}
+
+// QK^T of one page, lane = slot.  q comes from LDS (every lane reads the same
+// address: a broadcast), the G heads' pieces of a chunk one chunk ahead of their
+// use; the G heads are G independent chains of dot products over the 16-byte K
+// chunks.
+template <int D, int G>
+__device__ __forceinline__ void qk_page(const uint4 (&kc)[D / 8], const uint4* s_q, float (&z)[G]) {
+    constexpr int NC = D / 8;
+    uint4 qa[G];
 #pragma unroll
     for (int g = 0; g < G; ++g) {
-        // additive mask: a select here lets the compiler sink the whole QK
-        // product into a branch behind every load of the page
-        const float zz = fmaf(z[g], P.scale_log2, valid ? 0.f : -INFINITY);
-        const float mn = fmaxf(m[g], wave_max(zz));
-        float p = 0.f, alpha = 1.f;
-        if (mn != -INFINITY) {
-            p = exp2f(zz - mn);
-            alpha = exp2f(m[g] - mn);
-        }
-        // P enters the PV dot products as two bf16 parts, hi = bf16(p) and
-        // lo = bf16(p - hi): about 16 significant bits, fp32 accumulation
-        const uint16_t ph = f32_to_bf16(p);
-        s_p[0][g][lane] = ph;
-        s_p[1][g][lane] = f32_to_bf16(p - bf16_to_f32(ph));
-        l[g] = l[g] * alpha + wave_sum(p);
-        m[g] = mn;
-#pragma unroll
-        for (int j = 0; j < VJ; ++j) acc[g][j] *= alpha;
+        z[g] = 0.f;
+        qa[g] = s_q[g * NC];
     }
-    wave_lds_sync();
-    // PV, lane = dim: each 16-byte V unit holds 8 consecutive slots of one dim,
-    // i.e. 4 key pairs, matched by 4 bf16 pairs of p (broadcast reads), once for
-    // the high and once for the low part of p.
+#pragma unroll
+    for (int cc = 0; cc < NC; ++cc) {
+        uint4 qb[G];
+        if (cc + 1 < NC) {
+#pragma unroll
+            for (int g = 0; g < G; ++g) qb[g] = s_q[g * NC + cc + 1];
+        }
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+            z[g] = dot2(qa[g].x, kc[cc].x, z[g]);
+            z[g] = dot2(qa[g].y, kc[cc].y, z[g]);
+            z[g] = dot2(qa[g].z, kc[cc].z, z[g]);
+            z[g] = dot2(qa[g].w, kc[cc].w, z[g]);
+            pin(z[g]);
+        }
+        if (cc + 1 < NC) {
+#pragma unroll
+            for (int g = 0; g < G; ++g) qa[g] = qb[g];
+        }
+    }
+}
+
+// Online-softmax update with the scores of one page (slots base + lane; slots at
+// or beyond n_old and the expiring slot e are masked).  The page's weights go to
+// LDS as two bf16 parts, hi = bf16(p) and lo = bf16(p - hi), for the PV step.
+template <int D, int G>
+__device__ __forceinline__ void softmax_page(const float (&z)[G], float scale_log2, int base, int n_old, int e,
+                                             int lane, uint16_t (*s_p)[G][kPage], float (&m)[G], float (&l)[G],
+                                             float (&acc)[G][D / 64]) {
+    const int slot = base + lane;
+    const bool valid = slot < n_old && slot != e;
+    float zz[G], mn[G], p[G];
+    // the G heads' reductions are independent: issue them side by side
+#pragma unroll
+    for (int g = 0; g < G; ++g) zz[g] = fmaf(z[g], scale_log2, valid ? 0.f : -INFINITY);  // additive mask
+#pragma unroll
+    for (int g = 0; g < G; ++g) mn[g] = fmaxf(m[g], wave_max(zz[g]));
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+        float alpha = 1.f;
+        p[g] = 0.f;
+        if (mn[g] != -INFINITY) {
+            p[g] = exp2f(zz[g] - mn[g]);
+            alpha = exp2f(m[g] - mn[g]);
+        }
+        const uint16_t ph = f32_to_bf16(p[g]);
+        s_p[0][g][lane] = ph;
+        s_p[1][g][lane] = f32_to_bf16(p[g] - bf16_to_f32(ph));
+        l[g] *= alpha;
+        m[g] = mn[g];
+#pragma unroll
+        for (int j = 0; j < D / 64; ++j) acc[g][j] *= alpha;
+    }
+#pragma unroll
+    for (int g = 0; g < G; ++g) l[g] += wave_sum(p[g]);
+}
+
+// P.V of one page, lane = dim: each 16-byte V unit holds 8 consecutive slots of
+// one dim, i.e. 4 key pairs, matched by 4 bf16 pairs of p (broadcast reads),
+// once for the high and once for the low part of p.
+template <int D, int G>
+__device__ __forceinline__ void pv_page(const uint4 (&vc)[8][D / 64], const uint16_t (*s_p)[G][kPage],
+                                        float (&acc)[G][D / 64]) {
+    constexpr int VJ = D / 64;
 #pragma unroll
     for (int part = 0; part < 2; ++part) {
         uint4 pn[G];
@@ -281,157 +311,172 @@ __device__ __forceinline__ void attend_page(const PoolDev& P, int page, int base
             }
         }
     }
-    wave_lds_sync();  // s_p is rewritten by this wave's next page
 }
 
-// Head of work item `item`: the largest head index whose first item is <= item.
-__device__ __forceinline__ int item_head(const int32_t* s_prefix, int H, int item) {
-    int lo = 0, hi = H;  // s_prefix[lo] <= item < s_prefix[hi]
-    while (hi - lo > 1) {
-        const int mid = (lo + hi) >> 1;
-        if (s_prefix[mid] <= item) lo = mid; else hi = mid;
-    }
-    // the same in every lane; say so, so that head state, page ids and buffer
-    // resources live in scalar registers
-    return __builtin_amdgcn_readfirstlane(lo);
+// q of call head ch's G query heads: G * D bf16, contiguous in the input.
+__device__ __forceinline__ const uint16_t* q_group(const DecodeArgs& a, int ch) {
+    const CallHead c = call_head(a, ch);
+    return a.q + ((size_t)c.row * a.pool.n_q_heads + c.h * (a.pool.n_q_heads / a.pool.n_kv_heads)) * a.pool.head_dim;
 }
 
 template <int D, int G>
-__global__ __launch_bounds__(256, 4) void decode_attend_kernel(DecodeArgs a) {
-    constexpr int VJ = D / 64;  // dims per lane in PV
-    constexpr int NW = 4;       // waves per block
-    constexpr int QW = (G * D / 2 + 255) / 256;  // q dwords staged per thread
+__global__ __attribute__((amdgpu_flat_work_group_size(64 * kAttendWaves, 64 * kAttendWaves),
+                          amdgpu_waves_per_eu(2, 2)))
+void decode_attend_kernel(DecodeArgs a) {
+    constexpr int NT = 64 * kAttendWaves;
+    constexpr int VJ = D / 64;
+    constexpr int QV = G * D / 8;  // 16-byte pieces of one head group's q
+    constexpr int QR = (QV + 63) / 64;
+    constexpr int PSTR = G * (D + 2);
     const int H = a.n_call_heads;
     extern __shared__ int32_t s_dyn[];
-    int32_t* s_prefix = s_dyn;          // [H + 1] first item of each head
-    int32_t* s_nold = s_dyn + H + 1;    // [H] live count before this step
-    int32_t* s_exp = s_nold + H;        // [H] slot expiring at this step, or -1
-    __shared__ uint32_t s_q[G][D / 2];
-    __shared__ uint16_t s_p[NW][2][G][kPage];  // per wave: p high and low parts
-    __shared__ float s_m[NW][G], s_l[NW][G];
-    __shared__ float s_acc[NW][G][D];
-    __shared__ int s_scan[2 * NW + 1];
+    int32_t* s_pp = s_dyn;            // [H + 1] first page of each head on the call's page axis
+    int32_t* s_nold = s_pp + H + 1;   // [H] live count before this step
+    int32_t* s_exp = s_nold + H;      // [H] slot expiring at this step, or -1
+    int32_t* s_gh = s_exp + H;        // [H] global head id
+    __shared__ uint4 s_q[kAttendWaves][QV];
+    __shared__ uint16_t s_p[kAttendWaves][2][G][kPage];
+    __shared__ int s_scan[2 * kAttendWaves + 1];
 
     const PoolDev& P = a.pool;
     const int tid = threadIdx.x, lane = tid & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
 
-    // ---- work list: ceil(n_old / kChunk) items per head
-    const int per = (H + 255) / 256;
-    const int h0 = min(tid * per, H), h1 = min(h0 + per, H);
-    int local = 0;
-    for (int ch = h0; ch < h1; ++ch) {
-        const int32_t* hs = P.hstate + (size_t)call_head(a, ch).gh * kHS;
-        const int n = hs[kHsLive];
-        s_nold[ch] = n;
-        s_exp[ch] = hs[kHsExp];
-        const int c = (n + kChunk - 1) / kChunk;
-        s_prefix[ch] = c;
-        local += c;
+    // ---- plan: pages per head and their prefix (every block builds its own)
+    {
+        const int per = (H + NT - 1) / NT;
+        const int h0 = min(tid * per, H), h1 = min(h0 + per, H);
+        int local = 0;
+        for (int ch = h0; ch < h1; ++ch) {
+            const int gh = call_head(a, ch).gh;
+            const int32_t* hs = P.hstate + (size_t)gh * kHS;
+            const int n = hs[kHsLive];
+            s_nold[ch] = n;
+            s_exp[ch] = hs[kHsExp];
+            s_gh[ch] = gh;
+            const int c = (n + kPage - 1) / kPage;
+            s_pp[ch] = c;
+            local += c;
+        }
+        int total;
+        int off = block_excl_scan<NT>(local, &total, s_scan);
+        for (int ch = h0; ch < h1; ++ch) {
+            const int c = s_pp[ch];
+            s_pp[ch] = off;
+            off += c;
+        }
+        if (tid == 0) s_pp[H] = total;
+        __syncthreads();
+        if (blockIdx.x == 0)
+            for (int i = tid; i <= H; i += NT) P.prefix[i] = s_pp[i];
     }
-    int total;
-    int off = block_excl_scan<256>(local, &total, s_scan);
-    for (int ch = h0; ch < h1; ++ch) {
-        const int c = s_prefix[ch];
-        s_prefix[ch] = off;
-        off += c;
-    }
-    if (tid == 0) s_prefix[H] = total;
-    __syncthreads();
-    if (blockIdx.x == 0)
-        for (int i = tid; i <= H; i += 256) P.prefix[i] = s_prefix[i];
+    // ---- this wave's run of pages (no block-wide synchronisation below)
+    const int total = __builtin_amdgcn_readfirstlane(s_pp[H]);
+    const int W = min((int)gridDim.x * kAttendWaves, total);
+    const int w = blockIdx.x * kAttendWaves + wave;
+    if (w >= W) return;
+    const int p0 = (int)(((int64_t)w * total) / W);
+    const int p1 = (int)(((int64_t)(w + 1) * total) / W);
 
-    // page id of this wave's first page of an item (0 when the page is empty)
-    auto first_page = [&](int item) -> int {
-        if (item >= total) return 0;
-        const int hd = item_head(s_prefix, H, item);
-        const int pi = (item - __builtin_amdgcn_readfirstlane(s_prefix[hd])) * kChunkPages + wave;
-        if (pi * kPage >= __builtin_amdgcn_readfirstlane(s_nold[hd])) return 0;
-        return P.ptable[(size_t)call_head(a, hd).gh * P.pages_per_head + pi];
+    // page id and head of pages b0 + lane (a batch of 64): lane-parallel search
+    auto batch = [&](int b0, int& pid, int& hd) {
+        const int p = b0 + lane;
+        int lo = 0;
+        pid = 0;
+        if (p < p1) {
+            int hi = H;  // s_pp[lo] <= p < s_pp[hi]
+            while (hi - lo > 1) {
+                const int mid = (lo + hi) >> 1;
+                if (s_pp[mid] <= p) lo = mid; else hi = mid;
+            }
+            pid = P.ptable[(size_t)s_gh[lo] * P.pages_per_head + (p - s_pp[lo])];
+        }
+        hd = lo;
     };
-    int page_next = first_page(blockIdx.x);
+    auto load_q = [&](int ch, bool live, uint4 (&qr)[QR]) {
+        const __amdgpu_buffer_rsrc_t r = buffer_rsrc(q_group(a, ch), live ? QV * 16 : 0);
+#pragma unroll
+        for (int i = 0; i < QR; ++i) qr[i] = buffer_load16(r, (lane + 64 * i) * 16, 0);
+    };
+    auto store_q = [&](const uint4 (&qr)[QR]) {
+#pragma unroll
+        for (int i = 0; i < QR; ++i)
+            if (lane + 64 * i < QV) s_q[wave][lane + 64 * i] = qr[i];
+        wave_lds_sync();
+    };
 
-    for (int item = blockIdx.x; item < total; item += gridDim.x) {
-        const int tid = launder(threadIdx.x), lane = tid & 63;
-        const int hd = item_head(s_prefix, H, item);
-        const int chunk = item - __builtin_amdgcn_readfirstlane(s_prefix[hd]);
-        const CallHead c = call_head(a, hd);
+    int b0 = p0;
+    int cpid, chd, npid = 0, nhd = 0;
+    batch(b0, cpid, chd);
+    if (b0 + 64 < p1) batch(b0 + 64, npid, nhd);  // the next batch, in flight
+    int hd = __builtin_amdgcn_readfirstlane(chd);
+    int pid = __builtin_amdgcn_readfirstlane(cpid);
+    uint4 qr[QR];
+    load_q(hd, true, qr);
+    uint4 kc[D / 8], vc[8][VJ];
+    issue_k<D>(P, pid, true, lane, kc);
+    issue_v<D>(P, pid, true, lane, vc);
+    store_q(qr);
+
+    float m[G], l[G], acc[G][VJ];
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+        m[g] = -INFINITY;
+        l[g] = 0.f;
+#pragma unroll
+        for (int j = 0; j < VJ; ++j) acc[g][j] = 0.f;
+    }
+    for (int k = p0; k < p1; ++k) {
+        // page k+1: head and page id from the batch registers
+        const bool more = k + 1 < p1;
+        int idx = k + 1 - b0;
+        if (idx == 64) {
+            b0 += 64;
+            idx = 0;
+            cpid = npid;
+            chd = nhd;
+            if (b0 + 64 < p1) batch(b0 + 64, npid, nhd);
+        }
+        const int hd1 = more ? __builtin_amdgcn_readlane(chd, idx) : hd;
+        const int pid1 = more ? __builtin_amdgcn_readlane(cpid, idx) : 0;
+        const bool new_head = more && hd1 != hd;
         const int n_old = __builtin_amdgcn_readfirstlane(s_nold[hd]);
         const int e = __builtin_amdgcn_readfirstlane(s_exp[hd]);
-        const int pi0 = chunk * kChunkPages + wave;
-        const int page0 = page_next;
-        page_next = first_page(item + gridDim.x);  // lands while this item runs
+        const int base = (k - __builtin_amdgcn_readfirstlane(s_pp[hd])) * kPage;
 
-        // q loads first, then this wave's first K page, then the q hand-off
-        const uint32_t* qsrc =
-            reinterpret_cast<const uint32_t*>(a.q + ((size_t)c.row * P.n_q_heads + c.h * G) * D);
-        uint32_t qv[QW];
-#pragma unroll
-        for (int r = 0; r < QW; ++r) qv[r] = tid + r * 256 < G * D / 2 ? qsrc[tid + r * 256] : 0u;
-        uint4 kc[D / 8];
-        load_k_page<D>(P, page0, pi0 * kPage < n_old, lane, kc);
-#pragma unroll
-        for (int r = 0; r < QW; ++r) {
-            const int i = tid + r * 256;
-            if (i < G * D / 2) s_q[i / (D / 2)][i % (D / 2)] = qv[r];
-        }
-        __syncthreads();
+        float z[G];
+        qk_page<D, G>(kc, s_q[wave], z);
+        load_q(hd1, new_head, qr);           // the next head's q, if the run moves on
+        issue_k<D>(P, pid1, more, lane, kc);  // K registers are free again
+        softmax_page<D, G>(z, P.scale_log2, base, n_old, e, lane, s_p[wave], m, l, acc);
+        wave_lds_sync();
+        pv_page<D, G>(vc, s_p[wave], acc);
+        issue_v<D>(P, pid1, more, lane, vc);  // V registers are free again
+        wave_lds_sync();                      // s_p is rewritten by the next page
 
-        float m[G], l[G], acc[G][VJ];
+        if (!more || new_head) {
+            // the run leaves head hd: its partial goes to slot w + hd
+            float* part = P.partials + (size_t)(w + hd) * PSTR;
+            if (lane == 0) {
 #pragma unroll
-        for (int g = 0; g < G; ++g) {
-            m[g] = -INFINITY;
-            l[g] = 0.f;
-#pragma unroll
-            for (int j = 0; j < VJ; ++j) acc[g][j] = 0.f;
-        }
-        // wave w takes pages w, w+4, ... of the item (empty ones are no-ops)
-#pragma unroll
-        for (int k = 0; k < kPagesPerWave; ++k) {
-            const int pi = pi0 + k * NW;
-            const int base = pi * kPage;
-            int page = page0;
-            if (k > 0) {
-                page = base < n_old ? P.ptable[(size_t)c.gh * P.pages_per_head + pi] : 0;
-                load_k_page<D>(P, page, base < n_old, lane, kc);
-            }
-            attend_page<D, G>(P, page, base, n_old, e, kc, s_q, s_p[wave], lane, m, l, acc);
-        }
-        if (lane == 0) {
-#pragma unroll
-            for (int g = 0; g < G; ++g) {
-                s_m[wave][g] = m[g];
-                s_l[wave][g] = l[g];
-            }
-        }
-#pragma unroll
-        for (int g = 0; g < G; ++g)
-#pragma unroll
-            for (int j = 0; j < VJ; ++j) s_acc[wave][g][j * 64 + lane] = acc[g][j];
-        __syncthreads();
-
-        float* part = P.partials + (size_t)item * (G * (D + 2));
-        for (int i = tid; i < G * D; i += 256) {
-            const int g = i / D, d = i - g * D;
-            float M = s_m[0][g];
-#pragma unroll
-            for (int w = 1; w < NW; ++w) M = fmaxf(M, s_m[w][g]);
-            float o = 0.f, L = 0.f;
-            if (M != -INFINITY) {
-#pragma unroll
-                for (int w = 0; w < NW; ++w) {
-                    const float sc = exp2f(s_m[w][g] - M);
-                    o += sc * s_acc[w][g][d];
-                    L += sc * s_l[w][g];
+                for (int g = 0; g < G; ++g) {
+                    part[g] = m[g];
+                    part[G + g] = l[g];
                 }
             }
-            part[2 * G + g * D + d] = o;
-            if (d == 0) {
-                part[g] = M;
-                part[G + g] = L;
+#pragma unroll
+            for (int g = 0; g < G; ++g) {
+#pragma unroll
+                for (int j = 0; j < VJ; ++j) {
+                    part[2 * G + g * D + j * 64 + lane] = acc[g][j];
+                    acc[g][j] = 0.f;
+                }
+                m[g] = -INFINITY;
+                l[g] = 0.f;
             }
+            if (new_head) store_q(qr);
         }
-        __syncthreads();
+        hd = hd1;
     }
 }
 
@@ -443,25 +488,61 @@ __global__ __launch_bounds__(256, 4) void decode_attend_kernel(DecodeArgs a) {
 // ---------------------------------------------------------------------------
 
 // Log-sum-exp merge of a head's partials with the new token; bf16 output of the
-// head's G q heads.  256 threads; each owns NPAIR (q head, dim) outputs and keeps
-// a running max and sum over chunks of 16 partials.
+// head's G q heads.  256 threads, each owning NPAIR (q head, dim) outputs.  Once
+// the head's partial range is known every load goes out together: maxima and
+// sums of the partials (thread t takes q head t % G of partials t / G, t / G +
+// 256 / G, ...) and the accumulators of the first PF partials; a head with more
+// partials reads the remaining accumulators afterwards.
 template <int D, int G>
 __device__ void merge_head(const DecodeArgs& a, int ch) {
     const PoolDev& P = a.pool;
     constexpr int NPAIR = (G * D + 255) / 256;
     constexpr int PSTR = G * (D + 2);  // floats per partial
-    constexpr int CH = 16;
+    constexpr int PF = 64 / NPAIR;     // accumulators held in registers
+    constexpr int KT = G;              // partials per thread whose m, l stay in registers (n <= 256)
+    constexpr int STEP = 256 / G;
     __shared__ float s_zn[G];
-    __shared__ float s_mc[CH][G], s_lc[CH][G];
+    __shared__ float s_red[2][4][G];  // per wave: max, then sum
+    __shared__ float s_w[PF][G];      // weights of the first PF partials
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const CallHead c = call_head(a, ch);
-    const int i0 = P.prefix[ch];
-    const int n = P.prefix[ch + 1] - i0;
+    // partial slots of this head: w + ch for the waves w whose runs of the page
+    // axis meet the head's pages [pf, pl); wave of page p: ((p + 1) * W - 1) / total
+    const int pf = P.prefix[ch], pl = P.prefix[ch + 1], total = P.prefix[a.n_call_heads];
+    int i0 = 0, n = 0;
+    if (pl > pf) {
+        const int64_t W = min(a.n_waves, total);
+        const int wf = (int)(((int64_t)(pf + 1) * W - 1) / total);
+        const int wl = (int)(((int64_t)pl * W - 1) / total);
+        i0 = wf + ch;
+        n = wl - wf + 1;
+    }
     const float* part0 = P.partials + (size_t)i0 * PSTR;
     const uint16_t* qg = a.q + ((size_t)c.row * P.n_q_heads + c.h * G) * D;
     const uint16_t* kn = a.k + ((size_t)c.row * P.n_kv_heads + c.h) * D;
     const uint16_t* vn = a.v + ((size_t)c.row * P.n_kv_heads + c.h) * D;
+
+    // accumulators of the first PF partials, and every maximum and sum
+    float x[NPAIR][PF];
+#pragma unroll
+    for (int r = 0; r < NPAIR; ++r) {
+        const int p = tid + r * 256;
+#pragma unroll
+        for (int u = 0; u < PF; ++u)
+            x[r][u] = (u < n && p < G * D) ? part0[(size_t)u * PSTR + 2 * G + p] : 0.f;
+    }
+    const int gt = tid % G;
+    float mi[KT], li[KT];
+    float mloc = -INFINITY;
+#pragma unroll
+    for (int k = 0; k < KT; ++k) {
+        const int i = tid / G + k * STEP;
+        mi[k] = i < n ? part0[(size_t)i * PSTR + gt] : -INFINITY;
+        li[k] = i < n ? part0[(size_t)i * PSTR + G + gt] : 0.f;
+        mloc = fmaxf(mloc, mi[k]);
+    }
+    for (int i = tid / G + KT * STEP; i < n; i += STEP) mloc = fmaxf(mloc, part0[(size_t)i * PSTR + gt]);
 
     float vnew[NPAIR];
 #pragma unroll
@@ -479,62 +560,53 @@ __device__ void merge_head(const DecodeArgs& a, int ch) {
         if (lane == 0) s_zn[g] = zn;
     }
 
-    float M[NPAIR], L[NPAIR], o[NPAIR];
+    // maximum per q head: lanes l and l ^ o share a q head for o >= G
 #pragma unroll
-    for (int r = 0; r < NPAIR; ++r) {
-        M[r] = -INFINITY;
-        L[r] = 0.f;
-        o[r] = 0.f;
+    for (int o = 32; o >= G; o >>= 1) mloc = fmaxf(mloc, __shfl_xor(mloc, o, 64));
+    if (lane < G) s_red[0][wave][lane] = mloc;
+    __syncthreads();
+    float Mt = s_red[0][0][gt];
+#pragma unroll
+    for (int w = 1; w < 4; ++w) Mt = fmaxf(Mt, s_red[0][w][gt]);
+    float lloc = 0.f;
+#pragma unroll
+    for (int k = 0; k < KT; ++k) {
+        const int i = tid / G + k * STEP;
+        const float wgt = (i < n && Mt != -INFINITY) ? exp2f(mi[k] - Mt) : 0.f;
+        lloc = fmaf(wgt, li[k], lloc);
+        if (i < PF) s_w[i][gt] = wgt;
     }
-    for (int ib = 0; ib < n; ib += CH) {
-        const int cnt = min(CH, n - ib);
-        if (tid < cnt * G) {
-            const int i = tid / G, g = tid - i * G;
-            s_mc[i][g] = part0[(size_t)(ib + i) * PSTR + g];
-            s_lc[i][g] = part0[(size_t)(ib + i) * PSTR + G + g];
-        }
-        float x[NPAIR][CH];
+    if (Mt != -INFINITY)
+        for (int i = tid / G + KT * STEP; i < n; i += STEP)
+            lloc = fmaf(exp2f(part0[(size_t)i * PSTR + gt] - Mt), part0[(size_t)i * PSTR + G + gt], lloc);
 #pragma unroll
-        for (int r = 0; r < NPAIR; ++r) {
-            const int p = tid + r * 256;
-#pragma unroll
-            for (int u = 0; u < CH; ++u)
-                x[r][u] = (u < cnt && p < G * D) ? part0[(size_t)(ib + u) * PSTR + 2 * G + p] : 0.f;
-        }
-        __syncthreads();
-#pragma unroll
-        for (int r = 0; r < NPAIR; ++r) {
-            const int g = min((tid + r * 256) / D, G - 1);
-            float cm = -INFINITY;
-            for (int u = 0; u < cnt; ++u) cm = fmaxf(cm, s_mc[u][g]);
-            const float mn = fmaxf(M[r], cm);
-            if (mn != -INFINITY) {
-                const float sc = exp2f(M[r] - mn);
-                o[r] *= sc;
-                L[r] *= sc;
-#pragma unroll
-                for (int u = 0; u < CH; ++u) {
-                    if (u < cnt) {
-                        const float w = exp2f(s_mc[u][g] - mn);
-                        o[r] = fmaf(w, x[r][u], o[r]);
-                        L[r] = fmaf(w, s_lc[u][g], L[r]);
-                    }
-                }
-                M[r] = mn;
-            }
-        }
-        __syncthreads();
-    }
-    __syncthreads();  // s_zn
+    for (int o = 32; o >= G; o >>= 1) lloc += __shfl_xor(lloc, o, 64);
+    if (lane < G) s_red[1][wave][lane] = lloc;
+    __syncthreads();
+
     uint16_t* og = a.out + ((size_t)c.row * P.n_q_heads + c.h * G) * D;
 #pragma unroll
     for (int r = 0; r < NPAIR; ++r) {
         const int p = tid + r * 256;
         if (p < G * D) {
-            const float zn = s_zn[p / D];
-            const float mn = fmaxf(M[r], zn);
-            const float sc = exp2f(M[r] - mn), sn = exp2f(zn - mn);
-            og[p] = f32_to_bf16((o[r] * sc + sn * vnew[r]) / (L[r] * sc + sn));
+            const int g = p / D;
+            float M = s_red[0][0][g], L = 0.f;
+#pragma unroll
+            for (int w = 0; w < 4; ++w) {
+                M = fmaxf(M, s_red[0][w][g]);
+                L += s_red[1][w][g];
+            }
+            float o = 0.f;
+#pragma unroll
+            for (int u = 0; u < PF; ++u)
+                if (u < n) o = fmaf(s_w[u][g], x[r][u], o);
+            if (M != -INFINITY)
+                for (int u = PF; u < n; ++u)
+                    o = fmaf(exp2f(part0[(size_t)u * PSTR + g] - M), part0[(size_t)u * PSTR + 2 * G + p], o);
+            const float zn = s_zn[g];
+            const float mn = fmaxf(M, zn);
+            const float sc = M == -INFINITY ? 0.f : exp2f(M - mn), sn = exp2f(zn - mn);
+            og[p] = f32_to_bf16((o * sc + sn * vnew[r]) / (L * sc + sn));
         }
     }
 }
@@ -749,13 +821,13 @@ __global__ __launch_bounds__(64) void seq_release_kernel(PoolDev P, int seq) {
         for (int i = 0; i < kHS; ++i) hs[i] = i == kHsExp ? -1 : 0;
 }
 
-size_t decode_shm(const DecodeArgs& a) { return (size_t)(3 * a.n_call_heads + 1) * sizeof(int32_t); }
+size_t decode_shm(const DecodeArgs& a) { return (size_t)(4 * a.n_call_heads + 1) * sizeof(int32_t); }
 
 template <int D, int G>
 hipError_t launch_decode_t(const DecodeArgs& a, int grid, hipStream_t s, hipEvent_t* ev) {
     hipError_t err;
     if (ev && (err = hipEventRecord(ev[0], s)) != hipSuccess) return err;
-    hipLaunchKernelGGL((decode_attend_kernel<D, G>), dim3(grid), dim3(256), decode_shm(a), s, a);
+    hipLaunchKernelGGL((decode_attend_kernel<D, G>), dim3(grid), dim3(64 * kAttendWaves), decode_shm(a), s, a);
     if ((err = hipGetLastError()) != hipSuccess) return err;
     if (ev && (err = hipEventRecord(ev[1], s)) != hipSuccess) return err;
     hipLaunchKernelGGL((decode_merge_kernel<D, G>), dim3(2 * a.n_call_heads), dim3(256), 0, s, a);
@@ -767,9 +839,10 @@ hipError_t launch_decode_t(const DecodeArgs& a, int grid, hipStream_t s, hipEven
 template <int D, int G>
 int blocks_per_cu_t(const DecodeArgs& a) {
     int n = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_attend_kernel<D, G>, 256, decode_shm(a)) != hipSuccess)
-        return 1;
-    return n > 0 ? n : 1;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_attend_kernel<D, G>, 64 * kAttendWaves,
+                                                     decode_shm(a)) != hipSuccess)
+        return 0;
+    return n;
 }
 
 template <int D>
@@ -791,7 +864,7 @@ int blocks_per_cu_d(const DecodeArgs& a) {
         case 4: return blocks_per_cu_t<D, 4>(a);
         case 8: return blocks_per_cu_t<D, 8>(a);
     }
-    return 1;
+    return 0;
 }
 
 }  // namespace
