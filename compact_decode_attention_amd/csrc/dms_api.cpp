@@ -71,7 +71,7 @@ bool make_layout(const dms_pool_config* c, Layout* L, std::string* why) {
     sz[S_HSTATE] = (size_t)heads * dms::kHS * 4;
     sz[S_PTABLE] = (size_t)heads * L->pages_per_head * 4;
     sz[S_RING] = (size_t)heads * L->ring_len * 4;
-    sz[S_PART] = (size_t)L->max_items * g * (D + 2) * 4;
+    sz[S_PART] = (size_t)L->max_items * dms::part_stride(g, (int)D) * 4;
     sz[S_PREFIX] = (size_t)(L->max_call_heads + 1) * 4;
     sz[S_INV] = (size_t)c->n_kv_heads * c->max_positions * 4;
     sz[S_PCNT] = sz[S_INV];

@@ -13,7 +13,7 @@
 //   ptable   int32 [heads][pages_per_head]         page of slots 64j .. 64j+63
 //   ring     int32 [heads][ring_len]               entry of position s at s % w:
 //                                                  (slot << 1) | mark, -1 = none
-//   partials f32   [max_items][G*(head_dim+2)]     split-K partials {m[G], l[G], acc[G][D]},
+//   partials f32   [max_items][part_stride(G, D)] split-K partials {m[G], l[G], pad, acc[G][D]},
 //                                                  slot w + ch for wave w and call head ch
 //   prefix   int32 [max_call_heads + 1]            first page of each call head on the page
 //                                                  axis of the last decode launch
@@ -45,6 +45,9 @@ constexpr int kPage = 64;          // slots per page
 constexpr int kAttendWaves = DMS_ATTEND_WAVES;
 constexpr int kAttendBlocksPerCU = DMS_ATTEND_BLOCKS_PER_CU;
 constexpr int kMaxAttendBlocks = 4096 / kAttendWaves;
+// Split-K partial of G q heads: m[G], l[G], padding to 16 bytes, acc[G][D].
+constexpr int part_acc_off(int g) { return (2 * g + 3) & ~3; }
+constexpr int part_stride(int g, int d) { return part_acc_off(g) + g * d; }  // floats
 constexpr int kMaxCallSeqs = 256;  // sequences per kernel launch (larger calls are split)
 constexpr int kMaxCallHeads = 4032;  // heads per launch (4 ints of plan per head in LDS, < 64 KB)
 

@@ -327,7 +327,8 @@ void decode_attend_kernel(DecodeArgs a) {
     constexpr int VJ = D / 64;
     constexpr int QV = G * D / 8;  // 16-byte pieces of one head group's q
     constexpr int QR = (QV + 63) / 64;
-    constexpr int PSTR = G * (D + 2);
+    constexpr int PSTR = part_stride(G, D);
+    constexpr int ACC = part_acc_off(G);
     const int H = a.n_call_heads;
     extern __shared__ int32_t s_dyn[];
     int32_t* s_pp = s_dyn;            // [H + 1] first page of each head on the call's page axis
@@ -468,7 +469,7 @@ void decode_attend_kernel(DecodeArgs a) {
             for (int g = 0; g < G; ++g) {
 #pragma unroll
                 for (int j = 0; j < VJ; ++j) {
-                    part[2 * G + g * D + j * 64 + lane] = acc[g][j];
+                    part[ACC + g * D + j * 64 + lane] = acc[g][j];
                     acc[g][j] = 0.f;
                 }
                 m[g] = -INFINITY;
@@ -488,22 +489,27 @@ void decode_attend_kernel(DecodeArgs a) {
 // ---------------------------------------------------------------------------
 
 // Log-sum-exp merge of a head's partials with the new token; bf16 output of the
-// head's G q heads.  256 threads, each owning NPAIR (q head, dim) outputs.  Once
-// the head's partial range is known every load goes out together: maxima and
-// sums of the partials (thread t takes q head t % G of partials t / G, t / G +
-// 256 / G, ...) and the accumulators of the first PF partials; a head with more
-// partials reads the remaining accumulators afterwards.
+// head's G q heads.  256 threads.  Once the head's partial range is known the
+// loads go out together, 16 bytes per lane: thread t owns output float4 f = t % NF
+// for the partials u = t / NF, t / NF + NPH, ... (a round of RU of them in
+// registers), and the maxima and sums (thread t: q head t % G of partials t / G,
+// t / G + 256 / G, ...).  The NPH phases are summed through LDS.
 template <int D, int G>
 __device__ void merge_head(const DecodeArgs& a, int ch) {
     const PoolDev& P = a.pool;
-    constexpr int NPAIR = (G * D + 255) / 256;
-    constexpr int PSTR = G * (D + 2);  // floats per partial
-    constexpr int PF = 64 / NPAIR;     // accumulators held in registers
-    constexpr int KT = G;              // partials per thread whose m, l stay in registers (n <= 256)
+    constexpr int PSTR = part_stride(G, D);  // floats per partial
+    constexpr int ACC = part_acc_off(G);
+    constexpr int NF = G * D / 4;            // float4 outputs of the head
+    constexpr int NPH = 256 / NF;            // partial phases (NF divides 256)
+    constexpr int RU = 16;                   // accumulators per thread per round
     constexpr int STEP = 256 / G;
+    constexpr int KT = G;                    // partials per thread whose m, l stay in registers
+    constexpr int NW_MAX = KT * STEP;        // partials whose weights are kept in LDS (256)
+    static_assert(NF * NPH == 256, "output float4s must tile the block");
     __shared__ float s_zn[G];
     __shared__ float s_red[2][4][G];  // per wave: max, then sum
-    __shared__ float s_w[PF][G];      // weights of the first PF partials
+    __shared__ float s_w[NW_MAX][G];  // weights
+    __shared__ float4 s_o[NPH > 1 ? NPH - 1 : 1][NF];
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const CallHead c = call_head(a, ch);
@@ -522,15 +528,16 @@ __device__ void merge_head(const DecodeArgs& a, int ch) {
     const uint16_t* qg = a.q + ((size_t)c.row * P.n_q_heads + c.h * G) * D;
     const uint16_t* kn = a.k + ((size_t)c.row * P.n_kv_heads + c.h) * D;
     const uint16_t* vn = a.v + ((size_t)c.row * P.n_kv_heads + c.h) * D;
+    const int f = tid % NF, ph = tid / NF;
+    const int gf = (4 * f) / D;  // q head of this thread's outputs
 
-    // accumulators of the first PF partials, and every maximum and sum
-    float x[NPAIR][PF];
+    // first round of accumulators, and every maximum and sum
+    float4 xv[RU];
 #pragma unroll
-    for (int r = 0; r < NPAIR; ++r) {
-        const int p = tid + r * 256;
-#pragma unroll
-        for (int u = 0; u < PF; ++u)
-            x[r][u] = (u < n && p < G * D) ? part0[(size_t)u * PSTR + 2 * G + p] : 0.f;
+    for (int j = 0; j < RU; ++j) {
+        const int u = ph + j * NPH;
+        xv[j] = u < n ? *reinterpret_cast<const float4*>(part0 + (size_t)u * PSTR + ACC + 4 * f)
+                      : make_float4(0.f, 0.f, 0.f, 0.f);
     }
     const int gt = tid % G;
     float mi[KT], li[KT];
@@ -542,15 +549,9 @@ __device__ void merge_head(const DecodeArgs& a, int ch) {
         li[k] = i < n ? part0[(size_t)i * PSTR + G + gt] : 0.f;
         mloc = fmaxf(mloc, mi[k]);
     }
-    for (int i = tid / G + KT * STEP; i < n; i += STEP) mloc = fmaxf(mloc, part0[(size_t)i * PSTR + gt]);
-
-    float vnew[NPAIR];
-#pragma unroll
-    for (int r = 0; r < NPAIR; ++r) {
-        const int p = tid + r * 256;
-        vnew[r] = p < G * D ? bf16_to_f32(vn[p % D]) : 0.f;
-    }
-    // new-token score of each q head (one wave per q head)
+    for (int i = tid / G + NW_MAX; i < n; i += STEP) mloc = fmaxf(mloc, part0[(size_t)i * PSTR + gt]);
+    // the new token: its value row and the score of each q head (one wave per q head)
+    const uint2 vraw = *reinterpret_cast<const uint2*>(vn + (4 * f) % D);
     for (int g = wave; g < G; g += 4) {
         float dp = 0.f;
 #pragma unroll
@@ -574,41 +575,71 @@ __device__ void merge_head(const DecodeArgs& a, int ch) {
         const int i = tid / G + k * STEP;
         const float wgt = (i < n && Mt != -INFINITY) ? exp2f(mi[k] - Mt) : 0.f;
         lloc = fmaf(wgt, li[k], lloc);
-        if (i < PF) s_w[i][gt] = wgt;
+        s_w[i][gt] = wgt;
     }
     if (Mt != -INFINITY)
-        for (int i = tid / G + KT * STEP; i < n; i += STEP)
+        for (int i = tid / G + NW_MAX; i < n; i += STEP)
             lloc = fmaf(exp2f(part0[(size_t)i * PSTR + gt] - Mt), part0[(size_t)i * PSTR + G + gt], lloc);
 #pragma unroll
     for (int o = 32; o >= G; o >>= 1) lloc += __shfl_xor(lloc, o, 64);
     if (lane < G) s_red[1][wave][lane] = lloc;
     __syncthreads();
 
-    uint16_t* og = a.out + ((size_t)c.row * P.n_q_heads + c.h * G) * D;
+    float M = s_red[0][0][gf], L = 0.f;
 #pragma unroll
-    for (int r = 0; r < NPAIR; ++r) {
-        const int p = tid + r * 256;
-        if (p < G * D) {
-            const int g = p / D;
-            float M = s_red[0][0][g], L = 0.f;
+    for (int w = 0; w < 4; ++w) {
+        M = fmaxf(M, s_red[0][w][gf]);
+        L += s_red[1][w][gf];
+    }
+    auto weight = [&](int u) -> float {
+        if (u < NW_MAX) return s_w[u][gf];
+        return M == -INFINITY ? 0.f : exp2f(part0[(size_t)u * PSTR + gf] - M);
+    };
+    float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int u0 = 0; u0 < n; u0 += RU * NPH) {
+        if (u0 > 0) {  // a further round: its loads first
 #pragma unroll
-            for (int w = 0; w < 4; ++w) {
-                M = fmaxf(M, s_red[0][w][g]);
-                L += s_red[1][w][g];
+            for (int j = 0; j < RU; ++j) {
+                const int u = u0 + ph + j * NPH;
+                xv[j] = u < n ? *reinterpret_cast<const float4*>(part0 + (size_t)u * PSTR + ACC + 4 * f)
+                              : make_float4(0.f, 0.f, 0.f, 0.f);
             }
-            float o = 0.f;
+        }
 #pragma unroll
-            for (int u = 0; u < PF; ++u)
-                if (u < n) o = fmaf(s_w[u][g], x[r][u], o);
-            if (M != -INFINITY)
-                for (int u = PF; u < n; ++u)
-                    o = fmaf(exp2f(part0[(size_t)u * PSTR + g] - M), part0[(size_t)u * PSTR + 2 * G + p], o);
-            const float zn = s_zn[g];
-            const float mn = fmaxf(M, zn);
-            const float sc = M == -INFINITY ? 0.f : exp2f(M - mn), sn = exp2f(zn - mn);
-            og[p] = f32_to_bf16((o * sc + sn * vnew[r]) / (L * sc + sn));
+        for (int j = 0; j < RU; ++j) {
+            const int u = u0 + ph + j * NPH;
+            if (u < n) {
+                const float wgt = weight(u);
+                o.x = fmaf(wgt, xv[j].x, o.x);
+                o.y = fmaf(wgt, xv[j].y, o.y);
+                o.z = fmaf(wgt, xv[j].z, o.z);
+                o.w = fmaf(wgt, xv[j].w, o.w);
+            }
         }
     }
+    if (NPH > 1) {
+        if (ph > 0) s_o[ph - 1][f] = o;
+        __syncthreads();
+        if (ph > 0) return;
+#pragma unroll
+        for (int q = 0; q < NPH - 1; ++q) {
+            const float4 t = s_o[q][f];
+            o.x += t.x;
+            o.y += t.y;
+            o.z += t.z;
+            o.w += t.w;
+        }
+    }
+    const float zn = s_zn[gf];
+    const float mn = fmaxf(M, zn);
+    const float sc = M == -INFINITY ? 0.f : exp2f(M - mn), sn = exp2f(zn - mn);
+    const float den = 1.f / (L * sc + sn);
+    const float v0 = bf16_to_f32((uint16_t)(vraw.x & 0xffffu)), v1 = bf16_to_f32((uint16_t)(vraw.x >> 16));
+    const float v2 = bf16_to_f32((uint16_t)(vraw.y & 0xffffu)), v3 = bf16_to_f32((uint16_t)(vraw.y >> 16));
+    uint2 packed;
+    packed.x = (uint32_t)f32_to_bf16((o.x * sc + sn * v0) * den) | ((uint32_t)f32_to_bf16((o.y * sc + sn * v1) * den) << 16);
+    packed.y = (uint32_t)f32_to_bf16((o.z * sc + sn * v2) * den) | ((uint32_t)f32_to_bf16((o.w * sc + sn * v3) * den) << 16);
+    *reinterpret_cast<uint2*>(a.out + ((size_t)c.row * P.n_q_heads + c.h * G) * D + 4 * f) = packed;
 }
 
 // Mark the new token, expire position t-w if it was marked (its slot e is
