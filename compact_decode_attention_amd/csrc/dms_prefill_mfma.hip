@@ -32,6 +32,7 @@ namespace dms {
 namespace {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
 __device__ __forceinline__ bf16x8_t as_bf16x8(uint4 u) { return __builtin_bit_cast(bf16x8_t, u); }
@@ -94,30 +95,51 @@ __global__ __launch_bounds__(256) void prefill_vt_kernel(PrefillArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// masked prefill attention, one block = (kv head, 32-query tile), one wave per q head
+// masked prefill attention.  One block = (kv head, QT consecutive 32-query
+// tiles), 8 waves: wave qt * G + g computes q head h * G + g on query tile qt.
+// Key tiles of 32 are staged in LDS, double-buffered, by all threads of the
+// block: K as [D/8][32] 16-byte units (A operand of S^T = K Q^T: lane = key row,
+// 16 bytes = 8 dims), V as [4][D] units (A operand of O^T = V^T P^T: lane = dim,
+// 16 bytes = 8 keys).  While a tile is computed the next one is in flight.
+//
+// Key tiles of a block whose first query tile starts at t0b (xf = t0b - w):
+//   far field  the first U = #live[0, xf] pool slots: unmarked keys older than
+//              every query's window, visible to all queries of the block
+//   band       prompt keys in (xf, t0b + 32 QT), masked per (query, key) pair
 // ---------------------------------------------------------------------------
+constexpr int kPrefillWaves = 8;
+
 template <int D, int G>
-__global__ __launch_bounds__(64 * G) void prefill_attend_kernel(PrefillArgs a) {
-    constexpr int KS = D / 16;  // k-steps of S^T = K Q^T over the head dim
-    constexpr int DT = D / 32;  // 32-row tiles of O^T
+__global__ __attribute__((amdgpu_flat_work_group_size(64 * kPrefillWaves, 64 * kPrefillWaves),
+                          amdgpu_waves_per_eu(2, 2)))
+void prefill_attend_kernel(PrefillArgs a) {
+    constexpr int NT = 64 * kPrefillWaves;
+    constexpr int QT = kPrefillWaves / G;  // query tiles per block
+    constexpr int KS = D / 16;             // k-steps of S^T over the head dim
+    constexpr int DT = D / 32;             // 32-row tiles of O^T
+    constexpr int UNITS = 4 * D;           // 16-byte units of a K (or V) tile of 32 keys
+    static_assert(UNITS <= NT, "one unit of K and one of V per thread");
+    __shared__ uint4 s_k[2][D / 8][32];
+    __shared__ uint4 s_v[2][4][D];
+    __shared__ uint32_t s_marks[2];
     const PoolDev& P = a.pool;
     const int T = a.n_tokens, w = P.window, hkv = P.n_kv_heads, hq_n = P.n_q_heads;
-    const int nqt = (T + 31) / 32;
+    const int nqb = (T + 32 * QT - 1) / (32 * QT);
     // Blocks b, b+8, b+16, ... are placed on the same XCD; hand each XCD a run of
-    // consecutive (kv head, query tile) pairs so that a head's keys stay in that
-    // XCD's L2.  Later tiles (more keys) first.
-    const int total = hkv * nqt;
+    // consecutive (kv head, query block) pairs so that a head's keys stay in that
+    // XCD's L2.  Later query blocks (more keys) first.
+    const int total = hkv * nqb;
     const int per_xcd = (total + 7) / 8;
     const int pidx = (int)(blockIdx.x % 8) * per_xcd + (int)(blockIdx.x / 8);
     if (pidx >= total) return;
-    const int h = pidx / nqt;
-    const int t0 = (nqt - 1 - pidx % nqt) * 32;
-    const int lane = threadIdx.x & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int hq = h * G + wave;
+    const int h = pidx / nqb;
+    const int t0b = (nqb - 1 - pidx % nqb) * (32 * QT);
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int qt = wave / G, hq = h * G + wave % G;
     const int gh = (a.seq * P.n_layers + a.layer) * hkv + h;
     const int col = lane & 31, half = lane >> 5;
-    const int tq = t0 + col;  // this lane's query
+    const int tq = t0b + 32 * qt + col;  // this lane's query
     const float sl = P.scale_log2;
 
     // Q^T as the B operand: column = query, 8 consecutive dims per half-wave
@@ -127,121 +149,164 @@ __global__ __launch_bounds__(64 * G) void prefill_attend_kernel(PrefillArgs a) {
         qb[ks] = tq < T ? *reinterpret_cast<const uint4*>(a.q + ((size_t)tq * hq_n + hq) * D + ks * 16 + half * 8)
                         : make_uint4(0, 0, 0, 0);
 
+    // ---- the block's key tiles
+    const int xf = t0b - w;
+    const int U = xf >= 0 ? P.pcnt[(size_t)h * P.max_positions + xf] : 0;
+    const int nfar = (U + 31) / 32;
+    const int band0 = max(0, xf + 1) / 32 * 32;
+    const int kend = min(T, t0b + 32 * QT);
+    const int ntiles = nfar + (kend > band0 ? (kend - band0 + 31) / 32 : 0);
+    const int32_t* ptab = P.ptable + (size_t)gh * P.pages_per_head;
+    const uint16_t* vt = P.vt + (size_t)h * (P.max_pos32 / 8) * D * 8;
+
+    // Staging, thread t < UNITS: K unit t (chunk t / 32, key t % 32) and V unit t.
+    // K runs one tile ahead of V: while tile i is folded (scores S_i, computed one
+    // iteration earlier, and V_i) the block computes S_{i+1} from K_{i+1}, and the
+    // loads of K_{i+2} and V_{i+1} are in flight.
+    auto tile_kb = [&](int i) { return i < nfar ? 32 * i : band0 + 32 * (i - nfar); };
+    uint4 rk = make_uint4(0, 0, 0, 0), rv = make_uint4(0, 0, 0, 0);
+    bool rmark = false;
+    auto load_k = [&](int i) {
+        const int cc = tid >> 5, j = tid & 31;
+        const int kb = tile_kb(i);
+        if (tid < UNITS) {
+            if (i < nfar) {
+                const uint16_t* kp = P.kpages + (size_t)ptab[kb / kPage] * (kPage * D);
+                rk = *reinterpret_cast<const uint4*>(kp + ((size_t)cc * kPage + kb % kPage + j) * 8);
+            } else {
+                const int sk = kb + j;
+                rk = sk < T ? *reinterpret_cast<const uint4*>(a.k + ((size_t)sk * hkv + h) * D + cc * 8)
+                            : make_uint4(0, 0, 0, 0);
+            }
+        }
+    };
+    auto load_v = [&](int i) {
+        const int kb = tile_kb(i);
+        if (tid < UNITS) {
+            if (i < nfar) {
+                const uint16_t* vp = P.vpages + (size_t)ptab[kb / kPage] * (kPage * D);
+                rv = *reinterpret_cast<const uint4*>(vp + ((size_t)(kb % kPage / 8) * D) * 8 + (size_t)tid * 8);
+            } else {
+                rv = *reinterpret_cast<const uint4*>(vt + ((size_t)(kb / 8) * D) * 8 + (size_t)tid * 8);
+            }
+        }
+        if (i >= nfar && tid < 32) {
+            const int sk = kb + tid;
+            rmark = sk < T && a.logits[(size_t)sk * hkv + h] > 0.f;
+        }
+    };
+    auto store_k = [&](int i) {
+        if (tid < UNITS) s_k[i & 1][tid >> 5][tid & 31] = rk;
+    };
+    auto store_v = [&](int i) {
+        if (tid < UNITS) s_v[i & 1][tid / D][tid % D] = rv;
+        if (i >= nfar && wave == 0) {
+            const uint32_t mk = (uint32_t)__ballot(rmark);
+            if (lane == 0) s_marks[i & 1] = mk;
+        }
+    };
+    const int krow = swap23(col);  // key this lane feeds as A-operand row
+    auto scores = [&](int i) {
+        f32x16_t sc = f32x16_t{};
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+            sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(s_k[i & 1][2 * ks + half][krow]),
+                                                         as_bf16x8(qb[ks]), sc, 0, 0, 0);
+        return sc;
+    };
+
     f32x16_t o[DT];
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) o[dt] = f32x16_t{};
     float m = -INFINITY, lsum = 0.f;
-    const int krow = swap23(col);  // key this lane feeds as A-operand row
 
-    // fold one 32-key tile (scores in s) into the running state; valid per reg
-    auto fold = [&](f32x16_t s, const uint32_t (&vmask)[1], const uint4 (&va)[DT][2]) {
+    // prologue: K_0, V_0, K_1 in LDS, S_0
+    load_k(0);
+    load_v(0);
+    store_k(0);
+    store_v(0);
+    if (ntiles > 1) {
+        load_k(1);
+        store_k(1);
+    }
+    __syncthreads();
+    f32x16_t s = scores(0);
+    for (int i = 0; i < ntiles; ++i) {
+        const bool more = i + 1 < ntiles;
+        if (i + 2 < ntiles) load_k(i + 2);
+        if (more) load_v(i + 1);
+        f32x16_t s_next = f32x16_t{};
+        if (more) s_next = scores(i + 1);
+
+        // ---- fold tile i: row r of S_i holds key kb + (r & 7) + 8 half + 16 (r >> 3)
+        const int kb = tile_kb(i);
         float z[16];
-        float tmax = -INFINITY;
+        if (i < nfar && kb + 32 <= U) {
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            z[r] = ((vmask[0] >> r) & 1u) ? s[r] * sl : -INFINITY;
-            tmax = fmaxf(tmax, z[r]);
+            for (int r = 0; r < 16; ++r) z[r] = s[r];
+        } else if (i < nfar) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) z[r] = kb + (r & 7) + 8 * half + 16 * (r >> 3) < U ? s[r] : -INFINITY;
+        } else {
+            const uint32_t marks = s_marks[i & 1];
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int kr = (r & 7) + 8 * half + 16 * (r >> 3);
+                const int key = kb + kr;
+                const bool marked = (marks >> kr) & 1u;
+                const bool vis = key > xf && key <= tq && tq < T && (!marked || tq < key + w);
+                z[r] = vis ? s[r] : -INFINITY;
+            }
         }
-        tmax = fmaxf(tmax, xor32(tmax));
-        const float mn = fmaxf(m, tmax);
-        float alpha = 1.f;
+        float tmax = z[0];
+#pragma unroll
+        for (int r = 1; r < 16; ++r) tmax = fmaxf(tmax, z[r]);
+        tmax = fmaxf(tmax, xor32(tmax)) * sl;  // base-2 units (sl > 0)
+        // lazy rescale: the running maximum moves only when a score exceeds it by
+        // more than 8 (base 2), so weights stay below 256
+        const bool grow = tmax > m + 8.f;
+        if (__ballot(grow)) {
+            const float mn = grow ? tmax : m;
+            const float alpha = mn == -INFINITY ? 1.f : exp2f(m - mn);
+            lsum *= alpha;
+            m = mn;
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) o[dt][r] *= alpha;
+        }
         // P^T enters the PV product as two bf16 parts, hi = bf16(p) and
         // lo = bf16(p - hi): about 16 significant bits, fp32 accumulation
         uint32_t ph[8], pl[8];
-        if (mn == -INFINITY) {
+        float ps = 0.f;
+        const float nm = m == -INFINITY ? 0.f : -m;
 #pragma unroll
-            for (int i = 0; i < 8; ++i) ph[i] = pl[i] = 0;
-        } else {
-            alpha = exp2f(m - mn);
-            float ps = 0.f;
-#pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                const float p0 = exp2f(z[2 * i] - mn), p1 = exp2f(z[2 * i + 1] - mn);
-                ph[i] = pack_bf16x2(p0, p1);
-                pl[i] = pack_bf16x2(p0 - bf16_f(ph[i] & 0xffffu), p1 - bf16_f(ph[i] >> 16));
-                ps += p0 + p1;
-            }
-            lsum = lsum * alpha + ps;
-            m = mn;
+        for (int i2 = 0; i2 < 8; ++i2) {
+            const float p0 = m == -INFINITY ? 0.f : exp2f(fmaf(z[2 * i2], sl, nm));
+            const float p1 = m == -INFINITY ? 0.f : exp2f(fmaf(z[2 * i2 + 1], sl, nm));
+            const bf16x2_t hv = {(__bf16)p0, (__bf16)p1};
+            const bf16x2_t lv = {(__bf16)(p0 - (float)hv[0]), (__bf16)(p1 - (float)hv[1])};
+            ph[i2] = __builtin_bit_cast(uint32_t, hv);
+            pl[i2] = __builtin_bit_cast(uint32_t, lv);
+            ps += p0 + p1;
         }
+        lsum += ps;
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt) {
 #pragma unroll
-            for (int r = 0; r < 16; ++r) o[dt][r] *= alpha;
-#pragma unroll
             for (int kk = 0; kk < 2; ++kk) {
+                const uint4 va = s_v[i & 1][2 * kk + half][dt * 32 + col];
                 const uint4 hb = make_uint4(ph[4 * kk], ph[4 * kk + 1], ph[4 * kk + 2], ph[4 * kk + 3]);
                 const uint4 lb = make_uint4(pl[4 * kk], pl[4 * kk + 1], pl[4 * kk + 2], pl[4 * kk + 3]);
-                o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(va[dt][kk]), as_bf16x8(hb), o[dt], 0, 0, 0);
-                o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(va[dt][kk]), as_bf16x8(lb), o[dt], 0, 0, 0);
+                o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(va), as_bf16x8(hb), o[dt], 0, 0, 0);
+                o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(va), as_bf16x8(lb), o[dt], 0, 0, 0);
             }
         }
-    };
-
-    // ---- far field: the first U slots of the compacted store
-    const int xf = t0 - w;
-    const int U = xf >= 0 ? P.pcnt[(size_t)h * P.max_positions + xf] : 0;
-    for (int kb = 0; kb < U; kb += 32) {
-        const int page = P.ptable[(size_t)gh * P.pages_per_head + kb / kPage];
-        const uint16_t* kp = P.kpages + (size_t)page * (kPage * D);
-        const uint16_t* vp = P.vpages + (size_t)page * (kPage * D);
-        const int off = kb % kPage;
-        f32x16_t s = f32x16_t{};
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-            const uint4 ka = *reinterpret_cast<const uint4*>(kp + ((size_t)(2 * ks + half) * kPage + off + krow) * 8);
-            s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(ka), as_bf16x8(qb[ks]), s, 0, 0, 0);
-        }
-        uint4 va[DT][2];
-#pragma unroll
-        for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-            for (int kk = 0; kk < 2; ++kk)
-                va[dt][kk] = *reinterpret_cast<const uint4*>(
-                    vp + ((size_t)((off + 16 * kk + 8 * half) / 8) * D + dt * 32 + col) * 8);
-        uint32_t vmask[1] = {0};
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const int key = kb + (r & 7) + 8 * half + 16 * (r >> 3);
-            vmask[0] |= (key < U ? 1u : 0u) << r;
-        }
-        fold(s, vmask, va);
-    }
-
-    // ---- band: keys (t0 - w, t0 + 31], from the prompt, masked per pair
-    const int sb0 = max(0, t0 - w + 1);
-    const int kend = min(T, t0 + 32);
-    const uint16_t* vt = P.vt + (size_t)h * (P.max_pos32 / 8) * D * 8;
-    for (int kb = sb0 / 32 * 32; kb < kend; kb += 32) {
-        const int sk = kb + krow;
-        f32x16_t s = f32x16_t{};
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-            const uint4 ka = sk < T ? *reinterpret_cast<const uint4*>(a.k + ((size_t)sk * hkv + h) * D + ks * 16 + half * 8)
-                                    : make_uint4(0, 0, 0, 0);
-            s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(ka), as_bf16x8(qb[ks]), s, 0, 0, 0);
-        }
-        uint4 va[DT][2];
-#pragma unroll
-        for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-            for (int kk = 0; kk < 2; ++kk)
-                va[dt][kk] = *reinterpret_cast<const uint4*>(
-                    vt + ((size_t)((kb + 16 * kk + 8 * half) / 8) * D + dt * 32 + col) * 8);
-        // marks of the tile's 32 keys, one bit per key
-        const int sm = kb + col;
-        const bool mk = sm < T && a.logits[(size_t)sm * hkv + h] > 0.f;
-        const uint32_t marks = (uint32_t)__ballot(mk && half == 0);
-        uint32_t vmask[1] = {0};
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const int kr = (r & 7) + 8 * half + 16 * (r >> 3);
-            const int key = kb + kr;
-            const bool marked = (marks >> kr) & 1u;
-            const bool vis = key > xf && key <= tq && tq < T && (!marked || tq < key + w);
-            vmask[0] |= (vis ? 1u : 0u) << r;
-        }
-        fold(s, vmask, va);
+        // K_{i+2} replaces K_i (read for S_i one iteration ago), V_{i+1} replaces V_{i-1}
+        if (i + 2 < ntiles) store_k(i + 2);
+        if (more) store_v(i + 1);
+        __syncthreads();
+        s = s_next;
     }
 
     // ---- normalise and store: lane holds dims dt*32 + 8*(r/4) + 4*half + r%4 of query tq
@@ -263,10 +328,11 @@ __global__ __launch_bounds__(64 * G) void prefill_attend_kernel(PrefillArgs a) {
 
 template <int D, int G>
 hipError_t launch_attend_t(const PrefillArgs& a, hipStream_t s) {
-    const int nqt = (a.n_tokens + 31) / 32;
-    const int total = a.pool.n_kv_heads * nqt;
+    constexpr int QT = kPrefillWaves / G;
+    const int nqb = (a.n_tokens + 32 * QT - 1) / (32 * QT);
+    const int total = a.pool.n_kv_heads * nqb;
     const int grid = 8 * ((total + 7) / 8);
-    hipLaunchKernelGGL((prefill_attend_kernel<D, G>), dim3(grid), dim3(64 * G), 0, s, a);
+    hipLaunchKernelGGL((prefill_attend_kernel<D, G>), dim3(grid), dim3(64 * kPrefillWaves), 0, s, a);
     return hipGetLastError();
 }
 
