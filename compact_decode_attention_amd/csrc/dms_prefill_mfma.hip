@@ -207,11 +207,13 @@ void prefill_attend_kernel(PrefillArgs a) {
     };
     const int krow = swap23(col);  // key this lane feeds as A-operand row
     auto scores = [&](int i) {
+        uint4 ka[KS];  // every K operand of the tile first: one wait for LDS
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) ka[ks] = s_k[i & 1][2 * ks + half][krow];
         f32x16_t sc = f32x16_t{};
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks)
-            sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(s_k[i & 1][2 * ks + half][krow]),
-                                                         as_bf16x8(qb[ks]), sc, 0, 0, 0);
+            sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(ka[ks]), as_bf16x8(qb[ks]), sc, 0, 0, 0);
         return sc;
     };
 
@@ -230,33 +232,36 @@ void prefill_attend_kernel(PrefillArgs a) {
         store_k(1);
     }
     __syncthreads();
-    f32x16_t s = scores(0);
-    for (int i = 0; i < ntiles; ++i) {
+    // one tile: fold S_i (in cur) while S_{i+1} (into nxt) and the next loads run
+    auto step = [&](int i, const f32x16_t& cur, f32x16_t& nxt) {
         const bool more = i + 1 < ntiles;
         if (i + 2 < ntiles) load_k(i + 2);
-        if (more) load_v(i + 1);
-        f32x16_t s_next = f32x16_t{};
-        if (more) s_next = scores(i + 1);
+        if (more) {
+            load_v(i + 1);
+            nxt = scores(i + 1);
+        }
 
         // ---- fold tile i: row r of S_i holds key kb + (r & 7) + 8 half + 16 (r >> 3)
         const int kb = tile_kb(i);
         float z[16];
         if (i < nfar && kb + 32 <= U) {
 #pragma unroll
-            for (int r = 0; r < 16; ++r) z[r] = s[r];
+            for (int r = 0; r < 16; ++r) z[r] = cur[r];
         } else if (i < nfar) {
 #pragma unroll
-            for (int r = 0; r < 16; ++r) z[r] = kb + (r & 7) + 8 * half + 16 * (r >> 3) < U ? s[r] : -INFINITY;
+            for (int r = 0; r < 16; ++r) z[r] = kb + (r & 7) + 8 * half + 16 * (r >> 3) < U ? cur[r] : -INFINITY;
         } else {
+            // visible keys of this lane's query as one 32-bit mask over the tile:
+            // kb + kr <= tq, kb + kr > xf, and unmarked or kb + kr > tq - w
             const uint32_t marks = s_marks[i & 1];
+            auto above = [](int c) -> uint32_t {  // bits kr > c
+                return c < 0 ? 0xffffffffu : (c >= 31 ? 0u : (0xffffffffu << (c + 1)));
+            };
+            uint32_t vis = ~above(tq - kb) & above(xf - kb) & (~marks | above(tq - w - kb));
+            if (tq >= T) vis = 0;
+            vis >>= 8 * half;  // this lane's rows: kr = (r & 7) + 8 half + 16 (r >> 3)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int kr = (r & 7) + 8 * half + 16 * (r >> 3);
-                const int key = kb + kr;
-                const bool marked = (marks >> kr) & 1u;
-                const bool vis = key > xf && key <= tq && tq < T && (!marked || tq < key + w);
-                z[r] = vis ? s[r] : -INFINITY;
-            }
+            for (int r = 0; r < 16; ++r) z[r] = ((vis >> ((r & 7) + 16 * (r >> 3))) & 1u) ? cur[r] : -INFINITY;
         }
         float tmax = z[0];
 #pragma unroll
@@ -267,7 +272,7 @@ void prefill_attend_kernel(PrefillArgs a) {
         const bool grow = tmax > m + 8.f;
         if (__ballot(grow)) {
             const float mn = grow ? tmax : m;
-            const float alpha = mn == -INFINITY ? 1.f : exp2f(m - mn);
+            const float alpha = mn == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m - mn);
             lsum *= alpha;
             m = mn;
 #pragma unroll
@@ -276,14 +281,16 @@ void prefill_attend_kernel(PrefillArgs a) {
                 for (int r = 0; r < 16; ++r) o[dt][r] *= alpha;
         }
         // P^T enters the PV product as two bf16 parts, hi = bf16(p) and
-        // lo = bf16(p - hi): about 16 significant bits, fp32 accumulation
+        // lo = bf16(p - hi): about 16 significant bits, fp32 accumulation.
+        // (v_exp_f32: exact to about 1 ulp; results below 2^-126 flush to 0.)
         uint32_t ph[8], pl[8];
         float ps = 0.f;
-        const float nm = m == -INFINITY ? 0.f : -m;
+        const bool live = m != -INFINITY;
+        const float nm = live ? -m : 0.f;
 #pragma unroll
         for (int i2 = 0; i2 < 8; ++i2) {
-            const float p0 = m == -INFINITY ? 0.f : exp2f(fmaf(z[2 * i2], sl, nm));
-            const float p1 = m == -INFINITY ? 0.f : exp2f(fmaf(z[2 * i2 + 1], sl, nm));
+            const float p0 = live ? __builtin_amdgcn_exp2f(fmaf(z[2 * i2], sl, nm)) : 0.f;
+            const float p1 = live ? __builtin_amdgcn_exp2f(fmaf(z[2 * i2 + 1], sl, nm)) : 0.f;
             const bf16x2_t hv = {(__bf16)p0, (__bf16)p1};
             const bf16x2_t lv = {(__bf16)(p0 - (float)hv[0]), (__bf16)(p1 - (float)hv[1])};
             ph[i2] = __builtin_bit_cast(uint32_t, hv);
@@ -306,7 +313,12 @@ void prefill_attend_kernel(PrefillArgs a) {
         if (i + 2 < ntiles) store_k(i + 2);
         if (more) store_v(i + 1);
         __syncthreads();
-        s = s_next;
+    };
+    // S alternates between two register sets (no copies between iterations)
+    f32x16_t sa = scores(0), sb;
+    for (int i = 0; i < ntiles; i += 2) {
+        step(i, sa, sb);
+        if (i + 1 < ntiles) step(i + 1, sb, sa);
     }
 
     // ---- normalise and store: lane holds dims dt*32 + 8*(r/4) + 4*half + r%4 of query tq
