@@ -107,18 +107,24 @@ __global__ __launch_bounds__(256) void prefill_vt_kernel(PrefillArgs a) {
 //              every query's window, visible to all queries of the block
 //   band       prompt keys in (xf, t0b + 32 QT), masked per (query, key) pair
 // ---------------------------------------------------------------------------
-constexpr int kPrefillWaves = 8;
+#ifndef DMS_PREFILL_WAVES
+#define DMS_PREFILL_WAVES 8
+#endif
+constexpr int kPrefillWaves = DMS_PREFILL_WAVES;  // waves per block (tuning constant), at least G
+constexpr int prefill_waves(int g) { return kPrefillWaves > g ? kPrefillWaves : g; }
 
 template <int D, int G>
-__global__ __attribute__((amdgpu_flat_work_group_size(64 * kPrefillWaves, 64 * kPrefillWaves),
+__global__ __attribute__((amdgpu_flat_work_group_size(64 * prefill_waves(G), 64 * prefill_waves(G)),
                           amdgpu_waves_per_eu(2, 2)))
 void prefill_attend_kernel(PrefillArgs a) {
-    constexpr int NT = 64 * kPrefillWaves;
-    constexpr int QT = kPrefillWaves / G;  // query tiles per block
+    constexpr int NWV = prefill_waves(G);
+    constexpr int NT = 64 * NWV;
+    static_assert(NWV % G == 0, "a block holds whole kv-head groups");
+    constexpr int QT = NWV / G;  // query tiles per block
     constexpr int KS = D / 16;             // k-steps of S^T over the head dim
     constexpr int DT = D / 32;             // 32-row tiles of O^T
     constexpr int UNITS = 4 * D;           // 16-byte units of a K (or V) tile of 32 keys
-    static_assert(UNITS <= NT, "one unit of K and one of V per thread");
+    constexpr int UPT = (UNITS + NT - 1) / NT;  // units per thread
     __shared__ uint4 s_k[2][D / 8][32];
     __shared__ uint4 s_v[2][4][D];
     __shared__ uint32_t s_marks[2];
@@ -159,35 +165,48 @@ void prefill_attend_kernel(PrefillArgs a) {
     const int32_t* ptab = P.ptable + (size_t)gh * P.pages_per_head;
     const uint16_t* vt = P.vt + (size_t)h * (P.max_pos32 / 8) * D * 8;
 
-    // Staging, thread t < UNITS: K unit t (chunk t / 32, key t % 32) and V unit t.
+    // Staging, thread t: K units u = t, t + NT, ... (chunk u / 32, key u % 32) and the
+    // same V units.
     // K runs one tile ahead of V: while tile i is folded (scores S_i, computed one
     // iteration earlier, and V_i) the block computes S_{i+1} from K_{i+1}, and the
     // loads of K_{i+2} and V_{i+1} are in flight.
     auto tile_kb = [&](int i) { return i < nfar ? 32 * i : band0 + 32 * (i - nfar); };
-    uint4 rk = make_uint4(0, 0, 0, 0), rv = make_uint4(0, 0, 0, 0);
+    uint4 rk[UPT], rv[UPT];
     bool rmark = false;
+    // page ids of far-field tiles one step ahead of their use: pg1 = page of tile
+    // i+1 (for V), pg2 = page of tile i+2 (for K), pg3 requested for the next step
+    auto page_of = [&](int t) -> int { return t < nfar ? ptab[(32 * t) / kPage] : 0; };
+    int pg1 = ntiles > 1 ? page_of(1) : 0, pg2 = ntiles > 2 ? page_of(2) : 0, pg3 = 0;
     auto load_k = [&](int i) {
-        const int cc = tid >> 5, j = tid & 31;
         const int kb = tile_kb(i);
-        if (tid < UNITS) {
-            if (i < nfar) {
-                const uint16_t* kp = P.kpages + (size_t)ptab[kb / kPage] * (kPage * D);
-                rk = *reinterpret_cast<const uint4*>(kp + ((size_t)cc * kPage + kb % kPage + j) * 8);
-            } else {
-                const int sk = kb + j;
-                rk = sk < T ? *reinterpret_cast<const uint4*>(a.k + ((size_t)sk * hkv + h) * D + cc * 8)
-                            : make_uint4(0, 0, 0, 0);
+#pragma unroll
+        for (int x = 0; x < UPT; ++x) {
+            const int u = tid + x * NT;
+            const int cc = u >> 5, j = u & 31;
+            if (u < UNITS) {
+                if (i < nfar) {
+                    const uint16_t* kp = P.kpages + (size_t)(i == 0 ? page_of(0) : i == 1 ? pg1 : pg2) * (kPage * D);
+                    rk[x] = *reinterpret_cast<const uint4*>(kp + ((size_t)cc * kPage + kb % kPage + j) * 8);
+                } else {
+                    const int sk = kb + j;
+                    rk[x] = sk < T ? *reinterpret_cast<const uint4*>(a.k + ((size_t)sk * hkv + h) * D + cc * 8)
+                                   : make_uint4(0, 0, 0, 0);
+                }
             }
         }
     };
     auto load_v = [&](int i) {
         const int kb = tile_kb(i);
-        if (tid < UNITS) {
-            if (i < nfar) {
-                const uint16_t* vp = P.vpages + (size_t)ptab[kb / kPage] * (kPage * D);
-                rv = *reinterpret_cast<const uint4*>(vp + ((size_t)(kb % kPage / 8) * D) * 8 + (size_t)tid * 8);
-            } else {
-                rv = *reinterpret_cast<const uint4*>(vt + ((size_t)(kb / 8) * D) * 8 + (size_t)tid * 8);
+#pragma unroll
+        for (int x = 0; x < UPT; ++x) {
+            const int u = tid + x * NT;
+            if (u < UNITS) {
+                if (i < nfar) {
+                    const uint16_t* vp = P.vpages + (size_t)(i == 0 ? page_of(0) : pg1) * (kPage * D);
+                    rv[x] = *reinterpret_cast<const uint4*>(vp + ((size_t)(kb % kPage / 8) * D) * 8 + (size_t)u * 8);
+                } else {
+                    rv[x] = *reinterpret_cast<const uint4*>(vt + ((size_t)(kb / 8) * D) * 8 + (size_t)u * 8);
+                }
             }
         }
         if (i >= nfar && tid < 32) {
@@ -196,10 +215,18 @@ void prefill_attend_kernel(PrefillArgs a) {
         }
     };
     auto store_k = [&](int i) {
-        if (tid < UNITS) s_k[i & 1][tid >> 5][tid & 31] = rk;
+#pragma unroll
+        for (int x = 0; x < UPT; ++x) {
+            const int u = tid + x * NT;
+            if (u < UNITS) s_k[i & 1][u >> 5][u & 31] = rk[x];
+        }
     };
     auto store_v = [&](int i) {
-        if (tid < UNITS) s_v[i & 1][tid / D][tid % D] = rv;
+#pragma unroll
+        for (int x = 0; x < UPT; ++x) {
+            const int u = tid + x * NT;
+            if (u < UNITS) s_v[i & 1][u / D][u % D] = rv[x];
+        }
         if (i >= nfar && wave == 0) {
             const uint32_t mk = (uint32_t)__ballot(rmark);
             if (lane == 0) s_marks[i & 1] = mk;
@@ -235,11 +262,9 @@ void prefill_attend_kernel(PrefillArgs a) {
     // one tile: fold S_i (in cur) while S_{i+1} (into nxt) and the next loads run
     auto step = [&](int i, const f32x16_t& cur, f32x16_t& nxt) {
         const bool more = i + 1 < ntiles;
+        if (i + 3 < ntiles) pg3 = page_of(i + 3);
         if (i + 2 < ntiles) load_k(i + 2);
-        if (more) {
-            load_v(i + 1);
-            nxt = scores(i + 1);
-        }
+        if (more) load_v(i + 1);
 
         // ---- fold tile i: row r of S_i holds key kb + (r & 7) + 8 half + 16 (r >> 3)
         const int kb = tile_kb(i);
@@ -280,38 +305,57 @@ void prefill_attend_kernel(PrefillArgs a) {
 #pragma unroll
                 for (int r = 0; r < 16; ++r) o[dt][r] *= alpha;
         }
-        // P^T enters the PV product as two bf16 parts, hi = bf16(p) and
-        // lo = bf16(p - hi): about 16 significant bits, fp32 accumulation.
-        // (v_exp_f32: exact to about 1 ulp; results below 2^-126 flush to 0.)
+        // ---- branch-free part: S_{i+1} on the matrix cores (after the last tile
+        // the K buffer holds an older tile: the result is not used) interleaved
+        // with the weights of tile i on the vector ALUs.  P^T enters the PV
+        // product as two bf16 parts, hi = bf16(p) and lo = bf16(p - hi): about
+        // 16 significant bits, fp32 accumulation.  (v_exp_f32: exact to about
+        // 1 ulp; results below 2^-126 flush to 0.)
+        uint4 ka[KS];
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) ka[ks] = s_k[(i + 1) & 1][2 * ks + half][krow];
+        f32x16_t sc = f32x16_t{};
         uint32_t ph[8], pl[8];
         float ps = 0.f;
-        const bool live = m != -INFINITY;
-        const float nm = live ? -m : 0.f;
+        // m == -inf only while every score so far (this tile's included) is masked:
+        // then z = -inf and exp2(-inf) = 0
+        const float nm = m == -INFINITY ? 0.f : -m;
 #pragma unroll
         for (int i2 = 0; i2 < 8; ++i2) {
-            const float p0 = live ? __builtin_amdgcn_exp2f(fmaf(z[2 * i2], sl, nm)) : 0.f;
-            const float p1 = live ? __builtin_amdgcn_exp2f(fmaf(z[2 * i2 + 1], sl, nm)) : 0.f;
+            if (i2 % (8 / KS) == 0)
+                sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(ka[i2 / (8 / KS)]), as_bf16x8(qb[i2 / (8 / KS)]),
+                                                             sc, 0, 0, 0);
+            const float p0 = __builtin_amdgcn_exp2f(fmaf(z[2 * i2], sl, nm));
+            const float p1 = __builtin_amdgcn_exp2f(fmaf(z[2 * i2 + 1], sl, nm));
             const bf16x2_t hv = {(__bf16)p0, (__bf16)p1};
             const bf16x2_t lv = {(__bf16)(p0 - (float)hv[0]), (__bf16)(p1 - (float)hv[1])};
             ph[i2] = __builtin_bit_cast(uint32_t, hv);
             pl[i2] = __builtin_bit_cast(uint32_t, lv);
             ps += p0 + p1;
         }
+        nxt = sc;
         lsum += ps;
+        uint4 va[DT][2];
 #pragma unroll
-        for (int dt = 0; dt < DT; ++dt) {
+        for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
-            for (int kk = 0; kk < 2; ++kk) {
-                const uint4 va = s_v[i & 1][2 * kk + half][dt * 32 + col];
-                const uint4 hb = make_uint4(ph[4 * kk], ph[4 * kk + 1], ph[4 * kk + 2], ph[4 * kk + 3]);
-                const uint4 lb = make_uint4(pl[4 * kk], pl[4 * kk + 1], pl[4 * kk + 2], pl[4 * kk + 3]);
-                o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(va), as_bf16x8(hb), o[dt], 0, 0, 0);
-                o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(va), as_bf16x8(lb), o[dt], 0, 0, 0);
-            }
+            for (int kk = 0; kk < 2; ++kk) va[dt][kk] = s_v[i & 1][2 * kk + half][dt * 32 + col];
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) {
+            const uint4 hb = make_uint4(ph[4 * kk], ph[4 * kk + 1], ph[4 * kk + 2], ph[4 * kk + 3]);
+            const uint4 lb = make_uint4(pl[4 * kk], pl[4 * kk + 1], pl[4 * kk + 2], pl[4 * kk + 3]);
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt)
+                o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(va[dt][kk]), as_bf16x8(hb), o[dt], 0, 0, 0);
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt)
+                o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(va[dt][kk]), as_bf16x8(lb), o[dt], 0, 0, 0);
         }
         // K_{i+2} replaces K_i (read for S_i one iteration ago), V_{i+1} replaces V_{i-1}
         if (i + 2 < ntiles) store_k(i + 2);
         if (more) store_v(i + 1);
+        pg1 = pg2;
+        pg2 = pg3;
         __syncthreads();
     };
     // S alternates between two register sets (no copies between iterations)
@@ -340,11 +384,11 @@ void prefill_attend_kernel(PrefillArgs a) {
 
 template <int D, int G>
 hipError_t launch_attend_t(const PrefillArgs& a, hipStream_t s) {
-    constexpr int QT = kPrefillWaves / G;
+    constexpr int QT = prefill_waves(G) / G;
     const int nqb = (a.n_tokens + 32 * QT - 1) / (32 * QT);
     const int total = a.pool.n_kv_heads * nqb;
     const int grid = 8 * ((total + 7) / 8);
-    hipLaunchKernelGGL((prefill_attend_kernel<D, G>), dim3(grid), dim3(64 * kPrefillWaves), 0, s, a);
+    hipLaunchKernelGGL((prefill_attend_kernel<D, G>), dim3(grid), dim3(64 * prefill_waves(G)), 0, s, a);
     return hipGetLastError();
 }
 
