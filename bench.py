@@ -105,6 +105,12 @@ def live_counts(logits_hd, t_values, window):
     return csum[np.maximum(t - window + 1, 0)] + np.minimum(t + 1, window)
 
 
+def live_counts_all(logits, t, window):
+    """Live tokens of every head (columns of logits [positions][heads]) at position t."""
+    unmarked = np.sum(logits[:max(t - window + 1, 0)] <= 0, axis=0).astype(np.int64)
+    return unmarked + min(t + 1, window)
+
+
 def bf16_tensor(a, torch):
     return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16)
 
@@ -280,6 +286,91 @@ def bench_decode(args, torch, dms):
 
 
 # ---------------------------------------------------------------------------
+# batched ragged decode (the bandwidth-scale workload)
+# ---------------------------------------------------------------------------
+def bench_ragged(args, torch, dms):
+    """32 sequences with prompts of 4096..32768 tokens in one shared pool, 64
+    decode steps, one dms_decode_step per token over all sequences and layers.
+    Eviction logits (hence live sets, pages and bytes) come from the counter-based
+    generator; K/V/q values from torch's seeded device generator (their values do
+    not change the work)."""
+    wl = synth.WORKLOADS["qwen3-8b_batch32_ragged"]
+    inp = synth.SynthInputs(wl)
+    L, Hq, H, D, w, B, S = (wl.n_layers, wl.n_q_heads, wl.n_kv_heads, wl.head_dim, wl.window, wl.n_seqs,
+                            wl.gen_len)
+    ctx = [int(c) for c in inp.ctx_lens()]
+    dev = torch.device("cuda:0")
+    t0 = time.time()
+    logits = {}  # (seq, layer) -> [ctx + S][H]
+    pages = 0
+    for s_ in range(B):
+        for l in range(L):
+            lg = inp.logits(s_, l, 0, ctx[s_] + S)
+            logits[(s_, l)] = lg
+            n_end = live_counts_all(lg, ctx[s_] + S - 1, w)
+            pages += int(np.sum((n_end + 63) // 64))
+    pool = dms.Pool(n_layers=L, n_q_heads=Hq, n_kv_heads=H, head_dim=D, window=w, max_seqs=B,
+                    max_positions=max(ctx) + S, max_pages=pages, device=dev)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(wl.seed)
+    for s_ in range(B):
+        for l in range(L):
+            T = ctx[s_]
+            k = torch.randn((T, H, D), generator=gen, device=dev).to(torch.bfloat16)
+            v = torch.randn((T, H, D), generator=gen, device=dev).to(torch.bfloat16)
+            pool.prefill(s_, l, k, v, torch.from_numpy(logits[(s_, l)][:T]).to(dev))
+            del k, v
+    lg_steps = torch.from_numpy(np.stack([np.stack([logits[(s_, l)][ctx[s_]:ctx[s_] + S] for s_ in range(B)], axis=1)
+                                          for l in range(L)], axis=1)).to(dev)  # [S][L][B][H]
+    q = torch.randn((S, L, B, Hq, D), generator=gen, device=dev).to(torch.bfloat16)
+    kd = torch.randn((S, L, B, H, D), generator=gen, device=dev).to(torch.bfloat16)
+    vd = torch.randn((S, L, B, H, D), generator=gen, device=dev).to(torch.bfloat16)
+    out = torch.empty((L, B, Hq, D), dtype=torch.bfloat16, device=dev)
+    torch.cuda.synchronize()
+    log("ragged inputs ready in %.1fs (%d sequences, prompts %d..%d, %d pages)" % (time.time() - t0, B, min(ctx),
+                                                                                  max(ctx), pages))
+    seqs = list(range(B))
+    stream = torch.cuda.current_stream(dev)
+    dms.dms_timing_enable(pool.handle, True)
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0.record(stream)
+    for i in range(S):
+        pool.decode_step(seqs, 0, q[i], kd[i], vd[i], lg_steps[i], out)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    ms = ev0.elapsed_time(ev1)
+    tm = dms.dms_timing_read(pool.handle)
+    dms.dms_timing_enable(pool.handle, False)
+    # algorithmic bytes of the attention launches: live slots read before each append + q
+    kv_read = 0
+    for (s_, l), lg in logits.items():
+        for h in range(H):
+            kv_read += int(np.sum(live_counts(lg[:, h], np.arange(ctx[s_], ctx[s_] + S), w) - 1))
+    attend_bytes = kv_read * 2 * D * 2 + S * L * B * Hq * D * 2
+    achieved = attend_bytes / (tm.decode_attend_ms / 1e3) / 1e9
+    st, _ = pool.stats()
+    log("ragged decode: %.3f ms/step, %.1f tok/s; attention kernels %.1f GB/s (%.1f%% of peak)"
+        % (ms / S, B * S / (ms / 1e3), achieved, 100 * achieved / HBM_PEAK_GBPS))
+    res = {"workload": "%s: %d sequences, prompts U{%d..%d} (%d..%d drawn), %d layers, %d q / %d kv heads, "
+                       "head_dim %d, w %d, keep rate Beta(2,14) per (layer, kv head), %d decode steps, "
+                       "one shared page pool" % (wl.name, B, wl.ctx_len, wl.ctx_max, min(ctx), max(ctx), L, Hq, H,
+                                                 D, w, S),
+           "call": "one dms_decode_step per token over all %d sequences x %d layers (%d launches per step)"
+                   % (B, L, tm.decode_launches // S),
+           "tok_per_s": round(B * S / (ms / 1e3), 1), "ms_per_step": round(ms / S, 4),
+           "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                        "frac": round(achieved / HBM_PEAK_GBPS, 4), "kernel": "decode_attend_kernel<128,4>",
+                        "bytes_all_launches": int(attend_bytes), "launches": int(tm.decode_launches),
+                        "attend_ms_total": round(tm.decode_attend_ms, 3),
+                        "merge_ms_total": round(tm.decode_merge_ms, 3)},
+           "kv_gib": {"live": round(st.kv_bytes_live / 2**30, 3), "allocated": round(st.kv_bytes_allocated / 2**30, 3),
+                      "dense_equivalent": round(st.kv_bytes_dense_equiv / 2**30, 3)},
+           "data": "logits from the counter-based generator; K/V/q from torch's seeded device generator"}
+    pool.close()
+    return res
+
+
+# ---------------------------------------------------------------------------
 # prefill
 # ---------------------------------------------------------------------------
 def bench_prefill(args, torch, dms):
@@ -354,6 +445,7 @@ def main():
                     help="decode steps the oracle is timed on (all layers); 0 disables")
     ap.add_argument("--no-timing-pass", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--no-ragged", action="store_true", help="skip the 32-sequence ragged batch leg")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="first run a plain copy of this many MiB (for counter scaling)")
     args = ap.parse_args()
@@ -369,6 +461,7 @@ def main():
         copy_calibration(torch, args.copy_calibration_mib)
     dec = bench_decode(args, torch, dms)
     pre = None if args.no_prefill else bench_prefill(args, torch, dms)
+    rag = None if args.no_ragged else bench_ragged(args, torch, dms)
     rec = {
         "metric": METRIC,
         "value": round(dec["value"], 2),
@@ -390,6 +483,7 @@ def main():
         "modes_max_abs_diff": dec["modes_max_abs_diff"],
         "kv_gib": dec["kv_gib"],
         "prefill": pre,
+        "batched_ragged": rag,
     }
     print(json.dumps(rec), flush=True)
 

@@ -84,3 +84,88 @@ def test_llama32_1b_ctx8192_full_size():
 def test_tiny_workload_every_step():
     """1 layer, D=64, ctx 1024, 16 steps, w=256: every step checked."""
     run_workload("tiny_d64_ctx1024", steps=16, check_steps=set(range(16)))
+
+
+def test_qwen3_8b_batch32_ragged_full_size():
+    """32 sequences with prompts U{4096..32768} in one shared page pool, 36 layers,
+    64 decode steps, every step one call over all sequences and layers (split
+    into several launches).  Eviction logits of every head come from the
+    counter-based generator; K/V/q of four sampled (sequence, layer) pairs (the
+    shortest and longest prompt, first and last layer) too, and their outputs are
+    checked against the oracle; the other pairs take K/V/q from torch's seeded
+    device generator.  Live counts of every head checked exactly, live sets on a
+    sample."""
+    import torch
+    import compact_decode_attention_amd as dms
+    wl = synth.WORKLOADS["qwen3-8b_batch32_ragged"]
+    inp = synth.SynthInputs(wl)
+    L, Hq, H, D, w, B, S = (wl.n_layers, wl.n_q_heads, wl.n_kv_heads, wl.head_dim, wl.window, wl.n_seqs,
+                            wl.gen_len)
+    ctx = [int(c) for c in inp.ctx_lens()]
+    s_short, s_long = int(np.argmin(ctx)), int(np.argmax(ctx))
+    sampled = [(s_short, 0), (s_short, L - 1), (s_long, 0), (s_long, L - 1)]
+    dev = torch.device("cuda:0")
+    marks, pages = {}, 0
+    for s in range(B):
+        for l in range(L):
+            mk = oracle.marks(inp.logits(s, l, 0, ctx[s] + S))
+            marks[(s, l)] = mk
+            pages += sum((oracle.live_count(ctx[s] + S - 1, w, mk[:, h]) + 63) // 64 for h in range(H))
+    pool = dms.Pool(n_layers=L, n_q_heads=Hq, n_kv_heads=H, head_dim=D, window=w, max_seqs=B,
+                    max_positions=max(ctx) + S, max_pages=pages, device=dev)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(7)
+    host = {}
+    for s in range(B):
+        for l in range(L):
+            T = ctx[s]
+            if (s, l) in sampled:
+                K, V = inp.k(s, l, 0, T + S), inp.v(s, l, 0, T + S)
+                host[(s, l)] = (K, V, inp.q(s, l, T, S))
+                k, v = bf(K[:T], torch).to(dev), bf(V[:T], torch).to(dev)
+            else:
+                k = torch.randn((T, H, D), generator=gen, device=dev).to(torch.bfloat16)
+                v = torch.randn((T, H, D), generator=gen, device=dev).to(torch.bfloat16)
+            pool.prefill(s, l, k, v, torch.from_numpy(inp.logits(s, l, 0, T)).to(dev))
+    seqs = list(range(B))
+    check_steps = {0, S // 2, S - 1}
+    for i in range(S):
+        q = torch.randn((L, B, Hq, D), generator=gen, device=dev).to(torch.bfloat16)
+        k = torch.randn((L, B, H, D), generator=gen, device=dev).to(torch.bfloat16)
+        v = torch.randn((L, B, H, D), generator=gen, device=dev).to(torch.bfloat16)
+        for (s, l) in sampled:
+            K, V, Q = host[(s, l)]
+            t = ctx[s] + i
+            q[l, s] = bf(Q[i], torch).to(dev)
+            k[l, s] = bf(K[t], torch).to(dev)
+            v[l, s] = bf(V[t], torch).to(dev)
+        lg = torch.from_numpy(np.stack([np.stack([inp.logits(s, l, ctx[s] + i, 1)[0] for s in range(B)])
+                                        for l in range(L)])).to(dev)
+        out = torch.empty((L, B, Hq, D), dtype=torch.bfloat16, device=dev)
+        pool.decode_step(seqs, 0, q, k, v, lg, out)
+        if i in check_steps:
+            got = out.view(torch.int16).cpu().numpy().view(np.uint16)
+            for (s, l) in sampled:
+                K, V, Q = host[(s, l)]
+                t = ctx[s] + i
+                ref = oracle.attend(Q[i][None], [t], K[:t + 1], V[:t + 1], marks[(s, l)][:t + 1], w)[0]
+                assert_close(got[l, s], ref, "ragged step %d seq %d layer %d" % (i, s, l))
+    st_all, _ = pool.stats()
+    assert st_all.device_error == 0
+    total_live = 0
+    for s in range(B):
+        t = ctx[s] + S - 1
+        st, live = pool.stats(s, per_head=True)
+        assert st.position == t + 1
+        for l in range(L):
+            ref = [oracle.live_count(t, w, marks[(s, l)][:t + 1, h]) for h in range(H)]
+            assert np.array_equal(live[l], ref), (s, l)
+            total_live += sum(ref)
+    assert st_all.live_slots == total_live
+    rng = np.random.default_rng(3)
+    heads = [(s, l, h) for (s, l) in sampled for h in range(H)]
+    heads += [(int(rng.integers(B)), int(rng.integers(L)), int(rng.integers(H))) for _ in range(16)]
+    for (s, l, h) in heads:
+        t = ctx[s] + S - 1
+        assert np.array_equal(pool.export_live(s, l, h), oracle.live_positions(t, w, marks[(s, l)][:t + 1, h]))
+    pool.close()
