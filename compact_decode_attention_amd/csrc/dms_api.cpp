@@ -99,8 +99,8 @@ uint64_t mix64(uint64_t& s) {
 struct dms_pool {
     dms_pool_config cfg;
     bool timing = false;
-    std::vector<hipEvent_t> events;   // triples recorded by decode launches while timing
-    std::vector<hipEvent_t> pevents;  // triples recorded by prefills with output while timing
+    std::vector<hipEvent_t> events;   // 4 per decode launch while timing (attend, merge start/stop)
+    std::vector<hipEvent_t> pevents;  // 6 per prefill with output while timing (compaction, V copy, attend)
     Layout layout;
     dms::PoolDev dev;
     char* arena;
@@ -222,11 +222,11 @@ dms_status dms_pool_destroy(dms_pool* pool) {
 }
 
 namespace {
-// three fresh events appended to v (for one timed call), or nullptr on failure
-hipEvent_t* timing_events(std::vector<hipEvent_t>& v, hipError_t* err) {
+// n fresh events appended to v (for one timed call), or nullptr on failure
+hipEvent_t* timing_events(std::vector<hipEvent_t>& v, size_t n, hipError_t* err) {
     const size_t base = v.size();
-    v.resize(base + 3, nullptr);
-    for (size_t i = base; i < base + 3; ++i) {
+    v.resize(base + n, nullptr);
+    for (size_t i = base; i < base + n; ++i) {
         *err = hipEventCreate(&v[i]);
         if (*err != hipSuccess) return nullptr;
     }
@@ -258,17 +258,14 @@ dms_status dms_prefill(dms_pool* pool, int32_t seq, int32_t layer, int32_t n_tok
     hipError_t e = hipSuccess;
     hipEvent_t* ev = nullptr;
     if (pool->timing && out) {
-        ev = timing_events(pool->pevents, &e);
+        ev = timing_events(pool->pevents, 6, &e);
         if (!ev) return hip_fail(e, "timing event");
-        if ((e = hipEventRecord(ev[0], s)) != hipSuccess) return hip_fail(e, "timing event");
     }
-    e = dms::launch_prefill_compact(a, s);
+    e = dms::launch_prefill_compact(a, s, ev ? ev[0] : nullptr, ev ? ev[1] : nullptr);
     if (e != hipSuccess) return hip_fail(e, "prefill compaction launch");
     if (out) {
-        if (ev && (e = hipEventRecord(ev[1], s)) != hipSuccess) return hip_fail(e, "timing event");
-        e = dms::launch_prefill_attend(a, s);
+        e = dms::launch_prefill_attend(a, s, ev ? ev + 2 : nullptr);
         if (e != hipSuccess) return hip_fail(e, "prefill attention launch");
-        if (ev && (e = hipEventRecord(ev[2], s)) != hipSuccess) return hip_fail(e, "timing event");
     }
     pool->position(seq, layer) = n_tokens;
     g_err.clear();
@@ -325,7 +322,7 @@ dms_status dms_decode_step(dms_pool* pool, int32_t n_seqs, const int32_t* seq_id
         hipEvent_t* ev = nullptr;
         if (pool->timing) {
             hipError_t ce = hipSuccess;
-            ev = timing_events(pool->events, &ce);
+            ev = timing_events(pool->events, 4, &ce);
             if (!ev) return hip_fail(ce, "timing event");
         }
         hipError_t e = dms::launch_decode(a, (int)grid, st, ev);
@@ -438,23 +435,28 @@ dms_status dms_timing_read(dms_pool* pool, dms_timing* out) {
     hipError_t e = hipDeviceSynchronize();
     if (e != hipSuccess) return hip_fail(e, "synchronise");
     std::memset(out, 0, sizeof(*out));
-    auto sum = [&](std::vector<hipEvent_t>& v, double* first, double* second, int64_t* n) -> hipError_t {
-        *n = (int64_t)(v.size() / 3);
-        for (size_t i = 0; i + 2 < v.size(); i += 3) {
-            float t0 = 0, t1 = 0;
-            hipError_t r = hipEventElapsedTime(&t0, v[i], v[i + 1]);
-            if (r == hipSuccess) r = hipEventElapsedTime(&t1, v[i + 1], v[i + 2]);
-            if (r != hipSuccess) return r;
-            *first += t0;
-            *second += t1;
+    // events come in start/stop pairs; group g of each call adds to acc[slot[g]]
+    auto sum = [&](std::vector<hipEvent_t>& v, size_t per_call, const int* slot, double* const* acc,
+                   int64_t* n) -> hipError_t {
+        *n = (int64_t)(v.size() / per_call);
+        for (size_t i = 0; i + per_call <= v.size(); i += per_call) {
+            for (size_t g = 0; g < per_call / 2; ++g) {
+                float t = 0;
+                const hipError_t r = hipEventElapsedTime(&t, v[i + 2 * g], v[i + 2 * g + 1]);
+                if (r != hipSuccess) return r;
+                *acc[slot[g]] += t;
+            }
         }
         for (hipEvent_t ev : v) hipEventDestroy(ev);
         v.clear();
         return hipSuccess;
     };
-    e = sum(pool->events, &out->decode_attend_ms, &out->decode_merge_ms, &out->decode_launches);
-    if (e == hipSuccess)
-        e = sum(pool->pevents, &out->prefill_compact_ms, &out->prefill_attend_ms, &out->prefill_calls);
+    double* dacc[2] = {&out->decode_attend_ms, &out->decode_merge_ms};
+    const int dslot[2] = {0, 1};
+    e = sum(pool->events, 4, dslot, dacc, &out->decode_launches);
+    double* pacc[2] = {&out->prefill_compact_ms, &out->prefill_attend_ms};
+    const int pslot[3] = {0, 0, 1};  // compaction + V copy, attention
+    if (e == hipSuccess) e = sum(pool->pevents, 6, pslot, pacc, &out->prefill_calls);
     if (e != hipSuccess) return hip_fail(e, "event elapsed time");
     g_err.clear();
     return DMS_OK;

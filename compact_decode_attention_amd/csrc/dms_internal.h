@@ -112,13 +112,15 @@ struct PrefillArgs {
     int32_t seq, layer, n_tokens;
 };
 
-// ev (optional): two events recorded before the first and after the last
-// kernel of the decode launch
+// ev (optional, 4 events): start/stop of the attention kernel and of the merge
+// kernel, taken by the kernel dispatches (execution time only)
 hipError_t launch_decode(const DecodeArgs& a, int grid, hipStream_t s, hipEvent_t* ev);
 // blocks of the attention kernel one compute unit holds at once for this call (0: does not fit)
 int decode_blocks_per_cu(const DecodeArgs& a);
-hipError_t launch_prefill_compact(const PrefillArgs& a, hipStream_t s);
-hipError_t launch_prefill_attend(const PrefillArgs& a, hipStream_t s);
+// start / stop (optional): taken by the first and the last kernel dispatch
+hipError_t launch_prefill_compact(const PrefillArgs& a, hipStream_t s, hipEvent_t start, hipEvent_t stop);
+// ev (optional, 4 events): start/stop of the V copy kernel, then of the attention kernel
+hipError_t launch_prefill_attend(const PrefillArgs& a, hipStream_t s, hipEvent_t* ev);
 hipError_t launch_seq_release(const PoolDev& p, int32_t seq, hipStream_t s);
 int device_cu_count();
 

@@ -29,6 +29,7 @@
 // The kernel boundary orders every read of this step before every write.
 #include "dms_internal.h"
 
+#include <hip/hip_ext.h>
 #include <math.h>
 
 namespace dms {
@@ -854,17 +855,17 @@ __global__ __launch_bounds__(64) void seq_release_kernel(PoolDev P, int seq) {
 
 size_t decode_shm(const DecodeArgs& a) { return (size_t)(4 * a.n_call_heads + 1) * sizeof(int32_t); }
 
+// ev (optional): start/stop of the attention kernel, then of the merge kernel,
+// taken by the dispatches themselves (kernel execution only)
 template <int D, int G>
 hipError_t launch_decode_t(const DecodeArgs& a, int grid, hipStream_t s, hipEvent_t* ev) {
-    hipError_t err;
-    if (ev && (err = hipEventRecord(ev[0], s)) != hipSuccess) return err;
-    hipLaunchKernelGGL((decode_attend_kernel<D, G>), dim3(grid), dim3(64 * kAttendWaves), decode_shm(a), s, a);
-    if ((err = hipGetLastError()) != hipSuccess) return err;
-    if (ev && (err = hipEventRecord(ev[1], s)) != hipSuccess) return err;
-    hipLaunchKernelGGL((decode_merge_kernel<D, G>), dim3(2 * a.n_call_heads), dim3(256), 0, s, a);
-    if ((err = hipGetLastError()) != hipSuccess) return err;
-    if (ev && (err = hipEventRecord(ev[2], s)) != hipSuccess) return err;
-    return hipSuccess;
+    hipExtLaunchKernelGGL((decode_attend_kernel<D, G>), dim3(grid), dim3(64 * kAttendWaves), decode_shm(a), s,
+                          ev ? ev[0] : nullptr, ev ? ev[1] : nullptr, 0, a);
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+    hipExtLaunchKernelGGL((decode_merge_kernel<D, G>), dim3(2 * a.n_call_heads), dim3(256), 0, s,
+                          ev ? ev[2] : nullptr, ev ? ev[3] : nullptr, 0, a);
+    return hipGetLastError();
 }
 
 template <int D, int G>
@@ -910,15 +911,15 @@ int decode_blocks_per_cu(const DecodeArgs& a) {
     return a.pool.head_dim == 128 ? blocks_per_cu_d<128>(a) : blocks_per_cu_d<64>(a);
 }
 
-hipError_t launch_prefill_compact(const PrefillArgs& a, hipStream_t s) {
-    hipLaunchKernelGGL(prefill_scan_kernel, dim3(a.pool.n_kv_heads), dim3(1024), 0, s, a);
+hipError_t launch_prefill_compact(const PrefillArgs& a, hipStream_t s, hipEvent_t start, hipEvent_t stop) {
+    hipExtLaunchKernelGGL(prefill_scan_kernel, dim3(a.pool.n_kv_heads), dim3(1024), 0, s, start, nullptr, 0, a);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
     const dim3 grid((a.n_tokens + kPage - 1) / kPage, a.pool.n_kv_heads);
     if (a.pool.head_dim == 128)
-        hipLaunchKernelGGL(prefill_compact_kernel<128>, grid, dim3(256), 0, s, a);
+        hipExtLaunchKernelGGL(prefill_compact_kernel<128>, grid, dim3(256), 0, s, nullptr, stop, 0, a);
     else
-        hipLaunchKernelGGL(prefill_compact_kernel<64>, grid, dim3(256), 0, s, a);
+        hipExtLaunchKernelGGL(prefill_compact_kernel<64>, grid, dim3(256), 0, s, nullptr, stop, 0, a);
     return hipGetLastError();
 }
 

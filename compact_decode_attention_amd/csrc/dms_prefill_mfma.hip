@@ -26,6 +26,7 @@
 // tile is read by one block for all of them.
 #include "dms_internal.h"
 
+#include <hip/hip_ext.h>
 #include <math.h>
 
 namespace dms {
@@ -383,25 +384,27 @@ void prefill_attend_kernel(PrefillArgs a) {
 }
 
 template <int D, int G>
-hipError_t launch_attend_t(const PrefillArgs& a, hipStream_t s) {
+hipError_t launch_attend_t(const PrefillArgs& a, hipStream_t s, hipEvent_t* ev) {
     constexpr int QT = prefill_waves(G) / G;
     const int nqb = (a.n_tokens + 32 * QT - 1) / (32 * QT);
     const int total = a.pool.n_kv_heads * nqb;
     const int grid = 8 * ((total + 7) / 8);
-    hipLaunchKernelGGL((prefill_attend_kernel<D, G>), dim3(grid), dim3(64 * prefill_waves(G)), 0, s, a);
+    hipExtLaunchKernelGGL((prefill_attend_kernel<D, G>), dim3(grid), dim3(64 * prefill_waves(G)), 0, s,
+                          ev ? ev[2] : nullptr, ev ? ev[3] : nullptr, 0, a);
     return hipGetLastError();
 }
 
 template <int D>
-hipError_t launch_attend_d(const PrefillArgs& a, hipStream_t s) {
-    hipLaunchKernelGGL(prefill_vt_kernel<D>, dim3((a.n_tokens + 63) / 64, a.pool.n_kv_heads), dim3(256), 0, s, a);
+hipError_t launch_attend_d(const PrefillArgs& a, hipStream_t s, hipEvent_t* ev) {
+    hipExtLaunchKernelGGL(prefill_vt_kernel<D>, dim3((a.n_tokens + 63) / 64, a.pool.n_kv_heads), dim3(256), 0, s,
+                          ev ? ev[0] : nullptr, ev ? ev[1] : nullptr, 0, a);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
     switch (a.pool.n_q_heads / a.pool.n_kv_heads) {
-        case 1: return launch_attend_t<D, 1>(a, s);
-        case 2: return launch_attend_t<D, 2>(a, s);
-        case 4: return launch_attend_t<D, 4>(a, s);
-        case 8: return launch_attend_t<D, 8>(a, s);
+        case 1: return launch_attend_t<D, 1>(a, s, ev);
+        case 2: return launch_attend_t<D, 2>(a, s, ev);
+        case 4: return launch_attend_t<D, 4>(a, s, ev);
+        case 8: return launch_attend_t<D, 8>(a, s, ev);
     }
     return hipErrorInvalidValue;
 }
@@ -410,9 +413,9 @@ hipError_t launch_attend_d(const PrefillArgs& a, hipStream_t s) {
 
 // Runs after the compaction kernels of the same prefill (same stream): the far
 // field reads the pages and the live-count prefix they wrote.
-hipError_t launch_prefill_attend(const PrefillArgs& a, hipStream_t s) {
-    if (a.pool.head_dim == 128) return launch_attend_d<128>(a, s);
-    if (a.pool.head_dim == 64) return launch_attend_d<64>(a, s);
+hipError_t launch_prefill_attend(const PrefillArgs& a, hipStream_t s, hipEvent_t* ev) {
+    if (a.pool.head_dim == 128) return launch_attend_d<128>(a, s, ev);
+    if (a.pool.head_dim == 64) return launch_attend_d<64>(a, s, ev);
     return hipErrorInvalidValue;
 }
 

@@ -162,17 +162,16 @@ dms_status dms_export_live(dms_pool* pool, int32_t seq, int32_t layer, int32_t k
  * all layers (enqueued on `stream`).  The sequence may then be prefilled again. */
 dms_status dms_seq_release(dms_pool* pool, int32_t seq, void* stream);
 
-/* Kernel timing for measurement.  While enabled, every decode launch records
- * HIP events on its stream before its attention kernel, between that kernel and
- * its merge / append kernel, and after the latter; every prefill records events
- * around its compaction kernels and around its attention kernels.
- * dms_timing_read synchronises, adds up the elapsed times of everything
- * recorded since the last read (milliseconds), counts the calls, and releases
- * the events.  Disabled by default; enabling adds event records between kernels. */
+/* Kernel timing for measurement.  While enabled, the kernels of every decode
+ * launch and of every prefill that produces an output are dispatched with HIP
+ * start/stop events that the dispatches themselves record, so the times cover
+ * kernel execution only.  dms_timing_read synchronises, adds up the times of
+ * everything recorded since the last read (milliseconds), counts the calls, and
+ * releases the events.  Disabled by default. */
 typedef struct {
     double decode_attend_ms;   /* split-K attention kernels */
     double decode_merge_ms;    /* merge + evict/append kernels */
-    double prefill_compact_ms; /* mark scan + compaction kernels */
+    double prefill_compact_ms; /* mark scan + compaction kernels and the prompt-V copy */
     double prefill_attend_ms;  /* masked causal attention (MFMA) kernels */
     int64_t decode_launches;
     int64_t prefill_calls;     /* prefills that produced an output */
