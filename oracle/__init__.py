@@ -45,6 +45,14 @@ def load(so: str) -> ctypes.CDLL:
     lib.dms_oracle_live_positions.restype = i64
     lib.dms_oracle_attend.argtypes = [i32, i32, i32, i64, dbl, i64, vp, vp, i64, vp, vp, vp, vp]
     lib.dms_oracle_attend.restype = ctypes.c_int
+    lib.dms_oracle_e4m3_value.argtypes = [ctypes.c_uint8]
+    lib.dms_oracle_e4m3_value.restype = dbl
+    lib.dms_oracle_e4m3_encode.argtypes = [ctypes.c_float]
+    lib.dms_oracle_e4m3_encode.restype = ctypes.c_uint8
+    lib.dms_oracle_quantize_rows.argtypes = [vp, i64, i32, vp, vp]
+    lib.dms_oracle_quantize_rows.restype = None
+    lib.dms_oracle_attend_fp8.argtypes = [i32, i32, i32, i64, dbl, i64, vp, vp, i64, vp, vp, vp, vp, vp, vp]
+    lib.dms_oracle_attend_fp8.restype = ctypes.c_int
     return lib
 
 
@@ -107,6 +115,48 @@ class Oracle:
         return out
 
 
+    # ---- FP8 (E4M3) K/V
+    def e4m3_value(self, code: int) -> float:
+        return float(self.lib.dms_oracle_e4m3_value(int(code) & 0xFF))
+
+    def e4m3_encode(self, x: float) -> int:
+        return int(self.lib.dms_oracle_e4m3_encode(float(x)))
+
+    def quantize_rows(self, x: np.ndarray):
+        """x [..., D] bf16 bits -> (codes uint8 [..., D], scales float32 [...])."""
+        x = np.ascontiguousarray(x, np.uint16)
+        d = x.shape[-1]
+        rows = x.size // d
+        codes = np.empty(x.shape, np.uint8)
+        scales = np.empty(x.shape[:-1], np.float32)
+        self.lib.dms_oracle_quantize_rows(x.ctypes.data, rows, d, codes.ctypes.data, scales.ctypes.data)
+        return codes, scales
+
+    def attend_fp8(self, q: np.ndarray, query_pos, k8: np.ndarray, ks: np.ndarray, v8: np.ndarray,
+                   vs: np.ndarray, marks: np.ndarray, window: int, scale: float = 0.0) -> np.ndarray:
+        """q [nq][Hq][D] bf16 bits; k8/v8 [T][Hkv][D] E4M3 codes; ks/vs [T][Hkv]
+        scales; marks [T][Hkv].  Returns out [nq][Hq][D] float64."""
+        q = np.ascontiguousarray(q, np.uint16)
+        k8 = np.ascontiguousarray(k8, np.uint8)
+        v8 = np.ascontiguousarray(v8, np.uint8)
+        ks = np.ascontiguousarray(ks, np.float32)
+        vs = np.ascontiguousarray(vs, np.float32)
+        marks = np.ascontiguousarray(marks, np.uint8)
+        qp = np.ascontiguousarray(np.asarray(query_pos, np.int64).reshape(-1))
+        nq, hq, d = q.shape
+        nk, hkv, d2 = k8.shape
+        if d2 != d or v8.shape != k8.shape or ks.shape != (nk, hkv) or vs.shape != (nk, hkv) \
+                or marks.shape != (nk, hkv) or qp.shape[0] != nq:
+            raise ValueError("shape mismatch")
+        out = np.empty((nq, hq, d), np.float64)
+        rc = self.lib.dms_oracle_attend_fp8(hq, hkv, d, int(window), float(scale), nq, qp.ctypes.data,
+                                            q.ctypes.data, nk, k8.ctypes.data, ks.ctypes.data, v8.ctypes.data,
+                                            vs.ctypes.data, marks.ctypes.data, out.ctypes.data)
+        if rc != 0:
+            raise ValueError("query position outside the keys given")
+        return out
+
+
 def default() -> Oracle:
     return Oracle(_lib())
 
@@ -125,6 +175,22 @@ def live_count(t, window, marks_col):
 
 def attend(q, query_pos, k, v, marks_, window, scale=0.0):
     return default().attend(q, query_pos, k, v, marks_, window, scale)
+
+
+def e4m3_value(code):
+    return default().e4m3_value(code)
+
+
+def e4m3_encode(x):
+    return default().e4m3_encode(x)
+
+
+def quantize_rows(x):
+    return default().quantize_rows(x)
+
+
+def attend_fp8(q, query_pos, k8, ks, v8, vs, marks_, window, scale=0.0):
+    return default().attend_fp8(q, query_pos, k8, ks, v8, vs, marks_, window, scale)
 
 
 def kv_bytes_live(live_counts, head_dim: int) -> int:

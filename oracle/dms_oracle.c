@@ -35,6 +35,17 @@
  *
  * Arithmetic: inputs are bf16 bit patterns; every product, sum, exp and divide
  * is done in double.  Softmax subtracts the maximum visible score before exp.
+ *
+ * FP8 K/V (a compact store holding K and V as 8-bit floats; the FastDMS page
+ * [FD] lists FP8 KV caches beside BF16 ones): each (token, kv head) row of K,
+ * and of V, is stored as OCP FP8 E4M3 codes with one fp32 scale:
+ *   amax  = max_d |x_d|                       (x: the row's bf16 values)
+ *   scale = amax / 448 in fp32 (448 is the largest finite E4M3 value), or 1 for
+ *           an all-zero row
+ *   c_d   = the finite E4M3 value nearest to x_d / scale (fp32 quotient), ties
+ *           to the code with an even last bit; beyond +-448 that is +-448
+ *   x^_d  = value(c_d) * scale
+ * and attention reads x^ in place of x.
  */
 #include <math.h>
 #include <stdint.h>
@@ -138,3 +149,114 @@ int dms_oracle_attend(int32_t n_q_heads, int32_t n_kv_heads, int32_t head_dim,
     }
     return 0;
 }
+
+/* ---------------------------------------------------------------------------
+ * OCP FP8 E4M3: sign bit, 4 exponent bits (bias 7), 3 mantissa bits.
+ *   exponent field 0:     (-1)^s * 2^-6 * m / 8            (zero and subnormals)
+ *   exponent field 1..15: (-1)^s * 2^(e-7) * (1 + m / 8)
+ *   S.1111.111 is NaN; there is no infinity; the largest finite value is
+ *   S.1111.110 = 1.75 * 2^8 = 448.
+ * ------------------------------------------------------------------------- */
+double dms_oracle_e4m3_value(uint8_t code) {
+    const int sgn = code >> 7, e = (code >> 3) & 15, m = code & 7;
+    if (e == 15 && m == 7) return NAN;
+    const double mag = e == 0 ? ldexp((double)m / 8.0, -6) : ldexp(1.0 + (double)m / 8.0, e - 7);
+    return sgn ? -mag : mag;
+}
+
+/* The finite E4M3 code nearest to x (ties: the code with an even last bit);
+ * the sign of x is kept, so x in (-2^-10, 0] gives -0 (0x80) or +0.  NaN gives
+ * 0x7f.  Codes 0x00..0x7e are the non-negative finite values in increasing
+ * order, so the nearest one is found by walking them. */
+uint8_t dms_oracle_e4m3_encode(float x) {
+    if (isnan(x)) return 0x7f;
+    const uint8_t sgn = signbit(x) ? 0x80 : 0x00;
+    const double a = fabs((double)x);
+    uint8_t best = 0;
+    double best_d = a;  /* distance to code 0 (value 0) */
+    for (int c = 1; c <= 0x7e; ++c) {
+        const double d = fabs(dms_oracle_e4m3_value((uint8_t)c) - a);
+        if (d < best_d || (d == best_d && (c & 1) == 0)) {
+            best = (uint8_t)c;
+            best_d = d;
+        }
+    }
+    return (uint8_t)(sgn | best);
+}
+
+/* Quantise n_rows rows of d bf16 values each to E4M3 codes and one scale per row
+ * (see the header): codes[r*d + i], scales[r]. */
+void dms_oracle_quantize_rows(const uint16_t* x, int64_t n_rows, int32_t d, uint8_t* codes, float* scales) {
+#pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < n_rows; ++r) {
+        const uint16_t* row = x + r * d;
+        float amax = 0.0f;
+        for (int32_t i = 0; i < d; ++i) {
+            const float v = fabsf((float)bf16_bits_to_double(row[i]));
+            if (v > amax) amax = v;
+        }
+        const float scale = amax > 0.0f ? amax / 448.0f : 1.0f;
+        scales[r] = scale;
+        for (int32_t i = 0; i < d; ++i) codes[r * d + i] = dms_oracle_e4m3_encode((float)bf16_bits_to_double(row[i]) / scale);
+    }
+}
+
+/* Masked attention as dms_oracle_attend, with K and V given as E4M3 codes and
+ * one scale per (key, kv head) row:
+ *   k8, v8 [n_keys][n_kv_heads][head_dim] codes, ks, vs [n_keys][n_kv_heads] scales;
+ * key values value(k8) * ks, value values value(v8) * vs (double). */
+int dms_oracle_attend_fp8(int32_t n_q_heads, int32_t n_kv_heads, int32_t head_dim,
+                          int64_t window, double scale, int64_t n_queries,
+                          const int64_t* query_pos, const uint16_t* q, int64_t n_keys,
+                          const uint8_t* k8, const float* ks, const uint8_t* v8, const float* vs,
+                          const uint8_t* marks, double* out) {
+    const int32_t group = n_q_heads / n_kv_heads;
+    for (int64_t i = 0; i < n_queries; ++i)
+        if (query_pos[i] < 0 || query_pos[i] >= n_keys) return -1;
+    if (scale == 0.0) scale = 1.0 / sqrt((double)head_dim);
+    double table[256];
+    for (int c = 0; c < 256; ++c) table[c] = dms_oracle_e4m3_value((uint8_t)c);
+
+#pragma omp parallel
+    {
+        double* z = (double*)malloc(sizeof(double) * (size_t)n_keys);
+        double* qd = (double*)malloc(sizeof(double) * (size_t)head_dim);
+#pragma omp for schedule(dynamic, 1) collapse(2)
+        for (int64_t i = 0; i < n_queries; ++i) {
+            for (int32_t hq = 0; hq < n_q_heads; ++hq) {
+                const int64_t t = query_pos[i];
+                const int32_t h = hq / group;
+                const uint16_t* qrow = q + (i * n_q_heads + hq) * (int64_t)head_dim;
+                for (int32_t d = 0; d < head_dim; ++d) qd[d] = bf16_bits_to_double(qrow[d]);
+
+                double zmax = -INFINITY;
+                for (int64_t s = 0; s <= t; ++s) {
+                    if (!visible(t, s, marks[s * n_kv_heads + h], window)) continue;
+                    const uint8_t* krow = k8 + (s * n_kv_heads + h) * (int64_t)head_dim;
+                    const double kscale = (double)ks[s * n_kv_heads + h];
+                    double dot = 0.0;
+                    for (int32_t d = 0; d < head_dim; ++d) dot += qd[d] * (table[krow[d]] * kscale);
+                    z[s] = scale * dot;
+                    if (z[s] > zmax) zmax = z[s];
+                }
+
+                double* o = out + (i * n_q_heads + hq) * (int64_t)head_dim;
+                for (int32_t d = 0; d < head_dim; ++d) o[d] = 0.0;
+                double denom = 0.0;
+                for (int64_t s = 0; s <= t; ++s) {
+                    if (!visible(t, s, marks[s * n_kv_heads + h], window)) continue;
+                    const double wgt = exp(z[s] - zmax);
+                    const uint8_t* vrow = v8 + (s * n_kv_heads + h) * (int64_t)head_dim;
+                    const double vscale = (double)vs[s * n_kv_heads + h];
+                    denom += wgt;
+                    for (int32_t d = 0; d < head_dim; ++d) o[d] += wgt * (table[vrow[d]] * vscale);
+                }
+                for (int32_t d = 0; d < head_dim; ++d) o[d] /= denom;
+            }
+        }
+        free(qd);
+        free(z);
+    }
+    return 0;
+}
+
