@@ -23,6 +23,7 @@ HEADER = os.path.join(os.path.dirname(HERE), "include", "dms.h")
 
 DMS_OK, DMS_E_INVAL, DMS_E_NOMEM, DMS_E_CAPACITY, DMS_E_STATE, DMS_E_HIP = 0, -1, -2, -3, -4, -5
 DMS_PAGE_SLOTS = 64
+DMS_KV_BF16, DMS_KV_FP8_E4M3 = 0, 1
 _STATUS_NAMES = {0: "DMS_OK", -1: "DMS_E_INVAL", -2: "DMS_E_NOMEM", -3: "DMS_E_CAPACITY",
                  -4: "DMS_E_STATE", -5: "DMS_E_HIP"}
 
@@ -46,7 +47,8 @@ class dms_pool_config(ctypes.Structure):
         ("max_pages", ctypes.c_int64),
         ("softmax_scale", ctypes.c_float),
         ("page_order_seed", ctypes.c_uint32),
-        ("reserved", ctypes.c_int32 * 4),
+        ("kv_format", ctypes.c_int32),
+        ("reserved", ctypes.c_int32 * 3),
     ]
 
 
@@ -111,11 +113,13 @@ def lib() -> ctypes.CDLL:
             L.dms_decode_step.argtypes = [vp, i32, P(i32), i32, i32, vp, vp, vp, vp, vp, vp]
             L.dms_query_stats.argtypes = [vp, i32, P(dms_stats), P(i32)]
             L.dms_export_live.argtypes = [vp, i32, i32, i32, P(i32), i32, P(i32)]
+            L.dms_export_kv.argtypes = [vp, i32, i32, i32, i32, P(i32), vp, vp, P(ctypes.c_float),
+                                        P(ctypes.c_float), P(i32)]
             L.dms_seq_release.argtypes = [vp, i32, vp]
             L.dms_timing_enable.argtypes = [vp, i32]
             L.dms_timing_read.argtypes = [vp, P(dms_timing)]
             for f in (L.dms_pool_create, L.dms_pool_destroy, L.dms_prefill, L.dms_decode_step,
-                      L.dms_query_stats, L.dms_export_live, L.dms_seq_release,
+                      L.dms_query_stats, L.dms_export_live, L.dms_export_kv, L.dms_seq_release,
                       L.dms_timing_enable, L.dms_timing_read):
                 f.restype = ctypes.c_int32
             L.dms_last_error.argtypes = []
@@ -134,7 +138,7 @@ def _check(status: int):
 
 
 def make_config(n_layers, n_q_heads, n_kv_heads, head_dim, window, max_seqs, max_positions,
-                max_pages, softmax_scale=0.0, page_order_seed=0) -> dms_pool_config:
+                max_pages, softmax_scale=0.0, page_order_seed=0, kv_format=0) -> dms_pool_config:
     c = dms_pool_config()
     c.n_layers, c.n_q_heads, c.n_kv_heads, c.head_dim = n_layers, n_q_heads, n_kv_heads, head_dim
     c.window, c.max_seqs, c.max_positions = window, max_seqs, max_positions
@@ -142,6 +146,7 @@ def make_config(n_layers, n_q_heads, n_kv_heads, head_dim, window, max_seqs, max
     c.max_pages = max_pages
     c.softmax_scale = softmax_scale
     c.page_order_seed = page_order_seed
+    c.kv_format = kv_format
     return c
 
 
@@ -202,6 +207,26 @@ def dms_export_live(pool: int, seq: int, layer: int, kv_head: int, cap: int) -> 
     return buf[:n.value].copy()
 
 
+def dms_export_kv(pool: int, seq: int, layer: int, kv_head: int, cap: int, head_dim: int, fp8: bool):
+    """(positions int32 [n], k, v [n][head_dim] (uint16 bf16 bits, or uint8 E4M3 codes),
+    k_scale, v_scale float32 [n]) of what one (seq, layer, kv head) stores."""
+    dt = np.uint8 if fp8 else np.uint16
+    cap1 = max(cap, 1)
+    pos = np.zeros(cap1, np.int32)
+    k = np.zeros((cap1, head_dim), dt)
+    v = np.zeros((cap1, head_dim), dt)
+    ks = np.zeros(cap1, np.float32)
+    vs = np.zeros(cap1, np.float32)
+    n = ctypes.c_int32()
+    fp = ctypes.POINTER(ctypes.c_float)
+    _check(lib().dms_export_kv(ctypes.c_void_p(pool), seq, layer, kv_head, cap,
+                               pos.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)), ctypes.c_void_p(k.ctypes.data),
+                               ctypes.c_void_p(v.ctypes.data), ks.ctypes.data_as(fp), vs.ctypes.data_as(fp),
+                               ctypes.byref(n)))
+    m = n.value
+    return pos[:m].copy(), k[:m].copy(), v[:m].copy(), ks[:m].copy(), vs[:m].copy()
+
+
 def dms_seq_release(pool: int, seq: int, stream: int):
     _check(lib().dms_seq_release(ctypes.c_void_p(pool), seq, ctypes.c_void_p(stream)))
 
@@ -227,11 +252,12 @@ class Pool:
     """
 
     def __init__(self, n_layers, n_q_heads, n_kv_heads, head_dim, window, max_seqs, max_positions,
-                 max_pages, softmax_scale=0.0, page_order_seed=0, device="cuda"):
+                 max_pages, softmax_scale=0.0, page_order_seed=0, kv_format=0, device="cuda"):
         import torch
         self.torch = torch
         self.cfg = make_config(n_layers, n_q_heads, n_kv_heads, head_dim, window, max_seqs,
-                               max_positions, max_pages, softmax_scale, page_order_seed)
+                               max_positions, max_pages, softmax_scale, page_order_seed, kv_format)
+        self.fp8 = kv_format == DMS_KV_FP8_E4M3
         self.device = torch.device(device)
         self.nbytes = dms_pool_bytes(self.cfg)
         self.arena = torch.empty(self.nbytes + 256, dtype=torch.uint8, device=self.device)
@@ -291,6 +317,9 @@ class Pool:
 
     def export_live(self, seq, layer, kv_head):
         return dms_export_live(self.handle, seq, layer, kv_head, self.max_positions)
+
+    def export_kv(self, seq, layer, kv_head):
+        return dms_export_kv(self.handle, seq, layer, kv_head, self.max_positions, self.head_dim, self.fp8)
 
     def release(self, seq):
         dms_seq_release(self.handle, seq, self._stream())

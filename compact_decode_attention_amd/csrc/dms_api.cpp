@@ -28,7 +28,8 @@ dms_status hip_fail(hipError_t e, const char* what) {
 constexpr size_t kAlign = 256;
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
-enum Section { S_K, S_V, S_POS, S_STACK, S_HSTATE, S_PTABLE, S_RING, S_PART, S_PREFIX, S_INV, S_PCNT, S_VT, S_CTL, S_N };
+enum Section { S_K, S_V, S_KS, S_VS, S_POS, S_STACK, S_HSTATE, S_PTABLE, S_RING, S_PART, S_PREFIX, S_INV, S_PCNT,
+               S_VT, S_Q8, S_CTL, S_N };
 
 struct Layout {
     size_t off[S_N + 1];
@@ -51,7 +52,9 @@ bool make_layout(const dms_pool_config* c, Layout* L, std::string* why) {
     if (c->page_slots != 0 && c->page_slots != DMS_PAGE_SLOTS) return bad("page_slots must be 0 or 64");
     if (c->max_pages < 1 || c->max_pages > (int64_t)INT32_MAX) return bad("max_pages must be in [1, 2^31)");
     if (!(c->softmax_scale >= 0.f) || !std::isfinite(c->softmax_scale)) return bad("softmax_scale must be finite and >= 0");
-    for (int i = 0; i < 4; ++i)
+    if (c->kv_format != DMS_KV_BF16 && c->kv_format != DMS_KV_FP8_E4M3)
+        return bad("kv_format must be DMS_KV_BF16 or DMS_KV_FP8_E4M3");
+    for (int i = 0; i < 3; ++i)
         if (c->reserved[i] != 0) return bad("reserved fields must be 0");
     const int64_t heads = (int64_t)c->max_seqs * c->n_layers * c->n_kv_heads;
     if (heads > (int64_t)INT32_MAX / 4) return bad("max_seqs * n_layers * n_kv_heads too large");
@@ -63,9 +66,12 @@ bool make_layout(const dms_pool_config* c, Layout* L, std::string* why) {
     L->max_call_heads = (int32_t)std::min<int64_t>(heads, dms::kMaxCallHeads);
     // partial slots: one per (attention wave, call head) pair that can occur
     L->max_items = dms::kMaxAttendBlocks * dms::kAttendWaves + L->max_call_heads;
+    const bool fp8 = c->kv_format == DMS_KV_FP8_E4M3;
     size_t sz[S_N];
-    sz[S_K] = (size_t)c->max_pages * dms::kPage * D * 2;
+    sz[S_K] = (size_t)c->max_pages * dms::kPage * D * (fp8 ? 1 : 2);
     sz[S_V] = sz[S_K];
+    sz[S_KS] = fp8 ? (size_t)c->max_pages * dms::kPage * 4 : 0;
+    sz[S_VS] = sz[S_KS];
     sz[S_POS] = (size_t)c->max_pages * dms::kPage * 4;
     sz[S_STACK] = (size_t)c->max_pages * 4;
     sz[S_HSTATE] = (size_t)heads * dms::kHS * 4;
@@ -76,6 +82,7 @@ bool make_layout(const dms_pool_config* c, Layout* L, std::string* why) {
     sz[S_INV] = (size_t)c->n_kv_heads * c->max_positions * 4;
     sz[S_PCNT] = sz[S_INV];
     sz[S_VT] = (size_t)c->n_kv_heads * ((c->max_positions + 31) / 32 * 32) * D * 2;
+    sz[S_Q8] = fp8 ? (size_t)2 * c->max_positions * c->n_kv_heads * (D + 4) : 0;
     sz[S_CTL] = 64 * 4;
     size_t o = 0;
     for (int i = 0; i < S_N; ++i) {
@@ -148,6 +155,9 @@ dms_status dms_pool_create(const dms_pool_config* cfg, void* arena, size_t arena
     dms::PoolDev& d = p->dev;
     d.kpages = reinterpret_cast<uint16_t*>(a + L.off[S_K]);
     d.vpages = reinterpret_cast<uint16_t*>(a + L.off[S_V]);
+    d.kscale = reinterpret_cast<float*>(a + L.off[S_KS]);
+    d.vscale = reinterpret_cast<float*>(a + L.off[S_VS]);
+    d.q8 = reinterpret_cast<uint8_t*>(a + L.off[S_Q8]);
     d.slot_pos = reinterpret_cast<int32_t*>(a + L.off[S_POS]);
     d.stack = reinterpret_cast<int32_t*>(a + L.off[S_STACK]);
     d.hstate = reinterpret_cast<int32_t*>(a + L.off[S_HSTATE]);
@@ -170,6 +180,7 @@ dms_status dms_pool_create(const dms_pool_config* cfg, void* arena, size_t arena
     d.max_positions = cfg->max_positions;
     d.max_pos32 = (cfg->max_positions + 31) / 32 * 32;
     d.max_items = L.max_items;
+    d.fp8 = cfg->kv_format == DMS_KV_FP8_E4M3 ? 1 : 0;
     const double scale = cfg->softmax_scale > 0.f ? (double)cfg->softmax_scale : 1.0 / std::sqrt((double)cfg->head_dim);
     d.scale_log2 = (float)(scale * 1.4426950408889634);
 
@@ -365,8 +376,9 @@ dms_status dms_query_stats(dms_pool* pool, int32_t seq, dms_stats* out, int32_t*
             }
         }
     }
-    out->kv_bytes_live = out->live_slots * 2 * D * 2;
-    out->kv_bytes_allocated = out->pages_used * dms::kPage * 2 * D * 2;
+    const int64_t slot_bytes = c.kv_format == DMS_KV_FP8_E4M3 ? 2 * (D + 4) : 2 * D * 2;
+    out->kv_bytes_live = out->live_slots * slot_bytes;
+    out->kv_bytes_allocated = out->pages_used * dms::kPage * slot_bytes;
     out->kv_bytes_dense_equiv = dense_tokens * 2 * D * 2;
     out->pages_free = ctl[dms::kCtlTop];
     out->workspace_bytes = (int64_t)(pool->layout.off[S_N] - pool->layout.off[S_POS]);
@@ -409,6 +421,83 @@ dms_status dms_export_live(dms_pool* pool, int32_t seq, int32_t layer, int32_t k
         got += take;
     }
     std::sort(positions, positions + live);
+    g_err.clear();
+    return DMS_OK;
+}
+
+dms_status dms_export_kv(dms_pool* pool, int32_t seq, int32_t layer, int32_t kv_head, int32_t cap,
+                         int32_t* positions, void* k, void* v, float* k_scale, float* v_scale, int32_t* n) {
+    if (!pool || !n) return fail(DMS_E_INVAL, "pool and n must not be NULL");
+    const dms_pool_config& c = pool->cfg;
+    if (seq < 0 || seq >= c.max_seqs || layer < 0 || layer >= c.n_layers || kv_head < 0 || kv_head >= c.n_kv_heads)
+        return fail(DMS_E_INVAL, "(seq, layer, kv_head) out of range");
+    hipError_t e = hipDeviceSynchronize();
+    if (e != hipSuccess) return hip_fail(e, "synchronise");
+    const int64_t gh = ((int64_t)seq * c.n_layers + layer) * c.n_kv_heads + kv_head;
+    int32_t hs[dms::kHS];
+    e = hipMemcpy(hs, pool->dev.hstate + gh * dms::kHS, sizeof(hs), hipMemcpyDeviceToHost);
+    if (e != hipSuccess) return hip_fail(e, "read head state");
+    const int live = hs[dms::kHsLive], np = hs[dms::kHsPages];
+    *n = live;
+    if (live > cap) return fail(DMS_E_INVAL, "output arrays too small");
+    const bool fp8 = c.kv_format == DMS_KV_FP8_E4M3;
+    const int D = c.head_dim;
+    const size_t page_bytes = (size_t)dms::kPage * D * (fp8 ? 1 : 2);
+    std::vector<int32_t> pages((size_t)np);
+    if (np > 0) {
+        e = hipMemcpy(pages.data(), pool->dev.ptable + gh * pool->layout.pages_per_head, (size_t)np * 4,
+                      hipMemcpyDeviceToHost);
+        if (e != hipSuccess) return hip_fail(e, "read page table");
+    }
+    // rows in slot order, then sorted by position
+    std::vector<int32_t> pos((size_t)live);
+    std::vector<uint8_t> kr((size_t)live * D * (fp8 ? 1 : 2)), vr(kr.size());
+    std::vector<float> ksr((size_t)live, 1.f), vsr((size_t)live, 1.f);
+    std::vector<uint8_t> kpg(page_bytes), vpg(page_bytes);
+    std::vector<int32_t> spos(dms::kPage);
+    std::vector<float> ksc(dms::kPage), vsc(dms::kPage);
+    const char* kbase = reinterpret_cast<const char*>(pool->dev.kpages);
+    const char* vbase = reinterpret_cast<const char*>(pool->dev.vpages);
+    for (int j = 0; j < np && j * dms::kPage < live; ++j) {
+        const size_t pg = (size_t)pages[j];
+        e = hipMemcpy(spos.data(), pool->dev.slot_pos + pg * dms::kPage, dms::kPage * 4, hipMemcpyDeviceToHost);
+        if (e == hipSuccess) e = hipMemcpy(kpg.data(), kbase + pg * page_bytes, page_bytes, hipMemcpyDeviceToHost);
+        if (e == hipSuccess) e = hipMemcpy(vpg.data(), vbase + pg * page_bytes, page_bytes, hipMemcpyDeviceToHost);
+        if (e == hipSuccess && fp8) e = hipMemcpy(ksc.data(), pool->dev.kscale + pg * dms::kPage, dms::kPage * 4,
+                                                  hipMemcpyDeviceToHost);
+        if (e == hipSuccess && fp8) e = hipMemcpy(vsc.data(), pool->dev.vscale + pg * dms::kPage, dms::kPage * 4,
+                                                  hipMemcpyDeviceToHost);
+        if (e != hipSuccess) return hip_fail(e, "read pages");
+        for (int i = 0; i < dms::kPage && j * dms::kPage + i < live; ++i) {
+            const size_t r = (size_t)j * dms::kPage + i;
+            pos[r] = spos[i];
+            for (int d = 0; d < D; ++d) {
+                if (fp8) {  // K [D/16][64][16], V [4][D][16]
+                    kr[r * D + d] = kpg[((size_t)(d / 16) * dms::kPage + i) * 16 + d % 16];
+                    vr[r * D + d] = vpg[((size_t)(i / 16) * D + d) * 16 + i % 16];
+                } else {    // K [D/8][64][8], V [8][D][8] (2-byte values)
+                    std::memcpy(&kr[(r * D + d) * 2], &kpg[(((size_t)(d / 8) * dms::kPage + i) * 8 + d % 8) * 2], 2);
+                    std::memcpy(&vr[(r * D + d) * 2], &vpg[(((size_t)(i / 8) * D + d) * 8 + i % 8) * 2], 2);
+                }
+            }
+            if (fp8) {
+                ksr[r] = ksc[i];
+                vsr[r] = vsc[i];
+            }
+        }
+    }
+    std::vector<int> order((size_t)live);
+    for (int r = 0; r < live; ++r) order[r] = r;
+    std::sort(order.begin(), order.end(), [&](int x, int y) { return pos[x] < pos[y]; });
+    const size_t row = (size_t)D * (fp8 ? 1 : 2);
+    for (int i = 0; i < live; ++i) {
+        const int r = order[i];
+        if (positions) positions[i] = pos[r];
+        if (k) std::memcpy(static_cast<char*>(k) + i * row, &kr[r * row], row);
+        if (v) std::memcpy(static_cast<char*>(v) + i * row, &vr[r * row], row);
+        if (k_scale) k_scale[i] = ksr[r];
+        if (v_scale) v_scale[i] = vsr[r];
+    }
     g_err.clear();
     return DMS_OK;
 }

@@ -1,12 +1,18 @@
 // Internal layout of a DMS pool and the kernel launchers (not part of the ABI).
 //
-// Arena layout (every section 256-byte aligned):
+// Arena layout (every section 256-byte aligned).  K/V pages of bf16 pools:
 //   kpages   bf16 [max_pages][head_dim/8][64][8]   K, 16-byte dim chunks, key-major:
 //                                                  chunk c of 64 consecutive slots is
 //                                                  1 KB contiguous (lane = slot loads)
 //   vpages   bf16 [max_pages][8][head_dim][8]      V, 8-slot blocks, dim-major: the
 //                                                  16 bytes at (block, d) are 8
 //                                                  consecutive slots of dim d
+// K/V pages of FP8 pools (E4M3 codes, one fp32 scale per slot):
+//   kpages   u8   [max_pages][head_dim/16][64][16] K, 16 dims per 16-byte chunk, key-major
+//   vpages   u8   [max_pages][4][head_dim][16]     V, 16-slot blocks, dim-major
+//   kscale   f32  [max_pages][64], vscale f32 [max_pages][64]
+//   q8       prefill scratch: the prompt quantised, codes u8 [2][max_positions]
+//            [n_kv_heads][head_dim] (K, V) then scales f32 [2][max_positions][n_kv_heads]
 //   slot_pos int32 [max_pages][64]                 position held by each slot
 //   stack    int32 [max_pages]                     free pages, stack[0 .. top)
 //   hstate   int32 [heads][8]                      per-head record (kHs* below)
@@ -20,9 +26,10 @@
 //   inv      int32 [n_kv_heads][max_positions]     prefill scratch: slot -> position
 //   pcnt     int32 [n_kv_heads][max_positions]     prefill scratch: live tokens in [0, s]
 //   vt       bf16 [n_kv_heads][max_pos32/8][head_dim][8]
-//                                                  prefill scratch: the prompt's V with 8
-//                                                  consecutive tokens per 16 bytes
-//                                                  (max_pos32 = max_positions rounded up to 32)
+//                                                  prefill scratch: the prompt's V (FP8 pools:
+//                                                  its codes as bf16) with 8 consecutive tokens
+//                                                  per 16 bytes (max_pos32 = max_positions
+//                                                  rounded up to 32)
 //   ctl      int32 [64]                            pool counters (kCtl* below)
 // heads = max_seqs * n_layers * n_kv_heads, head id = (seq * n_layers + layer) * n_kv_heads + h.
 #pragma once
@@ -66,8 +73,11 @@ constexpr int kHS = 8;
 constexpr int kHsLive = 0, kHsPages = 1, kHsPos = 2, kHsExp = 3;
 
 struct PoolDev {
-    uint16_t* kpages;
+    uint16_t* kpages;  // bf16 pools; FP8 pools hold bytes here (see kp8 / vp8)
     uint16_t* vpages;
+    float* kscale;     // FP8 pools only
+    float* vscale;
+    uint8_t* q8;       // FP8 pools only: prefill scratch
     int32_t* slot_pos;
     int32_t* stack;
     int32_t* hstate;
@@ -83,8 +93,62 @@ struct PoolDev {
     int32_t n_layers, n_q_heads, n_kv_heads, head_dim;
     int32_t window, ring_len, pages_per_head, max_positions, max_pos32;
     int32_t max_items;
+    int32_t fp8;       // kv_format == DMS_KV_FP8_E4M3
     float scale_log2;  // softmax scale * log2(e): scores are kept in base-2 units
+    __host__ __device__ uint8_t* kp8() const { return reinterpret_cast<uint8_t*>(kpages); }
+    __host__ __device__ uint8_t* vp8() const { return reinterpret_cast<uint8_t*>(vpages); }
+    // prefill scratch of an FP8 pool: codes of tensor x (0 = K, 1 = V) and their scales
+    __host__ __device__ uint8_t* q8_codes(int x) const {
+        return q8 + (size_t)x * max_positions * n_kv_heads * head_dim;
+    }
+    __host__ __device__ float* q8_scales(int x) const {
+        return reinterpret_cast<float*>(q8 + (size_t)2 * max_positions * n_kv_heads * head_dim) +
+               (size_t)x * max_positions * n_kv_heads;
+    }
 };
+
+// ---- OCP FP8 E4M3 (FP8 pools) -------------------------------------------------
+// Code of x: the finite E4M3 value nearest to x, ties to the code with an even
+// last bit, +-448 beyond the largest finite value, the sign kept (so -0 and
+// values rounding to zero from below give 0x80); NaN gives 0x7f.
+__device__ __forceinline__ uint32_t e4m3_encode(float x) {
+    const uint32_t u = __float_as_uint(x);
+    const uint32_t sign = (u >> 24) & 0x80u;
+    const uint32_t a = u & 0x7fffffffu;
+    if (a > 0x7f800000u) return 0x7fu;
+    const float af = __uint_as_float(a);
+    if (af >= 448.0f) return sign | 0x7eu;
+    if (af < 0.015625f) {  // below 2^-6: multiples of 2^-9 (code = multiple, 8 = 2^-6)
+        return sign | (uint32_t)__builtin_rintf(af * 512.0f);
+    }
+    // normal: round the fp32 mantissa to 3 bits, nearest-even (a carry moves the exponent)
+    const uint32_t r = (a + 0x7ffffu + ((a >> 20) & 1u)) >> 20;
+    return sign | (((r >> 3) - 120u) << 3) | (r & 7u);
+}
+
+// Value of an E4M3 code (NaN codes are never stored).
+__device__ __forceinline__ float e4m3_to_f32(uint32_t c) {
+    const uint32_t e = (c >> 3) & 15u, m = c & 7u;
+    const float mag = e ? __uint_as_float(((e + 120u) << 23) | (m << 20)) : (float)m * 0x1p-9f;
+    return (c & 0x80u) ? -mag : mag;
+}
+
+// Two codes (bytes 0-1 or 2-3 of w) as a bf16 pair (low half = the lower byte):
+// exact, every E4M3 value is a bf16 value.
+__device__ __forceinline__ uint32_t fp8x2_lo(uint32_t w) {
+    return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, false));
+}
+__device__ __forceinline__ uint32_t fp8x2_hi(uint32_t w) {
+    return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, true));
+}
+// 8 codes as 8 bf16 values
+__device__ __forceinline__ uint4 fp8x8_bf16(uint2 w) {
+    return make_uint4(fp8x2_lo(w.x), fp8x2_hi(w.x), fp8x2_lo(w.y), fp8x2_hi(w.y));
+}
+
+// Row scale: amax / 448 in fp32 (1 for an all-zero row); codes are
+// e4m3_encode(x / scale) with the fp32 quotient.
+__device__ __forceinline__ float e4m3_row_scale(float amax) { return amax > 0.f ? amax / 448.0f : 1.0f; }
 
 struct DecodeArgs {
     PoolDev pool;

@@ -246,10 +246,11 @@ __device__ __forceinline__ void qk_page(const uint4 (&kc)[D / 8], const uint4* s
 // Online-softmax update with the scores of one page (slots base + lane; slots at
 // or beyond n_old and the expiring slot e are masked).  The page's weights go to
 // LDS as two bf16 parts, hi = bf16(p) and lo = bf16(p - hi), for the PV step.
-template <int D, int G>
+// (FP8 pages: the LDS weights are p times the slot's V scale vmul, l sums p.)
+template <int D, int G, bool F8>
 __device__ __forceinline__ void softmax_page(const float (&z)[G], float scale_log2, int base, int n_old, int e,
-                                             int lane, uint16_t (*s_p)[G][kPage], float (&m)[G], float (&l)[G],
-                                             float (&acc)[G][D / 64]) {
+                                             int lane, float vmul, uint16_t (*s_p)[G][kPage], float (&m)[G],
+                                             float (&l)[G], float (&acc)[G][D / 64]) {
     const int slot = base + lane;
     const bool valid = slot < n_old && slot != e;
     float zz[G], mn[G], p[G];
@@ -266,9 +267,10 @@ __device__ __forceinline__ void softmax_page(const float (&z)[G], float scale_lo
             p[g] = exp2f(zz[g] - mn[g]);
             alpha = exp2f(m[g] - mn[g]);
         }
-        const uint16_t ph = f32_to_bf16(p[g]);
+        const float pw = F8 ? p[g] * vmul : p[g];
+        const uint16_t ph = f32_to_bf16(pw);
         s_p[0][g][lane] = ph;
-        s_p[1][g][lane] = f32_to_bf16(p[g] - bf16_to_f32(ph));
+        s_p[1][g][lane] = f32_to_bf16(pw - bf16_to_f32(ph));
         l[g] *= alpha;
         m[g] = mn[g];
 #pragma unroll
@@ -314,13 +316,116 @@ __device__ __forceinline__ void pv_page(const uint4 (&vc)[8][D / 64], const uint
     }
 }
 
+// ---- FP8 pages (E4M3 codes, one fp32 scale per slot) -----------------------
+__device__ __forceinline__ float buffer_load4f(__amdgpu_buffer_rsrc_t r, int voff) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, voff, 0, 0));
+}
+
+// K chunks of one FP8 page (lane = slot; chunk cc = 16 dims of 64 slots, 1 KB
+// contiguous), then the K and V scales of slot lane (behind the K chunks in the
+// load queue, so waiting for them never waits for the page's V).
+template <int D>
+__device__ __forceinline__ void issue_k8(const PoolDev& P, int page, bool live, int lane, uint4 (&kc)[D / 16],
+                                         float& ks, float& vs) {
+    const __amdgpu_buffer_rsrc_t r = buffer_rsrc(P.kp8() + (size_t)page * (kPage * D), live ? kPage * D : 0);
+#pragma unroll
+    for (int cc = 0; cc < D / 16; ++cc) kc[cc] = buffer_load16(r, lane * 16, cc * kPage * 16);
+    ks = buffer_load4f(buffer_rsrc(P.kscale + (size_t)page * kPage, live ? kPage * 4 : 0), lane * 4);
+    vs = buffer_load4f(buffer_rsrc(P.vscale + (size_t)page * kPage, live ? kPage * 4 : 0), lane * 4);
+}
+
+// V units of one FP8 page (lane = dim: unit (b, j) holds slots 16b .. 16b+15 of
+// dim j*64 + lane).
+template <int D>
+__device__ __forceinline__ void issue_v8(const PoolDev& P, int page, bool live, int lane, uint4 (&vc)[4][D / 64]) {
+    const __amdgpu_buffer_rsrc_t r = buffer_rsrc(P.vp8() + (size_t)page * (kPage * D), live ? kPage * D : 0);
+#pragma unroll
+    for (int b = 0; b < 4; ++b)
+#pragma unroll
+        for (int j = 0; j < D / 64; ++j) vc[b][j] = buffer_load16(r, lane * 16, (b * D + j * 64) * 16);
+}
+
+// QK^T of one FP8 page, lane = slot: chunk cc (dims 16cc .. 16cc+15) against q
+// pieces 2cc and 2cc+1; the codes become bf16 pairs once for all G heads.  The
+// result is in code units (times the slot's K scale = the score).
+template <int D, int G>
+__device__ __forceinline__ void qk_page8(const uint4 (&kc)[D / 16], const uint4* s_q, float (&z)[G]) {
+    constexpr int NC = D / 8;
+#pragma unroll
+    for (int g = 0; g < G; ++g) z[g] = 0.f;
+#pragma unroll
+    for (int cc = 0; cc < D / 16; ++cc) {
+        const uint32_t k0 = fp8x2_lo(kc[cc].x), k1 = fp8x2_hi(kc[cc].x);
+        const uint32_t k2 = fp8x2_lo(kc[cc].y), k3 = fp8x2_hi(kc[cc].y);
+        const uint32_t k4 = fp8x2_lo(kc[cc].z), k5 = fp8x2_hi(kc[cc].z);
+        const uint32_t k6 = fp8x2_lo(kc[cc].w), k7 = fp8x2_hi(kc[cc].w);
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+            const uint4 qa = s_q[g * NC + 2 * cc], qb = s_q[g * NC + 2 * cc + 1];
+            z[g] = dot2(qa.x, k0, z[g]);
+            z[g] = dot2(qa.y, k1, z[g]);
+            z[g] = dot2(qa.z, k2, z[g]);
+            z[g] = dot2(qa.w, k3, z[g]);
+            z[g] = dot2(qb.x, k4, z[g]);
+            z[g] = dot2(qb.y, k5, z[g]);
+            z[g] = dot2(qb.z, k6, z[g]);
+            z[g] = dot2(qb.w, k7, z[g]);
+            pin(z[g]);
+        }
+    }
+}
+
+// P.V of one FP8 page, lane = dim: unit (b, j) holds 16 slots of one dim, i.e.
+// 8 key pairs, matched by two 16-byte pieces of p per part (the weights already
+// carry the slots' V scales).
+template <int D, int G>
+__device__ __forceinline__ void pv_page8(const uint4 (&vc)[4][D / 64], const uint16_t (*s_p)[G][kPage],
+                                         float (&acc)[G][D / 64]) {
+    constexpr int VJ = D / 64;
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+        uint32_t vb[VJ][8];
+#pragma unroll
+        for (int j = 0; j < VJ; ++j) {
+            vb[j][0] = fp8x2_lo(vc[b][j].x);
+            vb[j][1] = fp8x2_hi(vc[b][j].x);
+            vb[j][2] = fp8x2_lo(vc[b][j].y);
+            vb[j][3] = fp8x2_hi(vc[b][j].y);
+            vb[j][4] = fp8x2_lo(vc[b][j].z);
+            vb[j][5] = fp8x2_hi(vc[b][j].z);
+            vb[j][6] = fp8x2_lo(vc[b][j].w);
+            vb[j][7] = fp8x2_hi(vc[b][j].w);
+        }
+#pragma unroll
+        for (int part = 0; part < 2; ++part) {
+#pragma unroll
+            for (int g = 0; g < G; ++g) {
+                const uint4 pa = *reinterpret_cast<const uint4*>(&s_p[part][g][16 * b]);
+                const uint4 pb = *reinterpret_cast<const uint4*>(&s_p[part][g][16 * b + 8]);
+#pragma unroll
+                for (int j = 0; j < VJ; ++j) {
+                    acc[g][j] = dot2(pa.x, vb[j][0], acc[g][j]);
+                    acc[g][j] = dot2(pa.y, vb[j][1], acc[g][j]);
+                    acc[g][j] = dot2(pa.z, vb[j][2], acc[g][j]);
+                    acc[g][j] = dot2(pa.w, vb[j][3], acc[g][j]);
+                    acc[g][j] = dot2(pb.x, vb[j][4], acc[g][j]);
+                    acc[g][j] = dot2(pb.y, vb[j][5], acc[g][j]);
+                    acc[g][j] = dot2(pb.z, vb[j][6], acc[g][j]);
+                    acc[g][j] = dot2(pb.w, vb[j][7], acc[g][j]);
+                    pin(acc[g][j]);
+                }
+            }
+        }
+    }
+}
+
 // q of call head ch's G query heads: G * D bf16, contiguous in the input.
 __device__ __forceinline__ const uint16_t* q_group(const DecodeArgs& a, int ch) {
     const CallHead c = call_head(a, ch);
     return a.q + ((size_t)c.row * a.pool.n_q_heads + c.h * (a.pool.n_q_heads / a.pool.n_kv_heads)) * a.pool.head_dim;
 }
 
-template <int D, int G>
+template <int D, int G, bool F8>
 __global__ __attribute__((amdgpu_flat_work_group_size(64 * kAttendWaves, 64 * kAttendWaves),
                           amdgpu_waves_per_eu(2, 2)))
 void decode_attend_kernel(DecodeArgs a) {
@@ -415,9 +520,20 @@ void decode_attend_kernel(DecodeArgs a) {
     int pid = __builtin_amdgcn_readfirstlane(cpid);
     uint4 qr[QR];
     load_q(hd, true, qr);
-    uint4 kc[D / 8], vc[8][VJ];
-    issue_k<D>(P, pid, true, lane, kc);
-    issue_v<D>(P, pid, true, lane, vc);
+    // K and V registers of one page (FP8 pages: half as many, plus the slot's
+    // scales, loaded with K into ksn / vsn and taken over at the top of the page)
+    uint4 kc[F8 ? D / 16 : D / 8], vc[F8 ? 4 : 8][VJ];
+    float ksc = 1.f, vsc = 1.f, ksn = 1.f, vsn = 1.f;
+    auto ik = [&](int page, bool live) {
+        if constexpr (F8) issue_k8<D>(P, page, live, lane, kc, ksn, vsn);
+        else issue_k<D>(P, page, live, lane, kc);
+    };
+    auto iv = [&](int page, bool live) {
+        if constexpr (F8) issue_v8<D>(P, page, live, lane, vc);
+        else issue_v<D>(P, page, live, lane, vc);
+    };
+    ik(pid, true);
+    iv(pid, true);
     store_q(qr);
 
     float m[G], l[G], acc[G][VJ];
@@ -447,14 +563,23 @@ void decode_attend_kernel(DecodeArgs a) {
         const int base = (k - __builtin_amdgcn_readfirstlane(s_pp[hd])) * kPage;
 
         float z[G];
-        qk_page<D, G>(kc, s_q[wave], z);
-        load_q(hd1, new_head, qr);           // the next head's q, if the run moves on
-        issue_k<D>(P, pid1, more, lane, kc);  // K registers are free again
-        softmax_page<D, G>(z, P.scale_log2, base, n_old, e, lane, s_p[wave], m, l, acc);
+        if constexpr (F8) {
+            ksc = ksn;
+            vsc = vsn;
+            qk_page8<D, G>(kc, s_q[wave], z);
+#pragma unroll
+            for (int g = 0; g < G; ++g) z[g] *= ksc;
+        } else {
+            qk_page<D, G>(kc, s_q[wave], z);
+        }
+        load_q(hd1, new_head, qr);  // the next head's q, if the run moves on
+        ik(pid1, more);             // K registers are free again
+        softmax_page<D, G, F8>(z, P.scale_log2, base, n_old, e, lane, vsc, s_p[wave], m, l, acc);
         wave_lds_sync();
-        pv_page<D, G>(vc, s_p[wave], acc);
-        issue_v<D>(P, pid1, more, lane, vc);  // V registers are free again
-        wave_lds_sync();                      // s_p is rewritten by the next page
+        if constexpr (F8) pv_page8<D, G>(vc, s_p[wave], acc);
+        else pv_page<D, G>(vc, s_p[wave], acc);
+        iv(pid1, more);             // V registers are free again
+        wave_lds_sync();            // s_p is rewritten by the next page
 
         if (!more || new_head) {
             // the run leaves head hd: its partial goes to slot w + hd
@@ -495,7 +620,9 @@ void decode_attend_kernel(DecodeArgs a) {
 // for the partials u = t / NF, t / NF + NPH, ... (a round of RU of them in
 // registers), and the maxima and sums (thread t: q head t % G of partials t / G,
 // t / G + 256 / G, ...).  The NPH phases are summed through LDS.
-template <int D, int G>
+// (FP8 pools: the new token enters as its quantised K and V rows, value(code) *
+// row scale, like every stored token.)
+template <int D, int G, bool F8>
 __device__ void merge_head(const DecodeArgs& a, int ch) {
     const PoolDev& P = a.pool;
     constexpr int PSTR = part_stride(G, D);  // floats per partial
@@ -553,12 +680,26 @@ __device__ void merge_head(const DecodeArgs& a, int ch) {
     for (int i = tid / G + NW_MAX; i < n; i += STEP) mloc = fmaxf(mloc, part0[(size_t)i * PSTR + gt]);
     // the new token: its value row and the score of each q head (one wave per q head)
     const uint2 vraw = *reinterpret_cast<const uint2*>(vn + (4 * f) % D);
+    float kx[D / 64], ks = 1.f, vs = 1.f;
+#pragma unroll
+    for (int j = 0; j < D / 64; ++j) kx[j] = bf16_to_f32(kn[j * 64 + lane]);
+    if constexpr (F8) {
+        float ka = 0.f, va = 0.f;
+#pragma unroll
+        for (int j = 0; j < D / 64; ++j) {
+            ka = fmaxf(ka, fabsf(kx[j]));
+            va = fmaxf(va, fabsf(bf16_to_f32(vn[j * 64 + lane])));
+        }
+        ks = e4m3_row_scale(wave_max(ka));
+        vs = e4m3_row_scale(wave_max(va));
+#pragma unroll
+        for (int j = 0; j < D / 64; ++j) kx[j] = e4m3_to_f32(e4m3_encode(kx[j] / ks));
+    }
     for (int g = wave; g < G; g += 4) {
         float dp = 0.f;
 #pragma unroll
-        for (int j = 0; j < D / 64; ++j)
-            dp = fmaf(bf16_to_f32(qg[g * D + j * 64 + lane]), bf16_to_f32(kn[j * 64 + lane]), dp);
-        const float zn = wave_sum(dp) * P.scale_log2;
+        for (int j = 0; j < D / 64; ++j) dp = fmaf(bf16_to_f32(qg[g * D + j * 64 + lane]), kx[j], dp);
+        const float zn = F8 ? wave_sum(dp) * ks * P.scale_log2 : wave_sum(dp) * P.scale_log2;
         if (lane == 0) s_zn[g] = zn;
     }
 
@@ -635,8 +776,14 @@ __device__ void merge_head(const DecodeArgs& a, int ch) {
     const float mn = fmaxf(M, zn);
     const float sc = M == -INFINITY ? 0.f : exp2f(M - mn), sn = exp2f(zn - mn);
     const float den = 1.f / (L * sc + sn);
-    const float v0 = bf16_to_f32((uint16_t)(vraw.x & 0xffffu)), v1 = bf16_to_f32((uint16_t)(vraw.x >> 16));
-    const float v2 = bf16_to_f32((uint16_t)(vraw.y & 0xffffu)), v3 = bf16_to_f32((uint16_t)(vraw.y >> 16));
+    float v0 = bf16_to_f32((uint16_t)(vraw.x & 0xffffu)), v1 = bf16_to_f32((uint16_t)(vraw.x >> 16));
+    float v2 = bf16_to_f32((uint16_t)(vraw.y & 0xffffu)), v3 = bf16_to_f32((uint16_t)(vraw.y >> 16));
+    if constexpr (F8) {
+        v0 = e4m3_to_f32(e4m3_encode(v0 / vs)) * vs;
+        v1 = e4m3_to_f32(e4m3_encode(v1 / vs)) * vs;
+        v2 = e4m3_to_f32(e4m3_encode(v2 / vs)) * vs;
+        v3 = e4m3_to_f32(e4m3_encode(v3 / vs)) * vs;
+    }
     uint2 packed;
     packed.x = (uint32_t)f32_to_bf16((o.x * sc + sn * v0) * den) | ((uint32_t)f32_to_bf16((o.y * sc + sn * v1) * den) << 16);
     packed.y = (uint32_t)f32_to_bf16((o.z * sc + sn * v2) * den) | ((uint32_t)f32_to_bf16((o.w * sc + sn * v3) * den) << 16);
@@ -646,7 +793,8 @@ __device__ void merge_head(const DecodeArgs& a, int ch) {
 // Mark the new token, expire position t-w if it was marked (its slot e is
 // reused), otherwise take slot n_old (a page from the shared pool when a new
 // page starts), write K/V, and advance the head record.  One wave.
-template <int D>
+// FP8 pools store the token's K and V rows as E4M3 codes with their row scales.
+template <int D, bool F8>
 __device__ void append_head(const DecodeArgs& a, int ch) {
     constexpr int VJ = D / 64;
     const PoolDev& P = a.pool;
@@ -698,11 +846,49 @@ __device__ void append_head(const DecodeArgs& a, int ch) {
         }
     }
     const int j = slot % kPage;
-    uint16_t* kp = P.kpages + (size_t)page * (kPage * D);
-    uint16_t* vp = P.vpages + (size_t)page * (kPage * D);
-    if (lane < D / 8) *reinterpret_cast<uint4*>(kp + ((size_t)lane * kPage + j) * 8) = kchunk;
+    if constexpr (F8) {
+        float ka = 0.f, va = 0.f;
 #pragma unroll
-    for (int jj = 0; jj < VJ; ++jj) vp[((size_t)(j / 8) * D + jj * 64 + lane) * 8 + (j % 8)] = vv[jj];
+        for (int jj = 0; jj < VJ; ++jj) {
+            ka = fmaxf(ka, fabsf(bf16_to_f32(kn[jj * 64 + lane])));
+            va = fmaxf(va, fabsf(bf16_to_f32(vv[jj])));
+        }
+        const float ks = e4m3_row_scale(wave_max(ka)), vs = e4m3_row_scale(wave_max(va));
+        uint8_t* kp = P.kp8() + (size_t)page * (kPage * D);
+        uint8_t* vp = P.vp8() + (size_t)page * (kPage * D);
+        if (lane < D / 16) {  // 16 dims per lane: one 16-byte chunk
+            const uint4 x0 = *reinterpret_cast<const uint4*>(kn + lane * 16);
+            const uint4 x1 = *reinterpret_cast<const uint4*>(kn + lane * 16 + 8);
+            const uint32_t xw[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+            uint32_t cw[4];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                uint32_t c = 0;
+#pragma unroll
+                for (int h2 = 0; h2 < 2; ++h2) {
+                    const uint32_t wbits = xw[2 * q + h2];
+                    c |= e4m3_encode(bf16_to_f32((uint16_t)(wbits & 0xffffu)) / ks) << (16 * h2);
+                    c |= e4m3_encode(bf16_to_f32((uint16_t)(wbits >> 16)) / ks) << (16 * h2 + 8);
+                }
+                cw[q] = c;
+            }
+            *reinterpret_cast<uint4*>(kp + ((size_t)lane * kPage + j) * 16) = make_uint4(cw[0], cw[1], cw[2], cw[3]);
+        }
+#pragma unroll
+        for (int jj = 0; jj < VJ; ++jj)
+            vp[((size_t)(j / 16) * D + jj * 64 + lane) * 16 + (j % 16)] =
+                (uint8_t)e4m3_encode(bf16_to_f32(vv[jj]) / vs);
+        if (lane == 0) {
+            P.kscale[(size_t)page * kPage + j] = ks;
+            P.vscale[(size_t)page * kPage + j] = vs;
+        }
+    } else {
+        uint16_t* kp = P.kpages + (size_t)page * (kPage * D);
+        uint16_t* vp = P.vpages + (size_t)page * (kPage * D);
+        if (lane < D / 8) *reinterpret_cast<uint4*>(kp + ((size_t)lane * kPage + j) * 8) = kchunk;
+#pragma unroll
+        for (int jj = 0; jj < VJ; ++jj) vp[((size_t)(j / 8) * D + jj * 64 + lane) * 8 + (j % 8)] = vv[jj];
+    }
     if (lane == 0) {
         P.slot_pos[(size_t)page * kPage + j] = t;
         if (P.ring_len > 0) P.ring[(size_t)c.gh * P.ring_len + (t % P.window)] = (slot << 1) | mark;
@@ -718,13 +904,13 @@ __device__ void append_head(const DecodeArgs& a, int ch) {
     }
 }
 
-template <int D, int G>
+template <int D, int G, bool F8>
 __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeArgs a) {
     const int H = a.n_call_heads;
     if ((int)blockIdx.x < H) {
-        merge_head<D, G>(a, blockIdx.x);
+        merge_head<D, G, F8>(a, blockIdx.x);
     } else if (threadIdx.x < 64) {
-        append_head<D>(a, blockIdx.x - H);
+        append_head<D, F8>(a, blockIdx.x - H);
     }
 }
 
@@ -841,6 +1027,98 @@ __global__ __launch_bounds__(256) void prefill_compact_kernel(PrefillArgs a) {
     if (tid < kPage) P.slot_pos[(size_t)page * kPage + tid] = s_src[tid];
 }
 
+// FP8 pools: the prompt's K and V rows as E4M3 codes and row scales, into the
+// prefill scratch (row r = s * n_kv_heads + h of tensor x = K, V).  D / 8 lanes
+// per row, 8 dims each; the row maximum is reduced over the row's lanes.
+template <int D>
+__global__ __launch_bounds__(256) void prefill_quant_kernel(PrefillArgs a) {
+    constexpr int LPR = D / 8;
+    const PoolDev& P = a.pool;
+    const int64_t rows = (int64_t)a.n_tokens * P.n_kv_heads;  // per tensor
+    const int64_t gt = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    const int64_t row = gt / LPR;
+    const int part = (int)(gt % LPR);
+    const bool live = row < 2 * rows;
+    const int x = live && row >= rows ? 1 : 0;
+    const int64_t r = live ? row - x * rows : 0;
+    uint4 u = make_uint4(0, 0, 0, 0);
+    if (live) u = *reinterpret_cast<const uint4*>((x ? a.v : a.k) + r * D + part * 8);
+    const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+    float f[8];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        f[2 * i] = bf16_to_f32((uint16_t)(w[i] & 0xffffu));
+        f[2 * i + 1] = bf16_to_f32((uint16_t)(w[i] >> 16));
+    }
+    float am = 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) am = fmaxf(am, fabsf(f[i]));
+#pragma unroll
+    for (int o = 1; o < LPR; o <<= 1) am = fmaxf(am, __shfl_xor(am, o, 64));
+    const float sc = e4m3_row_scale(am);
+    uint32_t c[2] = {0u, 0u};
+#pragma unroll
+    for (int i = 0; i < 8; ++i) c[i / 4] |= e4m3_encode(f[i] / sc) << (8 * (i % 4));
+    if (live) {
+        *reinterpret_cast<uint2*>(P.q8_codes(x) + r * D + part * 8) = make_uint2(c[0], c[1]);
+        if (part == 0) P.q8_scales(x)[r] = sc;
+    }
+}
+
+// FP8 pools: gather the live rows' codes and scales into the head's pages, one
+// block per destination page (K chunks of 16 dims key-major; V through LDS into
+// 16-slot dim-major units).  Slots past the live count get zero codes and scales.
+template <int D>
+__global__ __launch_bounds__(256) void prefill_compact8_kernel(PrefillArgs a) {
+    constexpr int NC = D / 16;
+    const PoolDev& P = a.pool;
+    __shared__ int s_src[kPage];
+    __shared__ __attribute__((aligned(16))) uint8_t s_v[kPage][D + 16];
+    const int tid = threadIdx.x;
+    const int pj = blockIdx.x, h = blockIdx.y;
+    const int hkv = P.n_kv_heads;
+    const int gh = (a.seq * P.n_layers + a.layer) * hkv + h;
+    const int n = P.hstate[(size_t)gh * kHS + kHsLive];
+    if (pj * kPage >= n) return;
+    const int page = P.ptable[(size_t)gh * P.pages_per_head + pj];
+    const int cnt = min(kPage, n - pj * kPage);
+    if (tid < kPage) s_src[tid] = tid < cnt ? P.inv[(size_t)h * P.max_positions + pj * kPage + tid] : -1;
+    __syncthreads();
+    const uint8_t* kq = P.q8_codes(0);
+    const uint8_t* vq = P.q8_codes(1);
+    uint8_t* kp = P.kp8() + (size_t)page * (kPage * D);
+    uint8_t* vp = P.vp8() + (size_t)page * (kPage * D);
+    const uint4 zero = make_uint4(0, 0, 0, 0);
+    for (int u = tid; u < NC * kPage; u += 256) {
+        const int cc = u / kPage, j = u - cc * kPage;
+        const int s = s_src[j];
+        const uint4 val = s >= 0 ? *reinterpret_cast<const uint4*>(kq + ((size_t)s * hkv + h) * D + cc * 16) : zero;
+        *reinterpret_cast<uint4*>(kp + ((size_t)cc * kPage + j) * 16) = val;
+    }
+    for (int u = tid; u < kPage * NC; u += 256) {
+        const int j = u / NC, cc = u - j * NC;
+        const int s = s_src[j];
+        const uint4 val = s >= 0 ? *reinterpret_cast<const uint4*>(vq + ((size_t)s * hkv + h) * D + cc * 16) : zero;
+        *reinterpret_cast<uint4*>(&s_v[j][cc * 16]) = val;
+    }
+    __syncthreads();
+    for (int u = tid; u < 4 * D; u += 256) {
+        const int b = u / D, d = u - b * D;
+        uint32_t w4[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            w4[i] = (uint32_t)s_v[16 * b + 4 * i][d] | ((uint32_t)s_v[16 * b + 4 * i + 1][d] << 8) |
+                    ((uint32_t)s_v[16 * b + 4 * i + 2][d] << 16) | ((uint32_t)s_v[16 * b + 4 * i + 3][d] << 24);
+        *reinterpret_cast<uint4*>(vp + ((size_t)b * D + d) * 16) = make_uint4(w4[0], w4[1], w4[2], w4[3]);
+    }
+    if (tid < kPage) {
+        const int s = s_src[tid];
+        P.slot_pos[(size_t)page * kPage + tid] = s;
+        P.kscale[(size_t)page * kPage + tid] = s >= 0 ? P.q8_scales(0)[(size_t)s * hkv + h] : 0.f;
+        P.vscale[(size_t)page * kPage + tid] = s >= 0 ? P.q8_scales(1)[(size_t)s * hkv + h] : 0.f;
+    }
+}
+
 __global__ __launch_bounds__(64) void seq_release_kernel(PoolDev P, int seq) {
     const int gh = seq * P.n_layers * P.n_kv_heads + blockIdx.x;
     int32_t* hs = P.hstate + (size_t)gh * kHS;
@@ -857,24 +1135,31 @@ size_t decode_shm(const DecodeArgs& a) { return (size_t)(4 * a.n_call_heads + 1)
 
 // ev (optional): start/stop of the attention kernel, then of the merge kernel,
 // taken by the dispatches themselves (kernel execution only)
-template <int D, int G>
-hipError_t launch_decode_t(const DecodeArgs& a, int grid, hipStream_t s, hipEvent_t* ev) {
-    hipExtLaunchKernelGGL((decode_attend_kernel<D, G>), dim3(grid), dim3(64 * kAttendWaves), decode_shm(a), s,
+template <int D, int G, bool F8>
+hipError_t launch_decode_f(const DecodeArgs& a, int grid, hipStream_t s, hipEvent_t* ev) {
+    hipExtLaunchKernelGGL((decode_attend_kernel<D, G, F8>), dim3(grid), dim3(64 * kAttendWaves), decode_shm(a), s,
                           ev ? ev[0] : nullptr, ev ? ev[1] : nullptr, 0, a);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
-    hipExtLaunchKernelGGL((decode_merge_kernel<D, G>), dim3(2 * a.n_call_heads), dim3(256), 0, s,
+    hipExtLaunchKernelGGL((decode_merge_kernel<D, G, F8>), dim3(2 * a.n_call_heads), dim3(256), 0, s,
                           ev ? ev[2] : nullptr, ev ? ev[3] : nullptr, 0, a);
     return hipGetLastError();
 }
 
 template <int D, int G>
+hipError_t launch_decode_t(const DecodeArgs& a, int grid, hipStream_t s, hipEvent_t* ev) {
+    return a.pool.fp8 ? launch_decode_f<D, G, true>(a, grid, s, ev) : launch_decode_f<D, G, false>(a, grid, s, ev);
+}
+
+template <int D, int G>
 int blocks_per_cu_t(const DecodeArgs& a) {
     int n = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_attend_kernel<D, G>, 64 * kAttendWaves,
-                                                     decode_shm(a)) != hipSuccess)
-        return 0;
-    return n;
+    const hipError_t e =
+        a.pool.fp8 ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_attend_kernel<D, G, true>,
+                                                                  64 * kAttendWaves, decode_shm(a))
+                   : hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_attend_kernel<D, G, false>,
+                                                                  64 * kAttendWaves, decode_shm(a));
+    return e == hipSuccess ? n : 0;
 }
 
 template <int D>
@@ -912,14 +1197,27 @@ int decode_blocks_per_cu(const DecodeArgs& a) {
 }
 
 hipError_t launch_prefill_compact(const PrefillArgs& a, hipStream_t s, hipEvent_t start, hipEvent_t stop) {
+    const bool d128 = a.pool.head_dim == 128;
+    if (a.pool.fp8) {  // quantise the prompt first (the compaction gathers codes)
+        const int64_t threads = (int64_t)2 * a.n_tokens * a.pool.n_kv_heads * (a.pool.head_dim / 8);
+        const dim3 qgrid((unsigned)((threads + 255) / 256));
+        if (d128) hipExtLaunchKernelGGL(prefill_quant_kernel<128>, qgrid, dim3(256), 0, s, start, nullptr, 0, a);
+        else hipExtLaunchKernelGGL(prefill_quant_kernel<64>, qgrid, dim3(256), 0, s, start, nullptr, 0, a);
+        hipError_t err = hipGetLastError();
+        if (err != hipSuccess) return err;
+        start = nullptr;
+    }
     hipExtLaunchKernelGGL(prefill_scan_kernel, dim3(a.pool.n_kv_heads), dim3(1024), 0, s, start, nullptr, 0, a);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
     const dim3 grid((a.n_tokens + kPage - 1) / kPage, a.pool.n_kv_heads);
-    if (a.pool.head_dim == 128)
-        hipExtLaunchKernelGGL(prefill_compact_kernel<128>, grid, dim3(256), 0, s, nullptr, stop, 0, a);
-    else
-        hipExtLaunchKernelGGL(prefill_compact_kernel<64>, grid, dim3(256), 0, s, nullptr, stop, 0, a);
+    if (a.pool.fp8) {
+        if (d128) hipExtLaunchKernelGGL(prefill_compact8_kernel<128>, grid, dim3(256), 0, s, nullptr, stop, 0, a);
+        else hipExtLaunchKernelGGL(prefill_compact8_kernel<64>, grid, dim3(256), 0, s, nullptr, stop, 0, a);
+    } else {
+        if (d128) hipExtLaunchKernelGGL(prefill_compact_kernel<128>, grid, dim3(256), 0, s, nullptr, stop, 0, a);
+        else hipExtLaunchKernelGGL(prefill_compact_kernel<64>, grid, dim3(256), 0, s, nullptr, stop, 0, a);
+    }
     return hipGetLastError();
 }
 

@@ -63,9 +63,10 @@ __device__ __forceinline__ int swap23(int i) { return (i & ~12) | ((i & 4) << 1)
 
 // ---------------------------------------------------------------------------
 // prompt V -> vt[h][s/8][d][8] (8 consecutive tokens of one dim per 16 bytes),
-// zero beyond the prompt up to the next multiple of 32
+// zero beyond the prompt up to the next multiple of 32.  FP8 pools: the values
+// of the prompt V's codes (exact in bf16; the row scales are applied to P).
 // ---------------------------------------------------------------------------
-template <int D>
+template <int D, bool F8>
 __global__ __launch_bounds__(256) void prefill_vt_kernel(PrefillArgs a) {
     const PoolDev& P = a.pool;
     __shared__ uint16_t s_v[64][D + 8];
@@ -78,7 +79,12 @@ __global__ __launch_bounds__(256) void prefill_vt_kernel(PrefillArgs a) {
         const int j = u / NC, cc = u - j * NC;
         const int s = s0 + j;
         uint4 val = make_uint4(0, 0, 0, 0);
-        if (s < T) val = *reinterpret_cast<const uint4*>(a.v + ((size_t)s * hkv + h) * D + cc * 8);
+        if (s < T) {
+            if constexpr (F8)
+                val = fp8x8_bf16(*reinterpret_cast<const uint2*>(P.q8_codes(1) + ((size_t)s * hkv + h) * D + cc * 8));
+            else
+                val = *reinterpret_cast<const uint4*>(a.v + ((size_t)s * hkv + h) * D + cc * 8);
+        }
         *reinterpret_cast<uint4*>(&s_v[j][cc * 8]) = val;
     }
     __syncthreads();
@@ -114,7 +120,12 @@ __global__ __launch_bounds__(256) void prefill_vt_kernel(PrefillArgs a) {
 constexpr int kPrefillWaves = DMS_PREFILL_WAVES;  // waves per block (tuning constant), at least G
 constexpr int prefill_waves(int g) { return kPrefillWaves > g ? kPrefillWaves : g; }
 
-template <int D, int G>
+//
+// FP8 pools: K and V are staged as the bf16 values of their codes (far field
+// from the pages, band from the quantised prompt and its V copy) and the row
+// scales of the tile's keys go to LDS with V: a key's scores are multiplied by
+// its K scale before the softmax, its weights by its V scale before P.V.
+template <int D, int G, bool F8>
 __global__ __attribute__((amdgpu_flat_work_group_size(64 * prefill_waves(G), 64 * prefill_waves(G)),
                           amdgpu_waves_per_eu(2, 2)))
 void prefill_attend_kernel(PrefillArgs a) {
@@ -129,6 +140,7 @@ void prefill_attend_kernel(PrefillArgs a) {
     __shared__ uint4 s_k[2][D / 8][32];
     __shared__ uint4 s_v[2][4][D];
     __shared__ uint32_t s_marks[2];
+    __shared__ float4 s_ks[2][8], s_vs[2][8];  // FP8: K and V scales of the tile's 32 keys
     const PoolDev& P = a.pool;
     const int T = a.n_tokens, w = P.window, hkv = P.n_kv_heads, hq_n = P.n_q_heads;
     const int nqb = (T + 32 * QT - 1) / (32 * QT);
@@ -174,6 +186,7 @@ void prefill_attend_kernel(PrefillArgs a) {
     auto tile_kb = [&](int i) { return i < nfar ? 32 * i : band0 + 32 * (i - nfar); };
     uint4 rk[UPT], rv[UPT];
     bool rmark = false;
+    float rks = 0.f, rvs = 0.f;
     // page ids of far-field tiles one step ahead of their use: pg1 = page of tile
     // i+1 (for V), pg2 = page of tile i+2 (for K), pg3 requested for the next step
     auto page_of = [&](int t) -> int { return t < nfar ? ptab[(32 * t) / kPage] : 0; };
@@ -186,12 +199,24 @@ void prefill_attend_kernel(PrefillArgs a) {
             const int cc = u >> 5, j = u & 31;
             if (u < UNITS) {
                 if (i < nfar) {
-                    const uint16_t* kp = P.kpages + (size_t)(i == 0 ? page_of(0) : i == 1 ? pg1 : pg2) * (kPage * D);
-                    rk[x] = *reinterpret_cast<const uint4*>(kp + ((size_t)cc * kPage + kb % kPage + j) * 8);
+                    const size_t pg = (size_t)(i == 0 ? page_of(0) : i == 1 ? pg1 : pg2);
+                    if constexpr (F8) {  // 8 of the 16 dims of chunk cc / 2
+                        const uint8_t* kp = P.kp8() + pg * (kPage * D);
+                        rk[x] = fp8x8_bf16(*reinterpret_cast<const uint2*>(
+                            kp + ((size_t)(cc >> 1) * kPage + kb % kPage + j) * 16 + (cc & 1) * 8));
+                    } else {
+                        const uint16_t* kp = P.kpages + pg * (kPage * D);
+                        rk[x] = *reinterpret_cast<const uint4*>(kp + ((size_t)cc * kPage + kb % kPage + j) * 8);
+                    }
                 } else {
                     const int sk = kb + j;
-                    rk[x] = sk < T ? *reinterpret_cast<const uint4*>(a.k + ((size_t)sk * hkv + h) * D + cc * 8)
-                                   : make_uint4(0, 0, 0, 0);
+                    if constexpr (F8)
+                        rk[x] = sk < T ? fp8x8_bf16(*reinterpret_cast<const uint2*>(
+                                             P.q8_codes(0) + ((size_t)sk * hkv + h) * D + cc * 8))
+                                       : make_uint4(0, 0, 0, 0);
+                    else
+                        rk[x] = sk < T ? *reinterpret_cast<const uint4*>(a.k + ((size_t)sk * hkv + h) * D + cc * 8)
+                                       : make_uint4(0, 0, 0, 0);
                 }
             }
         }
@@ -203,8 +228,16 @@ void prefill_attend_kernel(PrefillArgs a) {
             const int u = tid + x * NT;
             if (u < UNITS) {
                 if (i < nfar) {
-                    const uint16_t* vp = P.vpages + (size_t)(i == 0 ? page_of(0) : pg1) * (kPage * D);
-                    rv[x] = *reinterpret_cast<const uint4*>(vp + ((size_t)(kb % kPage / 8) * D) * 8 + (size_t)u * 8);
+                    const size_t pg = (size_t)(i == 0 ? page_of(0) : pg1);
+                    if constexpr (F8) {  // keys kb % 64 + 8 (u / D) .. +7 of dim u % D: half a 16-slot unit
+                        const int k0 = kb % kPage + 8 * (u / D);
+                        const uint8_t* vp = P.vp8() + pg * (kPage * D);
+                        rv[x] = fp8x8_bf16(*reinterpret_cast<const uint2*>(
+                            vp + ((size_t)(k0 / 16) * D + u % D) * 16 + (k0 % 16)));
+                    } else {
+                        const uint16_t* vp = P.vpages + pg * (kPage * D);
+                        rv[x] = *reinterpret_cast<const uint4*>(vp + ((size_t)(kb % kPage / 8) * D) * 8 + (size_t)u * 8);
+                    }
                 } else {
                     rv[x] = *reinterpret_cast<const uint4*>(vt + ((size_t)(kb / 8) * D) * 8 + (size_t)u * 8);
                 }
@@ -213,6 +246,19 @@ void prefill_attend_kernel(PrefillArgs a) {
         if (i >= nfar && tid < 32) {
             const int sk = kb + tid;
             rmark = sk < T && a.logits[(size_t)sk * hkv + h] > 0.f;
+        }
+        if constexpr (F8) {
+            if (tid < 32) {
+                if (i < nfar) {
+                    const size_t sl0 = (size_t)(i == 0 ? page_of(0) : pg1) * kPage + kb % kPage + tid;
+                    rks = P.kscale[sl0];
+                    rvs = P.vscale[sl0];
+                } else {
+                    const int sk = kb + tid;
+                    rks = sk < T ? P.q8_scales(0)[(size_t)sk * hkv + h] : 0.f;
+                    rvs = sk < T ? P.q8_scales(1)[(size_t)sk * hkv + h] : 0.f;
+                }
+            }
         }
     };
     auto store_k = [&](int i) {
@@ -231,6 +277,12 @@ void prefill_attend_kernel(PrefillArgs a) {
         if (i >= nfar && wave == 0) {
             const uint32_t mk = (uint32_t)__ballot(rmark);
             if (lane == 0) s_marks[i & 1] = mk;
+        }
+        if constexpr (F8) {
+            if (tid < 32) {
+                reinterpret_cast<float*>(s_ks[i & 1])[tid] = rks;
+                reinterpret_cast<float*>(s_vs[i & 1])[tid] = rvs;
+            }
         }
     };
     const int krow = swap23(col);  // key this lane feeds as A-operand row
@@ -269,13 +321,33 @@ void prefill_attend_kernel(PrefillArgs a) {
 
         // ---- fold tile i: row r of S_i holds key kb + (r & 7) + 8 half + 16 (r >> 3)
         const int kb = tile_kb(i);
+        float cs[16], vsc[16];  // scores (FP8: times the keys' K scales); FP8: the keys' V scales
+        if constexpr (F8) {
+#pragma unroll
+            for (int q4 = 0; q4 < 4; ++q4) {  // rows r0 .. r0+3 hold keys 4 kk .. 4 kk + 3
+                const int kk = 2 * half + (q4 & 1) + 4 * (q4 >> 1);
+                const float4 k4 = s_ks[i & 1][kk], v4 = s_vs[i & 1][kk];
+                const int r0 = 4 * (q4 & 1) + 8 * (q4 >> 1);
+                cs[r0] = cur[r0] * k4.x;
+                cs[r0 + 1] = cur[r0 + 1] * k4.y;
+                cs[r0 + 2] = cur[r0 + 2] * k4.z;
+                cs[r0 + 3] = cur[r0 + 3] * k4.w;
+                vsc[r0] = v4.x;
+                vsc[r0 + 1] = v4.y;
+                vsc[r0 + 2] = v4.z;
+                vsc[r0 + 3] = v4.w;
+            }
+        } else {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) cs[r] = cur[r];
+        }
         float z[16];
         if (i < nfar && kb + 32 <= U) {
 #pragma unroll
-            for (int r = 0; r < 16; ++r) z[r] = cur[r];
+            for (int r = 0; r < 16; ++r) z[r] = cs[r];
         } else if (i < nfar) {
 #pragma unroll
-            for (int r = 0; r < 16; ++r) z[r] = kb + (r & 7) + 8 * half + 16 * (r >> 3) < U ? cur[r] : -INFINITY;
+            for (int r = 0; r < 16; ++r) z[r] = kb + (r & 7) + 8 * half + 16 * (r >> 3) < U ? cs[r] : -INFINITY;
         } else {
             // visible keys of this lane's query as one 32-bit mask over the tile:
             // kb + kr <= tq, kb + kr > xf, and unmarked or kb + kr > tq - w
@@ -287,7 +359,7 @@ void prefill_attend_kernel(PrefillArgs a) {
             if (tq >= T) vis = 0;
             vis >>= 8 * half;  // this lane's rows: kr = (r & 7) + 8 half + 16 (r >> 3)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) z[r] = ((vis >> ((r & 7) + 16 * (r >> 3))) & 1u) ? cur[r] : -INFINITY;
+            for (int r = 0; r < 16; ++r) z[r] = ((vis >> ((r & 7) + 16 * (r >> 3))) & 1u) ? cs[r] : -INFINITY;
         }
         float tmax = z[0];
 #pragma unroll
@@ -328,8 +400,9 @@ void prefill_attend_kernel(PrefillArgs a) {
                                                              sc, 0, 0, 0);
             const float p0 = __builtin_amdgcn_exp2f(fmaf(z[2 * i2], sl, nm));
             const float p1 = __builtin_amdgcn_exp2f(fmaf(z[2 * i2 + 1], sl, nm));
-            const bf16x2_t hv = {(__bf16)p0, (__bf16)p1};
-            const bf16x2_t lv = {(__bf16)(p0 - (float)hv[0]), (__bf16)(p1 - (float)hv[1])};
+            const float w0 = F8 ? p0 * vsc[2 * i2] : p0, w1 = F8 ? p1 * vsc[2 * i2 + 1] : p1;
+            const bf16x2_t hv = {(__bf16)w0, (__bf16)w1};
+            const bf16x2_t lv = {(__bf16)(w0 - (float)hv[0]), (__bf16)(w1 - (float)hv[1])};
             ph[i2] = __builtin_bit_cast(uint32_t, hv);
             pl[i2] = __builtin_bit_cast(uint32_t, lv);
             ps += p0 + p1;
@@ -389,15 +462,24 @@ hipError_t launch_attend_t(const PrefillArgs& a, hipStream_t s, hipEvent_t* ev) 
     const int nqb = (a.n_tokens + 32 * QT - 1) / (32 * QT);
     const int total = a.pool.n_kv_heads * nqb;
     const int grid = 8 * ((total + 7) / 8);
-    hipExtLaunchKernelGGL((prefill_attend_kernel<D, G>), dim3(grid), dim3(64 * prefill_waves(G)), 0, s,
-                          ev ? ev[2] : nullptr, ev ? ev[3] : nullptr, 0, a);
+    if (a.pool.fp8)
+        hipExtLaunchKernelGGL((prefill_attend_kernel<D, G, true>), dim3(grid), dim3(64 * prefill_waves(G)), 0, s,
+                              ev ? ev[2] : nullptr, ev ? ev[3] : nullptr, 0, a);
+    else
+        hipExtLaunchKernelGGL((prefill_attend_kernel<D, G, false>), dim3(grid), dim3(64 * prefill_waves(G)), 0, s,
+                              ev ? ev[2] : nullptr, ev ? ev[3] : nullptr, 0, a);
     return hipGetLastError();
 }
 
 template <int D>
 hipError_t launch_attend_d(const PrefillArgs& a, hipStream_t s, hipEvent_t* ev) {
-    hipExtLaunchKernelGGL(prefill_vt_kernel<D>, dim3((a.n_tokens + 63) / 64, a.pool.n_kv_heads), dim3(256), 0, s,
-                          ev ? ev[0] : nullptr, ev ? ev[1] : nullptr, 0, a);
+    const dim3 vgrid((a.n_tokens + 63) / 64, a.pool.n_kv_heads);
+    if (a.pool.fp8)
+        hipExtLaunchKernelGGL((prefill_vt_kernel<D, true>), vgrid, dim3(256), 0, s, ev ? ev[0] : nullptr,
+                              ev ? ev[1] : nullptr, 0, a);
+    else
+        hipExtLaunchKernelGGL((prefill_vt_kernel<D, false>), vgrid, dim3(256), 0, s, ev ? ev[0] : nullptr,
+                              ev ? ev[1] : nullptr, 0, a);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
     switch (a.pool.n_q_heads / a.pool.n_kv_heads) {

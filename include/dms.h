@@ -28,7 +28,8 @@
  *    are passed as their 16-bit patterns.  Rows are contiguous, 16-byte aligned.
  *  - `stream` is a hipStream_t (NULL = the legacy default stream).  Calls
  *    enqueue kernels and return without waiting, except dms_pool_create,
- *    dms_pool_destroy, dms_query_stats and dms_export_live, which synchronise.
+ *    dms_pool_destroy, dms_query_stats, dms_export_live and dms_export_kv, which
+ *    synchronise.
  *  - Errors found on the host are returned at once and nothing is enqueued.
  *    A device-side failure (the shared page pool running out) sets a sticky
  *    flag that the next synchronising call returns as DMS_E_CAPACITY.
@@ -63,6 +64,22 @@ enum {
  * wavefront's worth of keys. */
 #define DMS_PAGE_SLOTS 64
 
+/* Storage format of K and V in the compact store (dms_pool_config.kv_format).
+ *  DMS_KV_BF16      K and V rows as given (2 bytes per value).
+ *  DMS_KV_FP8_E4M3  every (token, kv head) row of K, and of V, is stored as
+ *                   OCP FP8 E4M3 codes (1 byte per value) with one fp32 scale:
+ *                   scale = amax / 448 in fp32 (amax = the row's largest |x|;
+ *                   1 for an all-zero row), code = the finite E4M3 value nearest
+ *                   to x / scale (fp32 quotient; ties to the even code; beyond
+ *                   +-448 it is +-448), and attention, in prefill and decode,
+ *                   reads value(code) * scale in place of x.  Halves the bytes
+ *                   decode streams.  (The FastDMS announcement on molayo1419.me
+ *                   compares against FP8 KV caches; the format follows the OCP
+ *                   8-bit floating point specification.)  K/V inputs must be
+ *                   finite. */
+#define DMS_KV_BF16 0
+#define DMS_KV_FP8_E4M3 1
+
 typedef struct dms_pool dms_pool; /* opaque; owned by the library */
 
 typedef struct {
@@ -79,7 +96,8 @@ typedef struct {
     uint32_t page_order_seed; /* 0: pages are handed out in ascending order; otherwise
                                  in a seeded shuffled order (physical placement must
                                  not change any result) */
-    int32_t reserved[4];   /* must be 0 */
+    int32_t kv_format;     /* DMS_KV_BF16 (0) or DMS_KV_FP8_E4M3 */
+    int32_t reserved[3];   /* must be 0 */
 } dms_pool_config;
 
 /* Bytes of device memory (the arena) a pool with this configuration needs, or 0
@@ -135,8 +153,9 @@ dms_status dms_decode_step(dms_pool* pool, int32_t n_seqs, const int32_t* seq_id
 
 typedef struct {
     int64_t live_slots;           /* tokens held, summed over the queried layers and kv heads */
-    int64_t kv_bytes_live;        /* live_slots * 2 (K,V) * head_dim * 2 bytes */
-    int64_t kv_bytes_allocated;   /* pages held * 64 slots * 2 * head_dim * 2 bytes */
+    int64_t kv_bytes_live;        /* live_slots * bytes per slot: 2 (K,V) * head_dim * 2 bytes
+                                     (bf16), or 2 * (head_dim + 4) bytes (FP8 codes + scales) */
+    int64_t kv_bytes_allocated;   /* pages held * 64 slots * bytes per slot */
     int64_t kv_bytes_dense_equiv; /* what a store keeping every token would hold */
     int64_t pages_used;           /* pages held by the queried sequence(s) */
     int64_t pages_free;           /* free pages in the whole pool */
@@ -157,6 +176,16 @@ dms_status dms_query_stats(dms_pool* pool, int32_t seq, dms_stats* out,
  * (DMS_E_INVAL if it exceeds cap). */
 dms_status dms_export_live(dms_pool* pool, int32_t seq, int32_t layer, int32_t kv_head,
                            int32_t* positions, int32_t cap, int32_t* n);
+
+/* Synchronise and copy what one (seq, layer, kv_head) stores, row by row in
+ * ascending position order, to host arrays:
+ *   positions int32 [cap]
+ *   k, v      [cap][head_dim]: bf16 bits (bf16 pools) or E4M3 codes (FP8 pools)
+ *   k_scale, v_scale fp32 [cap]: the row scales (FP8 pools), 1 (bf16 pools)
+ * Any output pointer may be NULL to skip it.  *n receives the row count
+ * (DMS_E_INVAL if it exceeds cap). */
+dms_status dms_export_kv(dms_pool* pool, int32_t seq, int32_t layer, int32_t kv_head, int32_t cap,
+                         int32_t* positions, void* k, void* v, float* k_scale, float* v_scale, int32_t* n);
 
 /* Return every page of a sequence to the shared pool and forget its tokens on
  * all layers (enqueued on `stream`).  The sequence may then be prefilled again. */

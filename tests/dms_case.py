@@ -60,7 +60,9 @@ class Case:
     max_pages: Optional[int] = None
     max_positions: Optional[int] = None
     zero_q: bool = False
+    kv_format: int = 0                     # 0 bf16, 1 FP8 E4M3 (oracle: quantize_rows + attend_fp8)
     data: dict = field(default_factory=dict)
+    q8: dict = field(default_factory=dict)
 
     @property
     def n_seqs(self):
@@ -97,15 +99,29 @@ class Case:
             max_pages = self.max_pages
         return dict(n_layers=self.n_layers, n_q_heads=self.n_q_heads, n_kv_heads=self.n_kv_heads,
                     head_dim=self.head_dim, window=self.window, max_seqs=self.n_seqs,
-                    max_positions=maxpos, max_pages=max_pages, page_order_seed=self.page_order_seed)
+                    max_positions=maxpos, max_pages=max_pages, page_order_seed=self.page_order_seed,
+                    kv_format=self.kv_format)
 
     # ---- oracle side
     def marks(self, s, l):
         return oracle.marks(self.data[(s, l)].logits)
 
+    def quantized(self, s, l):
+        """The oracle's E4M3 codes and row scales of every K and V row of (s, l)."""
+        if (s, l) not in self.q8:
+            d = self.data[(s, l)]
+            k8, ks = oracle.quantize_rows(d.k)
+            v8, vs = oracle.quantize_rows(d.v)
+            self.q8[(s, l)] = (k8, ks, v8, vs)
+        return self.q8[(s, l)]
+
     def oracle_out(self, s, l, t):
         d = self.data[(s, l)]
         m = self.marks(s, l)
+        if self.kv_format:
+            k8, ks, v8, vs = self.quantized(s, l)
+            return oracle.attend_fp8(d.q[t:t + 1], [t], k8[:t + 1], ks[:t + 1], v8[:t + 1], vs[:t + 1],
+                                     m[:t + 1], self.window)[0]
         return oracle.attend(d.q[t:t + 1], [t], d.k[:t + 1], d.v[:t + 1], m[:t + 1], self.window)[0]
 
     def oracle_live(self, s, l, h, t):
@@ -179,6 +195,28 @@ class Runner:
                     assert np.array_equal(got, ref), ("live set", s, l, h, t, len(got), len(ref))
                     assert live[l, h] == len(ref)
         return st
+
+    def check_kv(self, t_of_seq):
+        """Every (seq, layer, kv head): the stored rows, in position order, are
+        exactly the inputs' rows (bf16 pools) or the oracle's codes and scales of
+        them (FP8 pools) at the oracle's live positions."""
+        c = self.case
+        for s in range(c.n_seqs):
+            for l in range(c.n_layers):
+                d = c.data[(s, l)]
+                for h in range(c.n_kv_heads):
+                    pos, k, v, ks, vs = self.pool.export_kv(s, l, h)
+                    ref = c.oracle_live(s, l, h, t_of_seq[s])
+                    assert np.array_equal(pos, ref), ("kv positions", s, l, h)
+                    if c.kv_format:
+                        k8, kss, v8, vss = c.quantized(s, l)
+                        assert np.array_equal(k, k8[pos, h]), ("K codes", s, l, h)
+                        assert np.array_equal(v, v8[pos, h]), ("V codes", s, l, h)
+                        assert np.array_equal(ks, kss[pos, h]), ("K scales", s, l, h)
+                        assert np.array_equal(vs, vss[pos, h]), ("V scales", s, l, h)
+                    else:
+                        assert np.array_equal(k, d.k[pos, h]), ("K rows", s, l, h)
+                        assert np.array_equal(v, d.v[pos, h]), ("V rows", s, l, h)
 
     def check_outputs(self, out, i, seqs=None, layer0=0):
         c = self.case

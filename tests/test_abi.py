@@ -26,7 +26,7 @@ def qwen_cfg(**kw):
 def test_header_declares_the_boundary():
     names = dms.header_symbols()
     for n in ["dms_pool_bytes", "dms_pool_create", "dms_pool_destroy", "dms_prefill", "dms_decode_step",
-              "dms_query_stats", "dms_export_live", "dms_seq_release", "dms_timing_enable",
+              "dms_query_stats", "dms_export_live", "dms_export_kv", "dms_seq_release", "dms_timing_enable",
               "dms_timing_read", "dms_last_error"]:
         assert n in names, n
 
@@ -91,6 +91,24 @@ def test_pool_bytes_rejects_page_slots_and_reserved():
         dms.dms_pool_bytes(cfg)
 
 
+def test_kv_format_is_checked():
+    for bad in (-1, 2, 7):
+        with pytest.raises(dms.DMSError) as e:
+            dms.dms_pool_bytes(qwen_cfg(kv_format=bad))
+        assert "kv_format" in str(e.value)
+
+
+def test_fp8_pool_holds_codes_and_scales():
+    """An FP8 pool's pages take head_dim + 4 bytes per row (codes and an fp32
+    scale) instead of 2 * head_dim, plus the prompt scratch for its codes."""
+    pages = 36 * 8 * 131
+    b16 = dms.dms_pool_bytes(qwen_cfg())
+    f8 = dms.dms_pool_bytes(qwen_cfg(kv_format=dms.DMS_KV_FP8_E4M3))
+    saved = 2 * pages * 64 * (2 * 128 - (128 + 4))
+    scratch = 2 * 8320 * 8 * (128 + 4)
+    assert b16 - f8 == saved - scratch
+
+
 def test_window_beyond_positions_needs_no_ring():
     """Eviction disabled (window >= every position) keeps no window ring."""
     a = dms.dms_pool_bytes(qwen_cfg(window=1 << 20))
@@ -123,6 +141,7 @@ def test_calls_on_a_null_pool_fail_cleanly():
     assert L.dms_decode_step(None, 1, ids, 0, 1, None, None, None, None, None, None) == dms.DMS_E_INVAL
     assert L.dms_query_stats(None, 0, ctypes.byref(st), None) == dms.DMS_E_INVAL
     assert L.dms_export_live(None, 0, 0, 0, None, 0, ctypes.byref(n)) == dms.DMS_E_INVAL
+    assert L.dms_export_kv(None, 0, 0, 0, 0, None, None, None, None, None, ctypes.byref(n)) == dms.DMS_E_INVAL
     assert L.dms_seq_release(None, 0, None) == dms.DMS_E_INVAL
     assert L.dms_timing_enable(None, 1) == dms.DMS_E_INVAL
     assert L.dms_timing_read(None, None) == dms.DMS_E_INVAL

@@ -24,6 +24,7 @@ def run_case(case, check_live_every=1, layer_batched=True):
             worst = (max(worst[0], e[0]), max(worst[1], e[1]))
             if check_live_every and (i % check_live_every == 0 or i == case.steps - 1):
                 r.check_live([case.ctx_lens[s] + i for s in range(case.n_seqs)])
+        r.check_kv([case.ctx_lens[s] + case.steps - 1 for s in range(case.n_seqs)])
         return r, worst
     except Exception:
         r.close()
