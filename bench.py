@@ -51,6 +51,7 @@ def log(*a):
 TRAFFIC_SOURCES = ["compact_decode_attention_amd/csrc/dms_kernels.hip",
                    "compact_decode_attention_amd/csrc/dms_internal.h"]
 TRAFFIC_SUMMARY = "profiles/decode_attend_qwen3-8b_hbm_traffic.md"
+TRAFFIC_SUMMARY_FP8 = "profiles/decode_attend_fp8_qwen3-8b_hbm_traffic.md"
 
 
 def sources_sha256(paths):
@@ -61,12 +62,12 @@ def sources_sha256(paths):
     return h.hexdigest()
 
 
-def measured_traffic():
-    """HBM bytes per launch of the decode attention kernel from the committed
+def measured_traffic(summary=TRAFFIC_SUMMARY):
+    """HBM bytes per launch of a decode attention kernel from the committed
     rocprofv3 FETCH_SIZE / WRITE_SIZE summary (each scaled by the same counter's
     reading for a plain copy of known size), or None when the summary is missing
     or was taken on other kernel sources."""
-    path = os.path.join(ROOT, TRAFFIC_SUMMARY)
+    path = os.path.join(ROOT, summary)
     if not os.path.exists(path):
         return None
     kv = {}
@@ -118,7 +119,9 @@ def bf16_tensor(a, torch):
 # ---------------------------------------------------------------------------
 # decode
 # ---------------------------------------------------------------------------
-def bench_decode(args, torch, dms):
+def bench_decode(args, torch, dms, kv_format=0, modes=None, cpu_steps=None):
+    """The decode leg; kv_format 1 runs it on an FP8 (E4M3) pool."""
+    fp8 = kv_format == 1
     wl = synth.WORKLOADS[args.workload]
     if wl.prefill_only or wl.n_seqs != 1:
         raise SystemExit("decode workload must be a single-sequence decode workload")
@@ -152,8 +155,10 @@ def bench_decode(args, torch, dms):
     log("decode inputs ready in %.1fs (ctx %d, %d layers)" % (time.time() - t0, ctx, L))
 
     pool = dms.Pool(n_layers=L, n_q_heads=Hq, n_kv_heads=H, head_dim=D, window=w, max_seqs=1,
-                    max_positions=total, max_pages=L * H * ((total + 63) // 64), device=dev)
+                    max_positions=total, max_pages=L * H * ((total + 63) // 64), kv_format=kv_format,
+                    device=dev)
     stream = torch.cuda.current_stream(dev)
+    row_bytes = D + 4 if fp8 else 2 * D  # one stored K (or V) row
 
     def reset():
         pool.release(0)
@@ -191,7 +196,7 @@ def bench_decode(args, torch, dms):
         dout[i].copy_(so)
 
     runners = {"batched": run_batched, "per_layer": run_per_layer, "graph": run_graph}
-    modes = [m for m in args.modes.split(",") if m]
+    modes = modes or [m for m in args.modes.split(",") if m]
     results, outs = {}, {}
     for mode in modes:
         fn = runners[mode]
@@ -213,7 +218,7 @@ def bench_decode(args, torch, dms):
         st, _ = pool.stats(0)
         results[mode] = {"ms_per_step": ms / K, "tok_per_s": K / (ms / 1e3), "live_slots_end": int(st.live_slots)}
         outs[mode] = dout[:K].clone()
-        log("decode %s: %.4f ms/step, %.1f tok/s" % (mode, ms / K, K / (ms / 1e3)))
+        log("decode%s %s: %.4f ms/step, %.1f tok/s" % (" (fp8 pool)" if fp8 else "", mode, ms / K, K / (ms / 1e3)))
     # the modes cut the page axis at different points (split-K rounding may
     # differ in the last bits): report the largest difference to the first mode
     diff = {m: float((outs[m].float() - outs[modes[0]].float()).abs().max()) for m in modes[1:]}
@@ -224,9 +229,9 @@ def bench_decode(args, torch, dms):
                      for l in range(L)])  # [L][H][K]
     st, live_end = pool.stats(0, per_head=True)
     assert np.array_equal(live[:, :, -1], live_end), "live counts differ from the logits"
-    kv_read = int(np.sum(live - 1)) * 2 * D * 2
+    kv_read = int(np.sum(live - 1)) * 2 * row_bytes
     q_bytes = K * L * Hq * D * 2
-    step_bytes = kv_read + q_bytes + K * L * (Hq * D * 2 + H * 2 * D * 2 * 2 + H * 4)
+    step_bytes = kv_read + q_bytes + K * L * (Hq * D * 2 + H * 2 * (2 * D + row_bytes) + H * 4)
     attend_bytes = (kv_read + q_bytes) / K  # per launch of the attention kernel
 
     roofline = None
@@ -241,15 +246,17 @@ def bench_decode(args, torch, dms):
         avg_att, avg_mer = tm.decode_attend_ms / n, tm.decode_merge_ms / n
         achieved = attend_bytes / (avg_att / 1e3) / 1e9
         roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                    "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": measured_traffic(),
-                    "kernel": "decode_attend_kernel<128,4>", "avg_launch_us": round(avg_att * 1e3, 2),
+                    "frac": round(achieved / HBM_PEAK_GBPS, 4),
+                    "traffic": measured_traffic(TRAFFIC_SUMMARY_FP8 if fp8 else TRAFFIC_SUMMARY),
+                    "kernel": "decode_attend_kernel<128,4,%s>" % ("fp8" if fp8 else "bf16"),
+                    "avg_launch_us": round(avg_att * 1e3, 2),
                     "bytes_per_launch": int(attend_bytes), "launches": int(n),
                     "merge_kernel_avg_launch_us": round(avg_mer * 1e3, 2)}
-        log("decode attend kernel: %.2f us/launch, %.1f GB/s (%.1f%% of peak); merge kernel %.2f us"
-            % (avg_att * 1e3, achieved, 100 * achieved / HBM_PEAK_GBPS, avg_mer * 1e3))
+        log("decode attend kernel%s: %.2f us/launch, %.1f GB/s (%.1f%% of peak); merge kernel %.2f us"
+            % (" (fp8)" if fp8 else "", avg_att * 1e3, achieved, 100 * achieved / HBM_PEAK_GBPS, avg_mer * 1e3))
 
     cpu = None
-    S = min(args.cpu_baseline_steps, K)
+    S = min(args.cpu_baseline_steps if cpu_steps is None else cpu_steps, K)
     if S > 0:
         import oracle  # the CPU baseline is the oracle, timed as it stands
         cores = int(os.environ.get("OMP_NUM_THREADS", len(os.sched_getaffinity(0))))
@@ -446,6 +453,7 @@ def main():
     ap.add_argument("--no-timing-pass", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-ragged", action="store_true", help="skip the 32-sequence ragged batch leg")
+    ap.add_argument("--no-fp8", action="store_true", help="skip the FP8-pool decode leg")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="first run a plain copy of this many MiB (for counter scaling)")
     args = ap.parse_args()
@@ -460,6 +468,13 @@ def main():
     if args.copy_calibration_mib > 0:
         copy_calibration(torch, args.copy_calibration_mib)
     dec = bench_decode(args, torch, dms)
+    f8 = None
+    if not args.no_fp8:
+        d8 = bench_decode(args, torch, dms, kv_format=1, modes=["batched"], cpu_steps=0)
+        f8 = {"tok_per_s": round(d8["value"], 2), "ms_per_step": round(d8["ms_per_step"], 5),
+              "achieved_step_GBps": d8["achieved_step_GBps"], "roofline": d8["roofline"], "kv_gib": d8["kv_gib"],
+              "workload": "the decode workload above on an FP8 (OCP E4M3) pool: K/V rows stored as codes "
+                          "with one fp32 scale each, one dms_decode_step per token over all layers"}
     pre = None if args.no_prefill else bench_prefill(args, torch, dms)
     rag = None if args.no_ragged else bench_ragged(args, torch, dms)
     rec = {
@@ -482,6 +497,7 @@ def main():
         "modes": dec["modes"],
         "modes_max_abs_diff": dec["modes_max_abs_diff"],
         "kv_gib": dec["kv_gib"],
+        "fp8_kv": f8,
         "prefill": pre,
         "batched_ragged": rag,
     }

@@ -210,7 +210,8 @@ dms_status dms_pool_create(const dms_pool_config* cfg, void* arena, size_t arena
         dms::DecodeArgs probe{};
         probe.pool = d;
         probe.n_call_heads = L.max_call_heads;
-        p->attend_per_cu = std::min(dms::kAttendBlocksPerCU, dms::decode_blocks_per_cu(probe));
+        const int want = d.fp8 ? dms::kAttendBlocksPerCUFp8 : dms::kAttendBlocksPerCU;
+        p->attend_per_cu = std::min(want, dms::decode_blocks_per_cu(probe));
         if (p->attend_per_cu < 1) {
             delete p;
             return fail(DMS_E_INVAL, "the decode kernel does not fit a compute unit with this configuration");

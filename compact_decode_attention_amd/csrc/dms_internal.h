@@ -48,9 +48,13 @@ namespace dms {
 #ifndef DMS_ATTEND_BLOCKS_PER_CU
 #define DMS_ATTEND_BLOCKS_PER_CU 1
 #endif
+#ifndef DMS_ATTEND_BLOCKS_PER_CU_FP8
+#define DMS_ATTEND_BLOCKS_PER_CU_FP8 2
+#endif
 constexpr int kPage = 64;          // slots per page
 constexpr int kAttendWaves = DMS_ATTEND_WAVES;
-constexpr int kAttendBlocksPerCU = DMS_ATTEND_BLOCKS_PER_CU;
+constexpr int kAttendBlocksPerCU = DMS_ATTEND_BLOCKS_PER_CU;          // bf16 pools
+constexpr int kAttendBlocksPerCUFp8 = DMS_ATTEND_BLOCKS_PER_CU_FP8;   // FP8 pools (half the registers)
 constexpr int kMaxAttendBlocks = 4096 / kAttendWaves;
 // Split-K partial of G q heads: m[G], l[G], padding to 16 bytes, acc[G][D].
 constexpr int part_acc_off(int g) { return (2 * g + 3) & ~3; }

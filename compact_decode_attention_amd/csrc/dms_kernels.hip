@@ -246,13 +246,19 @@ __device__ __forceinline__ void qk_page(const uint4 (&kc)[D / 8], const uint4* s
 // Online-softmax update with the scores of one page (slots base + lane; slots at
 // or beyond n_old and the expiring slot e are masked).  The page's weights go to
 // LDS as two bf16 parts, hi = bf16(p) and lo = bf16(p - hi), for the PV step.
-// (FP8 pages: the LDS weights are p times the slot's V scale vmul, l sums p.)
+// (FP8 pages: one fp16 part, p times vmul / vmax, vmul = the slot's V scale and
+// vmax = the largest over the page's valid slots, returned for P.V; l sums p.)
 template <int D, int G, bool F8>
 __device__ __forceinline__ void softmax_page(const float (&z)[G], float scale_log2, int base, int n_old, int e,
                                              int lane, float vmul, uint16_t (*s_p)[G][kPage], float (&m)[G],
-                                             float (&l)[G], float (&acc)[G][D / 64]) {
+                                             float (&l)[G], float (&acc)[G][D / 64], float& vmax) {
     const int slot = base + lane;
     const bool valid = slot < n_old && slot != e;
+    float pscale = 1.f;
+    if constexpr (F8) {
+        vmax = wave_max(valid ? vmul : 0.f);
+        pscale = vmax > 0.f ? vmul * __builtin_amdgcn_rcpf(vmax) : 0.f;
+    }
     float zz[G], mn[G], p[G];
     // the G heads' reductions are independent: issue them side by side
 #pragma unroll
@@ -267,10 +273,13 @@ __device__ __forceinline__ void softmax_page(const float (&z)[G], float scale_lo
             p[g] = exp2f(zz[g] - mn[g]);
             alpha = exp2f(m[g] - mn[g]);
         }
-        const float pw = F8 ? p[g] * vmul : p[g];
-        const uint16_t ph = f32_to_bf16(pw);
-        s_p[0][g][lane] = ph;
-        s_p[1][g][lane] = f32_to_bf16(pw - bf16_to_f32(ph));
+        if constexpr (F8) {
+            s_p[0][g][lane] = __builtin_bit_cast(uint16_t, (_Float16)(p[g] * pscale));
+        } else {
+            const uint16_t ph = f32_to_bf16(p[g]);
+            s_p[0][g][lane] = ph;
+            s_p[1][g][lane] = f32_to_bf16(p[g] - bf16_to_f32(ph));
+        }
         l[g] *= alpha;
         m[g] = mn[g];
 #pragma unroll
@@ -317,6 +326,22 @@ __device__ __forceinline__ void pv_page(const uint4 (&vc)[8][D / 64], const uint
 }
 
 // ---- FP8 pages (E4M3 codes, one fp32 scale per slot) -----------------------
+typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+
+// a.lo*b.lo + a.hi*b.hi + c, fp16 pairs, fp32 accumulate
+__device__ __forceinline__ float dot2h(uint32_t a, uint32_t b, float c) {
+    return __builtin_amdgcn_fdot2(__builtin_bit_cast(half2_t, a), __builtin_bit_cast(half2_t, b), c, false);
+}
+
+// Two E4M3 codes (bytes 0-1 or 2-3 of w) as an fp16 pair: exact (every E4M3
+// value is an fp16 value).
+__device__ __forceinline__ uint32_t fp8x2_h_lo(uint32_t w) {
+    return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, false));
+}
+__device__ __forceinline__ uint32_t fp8x2_h_hi(uint32_t w) {
+    return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, true));
+}
+
 __device__ __forceinline__ float buffer_load4f(__amdgpu_buffer_rsrc_t r, int voff) {
     return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, voff, 0, 0));
 }
@@ -376,47 +401,54 @@ __device__ __forceinline__ void qk_page8(const uint4 (&kc)[D / 16], const uint4*
 }
 
 // P.V of one FP8 page, lane = dim: unit (b, j) holds 16 slots of one dim, i.e.
-// 8 key pairs, matched by two 16-byte pieces of p per part (the weights already
-// carry the slots' V scales).
+// 8 key pairs as fp16 pairs, matched by two 16-byte pieces of the page's fp16
+// weights (p times the slot's V scale over the page's largest, vmax); the
+// page's sums enter the accumulators times vmax.
 template <int D, int G>
 __device__ __forceinline__ void pv_page8(const uint4 (&vc)[4][D / 64], const uint16_t (*s_p)[G][kPage],
-                                         float (&acc)[G][D / 64]) {
+                                         float vmax, float (&acc)[G][D / 64]) {
     constexpr int VJ = D / 64;
+    float t[G][VJ];
+#pragma unroll
+    for (int g = 0; g < G; ++g)
+#pragma unroll
+        for (int j = 0; j < VJ; ++j) t[g][j] = 0.f;
 #pragma unroll
     for (int b = 0; b < 4; ++b) {
         uint32_t vb[VJ][8];
 #pragma unroll
         for (int j = 0; j < VJ; ++j) {
-            vb[j][0] = fp8x2_lo(vc[b][j].x);
-            vb[j][1] = fp8x2_hi(vc[b][j].x);
-            vb[j][2] = fp8x2_lo(vc[b][j].y);
-            vb[j][3] = fp8x2_hi(vc[b][j].y);
-            vb[j][4] = fp8x2_lo(vc[b][j].z);
-            vb[j][5] = fp8x2_hi(vc[b][j].z);
-            vb[j][6] = fp8x2_lo(vc[b][j].w);
-            vb[j][7] = fp8x2_hi(vc[b][j].w);
+            vb[j][0] = fp8x2_h_lo(vc[b][j].x);
+            vb[j][1] = fp8x2_h_hi(vc[b][j].x);
+            vb[j][2] = fp8x2_h_lo(vc[b][j].y);
+            vb[j][3] = fp8x2_h_hi(vc[b][j].y);
+            vb[j][4] = fp8x2_h_lo(vc[b][j].z);
+            vb[j][5] = fp8x2_h_hi(vc[b][j].z);
+            vb[j][6] = fp8x2_h_lo(vc[b][j].w);
+            vb[j][7] = fp8x2_h_hi(vc[b][j].w);
         }
 #pragma unroll
-        for (int part = 0; part < 2; ++part) {
+        for (int g = 0; g < G; ++g) {
+            const uint4 pa = *reinterpret_cast<const uint4*>(&s_p[0][g][16 * b]);
+            const uint4 pb = *reinterpret_cast<const uint4*>(&s_p[0][g][16 * b + 8]);
 #pragma unroll
-            for (int g = 0; g < G; ++g) {
-                const uint4 pa = *reinterpret_cast<const uint4*>(&s_p[part][g][16 * b]);
-                const uint4 pb = *reinterpret_cast<const uint4*>(&s_p[part][g][16 * b + 8]);
-#pragma unroll
-                for (int j = 0; j < VJ; ++j) {
-                    acc[g][j] = dot2(pa.x, vb[j][0], acc[g][j]);
-                    acc[g][j] = dot2(pa.y, vb[j][1], acc[g][j]);
-                    acc[g][j] = dot2(pa.z, vb[j][2], acc[g][j]);
-                    acc[g][j] = dot2(pa.w, vb[j][3], acc[g][j]);
-                    acc[g][j] = dot2(pb.x, vb[j][4], acc[g][j]);
-                    acc[g][j] = dot2(pb.y, vb[j][5], acc[g][j]);
-                    acc[g][j] = dot2(pb.z, vb[j][6], acc[g][j]);
-                    acc[g][j] = dot2(pb.w, vb[j][7], acc[g][j]);
-                    pin(acc[g][j]);
-                }
+            for (int j = 0; j < VJ; ++j) {
+                t[g][j] = dot2h(pa.x, vb[j][0], t[g][j]);
+                t[g][j] = dot2h(pa.y, vb[j][1], t[g][j]);
+                t[g][j] = dot2h(pa.z, vb[j][2], t[g][j]);
+                t[g][j] = dot2h(pa.w, vb[j][3], t[g][j]);
+                t[g][j] = dot2h(pb.x, vb[j][4], t[g][j]);
+                t[g][j] = dot2h(pb.y, vb[j][5], t[g][j]);
+                t[g][j] = dot2h(pb.z, vb[j][6], t[g][j]);
+                t[g][j] = dot2h(pb.w, vb[j][7], t[g][j]);
+                pin(t[g][j]);
             }
         }
     }
+#pragma unroll
+    for (int g = 0; g < G; ++g)
+#pragma unroll
+        for (int j = 0; j < VJ; ++j) acc[g][j] = fmaf(t[g][j], vmax, acc[g][j]);
 }
 
 // q of call head ch's G query heads: G * D bf16, contiguous in the input.
@@ -512,18 +544,27 @@ void decode_attend_kernel(DecodeArgs a) {
         wave_lds_sync();
     };
 
+    // page ids and heads of pages b0 .. b0+63 (cur) and b0+64 .. b0+127 (nxt)
     int b0 = p0;
     int cpid, chd, npid = 0, nhd = 0;
     batch(b0, cpid, chd);
     if (b0 + 64 < p1) batch(b0 + 64, npid, nhd);  // the next batch, in flight
+    auto head_at = [&](int j) {                   // j - b0 in [0, 128), wave-uniform
+        const int i = j - b0;
+        return i < 64 ? __builtin_amdgcn_readlane(chd, i) : __builtin_amdgcn_readlane(nhd, i - 64);
+    };
+    auto page_at = [&](int j) {
+        const int i = j - b0;
+        return i < 64 ? __builtin_amdgcn_readlane(cpid, i) : __builtin_amdgcn_readlane(npid, i - 64);
+    };
     int hd = __builtin_amdgcn_readfirstlane(chd);
-    int pid = __builtin_amdgcn_readfirstlane(cpid);
     uint4 qr[QR];
     load_q(hd, true, qr);
     // K and V registers of one page (FP8 pages: half as many, plus the slot's
-    // scales, loaded with K into ksn / vsn and taken over at the top of the page)
+    // scales, loaded with K into ksn / vsn and taken over at the top of the
+    // page); once consumed they are refilled with the next page.
     uint4 kc[F8 ? D / 16 : D / 8], vc[F8 ? 4 : 8][VJ];
-    float ksc = 1.f, vsc = 1.f, ksn = 1.f, vsn = 1.f;
+    float ksn = 1.f, vsn = 1.f;
     auto ik = [&](int page, bool live) {
         if constexpr (F8) issue_k8<D>(P, page, live, lane, kc, ksn, vsn);
         else issue_k<D>(P, page, live, lane, kc);
@@ -532,8 +573,8 @@ void decode_attend_kernel(DecodeArgs a) {
         if constexpr (F8) issue_v8<D>(P, page, live, lane, vc);
         else issue_v<D>(P, page, live, lane, vc);
     };
-    ik(pid, true);
-    iv(pid, true);
+    ik(__builtin_amdgcn_readfirstlane(cpid), true);
+    iv(__builtin_amdgcn_readfirstlane(cpid), true);
     store_q(qr);
 
     float m[G], l[G], acc[G][VJ];
@@ -545,26 +586,24 @@ void decode_attend_kernel(DecodeArgs a) {
         for (int j = 0; j < VJ; ++j) acc[g][j] = 0.f;
     }
     for (int k = p0; k < p1; ++k) {
-        // page k+1: head and page id from the batch registers
-        const bool more = k + 1 < p1;
-        int idx = k + 1 - b0;
-        if (idx == 64) {
+        if (k - b0 == 64) {  // page k enters the next batch
             b0 += 64;
-            idx = 0;
             cpid = npid;
             chd = nhd;
             if (b0 + 64 < p1) batch(b0 + 64, npid, nhd);
         }
-        const int hd1 = more ? __builtin_amdgcn_readlane(chd, idx) : hd;
-        const int pid1 = more ? __builtin_amdgcn_readlane(cpid, idx) : 0;
+        const bool more = k + 1 < p1;
+        const int hd1 = more ? head_at(k + 1) : hd;
         const bool new_head = more && hd1 != hd;
+        const int pid1 = more ? page_at(k + 1) : 0;
         const int n_old = __builtin_amdgcn_readfirstlane(s_nold[hd]);
         const int e = __builtin_amdgcn_readfirstlane(s_exp[hd]);
         const int base = (k - __builtin_amdgcn_readfirstlane(s_pp[hd])) * kPage;
 
         float z[G];
+        float vsc = 1.f, vmax = 1.f;
         if constexpr (F8) {
-            ksc = ksn;
+            const float ksc = ksn;
             vsc = vsn;
             qk_page8<D, G>(kc, s_q[wave], z);
 #pragma unroll
@@ -574,9 +613,9 @@ void decode_attend_kernel(DecodeArgs a) {
         }
         load_q(hd1, new_head, qr);  // the next head's q, if the run moves on
         ik(pid1, more);             // K registers are free again
-        softmax_page<D, G, F8>(z, P.scale_log2, base, n_old, e, lane, vsc, s_p[wave], m, l, acc);
+        softmax_page<D, G, F8>(z, P.scale_log2, base, n_old, e, lane, vsc, s_p[wave], m, l, acc, vmax);
         wave_lds_sync();
-        if constexpr (F8) pv_page8<D, G>(vc, s_p[wave], acc);
+        if constexpr (F8) pv_page8<D, G>(vc, s_p[wave], vmax, acc);
         else pv_page<D, G>(vc, s_p[wave], acc);
         iv(pid1, more);             // V registers are free again
         wave_lds_sync();            // s_p is rewritten by the next page
