@@ -119,8 +119,10 @@ def bf16_tensor(a, torch):
 # ---------------------------------------------------------------------------
 # decode
 # ---------------------------------------------------------------------------
-def bench_decode(args, torch, dms, kv_format=0, modes=None, cpu_steps=None):
-    """The decode leg; kv_format 1 runs it on an FP8 (E4M3) pool."""
+def bench_decode(args, torch, dms, kv_format=0, modes=None, cpu_steps=None, logit_channel=None):
+    """The decode leg; kv_format 1 runs it on an FP8 (E4M3) pool; logit_channel c
+    carries each token's eviction logit (as bf16) in channel c of its K row and
+    the pool reads it from there (no logits input; the same marks)."""
     fp8 = kv_format == 1
     wl = synth.WORKLOADS[args.workload]
     if wl.prefill_only or wl.n_seqs != 1:
@@ -139,6 +141,9 @@ def bench_decode(args, torch, dms, kv_format=0, modes=None, cpu_steps=None):
     pk, pv, plg, host_k, host_v, host_lg = [], [], [], [], [], []
     for l in range(L):
         k, v, lg = inp.k(0, l, 0, total), inp.v(0, l, 0, total), inp.logits(0, l, 0, total)
+        if logit_channel is not None:
+            u = lg.view(np.uint32).astype(np.uint64)
+            k[:, :, logit_channel] = ((u + 0x7FFF + ((u >> 16) & 1)) >> 16).astype(np.uint16)
         host_k.append(k)
         host_v.append(v)
         host_lg.append(lg)
@@ -156,18 +161,19 @@ def bench_decode(args, torch, dms, kv_format=0, modes=None, cpu_steps=None):
 
     pool = dms.Pool(n_layers=L, n_q_heads=Hq, n_kv_heads=H, head_dim=D, window=w, max_seqs=1,
                     max_positions=total, max_pages=L * H * ((total + 63) // 64), kv_format=kv_format,
-                    device=dev)
+                    logit_channel=logit_channel, device=dev)
+    from_k = logit_channel is not None  # the pool reads the logits from K
     stream = torch.cuda.current_stream(dev)
     row_bytes = D + 4 if fp8 else 2 * D  # one stored K (or V) row
 
     def reset():
         pool.release(0)
         for l in range(L):
-            pool.prefill(0, l, pk[l], pv[l], plg[l])
+            pool.prefill(0, l, pk[l], pv[l], None if from_k else plg[l])
         torch.cuda.synchronize()
 
     def run_batched(i):
-        pool.decode_step([0], 0, dq[i], dk[i], dv[i], dl[i], dout[i])
+        pool.decode_step([0], 0, dq[i], dk[i], dv[i], None if from_k else dl[i], dout[i])
 
     def run_per_layer(i):
         for l in range(L):
@@ -454,6 +460,7 @@ def main():
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-ragged", action="store_true", help="skip the 32-sequence ragged batch leg")
     ap.add_argument("--no-fp8", action="store_true", help="skip the FP8-pool decode leg")
+    ap.add_argument("--no-logit-channel", action="store_true", help="skip the K-channel-logits decode leg")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="first run a plain copy of this many MiB (for counter scaling)")
     args = ap.parse_args()
@@ -475,6 +482,14 @@ def main():
               "achieved_step_GBps": d8["achieved_step_GBps"], "roofline": d8["roofline"], "kv_gib": d8["kv_gib"],
               "workload": "the decode workload above on an FP8 (OCP E4M3) pool: K/V rows stored as codes "
                           "with one fp32 scale each, one dms_decode_step per token over all layers"}
+    lk = None
+    if not args.no_logit_channel:
+        dk_ = bench_decode(args, torch, dms, modes=["batched"], cpu_steps=0, logit_channel=0)
+        lk = {"tok_per_s": round(dk_["value"], 2), "ms_per_step": round(dk_["ms_per_step"], 5),
+              "attend_avg_launch_us": dk_["roofline"]["avg_launch_us"] if dk_["roofline"] else None,
+              "merge_avg_launch_us": dk_["roofline"]["merge_kernel_avg_launch_us"] if dk_["roofline"] else None,
+              "workload": "the decode workload above with each token's eviction logit carried (bf16) in "
+                          "channel 0 of its K rows and read by the pool from there (no logits input)"}
     pre = None if args.no_prefill else bench_prefill(args, torch, dms)
     rag = None if args.no_ragged else bench_ragged(args, torch, dms)
     rec = {
@@ -498,6 +513,7 @@ def main():
         "modes_max_abs_diff": dec["modes_max_abs_diff"],
         "kv_gib": dec["kv_gib"],
         "fp8_kv": f8,
+        "logits_from_k_channel": lk,
         "prefill": pre,
         "batched_ragged": rag,
     }

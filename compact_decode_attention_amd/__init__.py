@@ -24,6 +24,7 @@ HEADER = os.path.join(os.path.dirname(HERE), "include", "dms.h")
 DMS_OK, DMS_E_INVAL, DMS_E_NOMEM, DMS_E_CAPACITY, DMS_E_STATE, DMS_E_HIP = 0, -1, -2, -3, -4, -5
 DMS_PAGE_SLOTS = 64
 DMS_KV_BF16, DMS_KV_FP8_E4M3 = 0, 1
+DMS_LOGITS_INPUT, DMS_LOGITS_K_CHANNEL = 0, 1
 _STATUS_NAMES = {0: "DMS_OK", -1: "DMS_E_INVAL", -2: "DMS_E_NOMEM", -3: "DMS_E_CAPACITY",
                  -4: "DMS_E_STATE", -5: "DMS_E_HIP"}
 
@@ -48,7 +49,9 @@ class dms_pool_config(ctypes.Structure):
         ("softmax_scale", ctypes.c_float),
         ("page_order_seed", ctypes.c_uint32),
         ("kv_format", ctypes.c_int32),
-        ("reserved", ctypes.c_int32 * 3),
+        ("logit_source", ctypes.c_int32),
+        ("logit_channel", ctypes.c_int32),
+        ("reserved", ctypes.c_int32 * 1),
     ]
 
 
@@ -138,7 +141,9 @@ def _check(status: int):
 
 
 def make_config(n_layers, n_q_heads, n_kv_heads, head_dim, window, max_seqs, max_positions,
-                max_pages, softmax_scale=0.0, page_order_seed=0, kv_format=0) -> dms_pool_config:
+                max_pages, softmax_scale=0.0, page_order_seed=0, kv_format=0, logit_channel=None) -> dms_pool_config:
+    """logit_channel=None: eviction logits come from the calls' logits argument;
+    an int c: from channel c of each kv head's K row (logits may then be None)."""
     c = dms_pool_config()
     c.n_layers, c.n_q_heads, c.n_kv_heads, c.head_dim = n_layers, n_q_heads, n_kv_heads, head_dim
     c.window, c.max_seqs, c.max_positions = window, max_seqs, max_positions
@@ -147,6 +152,8 @@ def make_config(n_layers, n_q_heads, n_kv_heads, head_dim, window, max_seqs, max
     c.softmax_scale = softmax_scale
     c.page_order_seed = page_order_seed
     c.kv_format = kv_format
+    if logit_channel is not None:
+        c.logit_source, c.logit_channel = DMS_LOGITS_K_CHANNEL, logit_channel
     return c
 
 
@@ -252,11 +259,14 @@ class Pool:
     """
 
     def __init__(self, n_layers, n_q_heads, n_kv_heads, head_dim, window, max_seqs, max_positions,
-                 max_pages, softmax_scale=0.0, page_order_seed=0, kv_format=0, device="cuda"):
+                 max_pages, softmax_scale=0.0, page_order_seed=0, kv_format=0, logit_channel=None,
+                 device="cuda"):
         import torch
         self.torch = torch
         self.cfg = make_config(n_layers, n_q_heads, n_kv_heads, head_dim, window, max_seqs,
-                               max_positions, max_pages, softmax_scale, page_order_seed, kv_format)
+                               max_positions, max_pages, softmax_scale, page_order_seed, kv_format,
+                               logit_channel)
+        self.logits_from_k = logit_channel is not None
         self.fp8 = kv_format == DMS_KV_FP8_E4M3
         self.device = torch.device(device)
         self.nbytes = dms_pool_bytes(self.cfg)
@@ -291,7 +301,8 @@ class Pool:
         H, Hq, D = self.n_kv_heads, self.n_q_heads, self.head_dim
         kp = self._check_tensor(k, (T, H, D), torch.bfloat16, "k")
         vpp = self._check_tensor(v, (T, H, D), torch.bfloat16, "v")
-        lp = self._check_tensor(logits, (T, H), torch.float32, "logits")
+        lp = 0 if (logits is None and self.logits_from_k) else self._check_tensor(logits, (T, H), torch.float32,
+                                                                                   "logits")
         qp = self._check_tensor(q, (T, Hq, D), torch.bfloat16, "q") if q is not None else 0
         op = self._check_tensor(out, (T, Hq, D), torch.bfloat16, "out") if out is not None else 0
         dms_prefill(self.handle, seq, layer, T, qp, kp, vpp, lp, op, self._stream())
@@ -304,7 +315,8 @@ class Pool:
         qp = self._check_tensor(q, (L, n, Hq, D), torch.bfloat16, "q")
         kp = self._check_tensor(k, (L, n, H, D), torch.bfloat16, "k")
         vpp = self._check_tensor(v, (L, n, H, D), torch.bfloat16, "v")
-        lp = self._check_tensor(logits, (L, n, H), torch.float32, "logits")
+        lp = 0 if (logits is None and self.logits_from_k) else self._check_tensor(logits, (L, n, H), torch.float32,
+                                                                                   "logits")
         op = self._check_tensor(out, (L, n, Hq, D), torch.bfloat16, "out")
         dms_decode_step(self.handle, list(seq_ids), layer0, L, qp, kp, vpp, lp, op, self._stream())
 

@@ -54,8 +54,14 @@ bool make_layout(const dms_pool_config* c, Layout* L, std::string* why) {
     if (!(c->softmax_scale >= 0.f) || !std::isfinite(c->softmax_scale)) return bad("softmax_scale must be finite and >= 0");
     if (c->kv_format != DMS_KV_BF16 && c->kv_format != DMS_KV_FP8_E4M3)
         return bad("kv_format must be DMS_KV_BF16 or DMS_KV_FP8_E4M3");
-    for (int i = 0; i < 3; ++i)
-        if (c->reserved[i] != 0) return bad("reserved fields must be 0");
+    if (c->logit_source == DMS_LOGITS_INPUT) {
+        if (c->logit_channel != 0) return bad("logit_channel must be 0 unless logit_source is DMS_LOGITS_K_CHANNEL");
+    } else if (c->logit_source == DMS_LOGITS_K_CHANNEL) {
+        if (c->logit_channel < 0 || c->logit_channel >= c->head_dim) return bad("logit_channel must be in [0, head_dim)");
+    } else {
+        return bad("logit_source must be DMS_LOGITS_INPUT or DMS_LOGITS_K_CHANNEL");
+    }
+    if (c->reserved[0] != 0) return bad("reserved fields must be 0");
     const int64_t heads = (int64_t)c->max_seqs * c->n_layers * c->n_kv_heads;
     if (heads > (int64_t)INT32_MAX / 4) return bad("max_seqs * n_layers * n_kv_heads too large");
     if ((int64_t)c->n_layers * c->n_kv_heads > dms::kMaxCallHeads) return bad("n_layers * n_kv_heads too large");
@@ -181,6 +187,7 @@ dms_status dms_pool_create(const dms_pool_config* cfg, void* arena, size_t arena
     d.max_pos32 = (cfg->max_positions + 31) / 32 * 32;
     d.max_items = L.max_items;
     d.fp8 = cfg->kv_format == DMS_KV_FP8_E4M3 ? 1 : 0;
+    d.logit_ch = cfg->logit_source == DMS_LOGITS_K_CHANNEL ? cfg->logit_channel : -1;
     const double scale = cfg->softmax_scale > 0.f ? (double)cfg->softmax_scale : 1.0 / std::sqrt((double)cfg->head_dim);
     d.scale_log2 = (float)(scale * 1.4426950408889634);
 
@@ -253,7 +260,8 @@ dms_status dms_prefill(dms_pool* pool, int32_t seq, int32_t layer, int32_t n_tok
     if (seq < 0 || seq >= c.max_seqs) return fail(DMS_E_INVAL, "seq out of range");
     if (layer < 0 || layer >= c.n_layers) return fail(DMS_E_INVAL, "layer out of range");
     if (n_tokens < 1 || n_tokens > c.max_positions) return fail(DMS_E_INVAL, "n_tokens must be in [1, max_positions]");
-    if (!k || !v || !logits) return fail(DMS_E_INVAL, "k, v and logits must not be NULL");
+    const bool need_logits = c.logit_source == DMS_LOGITS_INPUT;
+    if (!k || !v || (need_logits && !logits)) return fail(DMS_E_INVAL, "k, v and logits must not be NULL");
     if (out && !q) return fail(DMS_E_INVAL, "q must not be NULL when out is given");
     if (pool->position(seq, layer) >= 0) return fail(DMS_E_STATE, "this (seq, layer) already holds tokens");
     dms::PrefillArgs a;
@@ -292,7 +300,8 @@ dms_status dms_decode_step(dms_pool* pool, int32_t n_seqs, const int32_t* seq_id
     if (n_seqs < 1 || n_seqs > c.max_seqs) return fail(DMS_E_INVAL, "n_seqs must be in [1, max_seqs]");
     if (!seq_ids) return fail(DMS_E_INVAL, "seq_ids is NULL");
     if (layer0 < 0 || n_layers < 1 || layer0 + n_layers > c.n_layers) return fail(DMS_E_INVAL, "layer range out of bounds");
-    if (!q || !k || !v || !logits || !out) return fail(DMS_E_INVAL, "q, k, v, logits and out must not be NULL");
+    if (!q || !k || !v || !out || (c.logit_source == DMS_LOGITS_INPUT && !logits))
+        return fail(DMS_E_INVAL, "q, k, v, logits and out must not be NULL");
     std::vector<char> seen((size_t)c.max_seqs, 0);
     for (int i = 0; i < n_seqs; ++i) {
         const int s = seq_ids[i];

@@ -98,6 +98,7 @@ struct PoolDev {
     int32_t window, ring_len, pages_per_head, max_positions, max_pos32;
     int32_t max_items;
     int32_t fp8;       // kv_format == DMS_KV_FP8_E4M3
+    int32_t logit_ch;  // channel of K holding the eviction logit, or -1: the logits input
     float scale_log2;  // softmax scale * log2(e): scores are kept in base-2 units
     __host__ __device__ uint8_t* kp8() const { return reinterpret_cast<uint8_t*>(kpages); }
     __host__ __device__ uint8_t* vp8() const { return reinterpret_cast<uint8_t*>(vpages); }
@@ -153,6 +154,15 @@ __device__ __forceinline__ uint4 fp8x8_bf16(uint2 w) {
 // Row scale: amax / 448 in fp32 (1 for an all-zero row); codes are
 // e4m3_encode(x / scale) with the fp32 quotient.
 __device__ __forceinline__ float e4m3_row_scale(float amax) { return amax > 0.f ? amax / 448.0f : 1.0f; }
+
+// Eviction logit of input row r (token s of a prefill; call row of a decode)
+// and kv head h: the logits input, or one channel of the row's K.
+__device__ __forceinline__ float eviction_logit(const PoolDev& P, const float* logits, const uint16_t* k, size_t r,
+                                                int h) {
+    if (P.logit_ch >= 0)
+        return __uint_as_float((uint32_t)k[(r * P.n_kv_heads + h) * P.head_dim + P.logit_ch] << 16);
+    return logits[r * P.n_kv_heads + h];
+}
 
 struct DecodeArgs {
     PoolDev pool;

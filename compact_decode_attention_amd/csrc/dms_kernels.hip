@@ -91,14 +91,6 @@ __device__ __forceinline__ float wave_sum(float x) {
 // arithmetic producing x stays ahead of the loads issued after this point.
 __device__ __forceinline__ void pin(float& x) { asm volatile("" : "+v"(x)); }
 
-// An opaque copy of x: values computed from it inside a loop cannot be hoisted
-// out of the loop (a persistent loop would otherwise keep every per-thread
-// address alive in registers across all its iterations).
-__device__ __forceinline__ int launder(int x) {
-    asm volatile("" : "+v"(x));
-    return x;
-}
-
 // Raw buffer resource over [base, base + bytes): loads beyond it return 0.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, int bytes) {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, bytes, 0x00020000);
@@ -164,13 +156,6 @@ __device__ __forceinline__ CallHead call_head(const DecodeArgs& a, int ch) {
     c.gh = ((a.seq_ids[si] * a.pool.n_layers) + a.layer0 + li) * hkv + h;
     c.row = li * a.n_seqs_total + a.seq_base + si;
     return c;
-}
-
-// Slot of the token at position s if it is marked (ring entry of s), else -1.
-__device__ __forceinline__ int marked_slot_at(const PoolDev& P, int gh, int s) {
-    if (P.ring_len <= 0 || s < 0) return -1;
-    const int r = P.ring[(size_t)gh * P.ring_len + (s % P.window)];
-    return (r >= 0 && (r & 1)) ? (r >> 1) : -1;
 }
 
 // ---------------------------------------------------------------------------
@@ -851,7 +836,7 @@ __device__ void append_head(const DecodeArgs& a, int ch) {
     uint16_t vv[VJ];
 #pragma unroll
     for (int jj = 0; jj < VJ; ++jj) vv[jj] = vn[jj * 64 + lane];
-    const int mark = a.logits[(size_t)c.row * P.n_kv_heads + c.h] > 0.f ? 1 : 0;
+    const int mark = eviction_logit(P, a.logits, a.k, c.row, c.h) > 0.f ? 1 : 0;
     // the entry of position t+1-w (expires at the next step); for w = 1 that is
     // the token written now
     const int sx = t + 1 - P.window;
@@ -969,13 +954,13 @@ __global__ __launch_bounds__(1024) void prefill_scan_kernel(PrefillArgs a) {
     const int s0 = min(tid * per, T), s1 = min(s0 + per, T);
     // live at the last position T-1: unmarked, or inside the window (s >= T - w)
     int cnt = 0;
-    for (int s = s0; s < s1; ++s) cnt += (s >= T - w || !(a.logits[(size_t)s * hkv + h] > 0.f)) ? 1 : 0;
+    for (int s = s0; s < s1; ++s) cnt += (s >= T - w || !(eviction_logit(P, a.logits, a.k, s, h) > 0.f)) ? 1 : 0;
     int n;
     int off = block_excl_scan<1024>(cnt, &n, s_scan);
     int32_t* inv = P.inv + (size_t)h * P.max_positions;
     int32_t* pcnt = P.pcnt + (size_t)h * P.max_positions;
     for (int s = s0; s < s1; ++s) {
-        if (s >= T - w || !(a.logits[(size_t)s * hkv + h] > 0.f)) inv[off++] = s;
+        if (s >= T - w || !(eviction_logit(P, a.logits, a.k, s, h) > 0.f)) inv[off++] = s;
         pcnt[s] = off;  // live tokens in [0, s]
     }
     const int np = (n + kPage - 1) / kPage;
@@ -1002,7 +987,7 @@ __global__ __launch_bounds__(1024) void prefill_scan_kernel(PrefillArgs a) {
         // the token expiring when position T is appended: T - w, if marked; it
         // lies in the window, so its slot is n - T + (T - w)
         int e = -1;
-        if (P.ring_len > 0 && T >= w && a.logits[(size_t)(T - w) * hkv + h] > 0.f) e = n - w;
+        if (P.ring_len > 0 && T >= w && eviction_logit(P, a.logits, a.k, T - w, h) > 0.f) e = n - w;
         for (int i = 0; i < kHS; ++i) hs[i] = 0;
         hs[kHsLive] = n;
         hs[kHsPages] = np;
@@ -1015,7 +1000,7 @@ __global__ __launch_bounds__(1024) void prefill_scan_kernel(PrefillArgs a) {
         int entry = -1;
         if (idx <= T - 1) {
             const int s = idx + w * ((T - 1 - idx) / w);
-            const int mark = a.logits[(size_t)s * hkv + h] > 0.f ? 1 : 0;
+            const int mark = eviction_logit(P, a.logits, a.k, s, h) > 0.f ? 1 : 0;
             entry = ((n - T + s) << 1) | mark;
         }
         P.ring[(size_t)gh * P.ring_len + idx] = entry;

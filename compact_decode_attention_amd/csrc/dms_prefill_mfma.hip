@@ -245,7 +245,7 @@ void prefill_attend_kernel(PrefillArgs a) {
         }
         if (i >= nfar && tid < 32) {
             const int sk = kb + tid;
-            rmark = sk < T && a.logits[(size_t)sk * hkv + h] > 0.f;
+            rmark = sk < T && eviction_logit(P, a.logits, a.k, sk, h) > 0.f;
         }
         if constexpr (F8) {
             if (tid < 32) {

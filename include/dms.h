@@ -80,6 +80,20 @@ enum {
 #define DMS_KV_BF16 0
 #define DMS_KV_FP8_E4M3 1
 
+/* Where the eviction logit of a (token, kv head) comes from
+ * (dms_pool_config.logit_source).
+ *  DMS_LOGITS_INPUT      the caller's logits array (prefill and decode calls).
+ *  DMS_LOGITS_K_CHANNEL  channel logit_channel of the token's K row for that kv
+ *                        head: one existing neuron of the attention layer emits
+ *                        the keep/evict signal ("NVIDIA veroeffentlicht
+ *                        Qwen3-8B-DMS-8x ..." news page, section "Technische
+ *                        Details und Implementierung"; stiva.ai "Nvidia DMS ...",
+ *                        section on the model managing its own memory).  The
+ *                        channel keeps its value in attention; the logits
+ *                        argument of the calls is ignored and may be NULL. */
+#define DMS_LOGITS_INPUT 0
+#define DMS_LOGITS_K_CHANNEL 1
+
 typedef struct dms_pool dms_pool; /* opaque; owned by the library */
 
 typedef struct {
@@ -97,7 +111,9 @@ typedef struct {
                                  in a seeded shuffled order (physical placement must
                                  not change any result) */
     int32_t kv_format;     /* DMS_KV_BF16 (0) or DMS_KV_FP8_E4M3 */
-    int32_t reserved[3];   /* must be 0 */
+    int32_t logit_source;  /* DMS_LOGITS_INPUT (0) or DMS_LOGITS_K_CHANNEL */
+    int32_t logit_channel; /* DMS_LOGITS_K_CHANNEL: channel in [0, head_dim); else 0 */
+    int32_t reserved[1];   /* must be 0 */
 } dms_pool_config;
 
 /* Bytes of device memory (the arena) a pool with this configuration needs, or 0
@@ -123,7 +139,8 @@ dms_status dms_pool_destroy(dms_pool* pool);
  * attention output of every position (query t sees the keys visible to t).
  *   q      bf16 [n_tokens][n_q_heads][head_dim]  (may be NULL when out is NULL)
  *   k, v   bf16 [n_tokens][n_kv_heads][head_dim]
- *   logits fp32 [n_tokens][n_kv_heads]
+ *   logits fp32 [n_tokens][n_kv_heads] (ignored, may be NULL, with
+ *          DMS_LOGITS_K_CHANNEL)
  *   out    bf16 [n_tokens][n_q_heads][head_dim] or NULL
  * q and k arrive after any positional encoding.  Returns DMS_E_STATE if this
  * (seq, layer) already holds tokens (release the sequence first). */
@@ -142,7 +159,8 @@ dms_status dms_prefill(dms_pool* pool, int32_t seq, int32_t layer, int32_t n_tok
  *           layer of the call
  *   q       bf16 [n_layers][n_seqs][n_q_heads][head_dim]
  *   k, v    bf16 [n_layers][n_seqs][n_kv_heads][head_dim]
- *   logits  fp32 [n_layers][n_seqs][n_kv_heads]
+ *   logits  fp32 [n_layers][n_seqs][n_kv_heads] (ignored, may be NULL, with
+ *           DMS_LOGITS_K_CHANNEL)
  *   out     bf16 [n_layers][n_seqs][n_q_heads][head_dim]
  * Each (seq, layer) keeps its own position counter; the new token's position
  * is that counter.  A model calls this once per layer (n_layers = 1); a caller

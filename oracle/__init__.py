@@ -41,6 +41,8 @@ def load(so: str) -> ctypes.CDLL:
     vp, i32, i64, dbl = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_double
     lib.dms_oracle_marks.argtypes = [vp, i64, vp]
     lib.dms_oracle_marks.restype = None
+    lib.dms_oracle_k_channel_logits.argtypes = [vp, i64, i32, i32, i32, vp]
+    lib.dms_oracle_k_channel_logits.restype = None
     lib.dms_oracle_live_positions.argtypes = [i64, i64, vp, i64, vp]
     lib.dms_oracle_live_positions.restype = i64
     lib.dms_oracle_attend.argtypes = [i32, i32, i32, i64, dbl, i64, vp, vp, i64, vp, vp, vp, vp]
@@ -76,6 +78,18 @@ class Oracle:
         lg = np.ascontiguousarray(logits, np.float32)
         out = np.empty(lg.shape, np.uint8)
         self.lib.dms_oracle_marks(lg.ctypes.data, lg.size, out.ctypes.data)
+        return out
+
+    def k_channel_logits(self, k: np.ndarray, channel: int) -> np.ndarray:
+        """k [..., Hkv, D] bf16 bits -> eviction logits float32 [..., Hkv] read
+        from channel `channel` of every K row."""
+        k = np.ascontiguousarray(k, np.uint16)
+        hkv, d = k.shape[-2], k.shape[-1]
+        if not 0 <= channel < d:
+            raise ValueError("channel out of range")
+        rows = k.size // (hkv * d)
+        out = np.empty(k.shape[:-1], np.float32)
+        self.lib.dms_oracle_k_channel_logits(k.ctypes.data, rows, hkv, d, int(channel), out.ctypes.data)
         return out
 
     def live_positions(self, t: int, window: int, marks_col: np.ndarray) -> np.ndarray:
@@ -163,6 +177,10 @@ def default() -> Oracle:
 
 def marks(logits):
     return default().marks(logits)
+
+
+def k_channel_logits(k, channel):
+    return default().k_channel_logits(k, channel)
 
 
 def live_positions(t, window, marks_col):

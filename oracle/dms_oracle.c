@@ -46,6 +46,13 @@
  *           to the code with an even last bit; beyond +-448 that is +-448
  *   x^_d  = value(c_d) * scale
  * and attention reads x^ in place of x.
+ *
+ * Eviction logits from a K channel ([MV] "Technische Details und
+ * Implementierung": a single neuron of the attention makes the eviction
+ * decisions; [ST] the first section: existing neurons of the attention layers
+ * are given the keep/evict signal): the logit of (token s, kv head h) is the
+ * value of channel c of the token's K row for h, k[s][h][c]; that channel keeps
+ * its value in attention.
  */
 #include <math.h>
 #include <stdint.h>
@@ -62,6 +69,16 @@ static double bf16_bits_to_double(uint16_t b) {
 /* Eviction marks: m = (logit > 0), one byte per logit ([ST] keep/evict signal). */
 void dms_oracle_marks(const float* logits, int64_t n, uint8_t* marks) {
     for (int64_t i = 0; i < n; ++i) marks[i] = logits[i] > 0.0f ? 1 : 0;
+}
+
+/* Eviction logits read from channel c of K ([MV] "Technische Details und
+ * Implementierung"; [ST]): k is bf16 [n_rows][n_kv_heads][d], out fp32
+ * [n_rows][n_kv_heads] = the value of k[r][h][c]. */
+void dms_oracle_k_channel_logits(const uint16_t* k, int64_t n_rows, int32_t n_kv_heads, int32_t d, int32_t c,
+                                 float* out) {
+    for (int64_t r = 0; r < n_rows; ++r)
+        for (int32_t h = 0; h < n_kv_heads; ++h)
+            out[r * n_kv_heads + h] = (float)bf16_bits_to_double(k[(r * n_kv_heads + h) * d + c]);
 }
 
 /* The visibility rule ([MV], [ST]): key position s is visible to query position

@@ -61,6 +61,7 @@ class Case:
     max_positions: Optional[int] = None
     zero_q: bool = False
     kv_format: int = 0                     # 0 bf16, 1 FP8 E4M3 (oracle: quantize_rows + attend_fp8)
+    logit_channel: Optional[int] = None    # logits carried by this K channel (the logits input unused)
     data: dict = field(default_factory=dict)
     q8: dict = field(default_factory=dict)
 
@@ -87,6 +88,12 @@ class Case:
                 else:
                     z = synth.normal_f32(self.seed, sid(synth.TAG_SCORE), 0, T * H).reshape(T, H)
                     lg = (-(self.keep_mu + z.astype(np.float64))).astype(np.float32)
+                if self.logit_channel is not None:
+                    # the logit travels in K: channel c holds bf16(logit); the
+                    # oracle reads it back from there
+                    u = lg.view(np.uint32).astype(np.uint64)
+                    k[:, :, self.logit_channel] = ((u + 0x7FFF + ((u >> 16) & 1)) >> 16).astype(np.uint16)
+                    lg = oracle.k_channel_logits(k, self.logit_channel)
                 self.data[(s, l)] = SeqData(q, k, v, lg)
         return self
 
@@ -100,7 +107,7 @@ class Case:
         return dict(n_layers=self.n_layers, n_q_heads=self.n_q_heads, n_kv_heads=self.n_kv_heads,
                     head_dim=self.head_dim, window=self.window, max_seqs=self.n_seqs,
                     max_positions=maxpos, max_pages=max_pages, page_order_seed=self.page_order_seed,
-                    kv_format=self.kv_format)
+                    kv_format=self.kv_format, logit_channel=self.logit_channel)
 
     # ---- oracle side
     def marks(self, s, l):
@@ -157,9 +164,9 @@ class Runner:
             T = c.ctx_lens[s]
             for l in range(c.n_layers):
                 d = c.data[(s, l)]
+                lg = None if c.logit_channel is not None else to_dev(d.logits[:T], torch, torch.float32)
                 self.pool.prefill(s, l, to_dev(d.k[:T], torch, torch.bfloat16),
-                                  to_dev(d.v[:T], torch, torch.bfloat16),
-                                  to_dev(d.logits[:T], torch, torch.float32))
+                                  to_dev(d.v[:T], torch, torch.bfloat16), lg)
 
     def step_inputs(self, i, seqs, layers):
         """Inputs of decode step i for the given seqs and layers, [layers][seqs]..."""
@@ -177,6 +184,8 @@ class Runner:
         n_layers = c.n_layers - layer0 if n_layers is None else n_layers
         layers = list(range(layer0, layer0 + n_layers))
         q, k, v, lg = self.step_inputs(i, seqs, layers)
+        if c.logit_channel is not None:
+            lg = None
         out = torch.empty((n_layers, len(seqs), c.n_q_heads, c.head_dim), dtype=torch.bfloat16, device="cuda")
         self.pool.decode_step(seqs, layer0, q, k, v, lg, out)
         return from_dev_bf16(out)

@@ -82,13 +82,26 @@ def test_pool_bytes_rejects_page_slots_and_reserved():
     with pytest.raises(dms.DMSError):
         dms.dms_pool_bytes(cfg)
     cfg = qwen_cfg()
-    cfg.reserved[2] = 1
+    cfg.reserved[0] = 1
     with pytest.raises(dms.DMSError):
         dms.dms_pool_bytes(cfg)
     cfg = qwen_cfg()
     cfg.softmax_scale = float("nan")
     with pytest.raises(dms.DMSError):
         dms.dms_pool_bytes(cfg)
+
+
+@pytest.mark.parametrize("source,channel,ok", [
+    (0, 0, True), (0, 3, False), (1, 0, True), (1, 127, True), (1, 128, False), (1, -1, False), (2, 0, False)])
+def test_logit_source_and_channel_are_checked(source, channel, ok):
+    cfg = qwen_cfg()
+    cfg.logit_source, cfg.logit_channel = source, channel
+    if ok:
+        assert dms.dms_pool_bytes(cfg) > 0
+    else:
+        with pytest.raises(dms.DMSError) as e:
+            dms.dms_pool_bytes(cfg)
+        assert "logit" in str(e.value)
 
 
 def test_kv_format_is_checked():
