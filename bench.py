@@ -447,6 +447,71 @@ def bench_prefill(args, torch, dms):
     return res
 
 
+def bench_extend(args, torch, dms):
+    """Chunked prefill of the 32K prompt through dms_extend: the first 8192 tokens
+    prefilled (no output), the other 24576 appended in 12 chunks of 2048 with
+    output (the same outputs as the one-shot prefill's rows 8192..), one layer's
+    inputs in 36 layer slots."""
+    wl = synth.WORKLOADS["qwen3-8b_prefill32k"]
+    inp = synth.SynthInputs(wl)
+    T, Hq, H, D, w, R = wl.ctx_len, wl.n_q_heads, wl.n_kv_heads, wl.head_dim, wl.window, wl.layer_repeats
+    P0, C = 8192, 2048
+    dev = torch.device("cuda:0")
+    lg = inp.logits(0, 0, 0, T)
+    q = bf16_tensor(inp.q(0, 0, 0, T), torch).to(dev)
+    k = bf16_tensor(inp.k(0, 0, 0, T), torch).to(dev)
+    v = bf16_tensor(inp.v(0, 0, 0, T), torch).to(dev)
+    dl = torch.from_numpy(lg).to(dev)
+    out = torch.empty((T, Hq, D), dtype=torch.bfloat16, device=dev)
+    pool = dms.Pool(n_layers=R, n_q_heads=Hq, n_kv_heads=H, head_dim=D, window=w, max_seqs=1,
+                    max_positions=T, max_pages=R * H * (T // 64), device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def setup():
+        pool.release(0)
+        for l in range(R):
+            pool.prefill(0, l, k[:P0], v[:P0], dl[:P0])
+
+    def run_chunks():
+        for t0 in range(P0, T, C):
+            for l in range(R):
+                pool.extend(0, l, k[t0:t0 + C], v[t0:t0 + C], dl[t0:t0 + C], q=q[t0:t0 + C], out=out[t0:t0 + C])
+
+    setup()
+    run_chunks()  # warm-up
+    setup()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    ev0.record(stream)
+    run_chunks()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    ms = ev0.elapsed_time(ev1)
+    setup()
+    torch.cuda.synchronize()
+    dms.dms_timing_enable(pool.handle, True)
+    run_chunks()
+    tm = dms.dms_timing_read(pool.handle)
+    dms.dms_timing_enable(pool.handle, False)
+    avg_att = tm.extend_attend_ms / tm.extend_calls
+    pairs = sum(int(np.sum(live_counts(lg[:, h], np.arange(P0, T), w))) for h in range(H))
+    flops = 4.0 * D * (Hq // H) * pairs / ((T - P0) // C)  # per launch (one chunk of one layer)
+    tflops = flops / (avg_att / 1e3) / 1e12
+    n_tok = T - P0
+    log("chunked extend: %.3f ms for %d chunks x %d layers (%.0f tok/s); attend kernel %.1f us = %.1f TFLOP/s "
+        "(%.1f%% of bf16 MFMA peak)" % (ms, (T - P0) // C, R, n_tok / (ms / 1e3), avg_att * 1e3, tflops,
+                                        100 * tflops / MFMA_BF16_PEAK_TFLOPS))
+    pool.close()
+    return {"workload": "%s as a chunked prefill: %d tokens prefilled, then %d chunks of %d appended with "
+                        "output by dms_extend, one layer's inputs in %d layer slots"
+                        % (wl.name, P0, (T - P0) // C, C, R),
+            "tok_per_s": round(n_tok / (ms / 1e3), 1), "ms_all_chunks_all_layers": round(ms, 4),
+            "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
+                         "unit": "TFLOP/s", "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4),
+                         "kernel": "prefill_attend_kernel<128,4,bf16,extend>", "avg_launch_us": round(avg_att * 1e3, 2),
+                         "flops_per_launch": flops}}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -461,6 +526,7 @@ def main():
     ap.add_argument("--no-ragged", action="store_true", help="skip the 32-sequence ragged batch leg")
     ap.add_argument("--no-fp8", action="store_true", help="skip the FP8-pool decode leg")
     ap.add_argument("--no-logit-channel", action="store_true", help="skip the K-channel-logits decode leg")
+    ap.add_argument("--no-extend", action="store_true", help="skip the chunked-prefill (dms_extend) leg")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="first run a plain copy of this many MiB (for counter scaling)")
     args = ap.parse_args()
@@ -491,6 +557,7 @@ def main():
               "workload": "the decode workload above with each token's eviction logit carried (bf16) in "
                           "channel 0 of its K rows and read by the pool from there (no logits input)"}
     pre = None if args.no_prefill else bench_prefill(args, torch, dms)
+    ext = None if args.no_extend else bench_extend(args, torch, dms)
     rag = None if args.no_ragged else bench_ragged(args, torch, dms)
     rec = {
         "metric": METRIC,
@@ -515,6 +582,7 @@ def main():
         "fp8_kv": f8,
         "logits_from_k_channel": lk,
         "prefill": pre,
+        "chunked_extend": ext,
         "batched_ragged": rag,
     }
     print(json.dumps(rec), flush=True)

@@ -63,6 +63,8 @@ class dms_timing(ctypes.Structure):
         ("prefill_attend_ms", ctypes.c_double),
         ("decode_launches", ctypes.c_int64),
         ("prefill_calls", ctypes.c_int64),
+        ("extend_attend_ms", ctypes.c_double),
+        ("extend_calls", ctypes.c_int64),
     ]
 
     def as_dict(self):
@@ -114,6 +116,7 @@ def lib() -> ctypes.CDLL:
             L.dms_pool_destroy.argtypes = [vp]
             L.dms_prefill.argtypes = [vp, i32, i32, i32, vp, vp, vp, vp, vp, vp]
             L.dms_decode_step.argtypes = [vp, i32, P(i32), i32, i32, vp, vp, vp, vp, vp, vp]
+            L.dms_extend.argtypes = [vp, i32, i32, i32, vp, vp, vp, vp, vp, vp]
             L.dms_query_stats.argtypes = [vp, i32, P(dms_stats), P(i32)]
             L.dms_export_live.argtypes = [vp, i32, i32, i32, P(i32), i32, P(i32)]
             L.dms_export_kv.argtypes = [vp, i32, i32, i32, i32, P(i32), vp, vp, P(ctypes.c_float),
@@ -121,7 +124,7 @@ def lib() -> ctypes.CDLL:
             L.dms_seq_release.argtypes = [vp, i32, vp]
             L.dms_timing_enable.argtypes = [vp, i32]
             L.dms_timing_read.argtypes = [vp, P(dms_timing)]
-            for f in (L.dms_pool_create, L.dms_pool_destroy, L.dms_prefill, L.dms_decode_step,
+            for f in (L.dms_pool_create, L.dms_pool_destroy, L.dms_prefill, L.dms_decode_step, L.dms_extend,
                       L.dms_query_stats, L.dms_export_live, L.dms_export_kv, L.dms_seq_release,
                       L.dms_timing_enable, L.dms_timing_read):
                 f.restype = ctypes.c_int32
@@ -182,6 +185,13 @@ def dms_prefill(pool: int, seq: int, layer: int, n_tokens: int, q: int, k: int, 
     vp = ctypes.c_void_p
     _check(lib().dms_prefill(vp(pool), seq, layer, n_tokens, vp(q or None), vp(k), vp(v), vp(logits),
                              vp(out or None), vp(stream)))
+
+
+def dms_extend(pool: int, seq: int, layer: int, n_tokens: int, q: int, k: int, v: int, logits: int, out: int,
+               stream: int):
+    vp = ctypes.c_void_p
+    _check(lib().dms_extend(vp(pool), seq, layer, n_tokens, vp(q or None), vp(k), vp(v), vp(logits or None),
+                            vp(out or None), vp(stream)))
 
 
 def dms_decode_step(pool: int, seq_ids: Sequence[int], layer0: int, n_layers: int, q: int, k: int,
@@ -306,6 +316,20 @@ class Pool:
         qp = self._check_tensor(q, (T, Hq, D), torch.bfloat16, "q") if q is not None else 0
         op = self._check_tensor(out, (T, Hq, D), torch.bfloat16, "out") if out is not None else 0
         dms_prefill(self.handle, seq, layer, T, qp, kp, vpp, lp, op, self._stream())
+
+    def extend(self, seq, layer, k, v, logits, q=None, out=None):
+        """Append k.shape[0] new tokens to (seq, layer); out (if given) gets their
+        attention outputs."""
+        torch = self.torch
+        T = k.shape[0]
+        H, Hq, D = self.n_kv_heads, self.n_q_heads, self.head_dim
+        kp = self._check_tensor(k, (T, H, D), torch.bfloat16, "k")
+        vpp = self._check_tensor(v, (T, H, D), torch.bfloat16, "v")
+        lp = 0 if (logits is None and self.logits_from_k) else self._check_tensor(logits, (T, H), torch.float32,
+                                                                                   "logits")
+        qp = self._check_tensor(q, (T, Hq, D), torch.bfloat16, "q") if q is not None else 0
+        op = self._check_tensor(out, (T, Hq, D), torch.bfloat16, "out") if out is not None else 0
+        dms_extend(self.handle, seq, layer, T, qp, kp, vpp, lp, op, self._stream())
 
     def decode_step(self, seq_ids, layer0, q, k, v, logits, out):
         torch = self.torch

@@ -114,6 +114,7 @@ struct dms_pool {
     bool timing = false;
     std::vector<hipEvent_t> events;   // 4 per decode launch while timing (attend, merge start/stop)
     std::vector<hipEvent_t> pevents;  // 6 per prefill with output while timing (compaction, V copy, attend)
+    std::vector<hipEvent_t> xevents;  // 4 per extend with output while timing (V copy, attend)
     Layout layout;
     dms::PoolDev dev;
     char* arena;
@@ -234,6 +235,7 @@ dms_status dms_pool_destroy(dms_pool* pool) {
     hipError_t e = hipDeviceSynchronize();
     for (hipEvent_t ev : pool->events) hipEventDestroy(ev);
     for (hipEvent_t ev : pool->pevents) hipEventDestroy(ev);
+    for (hipEvent_t ev : pool->xevents) hipEventDestroy(ev);
     delete pool;
     if (e != hipSuccess) return hip_fail(e, "synchronise");
     g_err.clear();
@@ -274,6 +276,7 @@ dms_status dms_prefill(dms_pool* pool, int32_t seq, int32_t layer, int32_t n_tok
     a.seq = seq;
     a.layer = layer;
     a.n_tokens = n_tokens;
+    a.t0 = 0;
     hipStream_t s = static_cast<hipStream_t>(stream);
     hipError_t e = hipSuccess;
     hipEvent_t* ev = nullptr;
@@ -288,6 +291,43 @@ dms_status dms_prefill(dms_pool* pool, int32_t seq, int32_t layer, int32_t n_tok
         if (e != hipSuccess) return hip_fail(e, "prefill attention launch");
     }
     pool->position(seq, layer) = n_tokens;
+    g_err.clear();
+    return DMS_OK;
+}
+
+dms_status dms_extend(dms_pool* pool, int32_t seq, int32_t layer, int32_t n_tokens, const void* q, const void* k,
+                      const void* v, const float* logits, void* out, void* stream) {
+    if (!pool) return fail(DMS_E_INVAL, "pool is NULL");
+    const dms_pool_config& c = pool->cfg;
+    if (seq < 0 || seq >= c.max_seqs) return fail(DMS_E_INVAL, "seq out of range");
+    if (layer < 0 || layer >= c.n_layers) return fail(DMS_E_INVAL, "layer out of range");
+    if (n_tokens < 1) return fail(DMS_E_INVAL, "n_tokens must be >= 1");
+    if (!k || !v || (c.logit_source == DMS_LOGITS_INPUT && !logits))
+        return fail(DMS_E_INVAL, "k, v and logits must not be NULL");
+    if (out && !q) return fail(DMS_E_INVAL, "q must not be NULL when out is given");
+    const int32_t t0 = pool->position(seq, layer);
+    if (t0 < 0) return fail(DMS_E_STATE, "extend on a (seq, layer) that was not prefilled");
+    if ((int64_t)t0 + n_tokens > c.max_positions) return fail(DMS_E_STATE, "the chunk runs past max_positions");
+    dms::PrefillArgs a;
+    a.pool = pool->dev;
+    a.q = static_cast<const uint16_t*>(q);
+    a.k = static_cast<const uint16_t*>(k);
+    a.v = static_cast<const uint16_t*>(v);
+    a.logits = logits;
+    a.out = static_cast<uint16_t*>(out);
+    a.seq = seq;
+    a.layer = layer;
+    a.n_tokens = n_tokens;
+    a.t0 = t0;
+    hipError_t e = hipSuccess;
+    hipEvent_t* ev = nullptr;
+    if (pool->timing && out) {
+        ev = timing_events(pool->xevents, 4, &e);
+        if (!ev) return hip_fail(e, "timing event");
+    }
+    e = dms::launch_extend(a, out != nullptr, static_cast<hipStream_t>(stream), ev);
+    if (e != hipSuccess) return hip_fail(e, "extend launch");
+    pool->position(seq, layer) = t0 + n_tokens;
     g_err.clear();
     return DMS_OK;
 }
@@ -556,6 +596,10 @@ dms_status dms_timing_read(dms_pool* pool, dms_timing* out) {
     double* pacc[2] = {&out->prefill_compact_ms, &out->prefill_attend_ms};
     const int pslot[3] = {0, 0, 1};  // compaction + V copy, attention
     if (e == hipSuccess) e = sum(pool->pevents, 6, pslot, pacc, &out->prefill_calls);
+    double vcopy = 0;
+    double* xacc[2] = {&vcopy, &out->extend_attend_ms};
+    const int xslot[2] = {0, 1};
+    if (e == hipSuccess) e = sum(pool->xevents, 4, xslot, xacc, &out->extend_calls);
     if (e != hipSuccess) return hip_fail(e, "event elapsed time");
     g_err.clear();
     return DMS_OK;

@@ -188,6 +188,7 @@ struct PrefillArgs {
     const float* logits;
     uint16_t* out;
     int32_t seq, layer, n_tokens;
+    int32_t t0;  // extend calls: position of input row 0 (the head's position counter); prefill: 0
 };
 
 // ev (optional, 4 events): start/stop of the attention kernel and of the merge
@@ -199,6 +200,12 @@ int decode_blocks_per_cu(const DecodeArgs& a);
 hipError_t launch_prefill_compact(const PrefillArgs& a, hipStream_t s, hipEvent_t start, hipEvent_t stop);
 // ev (optional, 4 events): start/stop of the V copy kernel, then of the attention kernel
 hipError_t launch_prefill_attend(const PrefillArgs& a, hipStream_t s, hipEvent_t* ev);
+// extend calls (several new tokens of one (seq, layer) appended to its store):
+// the prompt-side kernels of the chunk (FP8: quantisation; with output: V copy
+// and the attention of the chunk's queries over the store and the chunk),
+// then the slot assignment, page allocation, ring and record, then the writes
+hipError_t launch_extend(const PrefillArgs& a, bool with_out, hipStream_t s, hipEvent_t* ev);
+hipError_t launch_extend_attend(const PrefillArgs& a, hipStream_t s, hipEvent_t* ev);
 hipError_t launch_seq_release(const PoolDev& p, int32_t seq, hipStream_t s);
 int device_cu_count();
 

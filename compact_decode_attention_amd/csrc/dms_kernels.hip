@@ -1143,6 +1143,206 @@ __global__ __launch_bounds__(256) void prefill_compact8_kernel(PrefillArgs a) {
     }
 }
 
+// ---------------------------------------------------------------------------
+// extend: T new tokens (input rows r = 0 .. T-1 at positions t0 + r) appended
+// to the store of one (seq, layer), in position order, as T decode steps would.
+// Token t reuses the slot of the token t - w expiring at its step when that one
+// was marked, and takes the next fresh slot otherwise:
+//   slot(r) = slot(r - w)                  if t - w >= t0 was marked (a chain)
+//           = ring slot of t - w           if t0 - w <= t - w < t0 was marked
+//           = n_old + #fresh rows before r otherwise
+// The chains are resolved by pointer jumping (log2(T / w) rounds).  Only the
+// last token of each chain is still live after the chunk, so only it is written.
+// One block per kv head; slot of each row in inv, chain parents in pcnt.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ bool ext_marked(const PrefillArgs& a, int r, int h) {
+    return eviction_logit(a.pool, a.logits, a.k, r, h) > 0.f;
+}
+
+// the ring entry (slot << 1 | mark) of stored position u (t0 - w <= u < t0), or -1
+__device__ __forceinline__ int ext_ring(const PoolDev& P, int gh, int u) {
+    return (P.ring_len > 0 && u >= 0) ? P.ring[(size_t)gh * P.ring_len + u % P.window] : -1;
+}
+
+__global__ __launch_bounds__(1024) void extend_update_kernel(PrefillArgs a) {
+    const PoolDev& P = a.pool;
+    __shared__ int s_scan[2 * 16 + 1];
+    __shared__ int s_base, s_enext;
+    const int tid = threadIdx.x, h = blockIdx.x;
+    const int gh = (a.seq * P.n_layers + a.layer) * P.n_kv_heads + h;
+    int32_t* hs = P.hstate + (size_t)gh * kHS;
+    const int n_old = hs[kHsLive], np_old = hs[kHsPages];
+    const int T = a.n_tokens, t0 = a.t0, w = P.window;
+    int32_t* val = P.inv + (size_t)h * P.max_positions;   // slot of row r (roots: final)
+    int32_t* par = P.pcnt + (size_t)h * P.max_positions;  // chain parent of row r (itself at a root)
+    const bool evict = P.ring_len > 0;
+    const int per = (T + 1023) / 1024;
+    const int r0 = min(tid * per, T), r1 = min(r0 + per, T);
+    // fresh rows and their ranks
+    int cnt = 0;
+    for (int r = r0; r < r1; ++r) {
+        const int u = t0 + r - w;  // expires at this step if marked
+        bool reuse = false;
+        if (evict && u >= 0) {
+            if (u >= t0) reuse = ext_marked(a, u - t0, h);
+            else { const int e = ext_ring(P, gh, u); reuse = e >= 0 && (e & 1); }
+        }
+        par[r] = reuse ? -1 : r;
+        cnt += reuse ? 0 : 1;
+    }
+    int fresh;
+    int off = block_excl_scan<1024>(cnt, &fresh, s_scan);
+    for (int r = r0; r < r1; ++r) {
+        const int u = t0 + r - w;
+        if (par[r] == r) {
+            val[r] = n_old + off++;
+        } else if (u >= t0) {
+            par[r] = u - t0;
+        } else {
+            par[r] = r;
+            val[r] = ext_ring(P, gh, u) >> 1;
+        }
+    }
+    __syncthreads();
+    // pointer jumping: every parent read is an ancestor, so in-place is safe
+    for (;;) {
+        int changed = 0;
+        for (int r = r0; r < r1; ++r) {
+            const int p = par[r], pp = par[p];
+            if (pp != p) {
+                par[r] = pp;
+                changed = 1;
+            }
+        }
+        if (!__syncthreads_or(changed)) break;
+    }
+    for (int r = r0; r < r1; ++r) val[r] = val[par[r]];  // roots keep their value
+    // the slot expiring when position t0 + T is appended (before the ring changes)
+    if (tid == 0) {
+        int e = -1;
+        const int u = t0 + T - w;
+        if (evict && u >= 0) {
+            if (u >= t0) {
+                if (ext_marked(a, u - t0, h)) e = -2;  // a new row: its slot, below
+            } else {
+                const int re = ext_ring(P, gh, u);
+                if (re >= 0 && (re & 1)) e = re >> 1;
+            }
+        }
+        s_enext = e;
+    }
+    __syncthreads();
+    // pages for the fresh slots
+    const int n_new = n_old + fresh;
+    const int np_new = (n_new + kPage - 1) / kPage;
+    const int need = np_new - np_old;
+    if (tid == 0) {
+        s_base = 0;
+        if (need > 0) {
+            const int old = atomicSub(&P.ctl[kCtlTop], need);
+            if (old < need) {
+                atomicAdd(&P.ctl[kCtlTop], need);
+                atomicOr(&P.ctl[kCtlError], 1);
+                s_base = -1;
+            } else {
+                s_base = old;
+            }
+        }
+    }
+    __syncthreads();
+    if (s_base < 0) {  // pool exhausted: the sticky flag is set, the chunk is dropped
+        if (tid == 0) hs[kHsPos] = t0 + T;
+        for (int r = r0; r < r1; ++r) val[r] = -1;
+        return;
+    }
+    for (int j = tid; j < need; j += 1024)
+        P.ptable[(size_t)gh * P.pages_per_head + np_old + j] = P.stack[s_base - 1 - j];
+    // ring entries of the last w positions that are new
+    if (evict)
+        for (int r = max(0, T - w) + tid; r < T; r += 1024)
+            P.ring[(size_t)gh * P.ring_len + (t0 + r) % w] = (val[r] << 1) | (ext_marked(a, r, h) ? 1 : 0);
+    if (tid == 0) {
+        int e = s_enext;
+        if (e == -2) e = val[t0 + T - w - t0];
+        hs[kHsLive] = n_new;
+        hs[kHsPages] = np_new;
+        hs[kHsPos] = t0 + T;
+        hs[kHsExp] = e;
+    }
+}
+
+// K/V (FP8: codes and scales) of the rows still live after the chunk into their
+// slots: row r is overwritten within the chunk iff it is marked and r + w < T.
+// Grid (ceil(T / 64), n_kv_heads), 256 threads.
+template <int D, bool F8>
+__global__ __launch_bounds__(256) void extend_write_kernel(PrefillArgs a) {
+    const PoolDev& P = a.pool;
+    __shared__ int s_slot[64];
+    const int tid = threadIdx.x, h = blockIdx.y, rb = blockIdx.x * 64;
+    const int hkv = P.n_kv_heads, T = a.n_tokens, w = P.window;
+    const int gh = (a.seq * P.n_layers + a.layer) * hkv + h;
+    if (tid < 64) {
+        const int r = rb + tid;
+        int slot = -1;
+        if (r < T) {
+            slot = P.inv[(size_t)h * P.max_positions + r];
+            if (P.ring_len > 0 && r + w < T && ext_marked(a, r, h)) slot = -1;  // replaced within the chunk
+        }
+        s_slot[tid] = slot;
+    }
+    __syncthreads();
+    const int32_t* ptab = P.ptable + (size_t)gh * P.pages_per_head;
+    if constexpr (F8) {
+        constexpr int NC = D / 16;
+        for (int u = tid; u < 64 * NC; u += 256) {  // K: 16 codes per chunk
+            const int j = u / NC, cc = u - j * NC;
+            const int slot = s_slot[j];
+            if (slot < 0) continue;
+            const size_t row = (size_t)(rb + j) * hkv + h;
+            uint8_t* kp = P.kp8() + (size_t)ptab[slot / kPage] * (kPage * D);
+            *reinterpret_cast<uint4*>(kp + ((size_t)cc * kPage + slot % kPage) * 16) =
+                *reinterpret_cast<const uint4*>(P.q8_codes(0) + row * D + cc * 16);
+        }
+        for (int u = tid; u < 64 * D; u += 256) {  // V: one code per (row, dim)
+            const int j = u / D, d = u - j * D;
+            const int slot = s_slot[j];
+            if (slot < 0) continue;
+            const size_t row = (size_t)(rb + j) * hkv + h;
+            uint8_t* vp = P.vp8() + (size_t)ptab[slot / kPage] * (kPage * D);
+            vp[((size_t)(slot % kPage / 16) * D + d) * 16 + slot % 16] = P.q8_codes(1)[row * D + d];
+        }
+    } else {
+        constexpr int NC = D / 8;
+        for (int u = tid; u < 64 * NC; u += 256) {  // K: 8 dims per chunk
+            const int j = u / NC, cc = u - j * NC;
+            const int slot = s_slot[j];
+            if (slot < 0) continue;
+            const size_t row = (size_t)(rb + j) * hkv + h;
+            uint16_t* kp = P.kpages + (size_t)ptab[slot / kPage] * (kPage * D);
+            *reinterpret_cast<uint4*>(kp + ((size_t)cc * kPage + slot % kPage) * 8) =
+                *reinterpret_cast<const uint4*>(a.k + row * D + cc * 8);
+        }
+        for (int u = tid; u < 64 * D; u += 256) {  // V: one value per (row, dim)
+            const int j = u / D, d = u - j * D;
+            const int slot = s_slot[j];
+            if (slot < 0) continue;
+            const size_t row = (size_t)(rb + j) * hkv + h;
+            uint16_t* vp = P.vpages + (size_t)ptab[slot / kPage] * (kPage * D);
+            vp[((size_t)(slot % kPage / 8) * D + d) * 8 + slot % 8] = a.v[row * D + d];
+        }
+    }
+    if (tid < 64 && s_slot[tid] >= 0) {
+        const int slot = s_slot[tid];
+        const size_t sl = (size_t)ptab[slot / kPage] * kPage + slot % kPage;
+        P.slot_pos[sl] = a.t0 + rb + tid;
+        if constexpr (F8) {
+            const size_t row = (size_t)(rb + tid) * hkv + h;
+            P.kscale[sl] = P.q8_scales(0)[row];
+            P.vscale[sl] = P.q8_scales(1)[row];
+        }
+    }
+}
+
 __global__ __launch_bounds__(64) void seq_release_kernel(PoolDev P, int seq) {
     const int gh = seq * P.n_layers * P.n_kv_heads + blockIdx.x;
     int32_t* hs = P.hstate + (size_t)gh * kHS;
@@ -1241,6 +1441,30 @@ hipError_t launch_prefill_compact(const PrefillArgs& a, hipStream_t s, hipEvent_
     } else {
         if (d128) hipExtLaunchKernelGGL(prefill_compact_kernel<128>, grid, dim3(256), 0, s, nullptr, stop, 0, a);
         else hipExtLaunchKernelGGL(prefill_compact_kernel<64>, grid, dim3(256), 0, s, nullptr, stop, 0, a);
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_extend(const PrefillArgs& a, bool with_out, hipStream_t s, hipEvent_t* ev) {
+    const bool d128 = a.pool.head_dim == 128;
+    hipError_t err;
+    if (a.pool.fp8) {  // the chunk's codes and scales: read by the attention and the writes
+        const int64_t threads = (int64_t)2 * a.n_tokens * a.pool.n_kv_heads * (a.pool.head_dim / 8);
+        const dim3 qgrid((unsigned)((threads + 255) / 256));
+        if (d128) hipLaunchKernelGGL(prefill_quant_kernel<128>, qgrid, dim3(256), 0, s, a);
+        else hipLaunchKernelGGL(prefill_quant_kernel<64>, qgrid, dim3(256), 0, s, a);
+        if ((err = hipGetLastError()) != hipSuccess) return err;
+    }
+    if (with_out && (err = launch_extend_attend(a, s, ev)) != hipSuccess) return err;
+    hipLaunchKernelGGL(extend_update_kernel, dim3(a.pool.n_kv_heads), dim3(1024), 0, s, a);
+    if ((err = hipGetLastError()) != hipSuccess) return err;
+    const dim3 grid((a.n_tokens + 63) / 64, a.pool.n_kv_heads);
+    if (a.pool.fp8) {
+        if (d128) hipLaunchKernelGGL((extend_write_kernel<128, true>), grid, dim3(256), 0, s, a);
+        else hipLaunchKernelGGL((extend_write_kernel<64, true>), grid, dim3(256), 0, s, a);
+    } else {
+        if (d128) hipLaunchKernelGGL((extend_write_kernel<128, false>), grid, dim3(256), 0, s, a);
+        else hipLaunchKernelGGL((extend_write_kernel<64, false>), grid, dim3(256), 0, s, a);
     }
     return hipGetLastError();
 }

@@ -27,6 +27,7 @@
 #include "dms_internal.h"
 
 #include <hip/hip_ext.h>
+#include <limits.h>
 #include <math.h>
 
 namespace dms {
@@ -125,7 +126,14 @@ constexpr int prefill_waves(int g) { return kPrefillWaves > g ? kPrefillWaves : 
 // from the pages, band from the quantised prompt and its V copy) and the row
 // scales of the tile's keys go to LDS with V: a key's scores are multiplied by
 // its K scale before the softmax, its weights by its V scale before P.V.
-template <int D, int G, bool F8>
+//
+// EXT (extend calls: the T = n_tokens input rows are new tokens at positions
+// t0 .. t0+T-1 of a (seq, layer) whose store already holds n_old live tokens):
+// queries and band keys are input rows (the band rule is the same in rows as in
+// positions, with no far-field boundary); the far field is every stored slot
+// 0 .. n_old-1, in slot order, each visible to the rows below its expiry row X
+// (position + w - t0 if marked, else never), staged per tile with V.
+template <int D, int G, bool F8, bool EXT>
 __global__ __attribute__((amdgpu_flat_work_group_size(64 * prefill_waves(G), 64 * prefill_waves(G)),
                           amdgpu_waves_per_eu(2, 2)))
 void prefill_attend_kernel(PrefillArgs a) {
@@ -141,6 +149,7 @@ void prefill_attend_kernel(PrefillArgs a) {
     __shared__ uint4 s_v[2][4][D];
     __shared__ uint32_t s_marks[2];
     __shared__ float4 s_ks[2][8], s_vs[2][8];  // FP8: K and V scales of the tile's 32 keys
+    __shared__ int4 s_x[2][8];                  // EXT: expiry rows of the tile's 32 stored keys
     const PoolDev& P = a.pool;
     const int T = a.n_tokens, w = P.window, hkv = P.n_kv_heads, hq_n = P.n_q_heads;
     const int nqb = (T + 32 * QT - 1) / (32 * QT);
@@ -169,8 +178,9 @@ void prefill_attend_kernel(PrefillArgs a) {
                         : make_uint4(0, 0, 0, 0);
 
     // ---- the block's key tiles
-    const int xf = t0b - w;
-    const int U = xf >= 0 ? P.pcnt[(size_t)h * P.max_positions + xf] : 0;
+    const int xf = EXT ? -1 : t0b - w;
+    const int U = EXT ? P.hstate[(size_t)gh * kHS + kHsLive]
+                      : (xf >= 0 ? P.pcnt[(size_t)h * P.max_positions + xf] : 0);
     const int nfar = (U + 31) / 32;
     const int band0 = max(0, xf + 1) / 32 * 32;
     const int kend = min(T, t0b + 32 * QT);
@@ -187,6 +197,7 @@ void prefill_attend_kernel(PrefillArgs a) {
     uint4 rk[UPT], rv[UPT];
     bool rmark = false;
     float rks = 0.f, rvs = 0.f;
+    int rx = 0;
     // page ids of far-field tiles one step ahead of their use: pg1 = page of tile
     // i+1 (for V), pg2 = page of tile i+2 (for K), pg3 requested for the next step
     auto page_of = [&](int t) -> int { return t < nfar ? ptab[(32 * t) / kPage] : 0; };
@@ -247,6 +258,20 @@ void prefill_attend_kernel(PrefillArgs a) {
             const int sk = kb + tid;
             rmark = sk < T && eviction_logit(P, a.logits, a.k, sk, h) > 0.f;
         }
+        if constexpr (EXT) {
+            if (tid < 32 && i < nfar) {  // expiry row of stored slot kb + tid
+                rx = INT_MIN;
+                if (kb + tid < U) {
+                    const int pos = P.slot_pos[(size_t)(i == 0 ? page_of(0) : pg1) * kPage + kb % kPage + tid];
+                    int mk = 0;
+                    if (P.ring_len > 0 && pos >= a.t0 - w) {
+                        const int e = P.ring[(size_t)gh * P.ring_len + pos % w];
+                        mk = e >= 0 && (e & 1);
+                    }
+                    rx = mk ? pos + w - a.t0 : INT_MAX;
+                }
+            }
+        }
         if constexpr (F8) {
             if (tid < 32) {
                 if (i < nfar) {
@@ -277,6 +302,9 @@ void prefill_attend_kernel(PrefillArgs a) {
         if (i >= nfar && wave == 0) {
             const uint32_t mk = (uint32_t)__ballot(rmark);
             if (lane == 0) s_marks[i & 1] = mk;
+        }
+        if constexpr (EXT) {
+            if (tid < 32 && i < nfar) reinterpret_cast<int*>(s_x[i & 1])[tid] = rx;
         }
         if constexpr (F8) {
             if (tid < 32) {
@@ -342,7 +370,17 @@ void prefill_attend_kernel(PrefillArgs a) {
             for (int r = 0; r < 16; ++r) cs[r] = cur[r];
         }
         float z[16];
-        if (i < nfar && kb + 32 <= U) {
+        if (EXT && i < nfar) {  // stored keys: visible to the rows below their expiry row
+#pragma unroll
+            for (int q4 = 0; q4 < 4; ++q4) {
+                const int4 x4 = s_x[i & 1][2 * half + (q4 & 1) + 4 * (q4 >> 1)];
+                const int r0 = 4 * (q4 & 1) + 8 * (q4 >> 1);
+                z[r0] = tq < x4.x ? cs[r0] : -INFINITY;
+                z[r0 + 1] = tq < x4.y ? cs[r0 + 1] : -INFINITY;
+                z[r0 + 2] = tq < x4.z ? cs[r0 + 2] : -INFINITY;
+                z[r0 + 3] = tq < x4.w ? cs[r0 + 3] : -INFINITY;
+            }
+        } else if (i < nfar && kb + 32 <= U) {
 #pragma unroll
             for (int r = 0; r < 16; ++r) z[r] = cs[r];
         } else if (i < nfar) {
@@ -456,22 +494,22 @@ void prefill_attend_kernel(PrefillArgs a) {
     }
 }
 
-template <int D, int G>
+template <int D, int G, bool EXT>
 hipError_t launch_attend_t(const PrefillArgs& a, hipStream_t s, hipEvent_t* ev) {
     constexpr int QT = prefill_waves(G) / G;
     const int nqb = (a.n_tokens + 32 * QT - 1) / (32 * QT);
     const int total = a.pool.n_kv_heads * nqb;
     const int grid = 8 * ((total + 7) / 8);
     if (a.pool.fp8)
-        hipExtLaunchKernelGGL((prefill_attend_kernel<D, G, true>), dim3(grid), dim3(64 * prefill_waves(G)), 0, s,
-                              ev ? ev[2] : nullptr, ev ? ev[3] : nullptr, 0, a);
+        hipExtLaunchKernelGGL((prefill_attend_kernel<D, G, true, EXT>), dim3(grid), dim3(64 * prefill_waves(G)), 0,
+                              s, ev ? ev[2] : nullptr, ev ? ev[3] : nullptr, 0, a);
     else
-        hipExtLaunchKernelGGL((prefill_attend_kernel<D, G, false>), dim3(grid), dim3(64 * prefill_waves(G)), 0, s,
-                              ev ? ev[2] : nullptr, ev ? ev[3] : nullptr, 0, a);
+        hipExtLaunchKernelGGL((prefill_attend_kernel<D, G, false, EXT>), dim3(grid), dim3(64 * prefill_waves(G)), 0,
+                              s, ev ? ev[2] : nullptr, ev ? ev[3] : nullptr, 0, a);
     return hipGetLastError();
 }
 
-template <int D>
+template <int D, bool EXT>
 hipError_t launch_attend_d(const PrefillArgs& a, hipStream_t s, hipEvent_t* ev) {
     const dim3 vgrid((a.n_tokens + 63) / 64, a.pool.n_kv_heads);
     if (a.pool.fp8)
@@ -483,10 +521,10 @@ hipError_t launch_attend_d(const PrefillArgs& a, hipStream_t s, hipEvent_t* ev) 
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
     switch (a.pool.n_q_heads / a.pool.n_kv_heads) {
-        case 1: return launch_attend_t<D, 1>(a, s, ev);
-        case 2: return launch_attend_t<D, 2>(a, s, ev);
-        case 4: return launch_attend_t<D, 4>(a, s, ev);
-        case 8: return launch_attend_t<D, 8>(a, s, ev);
+        case 1: return launch_attend_t<D, 1, EXT>(a, s, ev);
+        case 2: return launch_attend_t<D, 2, EXT>(a, s, ev);
+        case 4: return launch_attend_t<D, 4, EXT>(a, s, ev);
+        case 8: return launch_attend_t<D, 8, EXT>(a, s, ev);
     }
     return hipErrorInvalidValue;
 }
@@ -496,8 +534,16 @@ hipError_t launch_attend_d(const PrefillArgs& a, hipStream_t s, hipEvent_t* ev) 
 // Runs after the compaction kernels of the same prefill (same stream): the far
 // field reads the pages and the live-count prefix they wrote.
 hipError_t launch_prefill_attend(const PrefillArgs& a, hipStream_t s, hipEvent_t* ev) {
-    if (a.pool.head_dim == 128) return launch_attend_d<128>(a, s, ev);
-    if (a.pool.head_dim == 64) return launch_attend_d<64>(a, s, ev);
+    if (a.pool.head_dim == 128) return launch_attend_d<128, false>(a, s, ev);
+    if (a.pool.head_dim == 64) return launch_attend_d<64, false>(a, s, ev);
+    return hipErrorInvalidValue;
+}
+
+// Extend calls: the chunk's queries over the store (read before the chunk's
+// tokens are written) and the chunk; after the FP8 quantisation of the chunk.
+hipError_t launch_extend_attend(const PrefillArgs& a, hipStream_t s, hipEvent_t* ev) {
+    if (a.pool.head_dim == 128) return launch_attend_d<128, true>(a, s, ev);
+    if (a.pool.head_dim == 64) return launch_attend_d<64, true>(a, s, ev);
     return hipErrorInvalidValue;
 }
 

@@ -169,6 +169,31 @@ dms_status dms_decode_step(dms_pool* pool, int32_t n_seqs, const int32_t* seq_id
                            int32_t layer0, int32_t n_layers, const void* q, const void* k,
                            const void* v, const float* logits, void* out, void* stream);
 
+/* Append n_tokens new tokens to one (sequence, layer) that already holds
+ * tokens, at positions t .. t+n_tokens-1 (t = its position counter): the same
+ * result as n_tokens decode steps of that (seq, layer), in position order (for
+ * each token: mark it from its logit, expire the token w positions earlier if
+ * that one was marked and reuse its slot, else take the next slot; attend over
+ * the live tokens at its own position, itself included), with every token's
+ * inputs given at once, as in chunked prefill or in the check of several
+ * proposed tokens.  Several expiries per call are the point of this entry: a
+ * slot can change hands several times within one call.  (Delayed eviction:
+ * "NVIDIA veroeffentlicht Qwen3-8B-DMS-8x ..." news page, section "Dynamic
+ * Memory Sparsification (DMS): Eine innovative Loesung"; stiva.ai "Nvidia DMS
+ * ...", section on delayed eviction; slots of evicted tokens reclaimed in a
+ * compact store: the FastDMS announcement on molayo1419.me, "What's the catch?"
+ * table.)
+ *   q      bf16 [n_tokens][n_q_heads][head_dim]  (may be NULL when out is NULL)
+ *   k, v   bf16 [n_tokens][n_kv_heads][head_dim]
+ *   logits fp32 [n_tokens][n_kv_heads] (ignored, may be NULL, with
+ *          DMS_LOGITS_K_CHANNEL)
+ *   out    bf16 [n_tokens][n_q_heads][head_dim] or NULL (no attention)
+ * Returns DMS_E_STATE if the (seq, layer) was not prefilled or the chunk would
+ * run past max_positions.  Uses the pool's prefill scratch: calls that touch
+ * one pool must be ordered (one stream). */
+dms_status dms_extend(dms_pool* pool, int32_t seq, int32_t layer, int32_t n_tokens, const void* q,
+                      const void* k, const void* v, const float* logits, void* out, void* stream);
+
 typedef struct {
     int64_t live_slots;           /* tokens held, summed over the queried layers and kv heads */
     int64_t kv_bytes_live;        /* live_slots * bytes per slot: 2 (K,V) * head_dim * 2 bytes
@@ -222,6 +247,8 @@ typedef struct {
     double prefill_attend_ms;  /* masked causal attention (MFMA) kernels */
     int64_t decode_launches;
     int64_t prefill_calls;     /* prefills that produced an output */
+    double extend_attend_ms;   /* attention (MFMA) kernels of extend calls with output */
+    int64_t extend_calls;      /* extend calls that produced an output */
 } dms_timing;
 dms_status dms_timing_enable(dms_pool* pool, int32_t enable);
 dms_status dms_timing_read(dms_pool* pool, dms_timing* out);
