@@ -74,7 +74,7 @@ constexpr int kCtlError = 1;  // sticky: nonzero once the page pool ran out
 //                    (position - w, if it was marked), or -1
 //   [4..7]           unused
 constexpr int kHS = 8;
-constexpr int kHsLive = 0, kHsPages = 1, kHsPos = 2, kHsExp = 3;
+constexpr int kHsLive = 0, kHsPages = 1, kHsPos = 2, kHsExp = 3;  // [0..3] is one 16-byte load
 
 struct PoolDev {
     uint16_t* kpages;  // bf16 pools; FP8 pools hold bytes here (see kp8 / vp8)

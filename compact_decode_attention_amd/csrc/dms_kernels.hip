@@ -466,21 +466,34 @@ void decode_attend_kernel(DecodeArgs a) {
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
 
-    // ---- plan: pages per head and their prefix (every block builds its own)
+    // ---- plan: pages per head and their prefix (every block builds its own);
+    // a thread's head records (16 bytes each) are all requested before any is used
     {
+        constexpr int MAXPER = (kMaxCallHeads + NT - 1) / NT;
         const int per = (H + NT - 1) / NT;
         const int h0 = min(tid * per, H), h1 = min(h0 + per, H);
+        int4 rec[MAXPER];
+        int ghs[MAXPER];
+#pragma unroll
+        for (int i = 0; i < MAXPER; ++i) {
+            if (h0 + i < h1) {
+                ghs[i] = call_head(a, h0 + i).gh;
+                rec[i] = *reinterpret_cast<const int4*>(P.hstate + (size_t)ghs[i] * kHS);
+            }
+        }
         int local = 0;
-        for (int ch = h0; ch < h1; ++ch) {
-            const int gh = call_head(a, ch).gh;
-            const int32_t* hs = P.hstate + (size_t)gh * kHS;
-            const int n = hs[kHsLive];
-            s_nold[ch] = n;
-            s_exp[ch] = hs[kHsExp];
-            s_gh[ch] = gh;
-            const int c = (n + kPage - 1) / kPage;
-            s_pp[ch] = c;
-            local += c;
+#pragma unroll
+        for (int i = 0; i < MAXPER; ++i) {
+            if (h0 + i < h1) {
+                const int ch = h0 + i;
+                const int n = rec[i].x;  // [kHsLive]
+                s_nold[ch] = n;
+                s_exp[ch] = rec[i].w;    // [kHsExp]
+                s_gh[ch] = ghs[i];
+                const int c = (n + kPage - 1) / kPage;
+                s_pp[ch] = c;
+                local += c;
+            }
         }
         int total;
         int off = block_excl_scan<NT>(local, &total, s_scan);
