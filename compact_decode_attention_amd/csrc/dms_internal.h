@@ -112,6 +112,35 @@ struct PoolDev {
     }
 };
 
+// ---- raw buffer loads ----------------------------------------------------------
+// Resource over [base, base + bytes): loads beyond it return 0 and touch no
+// memory, so a dead request is a load through a zero-size resource.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, int bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, bytes, 0x00020000);
+}
+
+__device__ __forceinline__ uint4 buffer_load16(__amdgpu_buffer_rsrc_t r, int voff, int soff) {
+    const auto v = __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0);
+    return make_uint4(v[0], v[1], v[2], v[3]);
+}
+
+__device__ __forceinline__ uint2 buffer_load8(__amdgpu_buffer_rsrc_t r, int voff, int soff) {
+    const auto v = __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, 0);
+    return make_uint2(v[0], v[1]);
+}
+
+__device__ __forceinline__ float buffer_load4f(__amdgpu_buffer_rsrc_t r, int voff) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, voff, 0, 0));
+}
+
+__device__ __forceinline__ int buffer_load4i(__amdgpu_buffer_rsrc_t r, int voff) {
+    return (int)__builtin_amdgcn_raw_buffer_load_b32(r, voff, 0, 0);
+}
+
+__device__ __forceinline__ uint32_t buffer_load2(__amdgpu_buffer_rsrc_t r, int voff) {
+    return (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(r, voff, 0, 0);
+}
+
 // ---- OCP FP8 E4M3 (FP8 pools) -------------------------------------------------
 // Code of x: the finite E4M3 value nearest to x, ties to the code with an even
 // last bit, +-448 beyond the largest finite value, the sign kept (so -0 and

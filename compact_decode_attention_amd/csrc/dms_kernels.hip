@@ -91,16 +91,6 @@ __device__ __forceinline__ float wave_sum(float x) {
 // arithmetic producing x stays ahead of the loads issued after this point.
 __device__ __forceinline__ void pin(float& x) { asm volatile("" : "+v"(x)); }
 
-// Raw buffer resource over [base, base + bytes): loads beyond it return 0.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, int bytes) {
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, bytes, 0x00020000);
-}
-
-__device__ __forceinline__ uint4 buffer_load16(__amdgpu_buffer_rsrc_t r, int voff, int soff) {
-    const auto v = __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0);
-    return make_uint4(v[0], v[1], v[2], v[3]);
-}
-
 __device__ __forceinline__ int wave_incl_scan(int x, int lane) {
 #pragma unroll
     for (int o = 1; o < 64; o <<= 1) {
@@ -325,10 +315,6 @@ __device__ __forceinline__ uint32_t fp8x2_h_lo(uint32_t w) {
 }
 __device__ __forceinline__ uint32_t fp8x2_h_hi(uint32_t w) {
     return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, true));
-}
-
-__device__ __forceinline__ float buffer_load4f(__amdgpu_buffer_rsrc_t r, int voff) {
-    return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, voff, 0, 0));
 }
 
 // K chunks of one FP8 page (lane = slot; chunk cc = 16 dims of 64 slots, 1 KB

@@ -27,6 +27,7 @@
 #include "dms_internal.h"
 
 #include <hip/hip_ext.h>
+#include <algorithm>
 #include <limits.h>
 #include <math.h>
 
@@ -187,129 +188,149 @@ void prefill_attend_kernel(PrefillArgs a) {
     const int ntiles = nfar + (kend > band0 ? (kend - band0 + 31) / 32 : 0);
     const int32_t* ptab = P.ptable + (size_t)gh * P.pages_per_head;
     const uint16_t* vt = P.vt + (size_t)h * (P.max_pos32 / 8) * D * 8;
+    const size_t rowk = (size_t)hkv * D;  // elements from one prompt row of K to the next
 
     // Staging, thread t: K units u = t, t + NT, ... (chunk u / 32, key u % 32) and the
     // same V units.
     // K runs one tile ahead of V: while tile i is folded (scores S_i, computed one
-    // iteration earlier, and V_i) the block computes S_{i+1} from K_{i+1}, and the
-    // loads of K_{i+2} and V_{i+1} are in flight.
+    // iteration earlier, and V_i) the block computes S_{i+1} from K_{i+1}.  The
+    // global loads run one step further ahead: those of K_{i+3} and V_{i+2} are
+    // issued in step i into one of two register sets and written to LDS at the
+    // end of step i+1, so every load has a whole step to land.  (FP8 codes are
+    // converted to bf16 when written.)  Every load is issued by every thread:
+    // rows past the prompt, units past the tile and tiles past the last are
+    // read through short or zero-size resources, return 0 and touch no memory,
+    // so each step issues the same loads and waits only for the older set.
     auto tile_kb = [&](int i) { return i < nfar ? 32 * i : band0 + 32 * (i - nfar); };
-    uint4 rk[UPT], rv[UPT];
-    bool rmark = false;
-    float rks = 0.f, rvs = 0.f;
-    int rx = 0;
-    // page ids of far-field tiles one step ahead of their use: pg1 = page of tile
-    // i+1 (for V), pg2 = page of tile i+2 (for K), pg3 requested for the next step
-    auto page_of = [&](int t) -> int { return t < nfar ? ptab[(32 * t) / kPage] : 0; };
-    int pg1 = ntiles > 1 ? page_of(1) : 0, pg2 = ntiles > 2 ? page_of(2) : 0, pg3 = 0;
-    auto load_k = [&](int i) {
+    // (Loaded values stay untouched in their registers until they are written:
+    // any use would make the wave wait for them in the step that issues them.)
+    uint4 rk[2][UPT], rv[2][UPT];
+    uint32_t rlg[2];             // band: bits of the eviction logit of key kb + (lane & 31) (K channel: bf16)
+    float rks[2], rvs[2];        // FP8: K and V scales of key kb + (lane & 31)
+    int rx[2];                   // EXT: expiry row of stored slot kb + (lane & 31)
+    const int kl = lane & 31;
+    constexpr int kFar = 1 << 30;  // an offset past every resource below
+    // resources are wave-uniform: base and size go through readfirstlane so that a
+    // value the compiler cannot prove uniform (a loaded page id) never turns a
+    // load into a per-lane loop
+    auto rsrc = [](const void* base, int bytes) {
+        const uint64_t b = reinterpret_cast<uint64_t>(base);
+        const uint64_t ub = (uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)b) |
+                            ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(b >> 32)) << 32);
+        return buffer_rsrc(reinterpret_cast<const void*>(ub), __builtin_amdgcn_readfirstlane(bytes));
+    };
+    // page id of far-field tile t: a scalar load (the page table is read-only
+    // here), so it is counted with the LDS operations, not with the tile loads
+    typedef const int32_t __attribute__((address_space(4))) cint32_t;
+    cint32_t* cptab = (cint32_t*)ptab;
+    auto page_of = [&](int t) -> int { return t < nfar ? cptab[(32 * t) / kPage] : 0; };
+    auto upage = [](int pg) -> size_t { return (size_t)(uint32_t)__builtin_amdgcn_readfirstlane(pg); };
+    auto rows_left = [&](int kb) { return kb + 32 <= T ? 32 : kb < T ? T - kb : 0; };  // prompt rows kb .. kb+31
+    auto load_k = [&](int i, int X, int pg) {
         const int kb = tile_kb(i);
+        const bool far = i < nfar, live = i < ntiles;
+        if constexpr (F8) {
+            const uint8_t* base = far ? P.kp8() + upage(pg) * (kPage * D) : P.q8_codes(0) + (size_t)kb * rowk + h * D;
+            const int bytes = !live ? 0 : far ? kPage * D : rows_left(kb) * (int)rowk;
+            const __amdgpu_buffer_rsrc_t r = rsrc(base, bytes);
 #pragma unroll
-        for (int x = 0; x < UPT; ++x) {
-            const int u = tid + x * NT;
-            const int cc = u >> 5, j = u & 31;
-            if (u < UNITS) {
-                if (i < nfar) {
-                    const size_t pg = (size_t)(i == 0 ? page_of(0) : i == 1 ? pg1 : pg2);
-                    if constexpr (F8) {  // 8 of the 16 dims of chunk cc / 2
-                        const uint8_t* kp = P.kp8() + pg * (kPage * D);
-                        rk[x] = fp8x8_bf16(*reinterpret_cast<const uint2*>(
-                            kp + ((size_t)(cc >> 1) * kPage + kb % kPage + j) * 16 + (cc & 1) * 8));
-                    } else {
-                        const uint16_t* kp = P.kpages + pg * (kPage * D);
-                        rk[x] = *reinterpret_cast<const uint4*>(kp + ((size_t)cc * kPage + kb % kPage + j) * 8);
-                    }
-                } else {
-                    const int sk = kb + j;
-                    if constexpr (F8)
-                        rk[x] = sk < T ? fp8x8_bf16(*reinterpret_cast<const uint2*>(
-                                             P.q8_codes(0) + ((size_t)sk * hkv + h) * D + cc * 8))
-                                       : make_uint4(0, 0, 0, 0);
-                    else
-                        rk[x] = sk < T ? *reinterpret_cast<const uint4*>(a.k + ((size_t)sk * hkv + h) * D + cc * 8)
-                                       : make_uint4(0, 0, 0, 0);
-                }
+            for (int x = 0; x < UPT; ++x) {
+                const int u = tid + x * NT, cc = u >> 5, j = u & 31;
+                const int off = u >= UNITS ? kFar
+                                : far      ? ((cc >> 1) * kPage + kb % kPage + j) * 16 + (cc & 1) * 8
+                                           : j * (int)rowk + cc * 8;
+                const uint2 c = buffer_load8(r, off, 0);
+                rk[X][x] = make_uint4(c.x, c.y, 0u, 0u);
+            }
+        } else {
+            const uint16_t* base = far ? P.kpages + upage(pg) * (kPage * D) : a.k + (size_t)kb * rowk + h * D;
+            const int bytes = !live ? 0 : far ? kPage * D * 2 : rows_left(kb) * (int)rowk * 2;
+            const __amdgpu_buffer_rsrc_t r = rsrc(base, bytes);
+#pragma unroll
+            for (int x = 0; x < UPT; ++x) {
+                const int u = tid + x * NT, cc = u >> 5, j = u & 31;
+                const int off = u >= UNITS ? kFar
+                                : far      ? ((cc * kPage + kb % kPage + j) * 8) * 2
+                                           : (j * (int)rowk + cc * 8) * 2;
+                rk[X][x] = buffer_load16(r, off, 0);
             }
         }
     };
-    auto load_v = [&](int i) {
+    auto load_v = [&](int i, int X, int pg) {
         const int kb = tile_kb(i);
+        const bool far = i < nfar, live = i < ntiles;
+        if (F8 && far) {  // keys kb % 64 + 8 (u / D) .. +7 of dim u % D: half a 16-slot unit
+            const __amdgpu_buffer_rsrc_t r = rsrc(P.vp8() + upage(pg) * (kPage * D), live ? kPage * D : 0);
 #pragma unroll
-        for (int x = 0; x < UPT; ++x) {
-            const int u = tid + x * NT;
-            if (u < UNITS) {
-                if (i < nfar) {
-                    const size_t pg = (size_t)(i == 0 ? page_of(0) : pg1);
-                    if constexpr (F8) {  // keys kb % 64 + 8 (u / D) .. +7 of dim u % D: half a 16-slot unit
-                        const int k0 = kb % kPage + 8 * (u / D);
-                        const uint8_t* vp = P.vp8() + pg * (kPage * D);
-                        rv[x] = fp8x8_bf16(*reinterpret_cast<const uint2*>(
-                            vp + ((size_t)(k0 / 16) * D + u % D) * 16 + (k0 % 16)));
-                    } else {
-                        const uint16_t* vp = P.vpages + pg * (kPage * D);
-                        rv[x] = *reinterpret_cast<const uint4*>(vp + ((size_t)(kb % kPage / 8) * D) * 8 + (size_t)u * 8);
-                    }
-                } else {
-                    rv[x] = *reinterpret_cast<const uint4*>(vt + ((size_t)(kb / 8) * D) * 8 + (size_t)u * 8);
-                }
+            for (int x = 0; x < UPT; ++x) {
+                const int u = tid + x * NT, k0 = kb % kPage + 8 * (u / D);
+                const uint2 c = buffer_load8(r, u >= UNITS ? kFar : ((k0 / 16) * D + u % D) * 16 + (k0 % 16), 0);
+                rv[X][x] = make_uint4(c.x, c.y, 0u, 0u);
+            }
+        } else {
+            const uint16_t* base = far ? P.vpages + upage(pg) * (kPage * D) + (size_t)(kb % kPage / 8) * D * 8
+                                       : vt + (size_t)(kb / 8) * D * 8;
+            const __amdgpu_buffer_rsrc_t r = rsrc(base, live ? UNITS * 16 : 0);
+#pragma unroll
+            for (int x = 0; x < UPT; ++x) {
+                const int u = tid + x * NT;
+                rv[X][x] = buffer_load16(r, u >= UNITS ? kFar : u * 16, 0);
             }
         }
-        if (i >= nfar && tid < 32) {
-            const int sk = kb + tid;
-            rmark = sk < T && eviction_logit(P, a.logits, a.k, sk, h) > 0.f;
+        // per-key data of the tile (lanes l and l + 32 read the same key)
+        const bool band = live && !far;
+        if (P.logit_ch >= 0) {
+            const __amdgpu_buffer_rsrc_t r =
+                rsrc(a.k + (size_t)kb * rowk + h * D + P.logit_ch, band ? rows_left(kb) * (int)rowk * 2 : 0);
+            rlg[X] = buffer_load2(r, kl * (int)rowk * 2);
+        } else {
+            const __amdgpu_buffer_rsrc_t r = rsrc(a.logits + (size_t)kb * hkv + h, band ? rows_left(kb) * hkv * 4 : 0);
+            rlg[X] = (uint32_t)buffer_load4i(r, kl * hkv * 4);
         }
         if constexpr (EXT) {
-            if (tid < 32 && i < nfar) {  // expiry row of stored slot kb + tid
-                rx = INT_MIN;
-                if (kb + tid < U) {
-                    const int pos = P.slot_pos[(size_t)(i == 0 ? page_of(0) : pg1) * kPage + kb % kPage + tid];
-                    int mk = 0;
-                    if (P.ring_len > 0 && pos >= a.t0 - w) {
-                        const int e = P.ring[(size_t)gh * P.ring_len + pos % w];
-                        mk = e >= 0 && (e & 1);
-                    }
-                    rx = mk ? pos + w - a.t0 : INT_MAX;
-                }
-            }
+            const __amdgpu_buffer_rsrc_t r = rsrc(P.inv + (size_t)h * P.max_positions, live && far ? U * 4 : 0);
+            rx[X] = buffer_load4i(r, (kb + kl) * 4);
         }
         if constexpr (F8) {
-            if (tid < 32) {
-                if (i < nfar) {
-                    const size_t sl0 = (size_t)(i == 0 ? page_of(0) : pg1) * kPage + kb % kPage + tid;
-                    rks = P.kscale[sl0];
-                    rvs = P.vscale[sl0];
-                } else {
-                    const int sk = kb + tid;
-                    rks = sk < T ? P.q8_scales(0)[(size_t)sk * hkv + h] : 0.f;
-                    rvs = sk < T ? P.q8_scales(1)[(size_t)sk * hkv + h] : 0.f;
-                }
+            if (far) {
+                const size_t sl0 = upage(pg) * kPage + kb % kPage;
+                rks[X] = buffer_load4f(rsrc(P.kscale + sl0, live ? 32 * 4 : 0), kl * 4);
+                rvs[X] = buffer_load4f(rsrc(P.vscale + sl0, live ? 32 * 4 : 0), kl * 4);
+            } else {
+                const int bytes = live ? rows_left(kb) * hkv * 4 : 0;
+                rks[X] = buffer_load4f(rsrc(P.q8_scales(0) + (size_t)kb * hkv + h, bytes), kl * hkv * 4);
+                rvs[X] = buffer_load4f(rsrc(P.q8_scales(1) + (size_t)kb * hkv + h, bytes), kl * hkv * 4);
             }
         }
     };
-    auto store_k = [&](int i) {
+    auto store_k = [&](int i, int X) {
 #pragma unroll
         for (int x = 0; x < UPT; ++x) {
             const int u = tid + x * NT;
-            if (u < UNITS) s_k[i & 1][u >> 5][u & 31] = rk[x];
+            if (u < UNITS)
+                s_k[i & 1][u >> 5][u & 31] = F8 ? fp8x8_bf16(make_uint2(rk[X][x].x, rk[X][x].y)) : rk[X][x];
         }
     };
-    auto store_v = [&](int i) {
+    auto store_v = [&](int i, int X) {
+        const bool far = i < nfar;
 #pragma unroll
         for (int x = 0; x < UPT; ++x) {
             const int u = tid + x * NT;
-            if (u < UNITS) s_v[i & 1][u / D][u % D] = rv[x];
+            if (u < UNITS)
+                s_v[i & 1][u / D][u % D] = (F8 && far) ? fp8x8_bf16(make_uint2(rv[X][x].x, rv[X][x].y)) : rv[X][x];
         }
-        if (i >= nfar && wave == 0) {
-            const uint32_t mk = (uint32_t)__ballot(rmark);
+        if (!far && wave == 0) {  // keys past the prompt read logit 0: unmarked
+            const float lg = __uint_as_float(P.logit_ch >= 0 ? rlg[X] << 16 : rlg[X]);
+            const uint32_t mk = (uint32_t)__ballot(lg > 0.f);
             if (lane == 0) s_marks[i & 1] = mk;
         }
         if constexpr (EXT) {
-            if (tid < 32 && i < nfar) reinterpret_cast<int*>(s_x[i & 1])[tid] = rx;
+            if (tid < 32 && far) reinterpret_cast<int*>(s_x[i & 1])[tid] = tile_kb(i) + tid < U ? rx[X] : INT_MIN;
         }
         if constexpr (F8) {
             if (tid < 32) {
-                reinterpret_cast<float*>(s_ks[i & 1])[tid] = rks;
-                reinterpret_cast<float*>(s_vs[i & 1])[tid] = rvs;
+                reinterpret_cast<float*>(s_ks[i & 1])[tid] = rks[X];
+                reinterpret_cast<float*>(s_vs[i & 1])[tid] = rvs[X];
             }
         }
     };
@@ -330,22 +351,27 @@ void prefill_attend_kernel(PrefillArgs a) {
     for (int dt = 0; dt < DT; ++dt) o[dt] = f32x16_t{};
     float m = -INFINITY, lsum = 0.f;
 
-    // prologue: K_0, V_0, K_1 in LDS, S_0
-    load_k(0);
-    load_v(0);
-    store_k(0);
-    store_v(0);
-    if (ntiles > 1) {
-        load_k(1);
-        store_k(1);
+    // prologue: K_0, V_0, K_1 in LDS, S_0; K_2 and V_1 in flight (register set 1)
+    int pg2, pg3;
+    {
+        const int pg0 = page_of(0), pg1 = page_of(1);
+        pg2 = page_of(2);
+        pg3 = page_of(3);
+        load_k(0, 0, pg0);
+        load_v(0, 0, pg0);
+        load_k(1, 1, pg1);
+        store_k(0, 0);
+        store_v(0, 0);
+        if (ntiles > 1) store_k(1, 1);
+        load_k(2, 1, pg2);
+        load_v(1, 1, pg1);
     }
     __syncthreads();
     // one tile: fold S_i (in cur) while S_{i+1} (into nxt) and the next loads run
-    auto step = [&](int i, const f32x16_t& cur, f32x16_t& nxt) {
-        const bool more = i + 1 < ntiles;
-        if (i + 3 < ntiles) pg3 = page_of(i + 3);
-        if (i + 2 < ntiles) load_k(i + 2);
-        if (more) load_v(i + 1);
+    auto step = [&](int i, const f32x16_t& cur, f32x16_t& nxt, int X) {
+        const int pg4 = page_of(i + 4);
+        load_k(i + 3, X, pg3);
+        load_v(i + 2, X, pg2);
 
         // ---- fold tile i: row r of S_i holds key kb + (r & 7) + 8 half + 16 (r >> 3)
         const int kb = tile_kb(i);
@@ -463,18 +489,20 @@ void prefill_attend_kernel(PrefillArgs a) {
             for (int dt = 0; dt < DT; ++dt)
                 o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(va[dt][kk]), as_bf16x8(lb), o[dt], 0, 0, 0);
         }
-        // K_{i+2} replaces K_i (read for S_i one iteration ago), V_{i+1} replaces V_{i-1}
-        if (i + 2 < ntiles) store_k(i + 2);
-        if (more) store_v(i + 1);
-        pg1 = pg2;
+        // K_{i+2} replaces K_i (read for S_i one iteration ago), V_{i+1} replaces
+        // V_{i-1}; both were loaded in step i-1 (the other register set)
+        if (i + 2 < ntiles) store_k(i + 2, X ^ 1);
+        if (i + 1 < ntiles) store_v(i + 1, X ^ 1);
         pg2 = pg3;
+        pg3 = pg4;
         __syncthreads();
     };
-    // S alternates between two register sets (no copies between iterations)
+    // S and the in-flight loads alternate between two register sets (no copies
+    // between iterations)
     f32x16_t sa = scores(0), sb;
     for (int i = 0; i < ntiles; i += 2) {
-        step(i, sa, sb);
-        if (i + 1 < ntiles) step(i + 1, sb, sa);
+        step(i, sa, sb, 0);
+        if (i + 1 < ntiles) step(i + 1, sb, sa, 1);
     }
 
     // ---- normalise and store: lane holds dims dt*32 + 8*(r/4) + 4*half + r%4 of query tq
@@ -492,6 +520,27 @@ void prefill_attend_kernel(PrefillArgs a) {
                 *reinterpret_cast<uint2*>(orow + d) = make_uint2(lo, hi);
             }
     }
+}
+
+// Extend calls: expiry row of every stored slot j < n_old of the (seq, layer),
+// relative to the chunk's first position t0: position + w - t0 if the token is
+// marked (its mark is in the window ring while it is within w of t0), else
+// INT_MAX.  Written to the inv scratch ([kv head][slot]), which the attention
+// reads per far-field tile and the chain resolution overwrites afterwards.
+__global__ __launch_bounds__(256) void extend_expiry_kernel(PrefillArgs a) {
+    const PoolDev& P = a.pool;
+    const int h = blockIdx.y, w = P.window;
+    const int gh = (a.seq * P.n_layers + a.layer) * P.n_kv_heads + h;
+    const int j = blockIdx.x * 256 + threadIdx.x;
+    if (j >= P.hstate[(size_t)gh * kHS + kHsLive]) return;
+    const int page = P.ptable[(size_t)gh * P.pages_per_head + j / kPage];
+    const int pos = P.slot_pos[(size_t)page * kPage + j % kPage];
+    int mk = 0;
+    if (P.ring_len > 0 && pos >= a.t0 - w) {
+        const int e = P.ring[(size_t)gh * P.ring_len + pos % w];
+        mk = e >= 0 && (e & 1);
+    }
+    P.inv[(size_t)h * P.max_positions + j] = mk ? pos + w - a.t0 : INT_MAX;
 }
 
 template <int D, int G, bool EXT>
@@ -520,6 +569,11 @@ hipError_t launch_attend_d(const PrefillArgs& a, hipStream_t s, hipEvent_t* ev) 
                               ev ? ev[1] : nullptr, 0, a);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
+    if (EXT) {  // the store holds at most t0 slots per head
+        hipLaunchKernelGGL(extend_expiry_kernel, dim3((unsigned)std::max(1, (a.t0 + 255) / 256), a.pool.n_kv_heads),
+                           dim3(256), 0, s, a);
+        if ((err = hipGetLastError()) != hipSuccess) return err;
+    }
     switch (a.pool.n_q_heads / a.pool.n_kv_heads) {
         case 1: return launch_attend_t<D, 1, EXT>(a, s, ev);
         case 2: return launch_attend_t<D, 2, EXT>(a, s, ev);
