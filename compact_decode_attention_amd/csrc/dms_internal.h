@@ -65,6 +65,16 @@ constexpr int kMaxCallHeads = 4032;  // heads per launch (4 ints of plan per hea
 // ctl words
 constexpr int kCtlTop = 0;    // free pages on the stack
 constexpr int kCtlError = 1;  // sticky: nonzero once the page pool ran out
+constexpr int kCtlVWide = 2;  // sticky: nonzero once a bf16 V value of magnitude >= 2^16 (or inf/NaN) was seen
+
+// Nonzero if one of the two bf16 values in w has magnitude >= 2^16, is inf or
+// is NaN (exponent field >= 143): such a value has no fp16 counterpart.
+__device__ __forceinline__ uint32_t bf16x2_wide(uint32_t w) {
+    return ((w & 0x7fffu) >= 0x4780u) | ((w & 0x7fff0000u) >= 0x47800000u);
+}
+__device__ __forceinline__ uint32_t bf16x8_wide(uint4 u) {
+    return bf16x2_wide(u.x) | bf16x2_wide(u.y) | bf16x2_wide(u.z) | bf16x2_wide(u.w);
+}
 
 // Per-head record, 8 int32:
 //   [0] n_live       tokens held, in slots 0 .. n_live-1

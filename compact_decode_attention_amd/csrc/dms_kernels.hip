@@ -909,8 +909,13 @@ __device__ void append_head(const DecodeArgs& a, int ch) {
         uint16_t* kp = P.kpages + (size_t)page * (kPage * D);
         uint16_t* vp = P.vpages + (size_t)page * (kPage * D);
         if (lane < D / 8) *reinterpret_cast<uint4*>(kp + ((size_t)lane * kPage + j) * 8) = kchunk;
+        uint32_t wide = 0;  // a stored V value without an fp16 counterpart: sticky pool flag
 #pragma unroll
-        for (int jj = 0; jj < VJ; ++jj) vp[((size_t)(j / 8) * D + jj * 64 + lane) * 8 + (j % 8)] = vv[jj];
+        for (int jj = 0; jj < VJ; ++jj) {
+            vp[((size_t)(j / 8) * D + jj * 64 + lane) * 8 + (j % 8)] = vv[jj];
+            wide |= bf16x2_wide(vv[jj]);
+        }
+        if (wide) atomicOr(&P.ctl[kCtlVWide], 1);
     }
     if (lane == 0) {
         P.slot_pos[(size_t)page * kPage + j] = t;
@@ -1032,12 +1037,15 @@ __global__ __launch_bounds__(256) void prefill_compact_kernel(PrefillArgs a) {
         const uint4 val = s >= 0 ? *reinterpret_cast<const uint4*>(a.k + ((size_t)s * hkv + h) * D + cc * 8) : zero;
         *reinterpret_cast<uint4*>(kp + ((size_t)cc * kPage + j) * 8) = val;
     }
+    uint32_t wide = 0;  // a stored V value without an fp16 counterpart: sticky pool flag
     for (int u = tid; u < kPage * NC; u += 256) {
         const int j = u / NC, cc = u - j * NC;
         const int s = s_src[j];
         const uint4 val = s >= 0 ? *reinterpret_cast<const uint4*>(a.v + ((size_t)s * hkv + h) * D + cc * 8) : zero;
+        wide |= bf16x8_wide(val);
         *reinterpret_cast<uint4*>(&s_v[j][cc * 8]) = val;
     }
+    if (wide) atomicOr(&P.ctl[kCtlVWide], 1);
     __syncthreads();
     for (int u = tid; u < 8 * D; u += 256) {
         const int b = u / D, d = u - b * D;
@@ -1321,14 +1329,18 @@ __global__ __launch_bounds__(256) void extend_write_kernel(PrefillArgs a) {
             *reinterpret_cast<uint4*>(kp + ((size_t)cc * kPage + slot % kPage) * 8) =
                 *reinterpret_cast<const uint4*>(a.k + row * D + cc * 8);
         }
+        uint32_t wide = 0;  // a stored V value without an fp16 counterpart: sticky pool flag
         for (int u = tid; u < 64 * D; u += 256) {  // V: one value per (row, dim)
             const int j = u / D, d = u - j * D;
             const int slot = s_slot[j];
             if (slot < 0) continue;
             const size_t row = (size_t)(rb + j) * hkv + h;
             uint16_t* vp = P.vpages + (size_t)ptab[slot / kPage] * (kPage * D);
-            vp[((size_t)(slot % kPage / 8) * D + d) * 8 + slot % 8] = a.v[row * D + d];
+            const uint16_t x = a.v[row * D + d];
+            wide |= bf16x2_wide(x);
+            vp[((size_t)(slot % kPage / 8) * D + d) * 8 + slot % 8] = x;
         }
+        if (wide) atomicOr(&P.ctl[kCtlVWide], 1);
     }
     if (tid < 64 && s_slot[tid] >= 0) {
         const int slot = s_slot[tid];

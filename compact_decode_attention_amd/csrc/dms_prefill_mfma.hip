@@ -36,9 +36,23 @@ namespace {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
 __device__ __forceinline__ bf16x8_t as_bf16x8(uint4 u) { return __builtin_bit_cast(bf16x8_t, u); }
+__device__ __forceinline__ f16x8_t as_f16x8(uint4 u) { return __builtin_bit_cast(f16x8_t, u); }
+
+// 8 bf16 values as 8 fp16 values: exact for |v| < 65536 down to 2^-17 (below
+// that, fp16 subnormal spacing 2^-24).  Pools whose V can exceed the fp16 range
+// never take this path (see the kernel below).
+__device__ __forceinline__ uint4 bf16x8_to_f16x8(uint4 u) {
+    auto cv = [](uint32_t w) -> uint32_t {
+        const f16x2_t h = {(_Float16)__uint_as_float(w << 16), (_Float16)__uint_as_float(w & 0xffff0000u)};
+        return __builtin_bit_cast(uint32_t, h);
+    };
+    return make_uint4(cv(u.x), cv(u.y), cv(u.z), cv(u.w));
+}
 
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
     auto rne = [](float f) -> uint32_t {
@@ -67,6 +81,8 @@ __device__ __forceinline__ int swap23(int i) { return (i & ~12) | ((i & 4) << 1)
 // prompt V -> vt[h][s/8][d][8] (8 consecutive tokens of one dim per 16 bytes),
 // zero beyond the prompt up to the next multiple of 32.  FP8 pools: the values
 // of the prompt V's codes (exact in bf16; the row scales are applied to P).
+// bf16 pools: a V value without an fp16 counterpart sets the pool's sticky
+// kCtlVWide flag, which keeps the attention on its bf16 path.
 // ---------------------------------------------------------------------------
 template <int D, bool F8>
 __global__ __launch_bounds__(256) void prefill_vt_kernel(PrefillArgs a) {
@@ -77,6 +93,7 @@ __global__ __launch_bounds__(256) void prefill_vt_kernel(PrefillArgs a) {
     const int T = a.n_tokens, hkv = P.n_kv_heads;
     const int T32 = (T + 31) / 32 * 32;
     constexpr int NC = D / 8;
+    uint32_t wide = 0;
     for (int u = tid; u < 64 * NC; u += 256) {
         const int j = u / NC, cc = u - j * NC;
         const int s = s0 + j;
@@ -87,8 +104,10 @@ __global__ __launch_bounds__(256) void prefill_vt_kernel(PrefillArgs a) {
             else
                 val = *reinterpret_cast<const uint4*>(a.v + ((size_t)s * hkv + h) * D + cc * 8);
         }
+        if (!F8) wide |= bf16x8_wide(val);
         *reinterpret_cast<uint4*>(&s_v[j][cc * 8]) = val;
     }
+    if (wide) atomicOr(&P.ctl[kCtlVWide], 1);
     __syncthreads();
     uint16_t* vt = P.vt + (size_t)h * (P.max_pos32 / 8) * D * 8;
     for (int u = tid; u < 8 * D; u += 256) {
@@ -134,10 +153,14 @@ constexpr int prefill_waves(int g) { return kPrefillWaves > g ? kPrefillWaves : 
 // positions, with no far-field boundary); the far field is every stored slot
 // 0 .. n_old-1, in slot order, each visible to the rows below its expiry row X
 // (position + w - t0 if marked, else never), staged per tile with V.
-template <int D, int G, bool F8, bool EXT>
-__global__ __attribute__((amdgpu_flat_work_group_size(64 * prefill_waves(G), 64 * prefill_waves(G)),
-                          amdgpu_waves_per_eu(2, 2)))
-void prefill_attend_kernel(PrefillArgs a) {
+//
+// H16 (bf16 pools whose V values all lie in the fp16 range): V is staged in LDS
+// as fp16 and P enters P.V as one fp16 part, p * 2^7 (11 significant bits;
+// the factor keeps small weights out of the fp16 subnormals and cancels in
+// O / l).  Otherwise (FP8 pools, or a bf16 pool that has held a V value of
+// magnitude 2^16 or more) P enters as two bf16 parts.
+template <int D, int G, bool F8, bool EXT, bool H16>
+__device__ __forceinline__ void prefill_attend_body(const PrefillArgs& a) {
     constexpr int NWV = prefill_waves(G);
     constexpr int NT = 64 * NWV;
     static_assert(NWV % G == 0, "a block holds whole kv-head groups");
@@ -317,7 +340,9 @@ void prefill_attend_kernel(PrefillArgs a) {
         for (int x = 0; x < UPT; ++x) {
             const int u = tid + x * NT;
             if (u < UNITS)
-                s_v[i & 1][u / D][u % D] = (F8 && far) ? fp8x8_bf16(make_uint2(rv[X][x].x, rv[X][x].y)) : rv[X][x];
+                s_v[i & 1][u / D][u % D] = (F8 && far) ? fp8x8_bf16(make_uint2(rv[X][x].x, rv[X][x].y))
+                                           : H16       ? bf16x8_to_f16x8(rv[X][x])
+                                                       : rv[X][x];
         }
         if (!far && wave == 0) {  // keys past the prompt read logit 0: unmarked
             const float lg = __uint_as_float(P.logit_ch >= 0 ? rlg[X] << 16 : rlg[X]);
@@ -455,8 +480,8 @@ void prefill_attend_kernel(PrefillArgs a) {
         uint32_t ph[8], pl[8];
         float ps = 0.f;
         // m == -inf only while every score so far (this tile's included) is masked:
-        // then z = -inf and exp2(-inf) = 0
-        const float nm = m == -INFINITY ? 0.f : -m;
+        // then z = -inf and exp2(-inf) = 0.  (H16: weights times 2^7, l alike.)
+        const float nm = (m == -INFINITY ? 0.f : -m) + (H16 ? 7.f : 0.f);
 #pragma unroll
         for (int i2 = 0; i2 < 8; ++i2) {
             if (i2 % (8 / KS) == 0)
@@ -464,11 +489,16 @@ void prefill_attend_kernel(PrefillArgs a) {
                                                              sc, 0, 0, 0);
             const float p0 = __builtin_amdgcn_exp2f(fmaf(z[2 * i2], sl, nm));
             const float p1 = __builtin_amdgcn_exp2f(fmaf(z[2 * i2 + 1], sl, nm));
-            const float w0 = F8 ? p0 * vsc[2 * i2] : p0, w1 = F8 ? p1 * vsc[2 * i2 + 1] : p1;
-            const bf16x2_t hv = {(__bf16)w0, (__bf16)w1};
-            const bf16x2_t lv = {(__bf16)(w0 - (float)hv[0]), (__bf16)(w1 - (float)hv[1])};
-            ph[i2] = __builtin_bit_cast(uint32_t, hv);
-            pl[i2] = __builtin_bit_cast(uint32_t, lv);
+            if constexpr (H16) {
+                const f16x2_t hv = {(_Float16)p0, (_Float16)p1};
+                ph[i2] = __builtin_bit_cast(uint32_t, hv);
+            } else {
+                const float w0 = F8 ? p0 * vsc[2 * i2] : p0, w1 = F8 ? p1 * vsc[2 * i2 + 1] : p1;
+                const bf16x2_t hv = {(__bf16)w0, (__bf16)w1};
+                const bf16x2_t lv = {(__bf16)(w0 - (float)hv[0]), (__bf16)(w1 - (float)hv[1])};
+                ph[i2] = __builtin_bit_cast(uint32_t, hv);
+                pl[i2] = __builtin_bit_cast(uint32_t, lv);
+            }
             ps += p0 + p1;
         }
         nxt = sc;
@@ -481,13 +511,21 @@ void prefill_attend_kernel(PrefillArgs a) {
 #pragma unroll
         for (int kk = 0; kk < 2; ++kk) {
             const uint4 hb = make_uint4(ph[4 * kk], ph[4 * kk + 1], ph[4 * kk + 2], ph[4 * kk + 3]);
-            const uint4 lb = make_uint4(pl[4 * kk], pl[4 * kk + 1], pl[4 * kk + 2], pl[4 * kk + 3]);
+            if constexpr (H16) {
 #pragma unroll
-            for (int dt = 0; dt < DT; ++dt)
-                o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(va[dt][kk]), as_bf16x8(hb), o[dt], 0, 0, 0);
+                for (int dt = 0; dt < DT; ++dt)
+                    o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(as_f16x8(va[dt][kk]), as_f16x8(hb), o[dt], 0, 0, 0);
+            } else {
+                const uint4 lb = make_uint4(pl[4 * kk], pl[4 * kk + 1], pl[4 * kk + 2], pl[4 * kk + 3]);
 #pragma unroll
-            for (int dt = 0; dt < DT; ++dt)
-                o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(va[dt][kk]), as_bf16x8(lb), o[dt], 0, 0, 0);
+                for (int dt = 0; dt < DT; ++dt)
+                    o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(va[dt][kk]), as_bf16x8(hb), o[dt], 0, 0,
+                                                                    0);
+#pragma unroll
+                for (int dt = 0; dt < DT; ++dt)
+                    o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(va[dt][kk]), as_bf16x8(lb), o[dt], 0, 0,
+                                                                    0);
+            }
         }
         // K_{i+2} replaces K_i (read for S_i one iteration ago), V_{i+1} replaces
         // V_{i-1}; both were loaded in step i-1 (the other register set)
@@ -519,6 +557,19 @@ void prefill_attend_kernel(PrefillArgs a) {
                 const uint32_t hi = (uint32_t)bf16_bits(o[dt][4 * r4 + 2] * inv) | ((uint32_t)bf16_bits(o[dt][4 * r4 + 3] * inv) << 16);
                 *reinterpret_cast<uint2*>(orow + d) = make_uint2(lo, hi);
             }
+    }
+}
+
+template <int D, int G, bool F8, bool EXT>
+__global__ __attribute__((amdgpu_flat_work_group_size(64 * prefill_waves(G), 64 * prefill_waves(G)),
+                          amdgpu_waves_per_eu(2, 2)))
+void prefill_attend_kernel(PrefillArgs a) {
+    if constexpr (F8) {
+        prefill_attend_body<D, G, true, EXT, false>(a);
+    } else {
+        typedef const int32_t __attribute__((address_space(4))) cint32_t;  // a scalar load
+        if (((cint32_t*)a.pool.ctl)[kCtlVWide] == 0) prefill_attend_body<D, G, false, EXT, true>(a);
+        else prefill_attend_body<D, G, false, EXT, false>(a);
     }
 }
 

@@ -211,3 +211,33 @@ def test_extend_32k_chunked_prefill_sampled_rows():
             assert np.array_equal(pool.export_live(0, 0, h), oracle.live_positions(T - 1, w, mk[:, h]))
     finally:
         pool.close()
+
+
+def test_extend_after_a_decode_step_stored_a_wide_v():
+    """A decode step appends a V row with values of magnitude 2^20 (no fp16
+    counterpart); the extend that follows reads it from the store and must
+    take the two-part bf16 weights: outputs match the oracle."""
+    import torch
+    import compact_decode_attention_amd as dms
+    T0, n, G, Hkv, D, w = 130, 70, 4, 2, 64, 1 << 20
+    total = T0 + 1 + n
+    q, k, v, lg = make_inputs(total, G * Hkv, Hkv, D, 17, "random")
+    v = v.copy()
+    f = (v[T0].astype(np.uint32) << 16).view(np.float32) * np.float32(2.0 ** 20)
+    v[T0] = (f.view(np.uint32) >> 16).astype(np.uint16)
+    mk = oracle.marks(lg)
+    pool = dms.Pool(n_layers=1, n_q_heads=G * Hkv, n_kv_heads=Hkv, head_dim=D, window=w, max_seqs=1,
+                    max_positions=total, max_pages=Hkv * 4)
+    try:
+        pool.prefill(0, 0, bf(k[:T0], torch).cuda(), bf(v[:T0], torch).cuda(), torch.from_numpy(lg[:T0]).cuda())
+        o = torch.empty((1, 1, G * Hkv, D), dtype=torch.bfloat16, device="cuda")
+        pool.decode_step([0], 0, bf(q[T0], torch).cuda().view(1, 1, -1, D), bf(k[T0], torch).cuda().view(1, 1, Hkv, D),
+                         bf(v[T0], torch).cuda().view(1, 1, Hkv, D), torch.from_numpy(lg[T0]).cuda().view(1, 1, Hkv), o)
+        t0 = T0 + 1
+        out = torch.empty((n, G * Hkv, D), dtype=torch.bfloat16, device="cuda")
+        pool.extend(0, 0, bf(k[t0:], torch).cuda(), bf(v[t0:], torch).cuda(), torch.from_numpy(lg[t0:]).cuda(),
+                    q=bf(q[t0:], torch).cuda(), out=out)
+        ref = oracle.attend(q[t0:], np.arange(t0, total), k, v, mk, w)
+        assert_close(out.view(torch.int16).cpu().numpy().view(np.uint16), ref, "extend after a wide V was stored")
+    finally:
+        pool.close()

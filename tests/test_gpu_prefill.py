@@ -106,3 +106,54 @@ def test_prefill_32k_sampled_rows():
     for h in range(Hkv):
         assert np.array_equal(pool.export_live(0, 0, h), oracle.live_positions(T - 1, w, mk[:, h]))
     pool.close()
+
+
+def scaled_bf16(bits, factor):
+    """bf16 bits of value * factor (factor a power of two: exact)."""
+    f = (bits.astype(np.uint32) << 16).view(np.float32) * np.float32(factor)
+    return (f.view(np.uint32) >> 16).astype(np.uint16)
+
+
+def prefill_and_check(pool, layer, q, k, v, lg, w, what):
+    import torch
+    T, Hq, D = q.shape
+    out = torch.empty((T, Hq, D), dtype=torch.bfloat16, device="cuda")
+    pool.prefill(0, layer, bf(k, torch).cuda(), bf(v, torch).cuda(), torch.from_numpy(lg).cuda(),
+                 q=bf(q, torch).cuda(), out=out)
+    got = out.view(torch.int16).cpu().numpy().view(np.uint16)
+    assert_close(got, oracle.attend(q, np.arange(T), k, v, oracle.marks(lg), w), what)
+
+
+def test_prefill_v_at_the_fp16_limit():
+    """V values of 65280 (the largest bf16 value below 2^16, exact in fp16)
+    keep the fp16 weights path: outputs match."""
+    import compact_decode_attention_amd as dms
+    T, G, Hkv, D, w = 200, 4, 2, 128, 24
+    q, k, v, lg = make_inputs(T, G * Hkv, Hkv, D, 41, "random")
+    v = v.copy()
+    v[::13, :, ::5] = 0x477F  # positive: the outputs are dominated by them, no cancellation
+    pool = dms.Pool(n_layers=1, n_q_heads=G * Hkv, n_kv_heads=Hkv, head_dim=D, window=w, max_seqs=1,
+                    max_positions=T, max_pages=Hkv * 4)
+    try:
+        prefill_and_check(pool, 0, q, k, v, lg, w, "V at +-65280")
+    finally:
+        pool.close()
+
+
+def test_prefill_v_beyond_fp16_range_switches_the_pool_to_bf16_weights():
+    """A V value of magnitude 2^16 or more has no fp16 counterpart: the pool
+    keeps its attention on the two-part bf16 weights from then on.  Layer 0's
+    prompt holds values times 2^20, layer 1's is ordinary; both match."""
+    import compact_decode_attention_amd as dms
+    T, G, Hkv, D, w = 300, 4, 2, 128, 32
+    pool = dms.Pool(n_layers=2, n_q_heads=G * Hkv, n_kv_heads=Hkv, head_dim=D, window=w, max_seqs=1,
+                    max_positions=T, max_pages=2 * Hkv * 5)
+    try:
+        q, k, v, lg = make_inputs(T, G * Hkv, Hkv, D, 43, "random")
+        vw = v.copy()
+        vw[7::29] = scaled_bf16(v[7::29] & 0x7fff, 2.0 ** 20)  # magnitudes: no cancellation between them
+        prefill_and_check(pool, 0, q, k, vw, lg, w, "V times 2^20 in some rows")
+        q, k, v, lg = make_inputs(T, G * Hkv, Hkv, D, 44, "random")
+        prefill_and_check(pool, 1, q, k, v, lg, w, "ordinary layer after a wide one")
+    finally:
+        pool.close()
