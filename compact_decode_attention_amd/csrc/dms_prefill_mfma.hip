@@ -1,4 +1,5 @@
-// Masked causal prefill attention on MFMA (gfx950, v_mfma_f32_32x32x16_bf16).
+// Masked causal prefill attention on MFMA (gfx950, v_mfma_f32_32x32x16_bf16 and
+// _f16).
 //
 // Query t sees key s iff s <= t and (s is unmarked or t < s + w) (DMS delayed
 // eviction: "NVIDIA veroeffentlicht Qwen3-8B-DMS-8x ..." news page, section
@@ -22,8 +23,8 @@
 // B-operand layout of the next MFMA, O^T += V^T P^T, so P never leaves
 // registers.  V^T's A operand (8 consecutive keys of one dim) is one 16-byte
 // unit of the dim-major V page (far field) or of the V copy (band).
-// The G waves of a block are the G q heads sharing one kv head, so each K/V
-// tile is read by one block for all of them.
+// The waves of a block are the G q heads sharing one kv head (for QT query
+// tiles), so each K/V tile is read by one block for all of them.
 #include "dms_internal.h"
 
 #include <hip/hip_ext.h>
@@ -128,7 +129,8 @@ __global__ __launch_bounds__(256) void prefill_vt_kernel(PrefillArgs a) {
 // Key tiles of 32 are staged in LDS, double-buffered, by all threads of the
 // block: K as [D/8][32] 16-byte units (A operand of S^T = K Q^T: lane = key row,
 // 16 bytes = 8 dims), V as [4][D] units (A operand of O^T = V^T P^T: lane = dim,
-// 16 bytes = 8 keys).  While a tile is computed the next one is in flight.
+// 16 bytes = 8 keys).  While tile i is folded, S_{i+1} is computed and the
+// global loads of K_{i+3} and V_{i+2} are in flight.
 //
 // Key tiles of a block whose first query tile starts at t0b (xf = t0b - w):
 //   far field  the first U = #live[0, xf] pool slots: unmarked keys older than
@@ -249,32 +251,44 @@ __device__ __forceinline__ void prefill_attend_body(const PrefillArgs& a) {
     auto page_of = [&](int t) -> int { return t < nfar ? cptab[(32 * t) / kPage] : 0; };
     auto upage = [](int pg) -> size_t { return (size_t)(uint32_t)__builtin_amdgcn_readfirstlane(pg); };
     auto rows_left = [&](int kb) { return kb + 32 <= T ? 32 : kb < T ? T - kb : 0; };  // prompt rows kb .. kb+31
+    const __amdgpu_buffer_rsrc_t rx_rsrc = rsrc(P.inv + (size_t)h * P.max_positions, EXT ? U * 4 : 0);
+    // Per-thread offsets that do not change from tile to tile (bytes; kFar for
+    // units past the tile): K unit (chunk cc, key j) in a page at slot 0 and in
+    // the prompt at row 0; V unit u of a tile.
+    int koff_far[UPT], koff_band[UPT], voff[UPT];
+#pragma unroll
+    for (int x = 0; x < UPT; ++x) {
+        const int u = tid + x * NT, cc = u >> 5, j = u & 31;
+        if constexpr (F8) {
+            koff_far[x] = u >= UNITS ? kFar : ((cc >> 1) * kPage + j) * 16 + (cc & 1) * 8;
+            koff_band[x] = u >= UNITS ? kFar : j * (int)rowk + cc * 8;
+            voff[x] = u >= UNITS ? kFar : ((8 * (u / D)) / 16 * D + u % D) * 16 + (8 * (u / D)) % 16;
+        } else {
+            koff_far[x] = u >= UNITS ? kFar : ((cc * kPage + j) * 8) * 2;
+            koff_band[x] = u >= UNITS ? kFar : (j * (int)rowk + cc * 8) * 2;
+            voff[x] = u >= UNITS ? kFar : u * 16;
+        }
+    }
+    constexpr int EB = F8 ? 1 : 2;  // bytes per stored K/V element
+    const char* const kfar0 = reinterpret_cast<const char*>(F8 ? (const void*)P.kp8() : (const void*)P.kpages);
+    const char* const vfar0 = reinterpret_cast<const char*>(F8 ? (const void*)P.vp8() : (const void*)P.vpages);
+    const char* const kband0 = F8 ? reinterpret_cast<const char*>(P.q8_codes(0) + h * D)
+                                  : reinterpret_cast<const char*>(a.k + h * D);
+    const int rowb = (int)rowk * EB;  // bytes from one prompt row of K to the next
     auto load_k = [&](int i, int X, int pg) {
         const int kb = tile_kb(i);
         const bool far = i < nfar, live = i < ntiles;
-        if constexpr (F8) {
-            const uint8_t* base = far ? P.kp8() + upage(pg) * (kPage * D) : P.q8_codes(0) + (size_t)kb * rowk + h * D;
-            const int bytes = !live ? 0 : far ? kPage * D : rows_left(kb) * (int)rowk;
-            const __amdgpu_buffer_rsrc_t r = rsrc(base, bytes);
+        const char* base = far ? kfar0 + upage(pg) * (kPage * D * EB) : kband0 + (size_t)kb * rowb;
+        const int bytes = !live ? 0 : far ? kPage * D * EB : rows_left(kb) * rowb;
+        const __amdgpu_buffer_rsrc_t r = rsrc(base, bytes);
+        const int slot16 = (kb % kPage) * 16;  // far: the tile's first slot within the page
 #pragma unroll
-            for (int x = 0; x < UPT; ++x) {
-                const int u = tid + x * NT, cc = u >> 5, j = u & 31;
-                const int off = u >= UNITS ? kFar
-                                : far      ? ((cc >> 1) * kPage + kb % kPage + j) * 16 + (cc & 1) * 8
-                                           : j * (int)rowk + cc * 8;
+        for (int x = 0; x < UPT; ++x) {
+            const int off = far ? koff_far[x] + slot16 : koff_band[x];
+            if constexpr (F8) {
                 const uint2 c = buffer_load8(r, off, 0);
                 rk[X][x] = make_uint4(c.x, c.y, 0u, 0u);
-            }
-        } else {
-            const uint16_t* base = far ? P.kpages + upage(pg) * (kPage * D) : a.k + (size_t)kb * rowk + h * D;
-            const int bytes = !live ? 0 : far ? kPage * D * 2 : rows_left(kb) * (int)rowk * 2;
-            const __amdgpu_buffer_rsrc_t r = rsrc(base, bytes);
-#pragma unroll
-            for (int x = 0; x < UPT; ++x) {
-                const int u = tid + x * NT, cc = u >> 5, j = u & 31;
-                const int off = u >= UNITS ? kFar
-                                : far      ? ((cc * kPage + kb % kPage + j) * 8) * 2
-                                           : (j * (int)rowk + cc * 8) * 2;
+            } else {
                 rk[X][x] = buffer_load16(r, off, 0);
             }
         }
@@ -283,22 +297,20 @@ __device__ __forceinline__ void prefill_attend_body(const PrefillArgs& a) {
         const int kb = tile_kb(i);
         const bool far = i < nfar, live = i < ntiles;
         if (F8 && far) {  // keys kb % 64 + 8 (u / D) .. +7 of dim u % D: half a 16-slot unit
-            const __amdgpu_buffer_rsrc_t r = rsrc(P.vp8() + upage(pg) * (kPage * D), live ? kPage * D : 0);
+            const __amdgpu_buffer_rsrc_t r =
+                rsrc(vfar0 + upage(pg) * (kPage * D) + (size_t)(kb % kPage / 16) * D * 16, live ? 2 * D * 16 : 0);
 #pragma unroll
             for (int x = 0; x < UPT; ++x) {
-                const int u = tid + x * NT, k0 = kb % kPage + 8 * (u / D);
-                const uint2 c = buffer_load8(r, u >= UNITS ? kFar : ((k0 / 16) * D + u % D) * 16 + (k0 % 16), 0);
+                const uint2 c = buffer_load8(r, voff[x], 0);
                 rv[X][x] = make_uint4(c.x, c.y, 0u, 0u);
             }
         } else {
-            const uint16_t* base = far ? P.vpages + upage(pg) * (kPage * D) + (size_t)(kb % kPage / 8) * D * 8
-                                       : vt + (size_t)(kb / 8) * D * 8;
+            const char* base = far ? vfar0 + upage(pg) * (kPage * D * 2) + (size_t)(kb % kPage / 8) * D * 16
+                                   : reinterpret_cast<const char*>(vt) + (size_t)(kb / 8) * D * 16;
             const __amdgpu_buffer_rsrc_t r = rsrc(base, live ? UNITS * 16 : 0);
 #pragma unroll
-            for (int x = 0; x < UPT; ++x) {
-                const int u = tid + x * NT;
-                rv[X][x] = buffer_load16(r, u >= UNITS ? kFar : u * 16, 0);
-            }
+            for (int x = 0; x < UPT; ++x) rv[X][x] = buffer_load16(r, F8 ? (tid + x * NT >= UNITS ? kFar : (tid + x * NT) * 16)
+                                                                    : voff[x], 0);
         }
         // per-key data of the tile (lanes l and l + 32 read the same key)
         const bool band = live && !far;
@@ -310,10 +322,7 @@ __device__ __forceinline__ void prefill_attend_body(const PrefillArgs& a) {
             const __amdgpu_buffer_rsrc_t r = rsrc(a.logits + (size_t)kb * hkv + h, band ? rows_left(kb) * hkv * 4 : 0);
             rlg[X] = (uint32_t)buffer_load4i(r, kl * hkv * 4);
         }
-        if constexpr (EXT) {
-            const __amdgpu_buffer_rsrc_t r = rsrc(P.inv + (size_t)h * P.max_positions, live && far ? U * 4 : 0);
-            rx[X] = buffer_load4i(r, (kb + kl) * 4);
-        }
+        if constexpr (EXT) rx[X] = buffer_load4i(rx_rsrc, (kb + kl) * 4 + (live && far ? 0 : kFar));
         if constexpr (F8) {
             if (far) {
                 const size_t sl0 = upage(pg) * kPage + kb % kPage;
@@ -393,62 +402,64 @@ __device__ __forceinline__ void prefill_attend_body(const PrefillArgs& a) {
     }
     __syncthreads();
     // one tile: fold S_i (in cur) while S_{i+1} (into nxt) and the next loads run
-    auto step = [&](int i, const f32x16_t& cur, f32x16_t& nxt, int X) {
+    auto step = [&](int i, f32x16_t& cur, f32x16_t& nxt, int X) {
         const int pg4 = page_of(i + 4);
         load_k(i + 3, X, pg3);
         load_v(i + 2, X, pg2);
 
         // ---- fold tile i: row r of S_i holds key kb + (r & 7) + 8 half + 16 (r >> 3)
         const int kb = tile_kb(i);
-        float cs[16], vsc[16];  // scores (FP8: times the keys' K scales); FP8: the keys' V scales
+        // z: the scores (FP8: times the keys' K scales) with invisible keys at
+        // -inf, computed in place in S_i's registers (dead after this step)
+        f32x16_t& z = cur;
+        float vsc[16];  // FP8: the keys' V scales
         if constexpr (F8) {
 #pragma unroll
             for (int q4 = 0; q4 < 4; ++q4) {  // rows r0 .. r0+3 hold keys 4 kk .. 4 kk + 3
                 const int kk = 2 * half + (q4 & 1) + 4 * (q4 >> 1);
                 const float4 k4 = s_ks[i & 1][kk], v4 = s_vs[i & 1][kk];
                 const int r0 = 4 * (q4 & 1) + 8 * (q4 >> 1);
-                cs[r0] = cur[r0] * k4.x;
-                cs[r0 + 1] = cur[r0 + 1] * k4.y;
-                cs[r0 + 2] = cur[r0 + 2] * k4.z;
-                cs[r0 + 3] = cur[r0 + 3] * k4.w;
+                z[r0] *= k4.x;
+                z[r0 + 1] *= k4.y;
+                z[r0 + 2] *= k4.z;
+                z[r0 + 3] *= k4.w;
                 vsc[r0] = v4.x;
                 vsc[r0 + 1] = v4.y;
                 vsc[r0 + 2] = v4.z;
                 vsc[r0 + 3] = v4.w;
             }
-        } else {
-#pragma unroll
-            for (int r = 0; r < 16; ++r) cs[r] = cur[r];
         }
-        float z[16];
         if (EXT && i < nfar) {  // stored keys: visible to the rows below their expiry row
 #pragma unroll
             for (int q4 = 0; q4 < 4; ++q4) {
                 const int4 x4 = s_x[i & 1][2 * half + (q4 & 1) + 4 * (q4 >> 1)];
                 const int r0 = 4 * (q4 & 1) + 8 * (q4 >> 1);
-                z[r0] = tq < x4.x ? cs[r0] : -INFINITY;
-                z[r0 + 1] = tq < x4.y ? cs[r0 + 1] : -INFINITY;
-                z[r0 + 2] = tq < x4.z ? cs[r0 + 2] : -INFINITY;
-                z[r0 + 3] = tq < x4.w ? cs[r0 + 3] : -INFINITY;
+                if (tq >= x4.x) z[r0] = -INFINITY;
+                if (tq >= x4.y) z[r0 + 1] = -INFINITY;
+                if (tq >= x4.z) z[r0 + 2] = -INFINITY;
+                if (tq >= x4.w) z[r0 + 3] = -INFINITY;
             }
-        } else if (i < nfar && kb + 32 <= U) {
-#pragma unroll
-            for (int r = 0; r < 16; ++r) z[r] = cs[r];
-        } else if (i < nfar) {
-#pragma unroll
-            for (int r = 0; r < 16; ++r) z[r] = kb + (r & 7) + 8 * half + 16 * (r >> 3) < U ? cs[r] : -INFINITY;
-        } else {
-            // visible keys of this lane's query as one 32-bit mask over the tile:
-            // kb + kr <= tq, kb + kr > xf, and unmarked or kb + kr > tq - w
-            const uint32_t marks = s_marks[i & 1];
-            auto above = [](int c) -> uint32_t {  // bits kr > c
-                return c < 0 ? 0xffffffffu : (c >= 31 ? 0u : (0xffffffffu << (c + 1)));
-            };
-            uint32_t vis = ~above(tq - kb) & above(xf - kb) & (~marks | above(tq - w - kb));
-            if (tq >= T) vis = 0;
+        } else if (!(i < nfar && kb + 32 <= U)) {  // (a whole far tile is visible as it is)
+            // visible keys of this lane's query as one 32-bit mask over the tile.
+            // Last far tile: kb + kr < U.  Band: kb + kr <= tq, kb + kr > xf,
+            // and unmarked or kb + kr > tq - w.
+            uint32_t vis;
+            if (i < nfar) {
+                vis = (1u << (U - kb)) - 1u;  // U - kb in [1, 31]
+            } else {
+                const uint32_t marks = s_marks[i & 1];
+                auto above = [](int c) -> uint32_t {  // bits kr > c
+                    return c < 0 ? 0xffffffffu : (c >= 31 ? 0u : (0xffffffffu << (c + 1)));
+                };
+                vis = ~above(tq - kb) & above(xf - kb) & (~marks | above(tq - w - kb));
+                if (tq >= T) vis = 0;
+            }
             vis >>= 8 * half;  // this lane's rows: kr = (r & 7) + 8 half + 16 (r >> 3)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) z[r] = ((vis >> ((r & 7) + 16 * (r >> 3))) & 1u) ? cs[r] : -INFINITY;
+            for (int r = 0; r < 16; ++r) {  // bit -> all-ones or zero, then a bit select
+                const int mk = __builtin_amdgcn_sbfe((int)vis, (r & 7) + 16 * (r >> 3), 1);
+                z[r] = __int_as_float((__float_as_int(z[r]) & mk) | (int)(0xff800000u & ~(uint32_t)mk));
+            }
         }
         float tmax = z[0];
 #pragma unroll
