@@ -125,7 +125,10 @@ __global__ __launch_bounds__(256) void prefill_vt_kernel(PrefillArgs a) {
 
 // ---------------------------------------------------------------------------
 // masked prefill attention.  One block = (kv head, QT consecutive 32-query
-// tiles), 8 waves: wave qt * G + g computes q head h * G + g on query tile qt.
+// tiles), max(4, G) waves: wave qt * G + g computes q head h * G + g on query
+// tile qt.  Two blocks share a compute unit (two waves per SIMD); blocks are
+// not synchronised with each other, so one block's matrix work overlaps the
+// other's vector work.
 // Key tiles of 32 are staged in LDS, double-buffered, by all threads of the
 // block: K as [D/8][32] 16-byte units (A operand of S^T = K Q^T: lane = key row,
 // 16 bytes = 8 dims), V as [4][D] units (A operand of O^T = V^T P^T: lane = dim,
@@ -138,9 +141,9 @@ __global__ __launch_bounds__(256) void prefill_vt_kernel(PrefillArgs a) {
 //   band       prompt keys in (xf, t0b + 32 QT), masked per (query, key) pair
 // ---------------------------------------------------------------------------
 #ifndef DMS_PREFILL_WAVES
-#define DMS_PREFILL_WAVES 8
+#define DMS_PREFILL_WAVES 4
 #endif
-constexpr int kPrefillWaves = DMS_PREFILL_WAVES;  // waves per block (tuning constant), at least G
+constexpr int kPrefillWaves = DMS_PREFILL_WAVES;  // waves per block (tuning constant; G if larger)
 constexpr int prefill_waves(int g) { return kPrefillWaves > g ? kPrefillWaves : g; }
 
 //
