@@ -954,18 +954,51 @@ __global__ __launch_bounds__(1024) void prefill_scan_kernel(PrefillArgs a) {
     const int hkv = P.n_kv_heads;
     const int gh = (a.seq * P.n_layers + a.layer) * hkv + h;
     const int T = a.n_tokens, w = P.window;
-    const int per = (T + 1023) / 1024;
-    const int s0 = min(tid * per, T), s1 = min(s0 + per, T);
-    // live at the last position T-1: unmarked, or inside the window (s >= T - w)
-    int cnt = 0;
-    for (int s = s0; s < s1; ++s) cnt += (s >= T - w || !(eviction_logit(P, a.logits, a.k, s, h) > 0.f)) ? 1 : 0;
-    int n;
-    int off = block_excl_scan<1024>(cnt, &n, s_scan);
     int32_t* inv = P.inv + (size_t)h * P.max_positions;
     int32_t* pcnt = P.pcnt + (size_t)h * P.max_positions;
-    for (int s = s0; s < s1; ++s) {
-        if (s >= T - w || !(eviction_logit(P, a.logits, a.k, s, h) > 0.f)) inv[off++] = s;
-        pcnt[s] = off;  // live tokens in [0, s]
+    // live at the last position T-1: unmarked, or inside the window (s >= T - w).
+    // Chunks of 8192 positions: wave v takes positions c0 + 512 v + 64 k + lane
+    // (k < 8; neighbouring lanes read and write neighbouring positions, all 8
+    // logits requested before any is used); ranks within the wave come from
+    // ballots, the waves' offsets from one exchange through LDS.
+    constexpr int KW = 8;
+    const int lane = tid & 63, wave = tid >> 6;
+    int n = 0;  // live positions before the current chunk
+    for (int c0 = 0; c0 < T; c0 += 16 * 64 * KW) {
+        const int seg0 = c0 + wave * 64 * KW + lane;
+        float lg[KW];
+#pragma unroll
+        for (int k = 0; k < KW; ++k) lg[k] = seg0 + 64 * k < T ? eviction_logit(P, a.logits, a.k, seg0 + 64 * k, h) : 0.f;
+        uint64_t bal[KW];
+        int wcount = 0;
+#pragma unroll
+        for (int k = 0; k < KW; ++k) {
+            const int s = seg0 + 64 * k;
+            bal[k] = __ballot(s < T && (s >= T - w || !(lg[k] > 0.f)));
+            wcount += __popcll(bal[k]);
+        }
+        if (lane == 0) s_scan[wave] = wcount;
+        __syncthreads();
+        int woff = 0, tot = 0;
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+            const int c = s_scan[v];
+            woff += v < wave ? c : 0;
+            tot += c;
+        }
+        __syncthreads();  // s_scan is rewritten by the next chunk
+        int off = n + woff;
+#pragma unroll
+        for (int k = 0; k < KW; ++k) {
+            const int s = seg0 + 64 * k;
+            const int rank = off + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(bal[k] >> 32),
+                                                                  __builtin_amdgcn_mbcnt_lo((uint32_t)bal[k], 0));
+            const int live = (int)((bal[k] >> lane) & 1u);
+            if (live) inv[rank] = s;
+            if (s < T) pcnt[s] = rank + live;  // live tokens in [0, s]
+            off += __popcll(bal[k]);
+        }
+        n += tot;
     }
     const int np = (n + kPage - 1) / kPage;
     if (tid == 0) {
