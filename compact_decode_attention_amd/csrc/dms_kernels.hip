@@ -1317,7 +1317,7 @@ __global__ __launch_bounds__(1024) void extend_update_kernel(PrefillArgs a) {
 template <int D, bool F8>
 __global__ __launch_bounds__(256) void extend_write_kernel(PrefillArgs a) {
     const PoolDev& P = a.pool;
-    __shared__ int s_slot[64];
+    __shared__ int s_slot[64], s_page[64];  // per row: destination slot (-1: not written) and its page
     const int tid = threadIdx.x, h = blockIdx.y, rb = blockIdx.x * 64;
     const int hkv = P.n_kv_heads, T = a.n_tokens, w = P.window;
     const int gh = (a.seq * P.n_layers + a.layer) * hkv + h;
@@ -1329,9 +1329,9 @@ __global__ __launch_bounds__(256) void extend_write_kernel(PrefillArgs a) {
             if (P.ring_len > 0 && r + w < T && ext_marked(a, r, h)) slot = -1;  // replaced within the chunk
         }
         s_slot[tid] = slot;
+        s_page[tid] = slot >= 0 ? P.ptable[(size_t)gh * P.pages_per_head + slot / kPage] : 0;
     }
     __syncthreads();
-    const int32_t* ptab = P.ptable + (size_t)gh * P.pages_per_head;
     if constexpr (F8) {
         constexpr int NC = D / 16;
         for (int u = tid; u < 64 * NC; u += 256) {  // K: 16 codes per chunk
@@ -1339,7 +1339,7 @@ __global__ __launch_bounds__(256) void extend_write_kernel(PrefillArgs a) {
             const int slot = s_slot[j];
             if (slot < 0) continue;
             const size_t row = (size_t)(rb + j) * hkv + h;
-            uint8_t* kp = P.kp8() + (size_t)ptab[slot / kPage] * (kPage * D);
+            uint8_t* kp = P.kp8() + (size_t)s_page[j] * (kPage * D);
             *reinterpret_cast<uint4*>(kp + ((size_t)cc * kPage + slot % kPage) * 16) =
                 *reinterpret_cast<const uint4*>(P.q8_codes(0) + row * D + cc * 16);
         }
@@ -1348,7 +1348,7 @@ __global__ __launch_bounds__(256) void extend_write_kernel(PrefillArgs a) {
             const int slot = s_slot[j];
             if (slot < 0) continue;
             const size_t row = (size_t)(rb + j) * hkv + h;
-            uint8_t* vp = P.vp8() + (size_t)ptab[slot / kPage] * (kPage * D);
+            uint8_t* vp = P.vp8() + (size_t)s_page[j] * (kPage * D);
             vp[((size_t)(slot % kPage / 16) * D + d) * 16 + slot % 16] = P.q8_codes(1)[row * D + d];
         }
     } else {
@@ -1358,26 +1358,29 @@ __global__ __launch_bounds__(256) void extend_write_kernel(PrefillArgs a) {
             const int slot = s_slot[j];
             if (slot < 0) continue;
             const size_t row = (size_t)(rb + j) * hkv + h;
-            uint16_t* kp = P.kpages + (size_t)ptab[slot / kPage] * (kPage * D);
+            uint16_t* kp = P.kpages + (size_t)s_page[j] * (kPage * D);
             *reinterpret_cast<uint4*>(kp + ((size_t)cc * kPage + slot % kPage) * 8) =
                 *reinterpret_cast<const uint4*>(a.k + row * D + cc * 8);
         }
         uint32_t wide = 0;  // a stored V value without an fp16 counterpart: sticky pool flag
-        for (int u = tid; u < 64 * D; u += 256) {  // V: one value per (row, dim)
-            const int j = u / D, d = u - j * D;
+        for (int u = tid; u < 64 * NC; u += 256) {  // V: 8 dims of a row per thread, one value per unit
+            const int j = u / NC, cc = u - j * NC;
             const int slot = s_slot[j];
             if (slot < 0) continue;
             const size_t row = (size_t)(rb + j) * hkv + h;
-            uint16_t* vp = P.vpages + (size_t)ptab[slot / kPage] * (kPage * D);
-            const uint16_t x = a.v[row * D + d];
-            wide |= bf16x2_wide(x);
-            vp[((size_t)(slot % kPage / 8) * D + d) * 8 + slot % 8] = x;
+            uint16_t* vp = P.vpages + (size_t)s_page[j] * (kPage * D) + (size_t)(slot % kPage / 8) * D * 8 + slot % 8;
+            const uint4 x = *reinterpret_cast<const uint4*>(a.v + row * D + cc * 8);
+            wide |= bf16x8_wide(x);
+            const uint32_t xw[4] = {x.x, x.y, x.z, x.w};
+#pragma unroll
+            for (int q = 0; q < 8; ++q)
+                vp[(size_t)(cc * 8 + q) * 8] = (uint16_t)(q & 1 ? xw[q / 2] >> 16 : xw[q / 2] & 0xffffu);
         }
         if (wide) atomicOr(&P.ctl[kCtlVWide], 1);
     }
     if (tid < 64 && s_slot[tid] >= 0) {
         const int slot = s_slot[tid];
-        const size_t sl = (size_t)ptab[slot / kPage] * kPage + slot % kPage;
+        const size_t sl = (size_t)s_page[tid] * kPage + slot % kPage;
         P.slot_pos[sl] = a.t0 + rb + tid;
         if constexpr (F8) {
             const size_t row = (size_t)(rb + tid) * hkv + h;
