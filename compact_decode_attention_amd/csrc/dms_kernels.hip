@@ -1193,7 +1193,8 @@ __global__ __launch_bounds__(256) void prefill_compact8_kernel(PrefillArgs a) {
 //           = n_old + #fresh rows before r otherwise
 // The chains are resolved by pointer jumping (log2(T / w) rounds).  Only the
 // last token of each chain is still live after the chunk, so only it is written.
-// One block per kv head; slot of each row in inv, chain parents in pcnt.
+// One block per kv head; slot of each row and chain parents in LDS (chunks up to
+// 4096 rows; else in the inv and pcnt scratch); the slots end in inv.
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ bool ext_marked(const PrefillArgs& a, int r, int h) {
     return eviction_logit(a.pool, a.logits, a.k, r, h) > 0.f;
@@ -1206,15 +1207,25 @@ __device__ __forceinline__ int ext_ring(const PoolDev& P, int gh, int u) {
 
 __global__ __launch_bounds__(1024) void extend_update_kernel(PrefillArgs a) {
     const PoolDev& P = a.pool;
+    constexpr int kLdsRows = 4096;  // chunks up to this many rows keep the arrays in LDS
     __shared__ int s_scan[2 * 16 + 1];
     __shared__ int s_base, s_enext;
+    __shared__ int s_val[kLdsRows], s_par[kLdsRows];
     const int tid = threadIdx.x, h = blockIdx.x;
     const int gh = (a.seq * P.n_layers + a.layer) * P.n_kv_heads + h;
     int32_t* hs = P.hstate + (size_t)gh * kHS;
     const int n_old = hs[kHsLive], np_old = hs[kHsPages];
     const int T = a.n_tokens, t0 = a.t0, w = P.window;
-    int32_t* val = P.inv + (size_t)h * P.max_positions;   // slot of row r (roots: final)
-    int32_t* par = P.pcnt + (size_t)h * P.max_positions;  // chain parent of row r (itself at a root)
+    const bool in_lds = T <= kLdsRows;
+    int32_t* const gval = P.inv + (size_t)h * P.max_positions;
+    int32_t* val = in_lds ? s_val : gval;                                    // slot of row r (roots: final)
+    int32_t* par = in_lds ? s_par : P.pcnt + (size_t)h * P.max_positions;  // chain parent of row r (itself at a root)
+    auto publish = [&]() {  // the write kernel reads the slots from the inv scratch
+        if (in_lds) {
+            __syncthreads();
+            for (int r = tid; r < T; r += 1024) gval[r] = s_val[r];
+        }
+    };
     const bool evict = P.ring_len > 0;
     const int per = (T + 1023) / 1024;
     const int r0 = min(tid * per, T), r1 = min(r0 + per, T);
@@ -1293,6 +1304,7 @@ __global__ __launch_bounds__(1024) void extend_update_kernel(PrefillArgs a) {
     if (s_base < 0) {  // pool exhausted: the sticky flag is set, the chunk is dropped
         if (tid == 0) hs[kHsPos] = t0 + T;
         for (int r = r0; r < r1; ++r) val[r] = -1;
+        publish();
         return;
     }
     for (int j = tid; j < need; j += 1024)
@@ -1309,6 +1321,7 @@ __global__ __launch_bounds__(1024) void extend_update_kernel(PrefillArgs a) {
         hs[kHsPos] = t0 + T;
         hs[kHsExp] = e;
     }
+    publish();
 }
 
 // K/V (FP8: codes and scales) of the rows still live after the chunk into their

@@ -241,3 +241,10 @@ def test_extend_after_a_decode_step_stored_a_wide_v():
         assert_close(out.view(torch.int16).cpu().numpy().view(np.uint16), ref, "extend after a wide V was stored")
     finally:
         pool.close()
+
+
+def test_extend_chunk_beyond_the_lds_rows():
+    """A 5000-token chunk (more rows than the slot assignment keeps in LDS, so
+    its chain arrays live in the scratch), w = 7 with random marks: chains of
+    ~700 reuses, outputs and the store against the oracle."""
+    run_extend(64, [5000], 7, marks="random", Hkv=1, G=2, D=64, seed=21)
