@@ -143,7 +143,12 @@ dms_status dms_pool_destroy(dms_pool* pool);
  *          DMS_LOGITS_K_CHANNEL)
  *   out    bf16 [n_tokens][n_q_heads][head_dim] or NULL
  * q and k arrive after any positional encoding.  Returns DMS_E_STATE if this
- * (seq, layer) already holds tokens (release the sequence first). */
+ * (seq, layer) already holds tokens (release the sequence first).
+ * Precision: fp32 accumulation; each output is within 2e-3 + 1e-2 |ref| of the
+ * masked attention over the inputs (FP8 pools: over value(code) * scale).  A
+ * bf16 pool that has seen a V value of magnitude 2^16 or more (in any prompt,
+ * chunk or decode step) keeps its prefill and extend attention on a slower
+ * path for good; the bound is the same. */
 dms_status dms_prefill(dms_pool* pool, int32_t seq, int32_t layer, int32_t n_tokens,
                        const void* q, const void* k, const void* v, const float* logits,
                        void* out, void* stream);
