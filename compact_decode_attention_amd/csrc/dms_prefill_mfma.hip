@@ -29,6 +29,7 @@
 
 #include <hip/hip_ext.h>
 #include <algorithm>
+#include <type_traits>
 #include <limits.h>
 #include <math.h>
 
@@ -278,9 +279,11 @@ __device__ __forceinline__ void prefill_attend_body(const PrefillArgs& a) {
     const char* const kband0 = F8 ? reinterpret_cast<const char*>(P.q8_codes(0) + h * D)
                                   : reinterpret_cast<const char*>(a.k + h * D);
     const int rowb = (int)rowk * EB;  // bytes from one prompt row of K to the next
-    auto load_k = [&](int i, int X, int pg) {
-        const int kb = tile_kb(i);
-        const bool far = i < nfar, live = i < ntiles;
+    // FP (compile time): tile i is a full far-field tile (no band, no bounds)
+    auto load_k = [&](int i, int X, int pg, auto fp) {
+        constexpr bool FP = decltype(fp)::value;
+        const int kb = FP ? 32 * i : tile_kb(i);
+        const bool far = FP || i < nfar, live = FP || i < ntiles;
         const char* base = far ? kfar0 + upage(pg) * (kPage * D * EB) : kband0 + (size_t)kb * rowb;
         const int bytes = !live ? 0 : far ? kPage * D * EB : rows_left(kb) * rowb;
         const __amdgpu_buffer_rsrc_t r = rsrc(base, bytes);
@@ -296,9 +299,10 @@ __device__ __forceinline__ void prefill_attend_body(const PrefillArgs& a) {
             }
         }
     };
-    auto load_v = [&](int i, int X, int pg) {
-        const int kb = tile_kb(i);
-        const bool far = i < nfar, live = i < ntiles;
+    auto load_v = [&](int i, int X, int pg, auto fp) {
+        constexpr bool FP = decltype(fp)::value;
+        const int kb = FP ? 32 * i : tile_kb(i);
+        const bool far = FP || i < nfar, live = FP || i < ntiles;
         if (F8 && far) {  // keys kb % 64 + 8 (u / D) .. +7 of dim u % D: half a 16-slot unit
             const __amdgpu_buffer_rsrc_t r =
                 rsrc(vfar0 + upage(pg) * (kPage * D) + (size_t)(kb % kPage / 16) * D * 16, live ? 2 * D * 16 : 0);
@@ -317,7 +321,8 @@ __device__ __forceinline__ void prefill_attend_body(const PrefillArgs& a) {
         }
         // per-key data of the tile (lanes l and l + 32 read the same key)
         const bool band = live && !far;
-        if (P.logit_ch >= 0) {
+        if (FP) {
+        } else if (P.logit_ch >= 0) {
             const __amdgpu_buffer_rsrc_t r =
                 rsrc(a.k + (size_t)kb * rowk + h * D + P.logit_ch, band ? rows_left(kb) * (int)rowk * 2 : 0);
             rlg[X] = buffer_load2(r, kl * (int)rowk * 2);
@@ -346,8 +351,8 @@ __device__ __forceinline__ void prefill_attend_body(const PrefillArgs& a) {
                 s_k[i & 1][u >> 5][u & 31] = F8 ? fp8x8_bf16(make_uint2(rk[X][x].x, rk[X][x].y)) : rk[X][x];
         }
     };
-    auto store_v = [&](int i, int X) {
-        const bool far = i < nfar;
+    auto store_v = [&](int i, int X, auto fp) {
+        const bool far = decltype(fp)::value || i < nfar;
 #pragma unroll
         for (int x = 0; x < UPT; ++x) {
             const int u = tid + x * NT;
@@ -394,24 +399,27 @@ __device__ __forceinline__ void prefill_attend_body(const PrefillArgs& a) {
         const int pg0 = page_of(0), pg1 = page_of(1);
         pg2 = page_of(2);
         pg3 = page_of(3);
-        load_k(0, 0, pg0);
-        load_v(0, 0, pg0);
-        load_k(1, 1, pg1);
+        const std::false_type gen;
+        load_k(0, 0, pg0, gen);
+        load_v(0, 0, pg0, gen);
+        load_k(1, 1, pg1, gen);
         store_k(0, 0);
-        store_v(0, 0);
+        store_v(0, 0, gen);
         if (ntiles > 1) store_k(1, 1);
-        load_k(2, 1, pg2);
-        load_v(1, 1, pg1);
+        load_k(2, 1, pg2, gen);
+        load_v(1, 1, pg1, gen);
     }
     __syncthreads();
-    // one tile: fold S_i (in cur) while S_{i+1} (into nxt) and the next loads run
-    auto step = [&](int i, f32x16_t& cur, f32x16_t& nxt, int X) {
+    // one tile: fold S_i (in cur) while S_{i+1} (into nxt) and the next loads run.
+    // fp (compile time): tiles i .. i+3 are full far-field tiles
+    auto step = [&](int i, f32x16_t& cur, f32x16_t& nxt, int X, auto fp) {
+        constexpr bool FP = decltype(fp)::value;
         const int pg4 = page_of(i + 4);
-        load_k(i + 3, X, pg3);
-        load_v(i + 2, X, pg2);
+        load_k(i + 3, X, pg3, fp);
+        load_v(i + 2, X, pg2, fp);
 
         // ---- fold tile i: row r of S_i holds key kb + (r & 7) + 8 half + 16 (r >> 3)
-        const int kb = tile_kb(i);
+        const int kb = FP ? 32 * i : tile_kb(i);
         // z: the scores (FP8: times the keys' K scales) with invisible keys at
         // -inf, computed in place in S_i's registers (dead after this step)
         f32x16_t& z = cur;
@@ -432,7 +440,7 @@ __device__ __forceinline__ void prefill_attend_body(const PrefillArgs& a) {
                 vsc[r0 + 3] = v4.w;
             }
         }
-        if (EXT && i < nfar) {  // stored keys: visible to the rows below their expiry row
+        if (EXT && (FP || i < nfar)) {  // stored keys: visible to the rows below their expiry row
 #pragma unroll
             for (int q4 = 0; q4 < 4; ++q4) {
                 const int4 x4 = s_x[i & 1][2 * half + (q4 & 1) + 4 * (q4 >> 1)];
@@ -442,7 +450,7 @@ __device__ __forceinline__ void prefill_attend_body(const PrefillArgs& a) {
                 if (tq >= x4.z) z[r0 + 2] = -INFINITY;
                 if (tq >= x4.w) z[r0 + 3] = -INFINITY;
             }
-        } else if (!(i < nfar && kb + 32 <= U)) {  // (a whole far tile is visible as it is)
+        } else if (!FP && !(i < nfar && kb + 32 <= U)) {  // (a whole far tile is visible as it is)
             // visible keys of this lane's query as one 32-bit mask over the tile.
             // Last far tile: kb + kr < U.  Band: kb + kr <= tq, kb + kr > xf,
             // and unmarked or kb + kr > tq - w.
@@ -543,18 +551,25 @@ __device__ __forceinline__ void prefill_attend_body(const PrefillArgs& a) {
         }
         // K_{i+2} replaces K_i (read for S_i one iteration ago), V_{i+1} replaces
         // V_{i-1}; both were loaded in step i-1 (the other register set)
-        if (i + 2 < ntiles) store_k(i + 2, X ^ 1);
-        if (i + 1 < ntiles) store_v(i + 1, X ^ 1);
+        if (FP || i + 2 < ntiles) store_k(i + 2, X ^ 1);
+        if (FP || i + 1 < ntiles) store_v(i + 1, X ^ 1, fp);
         pg2 = pg3;
         pg3 = pg4;
         __syncthreads();
     };
     // S and the in-flight loads alternate between two register sets (no copies
     // between iterations)
+    // (the far field first, in steps whose tiles and in-flight loads are all full
+    // far-field tiles, then the general steps)
     f32x16_t sa = scores(0), sb;
-    for (int i = 0; i < ntiles; i += 2) {
-        step(i, sa, sb, 0);
-        if (i + 1 < ntiles) step(i + 1, sb, sa, 1);
+    int i = 0;
+    for (; i + 5 <= nfar - 1; i += 2) {
+        step(i, sa, sb, 0, std::true_type());
+        step(i + 1, sb, sa, 1, std::true_type());
+    }
+    for (; i < ntiles; i += 2) {
+        step(i, sa, sb, 0, std::false_type());
+        if (i + 1 < ntiles) step(i + 1, sb, sa, 1, std::false_type());
     }
 
     // ---- normalise and store: lane holds dims dt*32 + 8*(r/4) + 4*half + r%4 of query tq
