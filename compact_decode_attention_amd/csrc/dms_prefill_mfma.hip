@@ -74,7 +74,16 @@ __device__ __forceinline__ uint16_t bf16_bits(float f) {
 
 __device__ __forceinline__ float bf16_f(uint32_t bits16) { return __uint_as_float(bits16 << 16); }
 
-__device__ __forceinline__ float xor32(float x) { return __shfl_xor(x, 32, 64); }
+// max and sum of x over lanes l and l ^ 32 (v_permlane32_swap exchanges the two
+// halves of the wave in one VALU instruction; either result pair holds x of both)
+__device__ __forceinline__ float max_xor32(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float sum_xor32(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
 
 // row index of the S^T tile -> key index within the 32-key tile: bits 2 and 3 swapped
 __device__ __forceinline__ int swap23(int i) { return (i & ~12) | ((i & 4) << 1) | ((i & 8) >> 1); }
@@ -347,7 +356,7 @@ __device__ __forceinline__ void prefill_attend_body(const PrefillArgs& a) {
 #pragma unroll
         for (int x = 0; x < UPT; ++x) {
             const int u = tid + x * NT;
-            if (u < UNITS)
+            if (UNITS % NT == 0 || u < UNITS)
                 s_k[i & 1][u >> 5][u & 31] = F8 ? fp8x8_bf16(make_uint2(rk[X][x].x, rk[X][x].y)) : rk[X][x];
         }
     };
@@ -356,7 +365,7 @@ __device__ __forceinline__ void prefill_attend_body(const PrefillArgs& a) {
 #pragma unroll
         for (int x = 0; x < UPT; ++x) {
             const int u = tid + x * NT;
-            if (u < UNITS)
+            if (UNITS % NT == 0 || u < UNITS)
                 s_v[i & 1][u / D][u % D] = (F8 && far) ? fp8x8_bf16(make_uint2(rv[X][x].x, rv[X][x].y))
                                            : H16       ? bf16x8_to_f16x8(rv[X][x])
                                                        : rv[X][x];
@@ -475,7 +484,7 @@ __device__ __forceinline__ void prefill_attend_body(const PrefillArgs& a) {
         float tmax = z[0];
 #pragma unroll
         for (int r = 1; r < 16; ++r) tmax = fmaxf(tmax, z[r]);
-        tmax = fmaxf(tmax, xor32(tmax)) * sl;  // base-2 units (sl > 0)
+        tmax = max_xor32(tmax) * sl;  // base-2 units (sl > 0)
         // lazy rescale: the running maximum moves only when a score exceeds it by
         // more than 8 (base 2), so weights stay below 256
         const bool grow = tmax > m + 8.f;
@@ -573,7 +582,7 @@ __device__ __forceinline__ void prefill_attend_body(const PrefillArgs& a) {
     }
 
     // ---- normalise and store: lane holds dims dt*32 + 8*(r/4) + 4*half + r%4 of query tq
-    const float ltot = lsum + xor32(lsum);
+    const float ltot = sum_xor32(lsum);
     if (tq < T) {
         const float inv = 1.f / ltot;
         uint16_t* orow = a.out + ((size_t)tq * hq_n + hq) * D;
