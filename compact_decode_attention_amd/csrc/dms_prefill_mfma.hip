@@ -288,13 +288,14 @@ __device__ __forceinline__ void prefill_attend_body(const PrefillArgs& a) {
     const char* const kband0 = F8 ? reinterpret_cast<const char*>(P.q8_codes(0) + h * D)
                                   : reinterpret_cast<const char*>(a.k + h * D);
     const int rowb = (int)rowk * EB;  // bytes from one prompt row of K to the next
-    // FP (compile time): tile i is a full far-field tile (no band, no bounds)
-    auto load_k = [&](int i, int X, int pg, auto fp) {
-        constexpr bool FP = decltype(fp)::value;
-        const int kb = FP ? 32 * i : tile_kb(i);
-        const bool far = FP || i < nfar, live = FP || i < ntiles;
+    // md (compile time): 1 if tile i is a full far-field tile, 2 if it is a full
+    // band tile (32 prompt rows), 0 if either may hold
+    auto load_k = [&](int i, int X, int pg, auto md) {
+        constexpr bool FP = decltype(md)::value == 1, BP = decltype(md)::value == 2;
+        const int kb = FP ? 32 * i : BP ? band0 + 32 * (i - nfar) : tile_kb(i);
+        const bool far = FP || (!BP && i < nfar), live = FP || BP || i < ntiles;
         const char* base = far ? kfar0 + upage(pg) * (kPage * D * EB) : kband0 + (size_t)kb * rowb;
-        const int bytes = !live ? 0 : far ? kPage * D * EB : rows_left(kb) * rowb;
+        const int bytes = !live ? 0 : far ? kPage * D * EB : (BP ? 32 : rows_left(kb)) * rowb;
         const __amdgpu_buffer_rsrc_t r = rsrc(base, bytes);
         const int slot16 = (kb % kPage) * 16;  // far: the tile's first slot within the page
 #pragma unroll
@@ -308,10 +309,11 @@ __device__ __forceinline__ void prefill_attend_body(const PrefillArgs& a) {
             }
         }
     };
-    auto load_v = [&](int i, int X, int pg, auto fp) {
-        constexpr bool FP = decltype(fp)::value;
-        const int kb = FP ? 32 * i : tile_kb(i);
-        const bool far = FP || i < nfar, live = FP || i < ntiles;
+    auto load_v = [&](int i, int X, int pg, auto md) {
+        constexpr bool FP = decltype(md)::value == 1, BP = decltype(md)::value == 2;
+        const int kb = FP ? 32 * i : BP ? band0 + 32 * (i - nfar) : tile_kb(i);
+        const bool far = FP || (!BP && i < nfar), live = FP || BP || i < ntiles;
+        const int rows = BP ? 32 : rows_left(kb);
         if (F8 && far) {  // keys kb % 64 + 8 (u / D) .. +7 of dim u % D: half a 16-slot unit
             const __amdgpu_buffer_rsrc_t r =
                 rsrc(vfar0 + upage(pg) * (kPage * D) + (size_t)(kb % kPage / 16) * D * 16, live ? 2 * D * 16 : 0);
@@ -333,20 +335,20 @@ __device__ __forceinline__ void prefill_attend_body(const PrefillArgs& a) {
         if (FP) {
         } else if (P.logit_ch >= 0) {
             const __amdgpu_buffer_rsrc_t r =
-                rsrc(a.k + (size_t)kb * rowk + h * D + P.logit_ch, band ? rows_left(kb) * (int)rowk * 2 : 0);
+                rsrc(a.k + (size_t)kb * rowk + h * D + P.logit_ch, band ? rows * (int)rowk * 2 : 0);
             rlg[X] = buffer_load2(r, kl * (int)rowk * 2);
         } else {
-            const __amdgpu_buffer_rsrc_t r = rsrc(a.logits + (size_t)kb * hkv + h, band ? rows_left(kb) * hkv * 4 : 0);
+            const __amdgpu_buffer_rsrc_t r = rsrc(a.logits + (size_t)kb * hkv + h, band ? rows * hkv * 4 : 0);
             rlg[X] = (uint32_t)buffer_load4i(r, kl * hkv * 4);
         }
-        if constexpr (EXT) rx[X] = buffer_load4i(rx_rsrc, (kb + kl) * 4 + (live && far ? 0 : kFar));
+        if constexpr (EXT && !BP) rx[X] = buffer_load4i(rx_rsrc, (kb + kl) * 4 + (live && far ? 0 : kFar));
         if constexpr (F8) {
             if (far) {
                 const size_t sl0 = upage(pg) * kPage + kb % kPage;
                 rks[X] = buffer_load4f(rsrc(P.kscale + sl0, live ? 32 * 4 : 0), kl * 4);
                 rvs[X] = buffer_load4f(rsrc(P.vscale + sl0, live ? 32 * 4 : 0), kl * 4);
             } else {
-                const int bytes = live ? rows_left(kb) * hkv * 4 : 0;
+                const int bytes = live ? rows * hkv * 4 : 0;
                 rks[X] = buffer_load4f(rsrc(P.q8_scales(0) + (size_t)kb * hkv + h, bytes), kl * hkv * 4);
                 rvs[X] = buffer_load4f(rsrc(P.q8_scales(1) + (size_t)kb * hkv + h, bytes), kl * hkv * 4);
             }
@@ -360,8 +362,9 @@ __device__ __forceinline__ void prefill_attend_body(const PrefillArgs& a) {
                 s_k[i & 1][u >> 5][u & 31] = F8 ? fp8x8_bf16(make_uint2(rk[X][x].x, rk[X][x].y)) : rk[X][x];
         }
     };
-    auto store_v = [&](int i, int X, auto fp) {
-        const bool far = decltype(fp)::value || i < nfar;
+    auto store_v = [&](int i, int X, auto md) {
+        constexpr int MD = decltype(md)::value;
+        const bool far = MD == 1 || (MD != 2 && i < nfar);
 #pragma unroll
         for (int x = 0; x < UPT; ++x) {
             const int u = tid + x * NT;
@@ -408,7 +411,7 @@ __device__ __forceinline__ void prefill_attend_body(const PrefillArgs& a) {
         const int pg0 = page_of(0), pg1 = page_of(1);
         pg2 = page_of(2);
         pg3 = page_of(3);
-        const std::false_type gen;
+        const std::integral_constant<int, 0> gen;
         load_k(0, 0, pg0, gen);
         load_v(0, 0, pg0, gen);
         load_k(1, 1, pg1, gen);
@@ -420,15 +423,16 @@ __device__ __forceinline__ void prefill_attend_body(const PrefillArgs& a) {
     }
     __syncthreads();
     // one tile: fold S_i (in cur) while S_{i+1} (into nxt) and the next loads run.
-    // fp (compile time): tiles i .. i+3 are full far-field tiles
-    auto step = [&](int i, f32x16_t& cur, f32x16_t& nxt, int X, auto fp) {
-        constexpr bool FP = decltype(fp)::value;
-        const int pg4 = page_of(i + 4);
-        load_k(i + 3, X, pg3, fp);
-        load_v(i + 2, X, pg2, fp);
+    // md (compile time): 1 if tiles i .. i+3 are full far-field tiles, 2 if they
+    // are full band tiles, 0 otherwise
+    auto step = [&](int i, f32x16_t& cur, f32x16_t& nxt, int X, auto md) {
+        constexpr bool FP = decltype(md)::value == 1, BP = decltype(md)::value == 2;
+        const int pg4 = BP ? 0 : page_of(i + 4);
+        load_k(i + 3, X, pg3, md);
+        load_v(i + 2, X, pg2, md);
 
         // ---- fold tile i: row r of S_i holds key kb + (r & 7) + 8 half + 16 (r >> 3)
-        const int kb = FP ? 32 * i : tile_kb(i);
+        const int kb = FP ? 32 * i : BP ? band0 + 32 * (i - nfar) : tile_kb(i);
         // z: the scores (FP8: times the keys' K scales) with invisible keys at
         // -inf, computed in place in S_i's registers (dead after this step)
         f32x16_t& z = cur;
@@ -449,7 +453,7 @@ __device__ __forceinline__ void prefill_attend_body(const PrefillArgs& a) {
                 vsc[r0 + 3] = v4.w;
             }
         }
-        if (EXT && (FP || i < nfar)) {  // stored keys: visible to the rows below their expiry row
+        if (EXT && !BP && (FP || i < nfar)) {  // stored keys: visible to the rows below their expiry row
 #pragma unroll
             for (int q4 = 0; q4 < 4; ++q4) {
                 const int4 x4 = s_x[i & 1][2 * half + (q4 & 1) + 4 * (q4 >> 1)];
@@ -459,12 +463,12 @@ __device__ __forceinline__ void prefill_attend_body(const PrefillArgs& a) {
                 if (tq >= x4.z) z[r0 + 2] = -INFINITY;
                 if (tq >= x4.w) z[r0 + 3] = -INFINITY;
             }
-        } else if (!FP && !(i < nfar && kb + 32 <= U)) {  // (a whole far tile is visible as it is)
+        } else if (!FP && (BP || !(i < nfar && kb + 32 <= U))) {  // (a whole far tile is visible as it is)
             // visible keys of this lane's query as one 32-bit mask over the tile.
             // Last far tile: kb + kr < U.  Band: kb + kr <= tq, kb + kr > xf,
             // and unmarked or kb + kr > tq - w.
             uint32_t vis;
-            if (i < nfar) {
+            if (!BP && i < nfar) {
                 vis = (1u << (U - kb)) - 1u;  // U - kb in [1, 31]
             } else {
                 const uint32_t marks = s_marks[i & 1];
@@ -474,11 +478,15 @@ __device__ __forceinline__ void prefill_attend_body(const PrefillArgs& a) {
                 vis = ~above(tq - kb) & above(xf - kb) & (~marks | above(tq - w - kb));
                 if (tq >= T) vis = 0;
             }
-            vis >>= 8 * half;  // this lane's rows: kr = (r & 7) + 8 half + 16 (r >> 3)
+            // (tiles every query of the wave sees whole, e.g. inside the window and
+            // below the diagonal, keep their scores as they are)
+            if (__ballot(vis != 0xffffffffu)) {
+                vis >>= 8 * half;  // this lane's rows: kr = (r & 7) + 8 half + 16 (r >> 3)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {  // bit -> all-ones or zero, then a bit select
-                const int mk = __builtin_amdgcn_sbfe((int)vis, (r & 7) + 16 * (r >> 3), 1);
-                z[r] = __int_as_float((__float_as_int(z[r]) & mk) | (int)(0xff800000u & ~(uint32_t)mk));
+                for (int r = 0; r < 16; ++r) {  // bit -> all-ones or zero, then a bit select
+                    const int mk = __builtin_amdgcn_sbfe((int)vis, (r & 7) + 16 * (r >> 3), 1);
+                    z[r] = __int_as_float((__float_as_int(z[r]) & mk) | (int)(0xff800000u & ~(uint32_t)mk));
+                }
             }
         }
         float tmax = z[0];
@@ -560,25 +568,36 @@ __device__ __forceinline__ void prefill_attend_body(const PrefillArgs& a) {
         }
         // K_{i+2} replaces K_i (read for S_i one iteration ago), V_{i+1} replaces
         // V_{i-1}; both were loaded in step i-1 (the other register set)
-        if (FP || i + 2 < ntiles) store_k(i + 2, X ^ 1);
-        if (FP || i + 1 < ntiles) store_v(i + 1, X ^ 1, fp);
+        if (FP || BP || i + 2 < ntiles) store_k(i + 2, X ^ 1);
+        if (FP || BP || i + 1 < ntiles) store_v(i + 1, X ^ 1, md);
         pg2 = pg3;
         pg3 = pg4;
         __syncthreads();
     };
     // S and the in-flight loads alternate between two register sets (no copies
     // between iterations)
-    // (the far field first, in steps whose tiles and in-flight loads are all full
-    // far-field tiles, then the general steps)
+    // (steps whose tile and in-flight loads are all full far-field tiles, then
+    // general steps up to the band, steps on full band tiles, general steps)
+    const std::integral_constant<int, 0> gen;
+    const std::integral_constant<int, 1> farc;
+    const std::integral_constant<int, 2> bandc;
     f32x16_t sa = scores(0), sb;
     int i = 0;
-    for (; i + 5 <= nfar - 1; i += 2) {
-        step(i, sa, sb, 0, std::true_type());
-        step(i + 1, sb, sa, 1, std::true_type());
+    for (; i + 6 <= nfar; i += 2) {
+        step(i, sa, sb, 0, farc);
+        step(i + 1, sb, sa, 1, farc);
+    }
+    for (; i < nfar && i < ntiles; i += 2) {
+        step(i, sa, sb, 0, gen);
+        if (i + 1 < ntiles) step(i + 1, sb, sa, 1, gen);
+    }
+    for (; i + 6 <= ntiles; i += 2) {
+        step(i, sa, sb, 0, bandc);
+        step(i + 1, sb, sa, 1, bandc);
     }
     for (; i < ntiles; i += 2) {
-        step(i, sa, sb, 0, std::false_type());
-        if (i + 1 < ntiles) step(i + 1, sb, sa, 1, std::false_type());
+        step(i, sa, sb, 0, gen);
+        if (i + 1 < ntiles) step(i + 1, sb, sa, 1, gen);
     }
 
     // ---- normalise and store: lane holds dims dt*32 + 8*(r/4) + 4*half + r%4 of query tq
