@@ -74,9 +74,13 @@ bool make_layout(const dms_pool_config* c, Layout* L, std::string* why) {
     L->max_items = dms::kMaxAttendBlocks * dms::kAttendWaves + L->max_call_heads;
     const bool fp8 = c->kv_format == DMS_KV_FP8_E4M3;
     size_t sz[S_N];
-    sz[S_K] = (size_t)c->max_pages * dms::kPage * D * (fp8 ? 1 : 2);
+    // K / V pages: the shared pool's max_pages, then pages_per_head scratch pages
+    // per kv head (extend calls gather the chunk's unmarked rows there)
+    const int64_t all_pages = c->max_pages + (int64_t)c->n_kv_heads * L->pages_per_head;
+    if (all_pages > (int64_t)INT32_MAX) return bad("max_pages + n_kv_heads * ceil(max_positions / 64) must be below 2^31");
+    sz[S_K] = (size_t)all_pages * dms::kPage * D * (fp8 ? 1 : 2);
     sz[S_V] = sz[S_K];
-    sz[S_KS] = fp8 ? (size_t)c->max_pages * dms::kPage * 4 : 0;
+    sz[S_KS] = fp8 ? (size_t)all_pages * dms::kPage * 4 : 0;
     sz[S_VS] = sz[S_KS];
     sz[S_POS] = (size_t)c->max_pages * dms::kPage * 4;
     sz[S_STACK] = (size_t)c->max_pages * 4;
@@ -114,7 +118,7 @@ struct dms_pool {
     bool timing = false;
     std::vector<hipEvent_t> events;   // 4 per decode launch while timing (attend, merge start/stop)
     std::vector<hipEvent_t> pevents;  // 6 per prefill with output while timing (compaction, V copy, attend)
-    std::vector<hipEvent_t> xevents;  // 4 per extend with output while timing (V copy, attend)
+    std::vector<hipEvent_t> xevents;  // 4 per extend with output while timing (preparation, attend)
     Layout layout;
     dms::PoolDev dev;
     char* arena;

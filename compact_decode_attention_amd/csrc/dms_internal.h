@@ -1,16 +1,19 @@
 // Internal layout of a DMS pool and the kernel launchers (not part of the ABI).
 //
-// Arena layout (every section 256-byte aligned).  K/V pages of bf16 pools:
-//   kpages   bf16 [max_pages][head_dim/8][64][8]   K, 16-byte dim chunks, key-major:
+// Arena layout (every section 256-byte aligned).  The page arrays (K, V and FP8
+// scales) hold NP = max_pages + n_kv_heads * pages_per_head pages: the shared
+// pool, then pages_per_head scratch pages per kv head, where an extend call
+// gathers the chunk's unmarked rows (xpage(h) below).  K/V pages of bf16 pools:
+//   kpages   bf16 [NP][head_dim/8][64][8]          K, 16-byte dim chunks, key-major:
 //                                                  chunk c of 64 consecutive slots is
 //                                                  1 KB contiguous (lane = slot loads)
-//   vpages   bf16 [max_pages][8][head_dim][8]      V, 8-slot blocks, dim-major: the
+//   vpages   bf16 [NP][8][head_dim][8]             V, 8-slot blocks, dim-major: the
 //                                                  16 bytes at (block, d) are 8
 //                                                  consecutive slots of dim d
 // K/V pages of FP8 pools (E4M3 codes, one fp32 scale per slot):
-//   kpages   u8   [max_pages][head_dim/16][64][16] K, 16 dims per 16-byte chunk, key-major
-//   vpages   u8   [max_pages][4][head_dim][16]     V, 16-slot blocks, dim-major
-//   kscale   f32  [max_pages][64], vscale f32 [max_pages][64]
+//   kpages   u8   [NP][head_dim/16][64][16]        K, 16 dims per 16-byte chunk, key-major
+//   vpages   u8   [NP][4][head_dim][16]            V, 16-slot blocks, dim-major
+//   kscale   f32  [NP][64], vscale f32 [NP][64]
 //   q8       prefill scratch: the prompt quantised, codes u8 [2][max_positions]
 //            [n_kv_heads][head_dim] (K, V) then scales f32 [2][max_positions][n_kv_heads]
 //   slot_pos int32 [max_pages][64]                 position held by each slot
@@ -24,7 +27,8 @@
 //   prefix   int32 [max_call_heads + 1]            first page of each call head on the page
 //                                                  axis of the last decode launch
 //   inv      int32 [n_kv_heads][max_positions]     prefill scratch: slot -> position
-//   pcnt     int32 [n_kv_heads][max_positions]     prefill scratch: live tokens in [0, s]
+//   pcnt     int32 [n_kv_heads][max_positions]     prefill scratch: live tokens in [0, s]; extend
+//                                                  calls: unmarked chunk rows in [0, r]
 //   vt       bf16 [n_kv_heads][max_pos32/8][head_dim][8]
 //                                                  prefill scratch: the prompt's V (FP8 pools:
 //                                                  its codes as bf16) with 8 consecutive tokens
@@ -120,6 +124,8 @@ struct PoolDev {
         return reinterpret_cast<float*>(q8 + (size_t)2 * max_positions * n_kv_heads * head_dim) +
                (size_t)x * max_positions * n_kv_heads;
     }
+    // first scratch page of kv head h (extend calls: the chunk's unmarked rows, in order)
+    __host__ __device__ int xpage(int h) const { return (int)max_pages + h * pages_per_head; }
 };
 
 // ---- raw buffer loads ----------------------------------------------------------
@@ -240,10 +246,13 @@ hipError_t launch_prefill_compact(const PrefillArgs& a, hipStream_t s, hipEvent_
 // ev (optional, 4 events): start/stop of the V copy kernel, then of the attention kernel
 hipError_t launch_prefill_attend(const PrefillArgs& a, hipStream_t s, hipEvent_t* ev);
 // extend calls (several new tokens of one (seq, layer) appended to its store):
-// the prompt-side kernels of the chunk (FP8: quantisation; with output: V copy
-// and the attention of the chunk's queries over the store and the chunk),
-// then the slot assignment, page allocation, ring and record, then the writes
+// the prompt-side kernels of the chunk (FP8: quantisation; with output: one
+// preparation kernel -- V copy, expiry rows of the stored slots, the chunk's
+// unmarked rows gathered into the scratch pages -- and the attention of the
+// chunk's queries over the store and the chunk), then the slot assignment, page
+// allocation, ring and record, then the writes
 hipError_t launch_extend(const PrefillArgs& a, bool with_out, hipStream_t s, hipEvent_t* ev);
+// ev (optional, 4 events): start/stop of the preparation kernel, then of the attention kernel
 hipError_t launch_extend_attend(const PrefillArgs& a, hipStream_t s, hipEvent_t* ev);
 hipError_t launch_seq_release(const PoolDev& p, int32_t seq, hipStream_t s);
 int device_cu_count();

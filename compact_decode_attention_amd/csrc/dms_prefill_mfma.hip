@@ -96,11 +96,11 @@ __device__ __forceinline__ int swap23(int i) { return (i & ~12) | ((i & 4) << 1)
 // kCtlVWide flag, which keeps the attention on its bf16 path.
 // ---------------------------------------------------------------------------
 template <int D, bool F8>
-__global__ __launch_bounds__(256) void prefill_vt_kernel(PrefillArgs a) {
+__device__ __forceinline__ void vt_block(const PrefillArgs& a, int bx, int h) {
     const PoolDev& P = a.pool;
     __shared__ uint16_t s_v[64][D + 8];
     const int tid = threadIdx.x;
-    const int s0 = blockIdx.x * 64, h = blockIdx.y;
+    const int s0 = bx * 64;
     const int T = a.n_tokens, hkv = P.n_kv_heads;
     const int T32 = (T + 31) / 32 * 32;
     constexpr int NC = D / 8;
@@ -131,6 +131,11 @@ __global__ __launch_bounds__(256) void prefill_vt_kernel(PrefillArgs a) {
             w4[i] = (uint32_t)s_v[8 * b + 2 * i][d] | ((uint32_t)s_v[8 * b + 2 * i + 1][d] << 16);
         *reinterpret_cast<uint4*>(vt + ((size_t)blk * D + d) * 8) = make_uint4(w4[0], w4[1], w4[2], w4[3]);
     }
+}
+
+template <int D, bool F8>
+__global__ __launch_bounds__(256) void prefill_vt_kernel(PrefillArgs a) {
+    vt_block<D, F8>(a, blockIdx.x, blockIdx.y);
 }
 
 // ---------------------------------------------------------------------------
@@ -216,11 +221,18 @@ __device__ __forceinline__ void prefill_attend_body(const PrefillArgs& a) {
         qb[ks] = tq < T ? *reinterpret_cast<const uint4*>(a.q + ((size_t)tq * hq_n + hq) * D + ks * 16 + half * 8)
                         : make_uint4(0, 0, 0, 0);
 
-    // ---- the block's key tiles
-    const int xf = EXT ? -1 : t0b - w;
+    // ---- the block's key tiles: far field, then the band (xf, kend) of prompt rows.
+    // Prefill: the far field is the first U slots of the compacted store (the
+    // unmarked keys at or below xf).  Extend: the U stored slots (each visible to
+    // the rows below its expiry row), then the first Uc gathered unmarked rows of
+    // the chunk (those at or below xf) in the scratch pages.
+    const int xf = t0b - w;
     const int U = EXT ? P.hstate[(size_t)gh * kHS + kHsLive]
                       : (xf >= 0 ? P.pcnt[(size_t)h * P.max_positions + xf] : 0);
-    const int nfar = (U + 31) / 32;
+    const int Uc = EXT && xf >= 0 ? P.pcnt[(size_t)h * P.max_positions + xf] : 0;
+    const int Ufar = EXT ? Uc : U;  // slots of the unmasked far segment (its last tile is cut at Ufar)
+    const int nfar1 = (U + 31) / 32;
+    const int nfar = nfar1 + (Uc + 31) / 32;
     const int band0 = max(0, xf + 1) / 32 * 32;
     const int kend = min(T, t0b + 32 * QT);
     const int ntiles = nfar + (kend > band0 ? (kend - band0 + 31) / 32 : 0);
@@ -239,7 +251,8 @@ __device__ __forceinline__ void prefill_attend_body(const PrefillArgs& a) {
     // rows past the prompt, units past the tile and tiles past the last are
     // read through short or zero-size resources, return 0 and touch no memory,
     // so each step issues the same loads and waits only for the older set.
-    auto tile_kb = [&](int i) { return i < nfar ? 32 * i : band0 + 32 * (i - nfar); };
+    // (far tiles: slot of the first key within the tile's segment; band: prompt row)
+    auto tile_kb = [&](int i) { return i < nfar1 ? 32 * i : i < nfar ? 32 * (i - nfar1) : band0 + 32 * (i - nfar); };
     // (Loaded values stay untouched in their registers until they are written:
     // any use would make the wave wait for them in the step that issues them.)
     uint4 rk[2][UPT], rv[2][UPT];
@@ -261,7 +274,9 @@ __device__ __forceinline__ void prefill_attend_body(const PrefillArgs& a) {
     // here), so it is counted with the LDS operations, not with the tile loads
     typedef const int32_t __attribute__((address_space(4))) cint32_t;
     cint32_t* cptab = (cint32_t*)ptab;
-    auto page_of = [&](int t) -> int { return t < nfar ? cptab[(32 * t) / kPage] : 0; };
+    auto page_of = [&](int t) -> int {
+        return t < nfar1 ? cptab[(32 * t) / kPage] : t < nfar ? P.xpage(h) + (32 * (t - nfar1)) / kPage : 0;
+    };
     auto upage = [](int pg) -> size_t { return (size_t)(uint32_t)__builtin_amdgcn_readfirstlane(pg); };
     auto rows_left = [&](int kb) { return kb + 32 <= T ? 32 : kb < T ? T - kb : 0; };  // prompt rows kb .. kb+31
     const __amdgpu_buffer_rsrc_t rx_rsrc = rsrc(P.inv + (size_t)h * P.max_positions, EXT ? U * 4 : 0);
@@ -341,7 +356,7 @@ __device__ __forceinline__ void prefill_attend_body(const PrefillArgs& a) {
             const __amdgpu_buffer_rsrc_t r = rsrc(a.logits + (size_t)kb * hkv + h, band ? rows * hkv * 4 : 0);
             rlg[X] = (uint32_t)buffer_load4i(r, kl * hkv * 4);
         }
-        if constexpr (EXT && !BP) rx[X] = buffer_load4i(rx_rsrc, (kb + kl) * 4 + (live && far ? 0 : kFar));
+        if constexpr (EXT && !BP) rx[X] = buffer_load4i(rx_rsrc, (kb + kl) * 4 + (live && (FP || i < nfar1) ? 0 : kFar));
         if constexpr (F8) {
             if (far) {
                 const size_t sl0 = upage(pg) * kPage + kb % kPage;
@@ -379,7 +394,8 @@ __device__ __forceinline__ void prefill_attend_body(const PrefillArgs& a) {
             if (lane == 0) s_marks[i & 1] = mk;
         }
         if constexpr (EXT) {
-            if (tid < 32 && far) reinterpret_cast<int*>(s_x[i & 1])[tid] = tile_kb(i) + tid < U ? rx[X] : INT_MIN;
+            if (tid < 32 && (MD == 1 || (MD != 2 && i < nfar1)))
+                reinterpret_cast<int*>(s_x[i & 1])[tid] = tile_kb(i) + tid < U ? rx[X] : INT_MIN;
         }
         if constexpr (F8) {
             if (tid < 32) {
@@ -453,7 +469,7 @@ __device__ __forceinline__ void prefill_attend_body(const PrefillArgs& a) {
                 vsc[r0 + 3] = v4.w;
             }
         }
-        if (EXT && !BP && (FP || i < nfar)) {  // stored keys: visible to the rows below their expiry row
+        if (EXT && !BP && (FP || i < nfar1)) {  // stored keys: visible to the rows below their expiry row
 #pragma unroll
             for (int q4 = 0; q4 < 4; ++q4) {
                 const int4 x4 = s_x[i & 1][2 * half + (q4 & 1) + 4 * (q4 >> 1)];
@@ -463,13 +479,13 @@ __device__ __forceinline__ void prefill_attend_body(const PrefillArgs& a) {
                 if (tq >= x4.z) z[r0 + 2] = -INFINITY;
                 if (tq >= x4.w) z[r0 + 3] = -INFINITY;
             }
-        } else if (!FP && (BP || !(i < nfar && kb + 32 <= U))) {  // (a whole far tile is visible as it is)
+        } else if (!FP && (BP || !(i < nfar && kb + 32 <= Ufar))) {  // (a whole far tile is visible as it is)
             // visible keys of this lane's query as one 32-bit mask over the tile.
-            // Last far tile: kb + kr < U.  Band: kb + kr <= tq, kb + kr > xf,
+            // Last far tile: kb + kr < Ufar.  Band: kb + kr <= tq, kb + kr > xf,
             // and unmarked or kb + kr > tq - w.
             uint32_t vis;
             if (!BP && i < nfar) {
-                vis = (1u << (U - kb)) - 1u;  // U - kb in [1, 31]
+                vis = (1u << (Ufar - kb)) - 1u;  // Ufar - kb in [1, 31]
             } else {
                 const uint32_t marks = s_marks[i & 1];
                 auto above = [](int c) -> uint32_t {  // bits kr > c
@@ -583,7 +599,7 @@ __device__ __forceinline__ void prefill_attend_body(const PrefillArgs& a) {
     const std::integral_constant<int, 2> bandc;
     f32x16_t sa = scores(0), sb;
     int i = 0;
-    for (; i + 6 <= nfar; i += 2) {
+    for (; i + 6 <= nfar1; i += 2) {
         step(i, sa, sb, 0, farc);
         step(i + 1, sb, sa, 1, farc);
     }
@@ -635,11 +651,11 @@ void prefill_attend_kernel(PrefillArgs a) {
 // marked (its mark is in the window ring while it is within w of t0), else
 // INT_MAX.  Written to the inv scratch ([kv head][slot]), which the attention
 // reads per far-field tile and the chain resolution overwrites afterwards.
-__global__ __launch_bounds__(256) void extend_expiry_kernel(PrefillArgs a) {
+__device__ __forceinline__ void expiry_block(const PrefillArgs& a, int bx, int h) {
     const PoolDev& P = a.pool;
-    const int h = blockIdx.y, w = P.window;
+    const int w = P.window;
     const int gh = (a.seq * P.n_layers + a.layer) * P.n_kv_heads + h;
-    const int j = blockIdx.x * 256 + threadIdx.x;
+    const int j = bx * 256 + threadIdx.x;
     if (j >= P.hstate[(size_t)gh * kHS + kHsLive]) return;
     const int page = P.ptable[(size_t)gh * P.pages_per_head + j / kPage];
     const int pos = P.slot_pos[(size_t)page * kPage + j % kPage];
@@ -649,6 +665,118 @@ __global__ __launch_bounds__(256) void extend_expiry_kernel(PrefillArgs a) {
         mk = e >= 0 && (e & 1);
     }
     P.inv[(size_t)h * P.max_positions + j] = mk ? pos + w - a.t0 : INT_MAX;
+}
+
+// Extend calls with output: the chunk's unmarked rows (never evicted, so every
+// query at least w rows later sees them) gathered in row order into the scratch
+// pages of their kv head, with the running count of unmarked rows per row in
+// pcnt.  The attention reads them as a dense far field, as the prefill reads
+// the compacted prompt.  Block bx of kv head h: rows 64bx .. 64bx+63; it
+// counts the unmarked rows before its segment itself (up to 8 logits per thread
+// per pass, all requested before any is used), and every copy load is issued
+// before the stores.
+template <int D, bool F8>
+__device__ __forceinline__ void compact_block(const PrefillArgs& a, int bx, int h) {
+    const PoolDev& P = a.pool;
+    __shared__ int s_prev[4];  // per wave: unmarked rows before the segment
+    __shared__ int s_row[64];  // the segment's unmarked rows, in order
+    __shared__ int s_n;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, r0 = bx * 64;
+    const int T = a.n_tokens, hkv = P.n_kv_heads;
+    int prev = 0;  // unmarked rows in [0, r0) seen by this wave (wave-uniform)
+    for (int c0 = 0; c0 < r0; c0 += 2048) {
+        bool u[8];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            const int c = c0 + 256 * k + tid;
+            u[k] = c < r0 && !(eviction_logit(P, a.logits, a.k, c, h) > 0.f);
+        }
+#pragma unroll
+        for (int k = 0; k < 8; ++k) prev += __popcll(__ballot(u[k]));
+    }
+    if (lane == 0) s_prev[wave] = prev;
+    const int r = r0 + lane;  // wave 0: the segment's rows
+    bool um = false;
+    int rank = 0;
+    if (wave == 0) {
+        um = r < T && !(eviction_logit(P, a.logits, a.k, r, h) > 0.f);
+        const uint64_t b = __ballot(um);
+        rank = __builtin_amdgcn_mbcnt_hi((uint32_t)(b >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)b, 0));
+        if (um) s_row[rank] = r;
+        if (lane == 0) s_n = __popcll(b);
+    }
+    __syncthreads();
+    const int n = s_n, base = s_prev[0] + s_prev[1] + s_prev[2] + s_prev[3];
+    if (wave == 0 && r < T) P.pcnt[(size_t)h * P.max_positions + r] = base + rank + (um ? 1 : 0);
+    const int xp = P.xpage(h);
+    if constexpr (F8) {
+        constexpr int NC = D / 16;
+        for (int u = tid; u < n * NC; u += 256) {  // K: 16 codes per chunk
+            const int j = u / NC, cc = u - j * NC, slot = base + j;
+            const size_t row = (size_t)s_row[j] * hkv + h;
+            uint8_t* kp = P.kp8() + (size_t)(xp + slot / kPage) * (kPage * D);
+            *reinterpret_cast<uint4*>(kp + ((size_t)cc * kPage + slot % kPage) * 16) =
+                *reinterpret_cast<const uint4*>(P.q8_codes(0) + row * D + cc * 16);
+        }
+        for (int u = tid; u < n * D; u += 256) {  // V: one code per (row, dim)
+            const int j = u / D, d = u - j * D, slot = base + j;
+            const size_t row = (size_t)s_row[j] * hkv + h;
+            uint8_t* vp = P.vp8() + (size_t)(xp + slot / kPage) * (kPage * D);
+            vp[((size_t)(slot % kPage / 16) * D + d) * 16 + slot % 16] = P.q8_codes(1)[row * D + d];
+        }
+        if (tid < n) {
+            const int slot = base + tid;
+            const size_t row = (size_t)s_row[tid] * hkv + h, sl = (size_t)(xp + slot / kPage) * kPage + slot % kPage;
+            P.kscale[sl] = P.q8_scales(0)[row];
+            P.vscale[sl] = P.q8_scales(1)[row];
+        }
+    } else {
+        // item u < n NC: K chunk u % NC of row u / NC; then the same for V
+        constexpr int NC = D / 8, IT = (64 * 2 * NC) / 256;
+        uint4 x[IT];
+#pragma unroll
+        for (int k = 0; k < IT; ++k) {
+            const int u = tid + 256 * k, uv = u - n * NC;
+            const bool isk = u < n * NC, isv = !isk && uv < n * NC;
+            const int j = isk ? u / NC : uv / NC, cc = isk ? u % NC : uv % NC;
+            x[k] = make_uint4(0, 0, 0, 0);
+            if (isk || isv) {
+                const size_t row = (size_t)s_row[j] * hkv + h;
+                x[k] = *reinterpret_cast<const uint4*>((isk ? a.k : a.v) + row * D + cc * 8);
+            }
+        }
+#pragma unroll
+        for (int k = 0; k < IT; ++k) {
+            const int u = tid + 256 * k, uv = u - n * NC;
+            const bool isk = u < n * NC, isv = !isk && uv < n * NC;
+            if (!isk && !isv) continue;
+            const int j = isk ? u / NC : uv / NC, cc = isk ? u % NC : uv % NC, slot = base + j;
+            if (isk) {
+                uint16_t* kp = P.kpages + (size_t)(xp + slot / kPage) * (kPage * D);
+                *reinterpret_cast<uint4*>(kp + ((size_t)cc * kPage + slot % kPage) * 8) = x[k];
+            } else {  // V: 8 dims of the row, one value per 8-slot unit
+                uint16_t* vp = P.vpages + (size_t)(xp + slot / kPage) * (kPage * D) +
+                               (size_t)(slot % kPage / 8) * D * 8 + slot % 8;
+                const uint32_t xw[4] = {x[k].x, x[k].y, x[k].z, x[k].w};
+#pragma unroll
+                for (int q = 0; q < 8; ++q)
+                    vp[(size_t)(cc * 8 + q) * 8] = (uint16_t)(q & 1 ? xw[q / 2] >> 16 : xw[q / 2] & 0xffffu);
+            }
+        }
+    }
+}
+
+
+// Extend calls with output: the three independent preparations of the attention
+// in one launch, blocks (x, kv head): the V copy of the chunk (x < NV), the
+// expiry rows of the stored slots (next NE), the gathered unmarked rows (rest).
+template <int D, bool F8>
+__global__ __launch_bounds__(256) void extend_prep_kernel(PrefillArgs a) {
+    const int nv = (a.n_tokens + 63) / 64, ne = max(1, (a.t0 + 255) / 256);
+    const int bx = blockIdx.x, h = blockIdx.y;
+    if (bx < nv) vt_block<D, F8>(a, bx, h);
+    else if (bx < nv + ne) expiry_block(a, bx - nv, h);
+    else compact_block<D, F8>(a, bx - nv - ne, h);
 }
 
 template <int D, int G, bool EXT>
@@ -668,20 +796,27 @@ hipError_t launch_attend_t(const PrefillArgs& a, hipStream_t s, hipEvent_t* ev) 
 
 template <int D, bool EXT>
 hipError_t launch_attend_d(const PrefillArgs& a, hipStream_t s, hipEvent_t* ev) {
-    const dim3 vgrid((a.n_tokens + 63) / 64, a.pool.n_kv_heads);
-    if (a.pool.fp8)
-        hipExtLaunchKernelGGL((prefill_vt_kernel<D, true>), vgrid, dim3(256), 0, s, ev ? ev[0] : nullptr,
-                              ev ? ev[1] : nullptr, 0, a);
-    else
-        hipExtLaunchKernelGGL((prefill_vt_kernel<D, false>), vgrid, dim3(256), 0, s, ev ? ev[0] : nullptr,
-                              ev ? ev[1] : nullptr, 0, a);
+    const int nv = (a.n_tokens + 63) / 64;
+    // extend: the store holds at most t0 slots per head (expiry rows), and the
+    // chunk's rows are gathered 64 per block
+    const dim3 vgrid(EXT ? nv + std::max(1, (a.t0 + 255) / 256) + nv : nv, a.pool.n_kv_heads);
+    if (a.pool.fp8) {
+        if (EXT)
+            hipExtLaunchKernelGGL((extend_prep_kernel<D, true>), vgrid, dim3(256), 0, s, ev ? ev[0] : nullptr,
+                                  ev ? ev[1] : nullptr, 0, a);
+        else
+            hipExtLaunchKernelGGL((prefill_vt_kernel<D, true>), vgrid, dim3(256), 0, s, ev ? ev[0] : nullptr,
+                                  ev ? ev[1] : nullptr, 0, a);
+    } else {
+        if (EXT)
+            hipExtLaunchKernelGGL((extend_prep_kernel<D, false>), vgrid, dim3(256), 0, s, ev ? ev[0] : nullptr,
+                                  ev ? ev[1] : nullptr, 0, a);
+        else
+            hipExtLaunchKernelGGL((prefill_vt_kernel<D, false>), vgrid, dim3(256), 0, s, ev ? ev[0] : nullptr,
+                                  ev ? ev[1] : nullptr, 0, a);
+    }
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
-    if (EXT) {  // the store holds at most t0 slots per head
-        hipLaunchKernelGGL(extend_expiry_kernel, dim3((unsigned)std::max(1, (a.t0 + 255) / 256), a.pool.n_kv_heads),
-                           dim3(256), 0, s, a);
-        if ((err = hipGetLastError()) != hipSuccess) return err;
-    }
     switch (a.pool.n_q_heads / a.pool.n_kv_heads) {
         case 1: return launch_attend_t<D, 1, EXT>(a, s, ev);
         case 2: return launch_attend_t<D, 2, EXT>(a, s, ev);

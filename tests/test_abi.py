@@ -113,8 +113,10 @@ def test_kv_format_is_checked():
 
 def test_fp8_pool_holds_codes_and_scales():
     """An FP8 pool's pages take head_dim + 4 bytes per row (codes and an fp32
-    scale) instead of 2 * head_dim, plus the prompt scratch for its codes."""
-    pages = 36 * 8 * 131
+    scale) instead of 2 * head_dim, plus the prompt scratch for its codes.  The
+    page arrays hold the shared pool and ceil(max_positions / 64) scratch pages
+    per kv head."""
+    pages = 36 * 8 * 131 + 8 * 130
     b16 = dms.dms_pool_bytes(qwen_cfg())
     f8 = dms.dms_pool_bytes(qwen_cfg(kv_format=dms.DMS_KV_FP8_E4M3))
     saved = 2 * pages * 64 * (2 * 128 - (128 + 4))
