@@ -248,3 +248,20 @@ def test_extend_chunk_beyond_the_lds_rows():
     its chain arrays live in the scratch), w = 7 with random marks: chains of
     ~700 reuses, outputs and the store against the oracle."""
     run_extend(64, [5000], 7, marks="random", Hkv=1, G=2, D=64, seed=21)
+
+
+@pytest.mark.parametrize("kv_format", [0, 1])
+def test_extend_gathered_rows_span_several_scratch_pages(kv_format):
+    """Unmarked chunk rows at least w rows before a query block are read from
+    the kv head's scratch pages they were gathered into.  With no token marked
+    and w = 16, a 700-row chunk gathers up to ~680 rows per kv head (11 pages,
+    a partial last tile), for both kv heads; a second chunk reuses the same
+    scratch pages with a shorter gather.  bf16 and FP8 pools."""
+    run_extend(40, [700, 90], 16, marks="none", kv_format=kv_format, seed=31 + kv_format)
+
+
+def test_extend_gathered_rows_with_mixed_marks_and_long_window():
+    """w = 128 and random marks: the gathered segment holds the unmarked rows at
+    or below each block's first row - w, the band the 160 rows after; chunk
+    sizes that are not multiples of 32 or 64."""
+    run_extend(300, [517, 3, 250], 128, marks="random", seed=41)
