@@ -303,8 +303,9 @@ __device__ __forceinline__ void prefill_attend_body(const PrefillArgs& a) {
     const char* const kband0 = F8 ? reinterpret_cast<const char*>(P.q8_codes(0) + h * D)
                                   : reinterpret_cast<const char*>(a.k + h * D);
     const int rowb = (int)rowk * EB;  // bytes from one prompt row of K to the next
-    // md (compile time): 1 if tile i is a full far-field tile, 2 if it is a full
-    // band tile (32 prompt rows), 0 if either may hold
+    // md (compile time): 1 if tile i is a full tile of the first far-field
+    // segment (the compacted prompt; extend: the stored slots), 2 if it is a full
+    // band tile (32 prompt rows), 0 if any kind may hold
     auto load_k = [&](int i, int X, int pg, auto md) {
         constexpr bool FP = decltype(md)::value == 1, BP = decltype(md)::value == 2;
         const int kb = FP ? 32 * i : BP ? band0 + 32 * (i - nfar) : tile_kb(i);
@@ -439,8 +440,8 @@ __device__ __forceinline__ void prefill_attend_body(const PrefillArgs& a) {
     }
     __syncthreads();
     // one tile: fold S_i (in cur) while S_{i+1} (into nxt) and the next loads run.
-    // md (compile time): 1 if tiles i .. i+3 are full far-field tiles, 2 if they
-    // are full band tiles, 0 otherwise
+    // md (compile time): 1 if tiles i .. i+3 are full tiles of the first
+    // far-field segment, 2 if they are full band tiles, 0 otherwise
     auto step = [&](int i, f32x16_t& cur, f32x16_t& nxt, int X, auto md) {
         constexpr bool FP = decltype(md)::value == 1, BP = decltype(md)::value == 2;
         const int pg4 = BP ? 0 : page_of(i + 4);
@@ -592,8 +593,9 @@ __device__ __forceinline__ void prefill_attend_body(const PrefillArgs& a) {
     };
     // S and the in-flight loads alternate between two register sets (no copies
     // between iterations)
-    // (steps whose tile and in-flight loads are all full far-field tiles, then
-    // general steps up to the band, steps on full band tiles, general steps)
+    // (steps whose tile and in-flight loads are all full tiles of the first
+    // far-field segment, then general steps up to the band (extend: through the
+    // gathered chunk rows), steps on full band tiles, general steps)
     const std::integral_constant<int, 0> gen;
     const std::integral_constant<int, 1> farc;
     const std::integral_constant<int, 2> bandc;
