@@ -117,7 +117,7 @@ struct dms_pool {
     dms_pool_config cfg;
     bool timing = false;
     std::vector<hipEvent_t> events;   // 4 per decode launch while timing (attend, merge start/stop)
-    std::vector<hipEvent_t> pevents;  // 6 per prefill with output while timing (compaction, V copy, attend)
+    std::vector<hipEvent_t> pevents;  // 4 per prefill with output while timing (compaction with V copy, attend)
     std::vector<hipEvent_t> xevents;  // 4 per extend with output while timing (preparation, attend)
     Layout layout;
     dms::PoolDev dev;
@@ -285,10 +285,10 @@ dms_status dms_prefill(dms_pool* pool, int32_t seq, int32_t layer, int32_t n_tok
     hipError_t e = hipSuccess;
     hipEvent_t* ev = nullptr;
     if (pool->timing && out) {
-        ev = timing_events(pool->pevents, 6, &e);
+        ev = timing_events(pool->pevents, 4, &e);
         if (!ev) return hip_fail(e, "timing event");
     }
-    e = dms::launch_prefill_compact(a, s, ev ? ev[0] : nullptr, ev ? ev[1] : nullptr);
+    e = dms::launch_prefill_compact(a, out != nullptr, s, ev ? ev[0] : nullptr, ev ? ev[1] : nullptr);
     if (e != hipSuccess) return hip_fail(e, "prefill compaction launch");
     if (out) {
         e = dms::launch_prefill_attend(a, s, ev ? ev + 2 : nullptr);
@@ -598,8 +598,8 @@ dms_status dms_timing_read(dms_pool* pool, dms_timing* out) {
     const int dslot[2] = {0, 1};
     e = sum(pool->events, 4, dslot, dacc, &out->decode_launches);
     double* pacc[2] = {&out->prefill_compact_ms, &out->prefill_attend_ms};
-    const int pslot[3] = {0, 0, 1};  // compaction + V copy, attention
-    if (e == hipSuccess) e = sum(pool->pevents, 6, pslot, pacc, &out->prefill_calls);
+    const int pslot[2] = {0, 1};  // compaction with the V copy, attention
+    if (e == hipSuccess) e = sum(pool->pevents, 4, pslot, pacc, &out->prefill_calls);
     double vcopy = 0;
     double* xacc[2] = {&vcopy, &out->extend_attend_ms};
     const int xslot[2] = {0, 1};

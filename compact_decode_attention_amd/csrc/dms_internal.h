@@ -236,14 +236,63 @@ struct PrefillArgs {
     int32_t t0;  // extend calls: position of input row 0 (the head's position counter); prefill: 0
 };
 
+// ---------------------------------------------------------------------------
+// prompt V -> vt[h][s/8][d][8] (8 consecutive tokens of one dim per 16 bytes),
+// zero beyond the prompt up to the next multiple of 32.  FP8 pools: the values
+// of the prompt V's codes (exact in bf16; the row scales are applied to P).
+// bf16 pools: a V value without an fp16 counterpart sets the pool's sticky
+// kCtlVWide flag, which keeps the attention on its bf16 path.
+// ---------------------------------------------------------------------------
+// Rows s0 .. s0+63 of kv head h, by the 256 threads of a block (all of them
+// call it together: it synchronises the block once), staged in s_v.
+template <int D, bool F8>
+__device__ __forceinline__ void vt_rows(const PrefillArgs& a, int s0, int h, uint16_t (*s_v)[D + 8]) {
+    const PoolDev& P = a.pool;
+    const int tid = threadIdx.x;
+    const int T = a.n_tokens, hkv = P.n_kv_heads;
+    const int T32 = (T + 31) / 32 * 32;
+    constexpr int NC = D / 8;
+    uint32_t wide = 0;
+    for (int u = tid; u < 64 * NC; u += 256) {
+        const int j = u / NC, cc = u - j * NC;
+        const int s = s0 + j;
+        uint4 val = make_uint4(0, 0, 0, 0);
+        if (s < T) {
+            if constexpr (F8)
+                val = fp8x8_bf16(*reinterpret_cast<const uint2*>(P.q8_codes(1) + ((size_t)s * hkv + h) * D + cc * 8));
+            else
+                val = *reinterpret_cast<const uint4*>(a.v + ((size_t)s * hkv + h) * D + cc * 8);
+        }
+        if (!F8) wide |= bf16x8_wide(val);
+        *reinterpret_cast<uint4*>(&s_v[j][cc * 8]) = val;
+    }
+    if (wide) atomicOr(&P.ctl[kCtlVWide], 1);
+    __syncthreads();
+    uint16_t* vt = P.vt + (size_t)h * (P.max_pos32 / 8) * D * 8;
+    for (int u = tid; u < 8 * D; u += 256) {
+        const int b = u / D, d = u - b * D;
+        const int blk = s0 / 8 + b;
+        if (blk * 8 >= T32) continue;
+        uint32_t w4[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            w4[i] = (uint32_t)s_v[8 * b + 2 * i][d] | ((uint32_t)s_v[8 * b + 2 * i + 1][d] << 16);
+        *reinterpret_cast<uint4*>(vt + ((size_t)blk * D + d) * 8) = make_uint4(w4[0], w4[1], w4[2], w4[3]);
+    }
+}
+
+
 // ev (optional, 4 events): start/stop of the attention kernel and of the merge
 // kernel, taken by the kernel dispatches (execution time only)
 hipError_t launch_decode(const DecodeArgs& a, int grid, hipStream_t s, hipEvent_t* ev);
 // blocks of the attention kernel one compute unit holds at once for this call (0: does not fit)
 int decode_blocks_per_cu(const DecodeArgs& a);
-// start / stop (optional): taken by the first and the last kernel dispatch
-hipError_t launch_prefill_compact(const PrefillArgs& a, hipStream_t s, hipEvent_t start, hipEvent_t stop);
-// ev (optional, 4 events): start/stop of the V copy kernel, then of the attention kernel
+// start / stop (optional): taken by the first and the last kernel dispatch.
+// with_vt: the compaction launch also copies the prompt V for the attention's band
+hipError_t launch_prefill_compact(const PrefillArgs& a, bool with_vt, hipStream_t s, hipEvent_t start,
+                                  hipEvent_t stop);
+// after launch_prefill_compact with with_vt; ev (optional, 2 events): start/stop of
+// the attention kernel
 hipError_t launch_prefill_attend(const PrefillArgs& a, hipStream_t s, hipEvent_t* ev);
 // extend calls (several new tokens of one (seq, layer) appended to its store):
 // the prompt-side kernels of the chunk (FP8: quantisation; with output: one

@@ -1045,12 +1045,19 @@ __global__ __launch_bounds__(1024) void prefill_scan_kernel(PrefillArgs a) {
 }
 
 // Gather the live rows into the head's pages: one block per destination page.
+// Blocks past the prompt's page count copy the prompt V for the attention's band
+// instead (vt_rows), alongside the gathering.
 template <int D>
 __global__ __launch_bounds__(256) void prefill_compact_kernel(PrefillArgs a) {
     constexpr int NC = D / 8;
     const PoolDev& P = a.pool;
     __shared__ int s_src[kPage];
     __shared__ uint16_t s_v[kPage][D + 8];
+    const int ncomp = (a.n_tokens + kPage - 1) / kPage;  // blocks past these copy the prompt V
+    if ((int)blockIdx.x >= ncomp) {
+        vt_rows<D, false>(a, ((int)blockIdx.x - ncomp) * 64, blockIdx.y, s_v);
+        return;
+    }
     const int tid = threadIdx.x;
     const int pj = blockIdx.x, h = blockIdx.y;
     const int hkv = P.n_kv_heads;
@@ -1132,12 +1139,19 @@ __global__ __launch_bounds__(256) void prefill_quant_kernel(PrefillArgs a) {
 // FP8 pools: gather the live rows' codes and scales into the head's pages, one
 // block per destination page (K chunks of 16 dims key-major; V through LDS into
 // 16-slot dim-major units).  Slots past the live count get zero codes and scales.
+// Blocks past the prompt's page count copy the values of the prompt V's codes.
 template <int D>
 __global__ __launch_bounds__(256) void prefill_compact8_kernel(PrefillArgs a) {
     constexpr int NC = D / 16;
     const PoolDev& P = a.pool;
     __shared__ int s_src[kPage];
     __shared__ __attribute__((aligned(16))) uint8_t s_v[kPage][D + 16];
+    __shared__ uint16_t s_vt[kPage][D + 8];
+    const int ncomp = (a.n_tokens + kPage - 1) / kPage;  // blocks past these copy the prompt V's values
+    if ((int)blockIdx.x >= ncomp) {
+        vt_rows<D, true>(a, ((int)blockIdx.x - ncomp) * 64, blockIdx.y, s_vt);
+        return;
+    }
     const int tid = threadIdx.x;
     const int pj = blockIdx.x, h = blockIdx.y;
     const int hkv = P.n_kv_heads;
@@ -1480,7 +1494,8 @@ int decode_blocks_per_cu(const DecodeArgs& a) {
     return a.pool.head_dim == 128 ? blocks_per_cu_d<128>(a) : blocks_per_cu_d<64>(a);
 }
 
-hipError_t launch_prefill_compact(const PrefillArgs& a, hipStream_t s, hipEvent_t start, hipEvent_t stop) {
+hipError_t launch_prefill_compact(const PrefillArgs& a, bool with_vt, hipStream_t s, hipEvent_t start,
+                                  hipEvent_t stop) {
     const bool d128 = a.pool.head_dim == 128;
     if (a.pool.fp8) {  // quantise the prompt first (the compaction gathers codes)
         const int64_t threads = (int64_t)2 * a.n_tokens * a.pool.n_kv_heads * (a.pool.head_dim / 8);
@@ -1494,7 +1509,10 @@ hipError_t launch_prefill_compact(const PrefillArgs& a, hipStream_t s, hipEvent_
     hipExtLaunchKernelGGL(prefill_scan_kernel, dim3(a.pool.n_kv_heads), dim3(1024), 0, s, start, nullptr, 0, a);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
-    const dim3 grid((a.n_tokens + kPage - 1) / kPage, a.pool.n_kv_heads);
+    // one block per page of live slots (those past the head's count return at
+    // once), then with_vt one block per 64 prompt rows for the V copy
+    const int ncomp = (a.n_tokens + kPage - 1) / kPage;
+    const dim3 grid(ncomp + (with_vt ? (a.n_tokens + 63) / 64 : 0), a.pool.n_kv_heads);
     if (a.pool.fp8) {
         if (d128) hipExtLaunchKernelGGL(prefill_compact8_kernel<128>, grid, dim3(256), 0, s, nullptr, stop, 0, a);
         else hipExtLaunchKernelGGL(prefill_compact8_kernel<64>, grid, dim3(256), 0, s, nullptr, stop, 0, a);

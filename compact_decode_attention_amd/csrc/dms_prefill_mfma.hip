@@ -88,55 +88,6 @@ __device__ __forceinline__ float sum_xor32(float x) {
 // row index of the S^T tile -> key index within the 32-key tile: bits 2 and 3 swapped
 __device__ __forceinline__ int swap23(int i) { return (i & ~12) | ((i & 4) << 1) | ((i & 8) >> 1); }
 
-// ---------------------------------------------------------------------------
-// prompt V -> vt[h][s/8][d][8] (8 consecutive tokens of one dim per 16 bytes),
-// zero beyond the prompt up to the next multiple of 32.  FP8 pools: the values
-// of the prompt V's codes (exact in bf16; the row scales are applied to P).
-// bf16 pools: a V value without an fp16 counterpart sets the pool's sticky
-// kCtlVWide flag, which keeps the attention on its bf16 path.
-// ---------------------------------------------------------------------------
-template <int D, bool F8>
-__device__ __forceinline__ void vt_block(const PrefillArgs& a, int bx, int h) {
-    const PoolDev& P = a.pool;
-    __shared__ uint16_t s_v[64][D + 8];
-    const int tid = threadIdx.x;
-    const int s0 = bx * 64;
-    const int T = a.n_tokens, hkv = P.n_kv_heads;
-    const int T32 = (T + 31) / 32 * 32;
-    constexpr int NC = D / 8;
-    uint32_t wide = 0;
-    for (int u = tid; u < 64 * NC; u += 256) {
-        const int j = u / NC, cc = u - j * NC;
-        const int s = s0 + j;
-        uint4 val = make_uint4(0, 0, 0, 0);
-        if (s < T) {
-            if constexpr (F8)
-                val = fp8x8_bf16(*reinterpret_cast<const uint2*>(P.q8_codes(1) + ((size_t)s * hkv + h) * D + cc * 8));
-            else
-                val = *reinterpret_cast<const uint4*>(a.v + ((size_t)s * hkv + h) * D + cc * 8);
-        }
-        if (!F8) wide |= bf16x8_wide(val);
-        *reinterpret_cast<uint4*>(&s_v[j][cc * 8]) = val;
-    }
-    if (wide) atomicOr(&P.ctl[kCtlVWide], 1);
-    __syncthreads();
-    uint16_t* vt = P.vt + (size_t)h * (P.max_pos32 / 8) * D * 8;
-    for (int u = tid; u < 8 * D; u += 256) {
-        const int b = u / D, d = u - b * D;
-        const int blk = s0 / 8 + b;
-        if (blk * 8 >= T32) continue;
-        uint32_t w4[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-            w4[i] = (uint32_t)s_v[8 * b + 2 * i][d] | ((uint32_t)s_v[8 * b + 2 * i + 1][d] << 16);
-        *reinterpret_cast<uint4*>(vt + ((size_t)blk * D + d) * 8) = make_uint4(w4[0], w4[1], w4[2], w4[3]);
-    }
-}
-
-template <int D, bool F8>
-__global__ __launch_bounds__(256) void prefill_vt_kernel(PrefillArgs a) {
-    vt_block<D, F8>(a, blockIdx.x, blockIdx.y);
-}
 
 // ---------------------------------------------------------------------------
 // masked prefill attention.  One block = (kv head, QT consecutive 32-query
@@ -775,8 +726,9 @@ __device__ __forceinline__ void compact_block(const PrefillArgs& a, int bx, int 
 template <int D, bool F8>
 __global__ __launch_bounds__(256) void extend_prep_kernel(PrefillArgs a) {
     const int nv = (a.n_tokens + 63) / 64, ne = max(1, (a.t0 + 255) / 256);
+    __shared__ uint16_t s_v[64][D + 8];
     const int bx = blockIdx.x, h = blockIdx.y;
-    if (bx < nv) vt_block<D, F8>(a, bx, h);
+    if (bx < nv) vt_rows<D, F8>(a, bx * 64, h, s_v);
     else if (bx < nv + ne) expiry_block(a, bx - nv, h);
     else compact_block<D, F8>(a, bx - nv - ne, h);
 }
@@ -789,36 +741,32 @@ hipError_t launch_attend_t(const PrefillArgs& a, hipStream_t s, hipEvent_t* ev) 
     const int grid = 8 * ((total + 7) / 8);
     if (a.pool.fp8)
         hipExtLaunchKernelGGL((prefill_attend_kernel<D, G, true, EXT>), dim3(grid), dim3(64 * prefill_waves(G)), 0,
-                              s, ev ? ev[2] : nullptr, ev ? ev[3] : nullptr, 0, a);
+                              s, ev ? ev[0] : nullptr, ev ? ev[1] : nullptr, 0, a);
     else
         hipExtLaunchKernelGGL((prefill_attend_kernel<D, G, false, EXT>), dim3(grid), dim3(64 * prefill_waves(G)), 0,
-                              s, ev ? ev[2] : nullptr, ev ? ev[3] : nullptr, 0, a);
+                              s, ev ? ev[0] : nullptr, ev ? ev[1] : nullptr, 0, a);
     return hipGetLastError();
 }
 
+// ev (optional): extend, 4 events (preparation, then attention start/stop);
+// prefill, 2 events (attention; its V copy ran with the compaction)
 template <int D, bool EXT>
 hipError_t launch_attend_d(const PrefillArgs& a, hipStream_t s, hipEvent_t* ev) {
-    const int nv = (a.n_tokens + 63) / 64;
-    // extend: the store holds at most t0 slots per head (expiry rows), and the
-    // chunk's rows are gathered 64 per block
-    const dim3 vgrid(EXT ? nv + std::max(1, (a.t0 + 255) / 256) + nv : nv, a.pool.n_kv_heads);
-    if (a.pool.fp8) {
-        if (EXT)
-            hipExtLaunchKernelGGL((extend_prep_kernel<D, true>), vgrid, dim3(256), 0, s, ev ? ev[0] : nullptr,
+    if (EXT) {
+        const int nv = (a.n_tokens + 63) / 64;
+        // the store holds at most t0 slots per head (expiry rows); the chunk's
+        // rows are copied and gathered 64 per block
+        const dim3 pgrid(nv + std::max(1, (a.t0 + 255) / 256) + nv, a.pool.n_kv_heads);
+        if (a.pool.fp8)
+            hipExtLaunchKernelGGL((extend_prep_kernel<D, true>), pgrid, dim3(256), 0, s, ev ? ev[0] : nullptr,
                                   ev ? ev[1] : nullptr, 0, a);
         else
-            hipExtLaunchKernelGGL((prefill_vt_kernel<D, true>), vgrid, dim3(256), 0, s, ev ? ev[0] : nullptr,
+            hipExtLaunchKernelGGL((extend_prep_kernel<D, false>), pgrid, dim3(256), 0, s, ev ? ev[0] : nullptr,
                                   ev ? ev[1] : nullptr, 0, a);
-    } else {
-        if (EXT)
-            hipExtLaunchKernelGGL((extend_prep_kernel<D, false>), vgrid, dim3(256), 0, s, ev ? ev[0] : nullptr,
-                                  ev ? ev[1] : nullptr, 0, a);
-        else
-            hipExtLaunchKernelGGL((prefill_vt_kernel<D, false>), vgrid, dim3(256), 0, s, ev ? ev[0] : nullptr,
-                                  ev ? ev[1] : nullptr, 0, a);
+        const hipError_t err = hipGetLastError();
+        if (err != hipSuccess) return err;
+        if (ev) ev += 2;
     }
-    hipError_t err = hipGetLastError();
-    if (err != hipSuccess) return err;
     switch (a.pool.n_q_heads / a.pool.n_kv_heads) {
         case 1: return launch_attend_t<D, 1, EXT>(a, s, ev);
         case 2: return launch_attend_t<D, 2, EXT>(a, s, ev);
