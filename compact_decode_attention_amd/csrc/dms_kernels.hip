@@ -86,6 +86,13 @@ __device__ __forceinline__ float wave_sum(float x) {
     return readlane_f(x, 63);
 }
 
+// x where c holds, zeros elsewhere, component by component (a select of the
+// whole vector struct is lowered through private memory)
+__device__ __forceinline__ uint4 keep_if(bool c, uint4 x) {
+    const uint32_t m = c ? ~0u : 0u;
+    return make_uint4(x.x & m, x.y & m, x.z & m, x.w & m);
+}
+
 // Scheduling fence for register values: an empty volatile asm that reads and
 // writes x.  Volatile asm keeps its place among memory operations, so the
 // arithmetic producing x stays ahead of the loads issued after this point.
@@ -1068,22 +1075,33 @@ __global__ __launch_bounds__(256) void prefill_compact_kernel(PrefillArgs a) {
     const int cnt = min(kPage, n - pj * kPage);
     if (tid < kPage) s_src[tid] = tid < cnt ? P.inv[(size_t)h * P.max_positions + pj * kPage + tid] : -1;
     __syncthreads();
-    uint16_t* kp = P.kpages + (size_t)page * (kPage * D);
+    uint16_t* __restrict__ kp = P.kpages + (size_t)page * (kPage * D);
     uint16_t* vp = P.vpages + (size_t)page * (kPage * D);
-    const uint4 zero = make_uint4(0, 0, 0, 0);
-    for (int u = tid; u < NC * kPage; u += 256) {
-        const int cc = u / kPage, j = u - cc * kPage;
-        const int s = s_src[j];
-        const uint4 val = s >= 0 ? *reinterpret_cast<const uint4*>(a.k + ((size_t)s * hkv + h) * D + cc * 8) : zero;
-        *reinterpret_cast<uint4*>(kp + ((size_t)cc * kPage + j) * 8) = val;
+    const uint16_t* __restrict__ kin = a.k;
+    const uint16_t* __restrict__ vin = a.v;
+    // Every K and V unit of the thread is requested before any is stored.  (Slots
+    // past the live count read row 0 and store zeros: every load is a plain
+    // global load, with the value selected afterwards.)
+    constexpr int UT = NC * kPage / 256;  // units per thread
+    static_assert(NC * kPage % 256 == 0, "K and V units tile the block");
+    uint4 kx[UT], vx[UT];
+#pragma unroll
+    for (int x = 0; x < UT; ++x) {
+        const int u = tid + 256 * x;
+        const int sk = s_src[u % kPage], sv = s_src[u / NC];
+        kx[x] = *reinterpret_cast<const uint4*>(kin + ((size_t)max(sk, 0) * hkv + h) * D + (u / kPage) * 8);
+        vx[x] = *reinterpret_cast<const uint4*>(vin + ((size_t)max(sv, 0) * hkv + h) * D + (u % NC) * 8);
     }
     uint32_t wide = 0;  // a stored V value without an fp16 counterpart: sticky pool flag
-    for (int u = tid; u < kPage * NC; u += 256) {
-        const int j = u / NC, cc = u - j * NC;
-        const int s = s_src[j];
-        const uint4 val = s >= 0 ? *reinterpret_cast<const uint4*>(a.v + ((size_t)s * hkv + h) * D + cc * 8) : zero;
+#pragma unroll
+    for (int x = 0; x < UT; ++x) {
+        const int u = tid + 256 * x;
+        const int j = u % kPage, cc = u / kPage;  // K unit: chunk cc of slot j
+        const int vj = u / NC, vc = u % NC;       // V unit: chunk vc of slot vj
+        *reinterpret_cast<uint4*>(kp + ((size_t)cc * kPage + j) * 8) = keep_if(s_src[j] >= 0, kx[x]);
+        const uint4 val = keep_if(s_src[vj] >= 0, vx[x]);
         wide |= bf16x8_wide(val);
-        *reinterpret_cast<uint4*>(&s_v[j][cc * 8]) = val;
+        *reinterpret_cast<uint4*>(&s_v[vj][vc * 8]) = val;
     }
     if (wide) atomicOr(&P.ctl[kCtlVWide], 1);
     __syncthreads();
@@ -1162,22 +1180,24 @@ __global__ __launch_bounds__(256) void prefill_compact8_kernel(PrefillArgs a) {
     const int cnt = min(kPage, n - pj * kPage);
     if (tid < kPage) s_src[tid] = tid < cnt ? P.inv[(size_t)h * P.max_positions + pj * kPage + tid] : -1;
     __syncthreads();
-    const uint8_t* kq = P.q8_codes(0);
-    const uint8_t* vq = P.q8_codes(1);
-    uint8_t* kp = P.kp8() + (size_t)page * (kPage * D);
+    const uint8_t* __restrict__ kq = P.q8_codes(0);
+    const uint8_t* __restrict__ vq = P.q8_codes(1);
+    uint8_t* __restrict__ kp = P.kp8() + (size_t)page * (kPage * D);
     uint8_t* vp = P.vp8() + (size_t)page * (kPage * D);
-    const uint4 zero = make_uint4(0, 0, 0, 0);
+    // (slots past the live count read row 0 and store zeros, as above)
+#pragma unroll
     for (int u = tid; u < NC * kPage; u += 256) {
         const int cc = u / kPage, j = u - cc * kPage;
         const int s = s_src[j];
-        const uint4 val = s >= 0 ? *reinterpret_cast<const uint4*>(kq + ((size_t)s * hkv + h) * D + cc * 16) : zero;
-        *reinterpret_cast<uint4*>(kp + ((size_t)cc * kPage + j) * 16) = val;
+        const uint4 x = *reinterpret_cast<const uint4*>(kq + ((size_t)max(s, 0) * hkv + h) * D + cc * 16);
+        *reinterpret_cast<uint4*>(kp + ((size_t)cc * kPage + j) * 16) = keep_if(s >= 0, x);
     }
+#pragma unroll
     for (int u = tid; u < kPage * NC; u += 256) {
         const int j = u / NC, cc = u - j * NC;
         const int s = s_src[j];
-        const uint4 val = s >= 0 ? *reinterpret_cast<const uint4*>(vq + ((size_t)s * hkv + h) * D + cc * 16) : zero;
-        *reinterpret_cast<uint4*>(&s_v[j][cc * 16]) = val;
+        const uint4 x = *reinterpret_cast<const uint4*>(vq + ((size_t)max(s, 0) * hkv + h) * D + cc * 16);
+        *reinterpret_cast<uint4*>(&s_v[j][cc * 16]) = keep_if(s >= 0, x);
     }
     __syncthreads();
     for (int u = tid; u < 4 * D; u += 256) {
