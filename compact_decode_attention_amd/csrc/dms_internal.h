@@ -80,6 +80,18 @@ __device__ __forceinline__ uint32_t bf16x8_wide(uint4 u) {
     return bf16x2_wide(u.x) | bf16x2_wide(u.y) | bf16x2_wide(u.z) | bf16x2_wide(u.w);
 }
 
+// 8 bf16 values as 8 fp16 values: exact for |v| < 65536 down to 2^-17 (below
+// that, fp16 subnormal spacing 2^-24).  Used only while no stored V value is
+// wide (the kCtlVWide flag is clear).
+__device__ __forceinline__ uint4 bf16x8_to_f16x8(uint4 u) {
+    typedef _Float16 f16x2_v __attribute__((ext_vector_type(2)));
+    auto cv = [](uint32_t w) -> uint32_t {
+        const f16x2_v x = {(_Float16)__uint_as_float(w << 16), (_Float16)__uint_as_float(w & 0xffff0000u)};
+        return __builtin_bit_cast(uint32_t, x);
+    };
+    return make_uint4(cv(u.x), cv(u.y), cv(u.z), cv(u.w));
+}
+
 // Per-head record, 8 int32:
 //   [0] n_live       tokens held, in slots 0 .. n_live-1
 //   [1] n_pages      pages in the head's page table

@@ -1105,13 +1105,19 @@ __global__ __launch_bounds__(256) void prefill_compact_kernel(PrefillArgs a) {
     }
     if (wide) atomicOr(&P.ctl[kCtlVWide], 1);
     __syncthreads();
+    // the page, and its fp16 copy in the kv head's scratch page pj, which the
+    // attention reads on its fp16-weights path (the copy is exact whenever that
+    // path runs: no stored V value is wide)
+    uint16_t* vh = P.vpages + (size_t)(P.xpage(h) + pj) * (kPage * D);
     for (int u = tid; u < 8 * D; u += 256) {
         const int b = u / D, d = u - b * D;
         uint32_t w4[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i)
             w4[i] = (uint32_t)s_v[8 * b + 2 * i][d] | ((uint32_t)s_v[8 * b + 2 * i + 1][d] << 16);
-        *reinterpret_cast<uint4*>(vp + ((size_t)b * D + d) * 8) = make_uint4(w4[0], w4[1], w4[2], w4[3]);
+        const uint4 x = make_uint4(w4[0], w4[1], w4[2], w4[3]);
+        *reinterpret_cast<uint4*>(vp + ((size_t)b * D + d) * 8) = x;
+        *reinterpret_cast<uint4*>(vh + ((size_t)b * D + d) * 8) = bf16x8_to_f16x8(x);
     }
     if (tid < kPage) P.slot_pos[(size_t)page * kPage + tid] = s_src[tid];
 }

@@ -45,16 +45,6 @@ typedef float f32x16_t __attribute__((ext_vector_type(16)));
 __device__ __forceinline__ bf16x8_t as_bf16x8(uint4 u) { return __builtin_bit_cast(bf16x8_t, u); }
 __device__ __forceinline__ f16x8_t as_f16x8(uint4 u) { return __builtin_bit_cast(f16x8_t, u); }
 
-// 8 bf16 values as 8 fp16 values: exact for |v| < 65536 down to 2^-17 (below
-// that, fp16 subnormal spacing 2^-24).  Pools whose V can exceed the fp16 range
-// never take this path (see the kernel below).
-__device__ __forceinline__ uint4 bf16x8_to_f16x8(uint4 u) {
-    auto cv = [](uint32_t w) -> uint32_t {
-        const f16x2_t h = {(_Float16)__uint_as_float(w << 16), (_Float16)__uint_as_float(w & 0xffff0000u)};
-        return __builtin_bit_cast(uint32_t, h);
-    };
-    return make_uint4(cv(u.x), cv(u.y), cv(u.z), cv(u.w));
-}
 
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
     auto rne = [](float f) -> uint32_t {
@@ -290,8 +280,12 @@ __device__ __forceinline__ void prefill_attend_body(const PrefillArgs& a) {
                 rv[X][x] = make_uint4(c.x, c.y, 0u, 0u);
             }
         } else {
-            const char* base = far ? vfar0 + upage(pg) * (kPage * D * 2) + (size_t)(kb % kPage / 8) * D * 16
-                                   : reinterpret_cast<const char*>(vt) + (size_t)(kb / 8) * D * 16;
+            // (prefill on fp16 weights: the far field's V from the fp16 copy the
+            // compaction left in the kv head's scratch pages, in slot order)
+            const char* base = !far ? reinterpret_cast<const char*>(vt) + (size_t)(kb / 8) * D * 16
+                               : H16 && !EXT ? vfar0 + (size_t)(P.xpage(h) + kb / kPage) * (kPage * D * 2) +
+                                                   (size_t)(kb % kPage / 8) * D * 16
+                                             : vfar0 + upage(pg) * (kPage * D * 2) + (size_t)(kb % kPage / 8) * D * 16;
             const __amdgpu_buffer_rsrc_t r = rsrc(base, live ? UNITS * 16 : 0);
 #pragma unroll
             for (int x = 0; x < UPT; ++x) rv[X][x] = buffer_load16(r, F8 ? (tid + x * NT >= UNITS ? kFar : (tid + x * NT) * 16)
@@ -336,9 +330,9 @@ __device__ __forceinline__ void prefill_attend_body(const PrefillArgs& a) {
         for (int x = 0; x < UPT; ++x) {
             const int u = tid + x * NT;
             if (UNITS % NT == 0 || u < UNITS)
-                s_v[i & 1][u / D][u % D] = (F8 && far) ? fp8x8_bf16(make_uint2(rv[X][x].x, rv[X][x].y))
-                                           : H16       ? bf16x8_to_f16x8(rv[X][x])
-                                                       : rv[X][x];
+                s_v[i & 1][u / D][u % D] = (F8 && far)           ? fp8x8_bf16(make_uint2(rv[X][x].x, rv[X][x].y))
+                                           : H16 && (EXT || !far) ? bf16x8_to_f16x8(rv[X][x])
+                                                                  : rv[X][x];
         }
         if (!far && wave == 0) {  // keys past the prompt read logit 0: unmarked
             const float lg = __uint_as_float(P.logit_ch >= 0 ? rlg[X] << 16 : rlg[X]);
