@@ -117,7 +117,11 @@ typedef struct {
 } dms_pool_config;
 
 /* Bytes of device memory (the arena) a pool with this configuration needs, or 0
- * if the configuration is invalid (dms_last_error() says why). */
+ * if the configuration is invalid (dms_last_error() says why).  Besides the
+ * max_pages shared pages it holds the head records, page tables, window rings,
+ * split-K partials and the prefill / extend scratch, which includes
+ * ceil(max_positions / 64) scratch pages per kv head (max_pages plus these must
+ * stay below 2^31). */
 size_t dms_pool_bytes(const dms_pool_config* cfg);
 
 /* Create a pool inside the caller's arena (device memory, >= dms_pool_bytes()
