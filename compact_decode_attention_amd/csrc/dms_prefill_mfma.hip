@@ -398,21 +398,18 @@ __device__ __forceinline__ void prefill_attend_body(const PrefillArgs& a) {
         // z: the scores (FP8: times the keys' K scales) with invisible keys at
         // -inf, computed in place in S_i's registers (dead after this step)
         f32x16_t& z = cur;
-        float vsc[16];  // FP8: the keys' V scales
+        // (FP8: rows r0 .. r0+3 hold keys 4 kk .. 4 kk + 3, whose K scales are
+        // applied here and whose V scales are read where the weights are formed)
+        auto scale_q4 = [&](int r) { return 2 * half + ((r >> 2) & 1) + 4 * (r >> 3); };  // kk of row r
         if constexpr (F8) {
 #pragma unroll
-            for (int q4 = 0; q4 < 4; ++q4) {  // rows r0 .. r0+3 hold keys 4 kk .. 4 kk + 3
-                const int kk = 2 * half + (q4 & 1) + 4 * (q4 >> 1);
-                const float4 k4 = s_ks[i & 1][kk], v4 = s_vs[i & 1][kk];
+            for (int q4 = 0; q4 < 4; ++q4) {
                 const int r0 = 4 * (q4 & 1) + 8 * (q4 >> 1);
+                const float4 k4 = s_ks[i & 1][scale_q4(r0)];
                 z[r0] *= k4.x;
                 z[r0 + 1] *= k4.y;
                 z[r0 + 2] *= k4.z;
                 z[r0 + 3] *= k4.w;
-                vsc[r0] = v4.x;
-                vsc[r0 + 1] = v4.y;
-                vsc[r0 + 2] = v4.z;
-                vsc[r0 + 3] = v4.w;
             }
         }
         if (EXT && !BP && (FP || i < nfar1)) {  // stored keys: visible to the rows below their expiry row
@@ -494,7 +491,12 @@ __device__ __forceinline__ void prefill_attend_body(const PrefillArgs& a) {
                 const f16x2_t hv = {(_Float16)p0, (_Float16)p1};
                 ph[i2] = __builtin_bit_cast(uint32_t, hv);
             } else {
-                const float w0 = F8 ? p0 * vsc[2 * i2] : p0, w1 = F8 ? p1 * vsc[2 * i2 + 1] : p1;
+                float w0 = p0, w1 = p1;
+                if constexpr (F8) {  // V scales of the keys in rows 2 i2 and 2 i2 + 1
+                    const float2 v2 = reinterpret_cast<const float2*>(&s_vs[i & 1][scale_q4(2 * i2)])[(i2 & 1)];
+                    w0 *= v2.x;
+                    w1 *= v2.y;
+                }
                 const bf16x2_t hv = {(__bf16)w0, (__bf16)w1};
                 const bf16x2_t lv = {(__bf16)(w0 - (float)hv[0]), (__bf16)(w1 - (float)hv[1])};
                 ph[i2] = __builtin_bit_cast(uint32_t, hv);
