@@ -93,6 +93,28 @@ __device__ __forceinline__ uint4 keep_if(bool c, uint4 x) {
     return make_uint4(x.x & m, x.y & m, x.z & m, x.w & m);
 }
 
+// Reduce x over the lanes that share lane % G (G a power of two up to 32) with
+// op, all on the VALU: the halves and quarters of the wave are exchanged by
+// v_permlane32_swap / v_permlane16_swap (either result pair holds x of both
+// partners), the lanes of a 16-lane row by DPP rotations (combining lane l with
+// l + o mod 16 for o = 8, 4, ... covers the row's lanes with l's residue).
+template <int G, typename Op>
+__device__ __forceinline__ float reduce_mod_g(float x, Op op) {
+    if constexpr (G <= 32) {
+        const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+        x = op(__uint_as_float(r[0]), __uint_as_float(r[1]));
+    }
+    if constexpr (G <= 16) {
+        const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+        x = op(__uint_as_float(r[0]), __uint_as_float(r[1]));
+    }
+    if constexpr (G <= 8) x = op(x, dpp_f<0x128>(x, x));  // row_ror:8
+    if constexpr (G <= 4) x = op(x, dpp_f<0x124>(x, x));  // row_ror:4
+    if constexpr (G <= 2) x = op(x, dpp_f<0x122>(x, x));  // row_ror:2
+    if constexpr (G <= 1) x = op(x, dpp_f<0x121>(x, x));  // row_ror:1
+    return x;
+}
+
 // Scheduling fence for register values: an empty volatile asm that reads and
 // writes x.  Volatile asm keeps its place among memory operations, so the
 // arithmetic producing x stays ahead of the loads issued after this point.
@@ -733,9 +755,8 @@ __device__ void merge_head(const DecodeArgs& a, int ch) {
         if (lane == 0) s_zn[g] = zn;
     }
 
-    // maximum per q head: lanes l and l ^ o share a q head for o >= G
-#pragma unroll
-    for (int o = 32; o >= G; o >>= 1) mloc = fmaxf(mloc, __shfl_xor(mloc, o, 64));
+    // maximum per q head: the lanes with the same lane % G hold the same q head
+    mloc = reduce_mod_g<G>(mloc, [](float a, float b) { return fmaxf(a, b); });
     if (lane < G) s_red[0][wave][lane] = mloc;
     __syncthreads();
     float Mt = s_red[0][0][gt];
@@ -752,8 +773,7 @@ __device__ void merge_head(const DecodeArgs& a, int ch) {
     if (Mt != -INFINITY)
         for (int i = tid / G + NW_MAX; i < n; i += STEP)
             lloc = fmaf(exp2f(part0[(size_t)i * PSTR + gt] - Mt), part0[(size_t)i * PSTR + G + gt], lloc);
-#pragma unroll
-    for (int o = 32; o >= G; o >>= 1) lloc += __shfl_xor(lloc, o, 64);
+    lloc = reduce_mod_g<G>(lloc, [](float a, float b) { return a + b; });
     if (lane < G) s_red[1][wave][lane] = lloc;
     __syncthreads();
 
