@@ -5,9 +5,7 @@ rule and its sources).  Only ``tests/``, ``__graft_entry__.smoke()`` and the
 CPU-baseline leg of ``bench.py`` may import this package; the GPU library never
 does, and this package imports nothing from it.
 
-Everything here is argument marshalling around dms_oracle.c, plus the byte
-accounting of a live set (live count x 2 tensors x head_dim x 2 bytes), which is
-the definition of the "KV bytes" a compact store holds.
+Everything here is argument marshalling around dms_oracle.c.
 """
 from __future__ import annotations
 
@@ -55,6 +53,10 @@ def load(so: str) -> ctypes.CDLL:
     lib.dms_oracle_quantize_rows.restype = None
     lib.dms_oracle_attend_fp8.argtypes = [i32, i32, i32, i64, dbl, i64, vp, vp, i64, vp, vp, vp, vp, vp, vp]
     lib.dms_oracle_attend_fp8.restype = ctypes.c_int
+    lib.dms_oracle_row_bytes.argtypes = [i32, i32]
+    lib.dms_oracle_row_bytes.restype = i64
+    lib.dms_oracle_kv_bytes.argtypes = [i64, i64, vp, i32, i32, i32, i64, vp]
+    lib.dms_oracle_kv_bytes.restype = None
     return lib
 
 
@@ -170,6 +172,22 @@ class Oracle:
             raise ValueError("query position outside the keys given")
         return out
 
+    # ---- bytes a compact store holds
+    def row_bytes(self, head_dim: int, fp8: bool = False) -> int:
+        return int(self.lib.dms_oracle_row_bytes(int(head_dim), 1 if fp8 else 0))
+
+    def kv_bytes(self, t: int, window: int, marks: np.ndarray, head_dim: int, fp8: bool = False,
+                 page_slots: int = 64):
+        """(live, allocated, dense-equivalent) bytes of one (seq, layer) after
+        the token at position t; marks [>t][Hkv]."""
+        m = np.ascontiguousarray(marks, np.uint8)
+        if m.ndim != 2 or t >= m.shape[0]:
+            raise ValueError("marks must be [positions > t][n_kv_heads]")
+        out = np.zeros(3, np.int64)
+        self.lib.dms_oracle_kv_bytes(int(t), int(window), m.ctypes.data, m.shape[1], int(head_dim),
+                                     1 if fp8 else 0, int(page_slots), out.ctypes.data)
+        return int(out[0]), int(out[1]), int(out[2])
+
 
 def default() -> Oracle:
     return Oracle(_lib())
@@ -211,7 +229,9 @@ def attend_fp8(q, query_pos, k8, ks, v8, vs, marks_, window, scale=0.0):
     return default().attend_fp8(q, query_pos, k8, ks, v8, vs, marks_, window, scale)
 
 
-def kv_bytes_live(live_counts, head_dim: int) -> int:
-    """Bytes a compact store needs for the given live counts: K and V rows of
-    head_dim bf16 values each."""
-    return int(np.sum(np.asarray(live_counts, np.int64))) * 2 * head_dim * 2
+def row_bytes(head_dim, fp8=False):
+    return default().row_bytes(head_dim, fp8)
+
+
+def kv_bytes(t, window, marks_, head_dim, fp8=False, page_slots=64):
+    return default().kv_bytes(t, window, marks_, head_dim, fp8, page_slots)

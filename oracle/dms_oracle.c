@@ -104,6 +104,40 @@ int64_t dms_oracle_live_positions(int64_t t, int64_t window, const uint8_t* mark
     return n;
 }
 
+/* Bytes of one stored K (or V) row of head_dim values: bf16 values take 2
+ * bytes each; an FP8 row takes one byte per E4M3 code plus its fp32 scale. */
+int64_t dms_oracle_row_bytes(int32_t head_dim, int32_t fp8) {
+    return fp8 ? (int64_t)head_dim * 1 + 4 : (int64_t)head_dim * 2;
+}
+
+/* What a compact KV store holds for one (sequence, layer) once the token at
+ * query position t is in.  The FastDMS announcement (molayo1419.me) reports KV
+ * memory as real allocator memory (its memory table), for a store that drops
+ * evicted tokens and reclaims their slots (its release paragraph and the
+ * "What's the catch?" table); the bytes therefore follow the live sets:
+ *   marks [n_kv_heads columns, row s = position s], rows 0 .. t read
+ *   out[0] live      = sum over kv heads h of |V_h(t)| * 2 * row_bytes
+ *                      (one K and one V row per live token)
+ *   out[1] allocated = sum over kv heads h of ceil(|V_h(t)| / page_slots)
+ *                      * page_slots * 2 * row_bytes  (whole pages; the live
+ *                      tokens of a head fill its slots densely because a freed
+ *                      slot is taken by the next token)
+ *   out[2] dense     = (t + 1) * n_kv_heads * 2 * head_dim * 2
+ *                      (every token kept, bf16: the eviction-disabled store)
+ * |V_h(t)| is counted with the visibility rule, token by token. */
+void dms_oracle_kv_bytes(int64_t t, int64_t window, const uint8_t* marks, int32_t n_kv_heads,
+                         int32_t head_dim, int32_t fp8, int64_t page_slots, int64_t* out) {
+    const int64_t row = dms_oracle_row_bytes(head_dim, fp8);
+    out[0] = out[1] = 0;
+    for (int32_t h = 0; h < n_kv_heads; ++h) {
+        int64_t n = 0;
+        for (int64_t s = 0; s <= t; ++s) n += visible(t, s, marks[s * n_kv_heads + h], window);
+        out[0] += n * 2 * row;
+        out[1] += (n + page_slots - 1) / page_slots * page_slots * 2 * row;
+    }
+    out[2] = (t + 1) * n_kv_heads * 2 * (int64_t)head_dim * 2;
+}
+
 /* Masked attention over the full K/V of one (sequence, layer).
  *
  *   q     [n_queries][n_q_heads][head_dim]   bf16 bits, row i is the query at

@@ -11,6 +11,10 @@ oracle disagrees with one of:
   one key is visible, the plain mean when all scores are equal, a per-position
   histogram with one-hot values, the kv-head a q head reads when values are
   constant per kv head;
+* the bytes a compact store holds: the KV-memory figures the FastDMS
+  announcement prints (tests/golden/fastdms_memory_table.json), the byte sizes
+  of the rows the live sets retain, and the pages a slot free-list simulation
+  fills;
 * library routines: torch's scaled_dot_product_attention in float64 with a
   causal mask (eviction disabled: the 1M-token window the FastDMS quality
   method uses as its reference), with a band mask (every token marked: a
@@ -291,6 +295,110 @@ def pin_query_subset_matches_rows(orc):
     assert np.array_equal(sub, full[pick])
 
 
+# ---------------------------------------------------------------------------
+# pins on the bytes a compact store holds
+# ---------------------------------------------------------------------------
+
+def simulate_slots(marks_col, window):
+    """Single-token decode of one head with an explicit slot free list: token t
+    takes the slot of the token leaving at step t (t - w, if marked), else a
+    fresh slot.  Returns the slots in use after each step (the high-water mark)."""
+    free, slot_of, used, out = [], {}, 0, []
+    for t, m in enumerate(marks_col):
+        u = t - window
+        if u >= 0 and marks_col[u]:
+            free.append(slot_of.pop(u))
+        if free:
+            slot_of[t] = free.pop()
+        else:
+            slot_of[t] = used
+            used += 1
+        out.append(used)
+    return out
+
+
+def pin_kv_bytes_reproduce_memory_table(orc):
+    """Eviction disabled, the Llama-3.2-1B shape: the store's bytes for 10240
+    token slots round to the FastDMS memory table's vLLM BF16 figure, and the
+    code bytes of the FP8 rows (without the row scales) to its vLLM FP8 figure;
+    the job's own 8320 tokens do not reproduce the printed value."""
+    with open(os.path.join(GOLDEN, "fastdms_memory_table.json")) as f:
+        tab = json.load(f)
+    sh, printed = tab["shape"], tab["printed_gib"]
+    L, H, D = sh["n_layers"], sh["n_kv_heads"], sh["head_dim"]
+    slots = 10240
+    marks = np.zeros((slots, H), np.uint8)
+    live, alloc, dense = orc.kv_bytes(slots - 1, 1 << 20, marks, D)
+    assert live == dense == alloc
+    assert round(L * live / 2**30, 3) == printed["vllm_bf16"]
+    _, scales = orc.quantize_rows(np.zeros((1, D), np.uint16))
+    live8, _, _ = orc.kv_bytes(slots - 1, 1 << 20, marks, D, fp8=True)
+    codes_only = live8 - slots * H * 2 * scales.itemsize
+    assert round(L * codes_only / 2**30, 3) == printed["vllm_fp8"]
+    job = sh["ctx_len"] + sh["gen_len"]
+    live_job, _, _ = orc.kv_bytes(job - 1, 1 << 20, marks[:job], D)
+    assert round(L * live_job / 2**30, 3) != printed["vllm_bf16"]
+
+
+def pin_kv_bytes_are_the_rows_held(orc):
+    """Live bytes = the bytes of the K and V rows the live sets retain (rows of
+    the inputs for bf16 stores, the quantiser's codes and scales for FP8),
+    with the live sets from the event-driven simulation."""
+    rng = np.random.default_rng(21)
+    for D, H, T, w in ((64, 3, 90, 7), (128, 2, 140, 33)):
+        k = _bf16((T, H, D), 23, 2)
+        v = _bf16((T, H, D), 23, 3)
+        k8, ks = orc.quantize_rows(k)
+        v8, vs = orc.quantize_rows(v)
+        marks = (rng.random((T, H)) < 0.6).astype(np.uint8)
+        sets = [simulate_live_sets(marks[:, h], w) for h in range(H)]
+        for t in (0, w - 1, w, T // 2, T - 1):
+            held = sum(k[s, h].nbytes + v[s, h].nbytes for h in range(H) for s in sets[h][t])
+            held8 = sum(k8[s, h].nbytes + ks[s, h].nbytes + v8[s, h].nbytes + vs[s, h].nbytes
+                        for h in range(H) for s in sets[h][t])
+            assert orc.kv_bytes(t, w, marks, D)[0] == held, (D, t)
+            assert orc.kv_bytes(t, w, marks, D, fp8=True)[0] == held8, (D, t)
+            dense = sum(k[s, h].nbytes + v[s, h].nbytes for h in range(H) for s in range(t + 1))
+            assert orc.kv_bytes(t, w, marks, D)[2] == dense, (D, t)
+            assert orc.kv_bytes(t, w, marks, D, fp8=True)[2] == dense, (D, t)
+
+
+def pin_kv_bytes_allocated_pages(orc):
+    """Allocated bytes = whole pages of 64 slots over the slots a head has used,
+    with the slots from the free-list simulation (a freed slot is taken by the
+    next token, so no head ever leaves a hole)."""
+    rng = np.random.default_rng(22)
+    D, H, T = 64, 4, 700
+    row = _bf16((1, 1, D), 24, 2)[0, 0]
+    for w in (1, 16, 130):
+        for rate in (0.0, 0.5, 0.95, 1.0):
+            marks = (rng.random((T, H)) < rate).astype(np.uint8)
+            used = [simulate_slots(marks[:, h], w) for h in range(H)]
+            for t in (0, 63, 64, 65, 300, T - 1):
+                pages = sum(-(-used[h][t] // 64) for h in range(H))
+                live = sum(used[h][t] for h in range(H))
+                got = orc.kv_bytes(t, w, marks, D)
+                assert got[1] == pages * 64 * 2 * row.nbytes, (w, rate, t)
+                assert got[0] == live * 2 * row.nbytes, (w, rate, t)
+            assert orc.kv_bytes(T - 1, w, marks, D, page_slots=32)[1] == \
+                sum(-(-used[h][T - 1] // 32) for h in range(H)) * 32 * 2 * row.nbytes
+
+
+def pin_kv_bytes_extremes(orc):
+    """Nothing ever expires (the 1M-token window, or no marks): live = dense.
+    Every token marked: a window of min(t+1, w) rows per head."""
+    T, H, D = 300, 5, 128
+    rng = np.random.default_rng(25)
+    some = (rng.random((T, H)) < 0.5).astype(np.uint8)
+    for t in (0, 10, 299):
+        assert orc.kv_bytes(t, 1 << 20, some, D)[0] == orc.kv_bytes(t, 1 << 20, some, D)[2]
+        assert orc.kv_bytes(t, 3, np.zeros((T, H), np.uint8), D)[0] == orc.kv_bytes(t, 3, some, D)[2]
+        for w in (1, 7, 64):
+            live, alloc, _ = orc.kv_bytes(t, w, np.ones((T, H), np.uint8), D)
+            assert live == H * min(t + 1, w) * 2 * 2 * D
+            assert alloc == H * 64 * 2 * 2 * D
+
+
 ALL_PINS = [
     pin_marks,
     pin_live_sets_hand,
@@ -305,4 +413,8 @@ ALL_PINS = [
     pin_one_hot_histogram,
     pin_gqa_constant_values,
     pin_query_subset_matches_rows,
+    pin_kv_bytes_reproduce_memory_table,
+    pin_kv_bytes_are_the_rows_held,
+    pin_kv_bytes_allocated_pages,
+    pin_kv_bytes_extremes,
 ]

@@ -33,6 +33,10 @@ MUTANTS = [
     ("scale_dropped", "z[s] = scale * dot;", "z[s] = dot;"),
     ("keys_as_values", "const uint16_t* vrow = v +", "const uint16_t* vrow = k +"),
     ("no_normalisation", "o[d] /= denom;", "o[d] /= 1.0;"),
+    ("kv_bytes_k_rows_only", "out[0] += n * 2 * row;", "out[0] += n * row;"),
+    ("pages_rounded_down", "(n + page_slots - 1) / page_slots * page_slots", "n / page_slots * page_slots"),
+    ("fp8_rows_without_scale", "(int64_t)head_dim * 1 + 4", "(int64_t)head_dim * 1"),
+    ("dense_without_current_token", "out[2] = (t + 1) *", "out[2] = t *"),
     ("marks_of_wrong_head", "marks[s * n_kv_heads + h], window)) continue;\n                    const uint16_t* krow",
      "marks[s * n_kv_heads + (h + 1) % n_kv_heads], window)) continue;\n                    const uint16_t* krow"),
 ]
