@@ -203,7 +203,9 @@ def dms_decode_step(pool: int, seq_ids: Sequence[int], layer0: int, n_layers: in
 
 
 def dms_query_stats(pool: int, seq: int, n_layers: int = 0, n_kv_heads: int = 0, raise_on_error=True):
-    """Returns (dms_stats, live counts [n_layers][n_kv_heads] or None, status)."""
+    """Returns (dms_stats, live counts [n_layers][n_kv_heads] or None, status).
+    With raise_on_error false, a sticky device status (DMS_E_CAPACITY or
+    DMS_E_STATE) is returned instead of raised; the stats are filled in."""
     st = dms_stats()
     live = None
     ptr = None
@@ -211,7 +213,7 @@ def dms_query_stats(pool: int, seq: int, n_layers: int = 0, n_kv_heads: int = 0,
         live = np.zeros((n_layers, n_kv_heads), np.int32)
         ptr = live.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
     rc = lib().dms_query_stats(ctypes.c_void_p(pool), seq, ctypes.byref(st), ptr)
-    if rc != DMS_OK and (raise_on_error or rc != DMS_E_CAPACITY):
+    if rc != DMS_OK and (raise_on_error or rc not in (DMS_E_CAPACITY, DMS_E_STATE)):
         _check(rc)
     return st, live, rc
 

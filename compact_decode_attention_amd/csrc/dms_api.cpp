@@ -114,6 +114,27 @@ uint64_t mix64(uint64_t& s) {
 }  // namespace
 
 struct dms_pool {
+    // streams the pool's work was enqueued on (synchronising calls wait for
+    // these, not for the whole device); beyond kMaxStreams distinct streams the
+    // synchronising calls fall back to the whole device
+    static constexpr int kMaxStreams = 16;
+    hipStream_t streams[kMaxStreams];
+    int n_streams = 0;
+    bool streams_overflow = false;
+    void note(hipStream_t s) {
+        for (int i = 0; i < n_streams; ++i)
+            if (streams[i] == s) return;
+        if (n_streams < kMaxStreams) streams[n_streams++] = s;
+        else streams_overflow = true;
+    }
+    hipError_t sync() const {
+        if (streams_overflow) return hipDeviceSynchronize();
+        for (int i = 0; i < n_streams; ++i) {
+            const hipError_t e = hipStreamSynchronize(streams[i]);
+            if (e != hipSuccess) return e;
+        }
+        return hipSuccess;
+    }
     dms_pool_config cfg;
     bool timing = false;
     std::vector<hipEvent_t> events;   // 4 per decode launch while timing (attend, merge start/stop)
@@ -123,6 +144,8 @@ struct dms_pool {
     dms::PoolDev dev;
     char* arena;
     std::vector<int32_t> pos;  // [max_seqs][n_layers]: next position, -1 = empty
+    std::vector<uint32_t> seen;  // [max_seqs]: call stamp of the last decode call naming the sequence
+    uint32_t call_stamp = 0;
     int cu_count;
     int attend_per_cu;  // attention blocks per compute unit (checked once, for the largest call)
     int32_t& position(int seq, int layer) { return pos[(size_t)seq * cfg.n_layers + layer]; }
@@ -156,11 +179,13 @@ dms_status dms_pool_create(const dms_pool_config* cfg, void* arena, size_t arena
     hipStream_t s = static_cast<hipStream_t>(stream);
 
     dms_pool* p = new dms_pool();
+    p->note(s);
     p->cfg = *cfg;
     if (p->cfg.page_slots == 0) p->cfg.page_slots = DMS_PAGE_SLOTS;
     p->layout = L;
     p->arena = static_cast<char*>(arena);
     p->pos.assign((size_t)cfg->max_seqs * cfg->n_layers, -1);
+    p->seen.assign((size_t)cfg->max_seqs, 0);
     p->cu_count = dms::device_cu_count();
     char* a = p->arena;
     dms::PoolDev& d = p->dev;
@@ -236,10 +261,10 @@ dms_status dms_pool_create(const dms_pool_config* cfg, void* arena, size_t arena
 
 dms_status dms_pool_destroy(dms_pool* pool) {
     if (!pool) return fail(DMS_E_INVAL, "pool is NULL");
-    hipError_t e = hipDeviceSynchronize();
-    for (hipEvent_t ev : pool->events) hipEventDestroy(ev);
-    for (hipEvent_t ev : pool->pevents) hipEventDestroy(ev);
-    for (hipEvent_t ev : pool->xevents) hipEventDestroy(ev);
+    hipError_t e = pool->sync();
+    for (hipEvent_t ev : pool->events) (void)hipEventDestroy(ev);
+    for (hipEvent_t ev : pool->pevents) (void)hipEventDestroy(ev);
+    for (hipEvent_t ev : pool->xevents) (void)hipEventDestroy(ev);
     delete pool;
     if (e != hipSuccess) return hip_fail(e, "synchronise");
     g_err.clear();
@@ -282,6 +307,7 @@ dms_status dms_prefill(dms_pool* pool, int32_t seq, int32_t layer, int32_t n_tok
     a.n_tokens = n_tokens;
     a.t0 = 0;
     hipStream_t s = static_cast<hipStream_t>(stream);
+    pool->note(s);
     hipError_t e = hipSuccess;
     hipEvent_t* ev = nullptr;
     if (pool->timing && out) {
@@ -329,6 +355,7 @@ dms_status dms_extend(dms_pool* pool, int32_t seq, int32_t layer, int32_t n_toke
         ev = timing_events(pool->xevents, 4, &e);
         if (!ev) return hip_fail(e, "timing event");
     }
+    pool->note(static_cast<hipStream_t>(stream));
     e = dms::launch_extend(a, out != nullptr, static_cast<hipStream_t>(stream), ev);
     if (e != hipSuccess) return hip_fail(e, "extend launch");
     pool->position(seq, layer) = t0 + n_tokens;
@@ -336,9 +363,26 @@ dms_status dms_extend(dms_pool* pool, int32_t seq, int32_t layer, int32_t n_toke
     return DMS_OK;
 }
 
-dms_status dms_decode_step(dms_pool* pool, int32_t n_seqs, const int32_t* seq_ids, int32_t layer0, int32_t n_layers,
-                           const void* q, const void* k, const void* v, const float* logits, void* out,
-                           void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Bytes of split-K partials and page-axis prefix one decode launch of up to
+// `heads` call heads needs at most (the largest attention grid the pool uses).
+size_t decode_scratch_bytes(const dms_pool* pool, int heads) {
+    const dms_pool_config& c = pool->cfg;
+    const int64_t blocks = std::min<int64_t>((int64_t)pool->cu_count * pool->attend_per_cu, dms::kMaxAttendBlocks);
+    const int64_t items = blocks * dms::kAttendWaves + heads;
+    const size_t part = (size_t)items * dms::part_stride(c.n_q_heads / c.n_kv_heads, c.head_dim) * 4;
+    return align_up(part) + (size_t)(heads + 1) * 4;
+}
+
+// One decode step; the partials and prefix live in the pool's arena, or (with
+// scratch) in the given device buffer.  Allocates nothing per call: no device
+// memory, no host containers; with scratch, no timing events either.
+dms_status decode_step(dms_pool* pool, int32_t n_seqs, const int32_t* seq_ids, int32_t layer0, int32_t n_layers,
+                       const void* q, const void* k, const void* v, const float* logits, void* out, void* stream,
+                       char* scratch, size_t scratch_bytes) {
     if (!pool) return fail(DMS_E_INVAL, "pool is NULL");
     const dms_pool_config& c = pool->cfg;
     if (n_seqs < 1 || n_seqs > c.max_seqs) return fail(DMS_E_INVAL, "n_seqs must be in [1, max_seqs]");
@@ -346,12 +390,23 @@ dms_status dms_decode_step(dms_pool* pool, int32_t n_seqs, const int32_t* seq_id
     if (layer0 < 0 || n_layers < 1 || layer0 + n_layers > c.n_layers) return fail(DMS_E_INVAL, "layer range out of bounds");
     if (!q || !k || !v || !out || (c.logit_source == DMS_LOGITS_INPUT && !logits))
         return fail(DMS_E_INVAL, "q, k, v, logits and out must not be NULL");
-    std::vector<char> seen((size_t)c.max_seqs, 0);
+    const int hkv = c.n_kv_heads;
+    const int per_launch = std::max(1, std::min(dms::kMaxCallSeqs, dms::kMaxCallHeads / (n_layers * hkv)));
+    if (scratch) {
+        const size_t need = decode_scratch_bytes(pool, std::min(n_seqs, per_launch) * n_layers * hkv);
+        if (need > scratch_bytes)
+            return fail(DMS_E_INVAL, "this call needs " + std::to_string(need) + " bytes of decode scratch, above the " +
+                                         std::to_string(scratch_bytes) + " the static array holds");
+    }
+    if (++pool->call_stamp == 0) {  // the stamp wrapped: forget every older stamp
+        std::fill(pool->seen.begin(), pool->seen.end(), 0u);
+        pool->call_stamp = 1;
+    }
     for (int i = 0; i < n_seqs; ++i) {
         const int s = seq_ids[i];
         if (s < 0 || s >= c.max_seqs) return fail(DMS_E_INVAL, "seq id out of range");
-        if (seen[s]) return fail(DMS_E_INVAL, "seq ids must be distinct");
-        seen[s] = 1;
+        if (pool->seen[s] == pool->call_stamp) return fail(DMS_E_INVAL, "seq ids must be distinct");
+        pool->seen[s] = pool->call_stamp;
         for (int l = layer0; l < layer0 + n_layers; ++l) {
             const int p = pool->position(s, l);
             if (p < 0) return fail(DMS_E_STATE, "decode on a (seq, layer) that was not prefilled");
@@ -359,11 +414,16 @@ dms_status dms_decode_step(dms_pool* pool, int32_t n_seqs, const int32_t* seq_id
         }
     }
     hipStream_t st = static_cast<hipStream_t>(stream);
-    const int hkv = c.n_kv_heads;
-    const int per_launch = std::max(1, std::min(dms::kMaxCallSeqs, dms::kMaxCallHeads / (n_layers * hkv)));
+    pool->note(st);
     for (int sb = 0; sb < n_seqs; sb += per_launch) {
         dms::DecodeArgs a;
         a.pool = pool->dev;
+        if (scratch) {  // every launch of the call reuses the buffer, in stream order
+            a.pool.partials = reinterpret_cast<float*>(scratch);
+            const int heads = std::min(per_launch, n_seqs - sb) * n_layers * hkv;
+            a.pool.prefix = reinterpret_cast<int32_t*>(scratch + decode_scratch_bytes(pool, heads) -
+                                                       (size_t)(heads + 1) * 4);
+        }
         a.q = static_cast<const uint16_t*>(q);
         a.k = static_cast<const uint16_t*>(k);
         a.v = static_cast<const uint16_t*>(v);
@@ -385,7 +445,7 @@ dms_status dms_decode_step(dms_pool* pool, int32_t n_seqs, const int32_t* seq_id
         grid = std::max<int64_t>(1, std::min<int64_t>(grid, (bound + dms::kAttendWaves - 1) / dms::kAttendWaves));
         a.n_waves = (int32_t)grid * dms::kAttendWaves;
         hipEvent_t* ev = nullptr;
-        if (pool->timing) {
+        if (pool->timing && !scratch) {
             hipError_t ce = hipSuccess;
             ev = timing_events(pool->events, 4, &ce);
             if (!ev) return hip_fail(ce, "timing event");
@@ -399,12 +459,22 @@ dms_status dms_decode_step(dms_pool* pool, int32_t n_seqs, const int32_t* seq_id
     return DMS_OK;
 }
 
+}  // namespace
+
+extern "C" {
+
+dms_status dms_decode_step(dms_pool* pool, int32_t n_seqs, const int32_t* seq_ids, int32_t layer0, int32_t n_layers,
+                           const void* q, const void* k, const void* v, const float* logits, void* out,
+                           void* stream) {
+    return decode_step(pool, n_seqs, seq_ids, layer0, n_layers, q, k, v, logits, out, stream, nullptr, 0);
+}
+
 dms_status dms_query_stats(dms_pool* pool, int32_t seq, dms_stats* out, int32_t* live_per_layer_head) {
     if (!pool || !out) return fail(DMS_E_INVAL, "pool and out must not be NULL");
     const dms_pool_config& c = pool->cfg;
     if (seq < -1 || seq >= c.max_seqs) return fail(DMS_E_INVAL, "seq out of range");
     if (live_per_layer_head && seq < 0) return fail(DMS_E_INVAL, "live_per_layer_head needs seq >= 0");
-    hipError_t e = hipDeviceSynchronize();
+    hipError_t e = pool->sync();
     if (e != hipSuccess) return hip_fail(e, "synchronise");
     const int64_t per_seq = (int64_t)c.n_layers * c.n_kv_heads;
     const int s0 = seq < 0 ? 0 : seq, s1 = seq < 0 ? c.max_seqs : seq + 1;
@@ -437,8 +507,10 @@ dms_status dms_query_stats(dms_pool* pool, int32_t seq, dms_stats* out, int32_t*
     out->pages_free = ctl[dms::kCtlTop];
     out->workspace_bytes = (int64_t)(pool->layout.off[S_N] - pool->layout.off[S_POS]);
     out->position = seq >= 0 ? pool->position(seq, 0) : -1;
-    out->device_error = ctl[dms::kCtlError] ? DMS_E_CAPACITY : DMS_OK;
+    out->device_error = ctl[dms::kCtlError] ? DMS_E_CAPACITY : (ctl[dms::kCtlPosError] ? DMS_E_STATE : DMS_OK);
     if (ctl[dms::kCtlError]) return fail(DMS_E_CAPACITY, "the shared page pool ran out on the device");
+    if (ctl[dms::kCtlPosError])
+        return fail(DMS_E_STATE, "a decode or extend call ran past max_positions on the device (tokens dropped)");
     g_err.clear();
     return DMS_OK;
 }
@@ -449,7 +521,7 @@ dms_status dms_export_live(dms_pool* pool, int32_t seq, int32_t layer, int32_t k
     const dms_pool_config& c = pool->cfg;
     if (seq < 0 || seq >= c.max_seqs || layer < 0 || layer >= c.n_layers || kv_head < 0 || kv_head >= c.n_kv_heads)
         return fail(DMS_E_INVAL, "(seq, layer, kv_head) out of range");
-    hipError_t e = hipDeviceSynchronize();
+    hipError_t e = pool->sync();
     if (e != hipSuccess) return hip_fail(e, "synchronise");
     const int64_t gh = ((int64_t)seq * c.n_layers + layer) * c.n_kv_heads + kv_head;
     int32_t hs[dms::kHS];
@@ -485,7 +557,7 @@ dms_status dms_export_kv(dms_pool* pool, int32_t seq, int32_t layer, int32_t kv_
     const dms_pool_config& c = pool->cfg;
     if (seq < 0 || seq >= c.max_seqs || layer < 0 || layer >= c.n_layers || kv_head < 0 || kv_head >= c.n_kv_heads)
         return fail(DMS_E_INVAL, "(seq, layer, kv_head) out of range");
-    hipError_t e = hipDeviceSynchronize();
+    hipError_t e = pool->sync();
     if (e != hipSuccess) return hip_fail(e, "synchronise");
     const int64_t gh = ((int64_t)seq * c.n_layers + layer) * c.n_kv_heads + kv_head;
     int32_t hs[dms::kHS];
@@ -559,6 +631,7 @@ dms_status dms_export_kv(dms_pool* pool, int32_t seq, int32_t layer, int32_t kv_
 dms_status dms_seq_release(dms_pool* pool, int32_t seq, void* stream) {
     if (!pool) return fail(DMS_E_INVAL, "pool is NULL");
     if (seq < 0 || seq >= pool->cfg.max_seqs) return fail(DMS_E_INVAL, "seq out of range");
+    pool->note(static_cast<hipStream_t>(stream));
     hipError_t e = dms::launch_seq_release(pool->dev, seq, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return hip_fail(e, "release launch");
     for (int l = 0; l < pool->cfg.n_layers; ++l) pool->position(seq, l) = -1;
@@ -575,7 +648,7 @@ dms_status dms_timing_enable(dms_pool* pool, int32_t enable) {
 
 dms_status dms_timing_read(dms_pool* pool, dms_timing* out) {
     if (!pool || !out) return fail(DMS_E_INVAL, "NULL argument");
-    hipError_t e = hipDeviceSynchronize();
+    hipError_t e = pool->sync();
     if (e != hipSuccess) return hip_fail(e, "synchronise");
     std::memset(out, 0, sizeof(*out));
     // events come in start/stop pairs; group g of each call adds to acc[slot[g]]
@@ -590,7 +663,7 @@ dms_status dms_timing_read(dms_pool* pool, dms_timing* out) {
                 *acc[slot[g]] += t;
             }
         }
-        for (hipEvent_t ev : v) hipEventDestroy(ev);
+        for (hipEvent_t ev : v) (void)hipEventDestroy(ev);
         v.clear();
         return hipSuccess;
     };

@@ -70,6 +70,8 @@ constexpr int kMaxCallHeads = 4032;  // heads per launch (4 ints of plan per hea
 constexpr int kCtlTop = 0;    // free pages on the stack
 constexpr int kCtlError = 1;  // sticky: nonzero once the page pool ran out
 constexpr int kCtlVWide = 2;  // sticky: nonzero once a bf16 V value of magnitude >= 2^16 (or inf/NaN) was seen
+constexpr int kCtlPosError = 3;  // sticky: nonzero once a decode or extend call ran past max_positions (the
+                                 // device's position counters decide; tokens past the limit are dropped)
 
 // Nonzero if one of the two bf16 values in w has magnitude >= 2^16, is inf or
 // is NaN (exponent field >= 143): such a value has no fp16 counterpart.

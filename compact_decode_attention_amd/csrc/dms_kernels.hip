@@ -266,7 +266,7 @@ __device__ __forceinline__ void softmax_page(const float (&z)[G], float scale_lo
     float zz[G], mn[G], p[G];
     // the G heads' reductions are independent: issue them side by side
 #pragma unroll
-    for (int g = 0; g < G; ++g) zz[g] = fmaf(z[g], scale_log2, valid ? 0.f : -INFINITY);  // additive mask
+    for (int g = 0; g < G; ++g) zz[g] = valid ? z[g] * scale_log2 : -INFINITY;  // masked by a select
 #pragma unroll
     for (int g = 0; g < G; ++g) mn[g] = fmaxf(m[g], wave_max(zz[g]));
 #pragma unroll
@@ -844,6 +844,11 @@ __device__ void merge_head(const DecodeArgs& a, int ch) {
 // reused), otherwise take slot n_old (a page from the shared pool when a new
 // page starts), write K/V, and advance the head record.  One wave.
 // FP8 pools store the token's K and V rows as E4M3 codes with their row scales.
+// A page fresh from the shared pool may hold rows of a released sequence: its
+// other 63 slots are cleared, so the slots past a head's live count always
+// hold zeros.  The record's position is authoritative (calls replayed from a
+// captured graph advance it without the host): at max_positions the token is
+// dropped and the pool's sticky position flag is set.
 template <int D, bool F8>
 __device__ void append_head(const DecodeArgs& a, int ch) {
     constexpr int VJ = D / 64;
@@ -855,6 +860,10 @@ __device__ void append_head(const DecodeArgs& a, int ch) {
     const int n_pages = hs[kHsPages];
     const int t = hs[kHsPos];
     const int e = hs[kHsExp];
+    if (t >= P.max_positions) {
+        if (lane == 0) atomicOr(&P.ctl[kCtlPosError], 1);
+        return;
+    }
     const uint16_t* kn = a.k + ((size_t)c.row * P.n_kv_heads + c.h) * D;
     const uint16_t* vn = a.v + ((size_t)c.row * P.n_kv_heads + c.h) * D;
     uint4 kchunk = make_uint4(0, 0, 0, 0);
@@ -869,6 +878,7 @@ __device__ void append_head(const DecodeArgs& a, int ch) {
     const int ring_next = (P.ring_len > 0 && sx >= 0 && P.window > 1)
                               ? P.ring[(size_t)c.gh * P.ring_len + (sx % P.window)] : -1;
     int slot, n_new, np = n_pages, page;
+    bool fresh = false;  // a page just taken from the shared pool (the token goes to its slot 0)
     if (e >= 0) {
         slot = e;
         n_new = n_old;
@@ -891,6 +901,7 @@ __device__ void append_head(const DecodeArgs& a, int ch) {
             if (page < 0) return;  // pool exhausted: the sticky flag is set, the token is dropped
             if (lane == 0) P.ptable[(size_t)c.gh * P.pages_per_head + slot / kPage] = page;
             np = slot / kPage + 1;
+            fresh = true;
         } else {
             page = P.ptable[(size_t)c.gh * P.pages_per_head + slot / kPage];
         }
@@ -924,10 +935,28 @@ __device__ void append_head(const DecodeArgs& a, int ch) {
             }
             *reinterpret_cast<uint4*>(kp + ((size_t)lane * kPage + j) * 16) = make_uint4(cw[0], cw[1], cw[2], cw[3]);
         }
+        if (fresh) {  // j = 0: slots 1..63 cleared (codes and scales), V units written whole
+            if (lane > 0) {
 #pragma unroll
-        for (int jj = 0; jj < VJ; ++jj)
-            vp[((size_t)(j / 16) * D + jj * 64 + lane) * 16 + (j % 16)] =
-                (uint8_t)e4m3_encode(bf16_to_f32(vv[jj]) / vs);
+                for (int cc = 0; cc < D / 16; ++cc)
+                    *reinterpret_cast<uint4*>(kp + ((size_t)cc * kPage + lane) * 16) = make_uint4(0, 0, 0, 0);
+                P.kscale[(size_t)page * kPage + lane] = 0.f;
+                P.vscale[(size_t)page * kPage + lane] = 0.f;
+            }
+#pragma unroll
+            for (int jj = 0; jj < VJ; ++jj) {
+                const uint32_t code = e4m3_encode(bf16_to_f32(vv[jj]) / vs);
+#pragma unroll
+                for (int b = 0; b < 4; ++b)
+                    *reinterpret_cast<uint4*>(vp + ((size_t)b * D + jj * 64 + lane) * 16) =
+                        make_uint4(b == 0 ? code : 0u, 0, 0, 0);
+            }
+        } else {
+#pragma unroll
+            for (int jj = 0; jj < VJ; ++jj)
+                vp[((size_t)(j / 16) * D + jj * 64 + lane) * 16 + (j % 16)] =
+                    (uint8_t)e4m3_encode(bf16_to_f32(vv[jj]) / vs);
+        }
         if (lane == 0) {
             P.kscale[(size_t)page * kPage + j] = ks;
             P.vscale[(size_t)page * kPage + j] = vs;
@@ -937,10 +966,26 @@ __device__ void append_head(const DecodeArgs& a, int ch) {
         uint16_t* vp = P.vpages + (size_t)page * (kPage * D);
         if (lane < D / 8) *reinterpret_cast<uint4*>(kp + ((size_t)lane * kPage + j) * 8) = kchunk;
         uint32_t wide = 0;  // a stored V value without an fp16 counterpart: sticky pool flag
+        if (fresh) {  // j = 0: slots 1..63 cleared, V units written whole
+            if (lane > 0) {
 #pragma unroll
-        for (int jj = 0; jj < VJ; ++jj) {
-            vp[((size_t)(j / 8) * D + jj * 64 + lane) * 8 + (j % 8)] = vv[jj];
-            wide |= bf16x2_wide(vv[jj]);
+                for (int cc = 0; cc < D / 8; ++cc)
+                    *reinterpret_cast<uint4*>(kp + ((size_t)cc * kPage + lane) * 8) = make_uint4(0, 0, 0, 0);
+            }
+#pragma unroll
+            for (int jj = 0; jj < VJ; ++jj) {
+#pragma unroll
+                for (int b = 0; b < 8; ++b)
+                    *reinterpret_cast<uint4*>(vp + ((size_t)b * D + jj * 64 + lane) * 8) =
+                        make_uint4(b == 0 ? (uint32_t)vv[jj] : 0u, 0, 0, 0);
+                wide |= bf16x2_wide(vv[jj]);
+            }
+        } else {
+#pragma unroll
+            for (int jj = 0; jj < VJ; ++jj) {
+                vp[((size_t)(j / 8) * D + jj * 64 + lane) * 8 + (j % 8)] = vv[jj];
+                wide |= bf16x2_wide(vv[jj]);
+            }
         }
         if (wide) atomicOr(&P.ctl[kCtlVWide], 1);
     }
@@ -1255,6 +1300,9 @@ __global__ __launch_bounds__(256) void prefill_compact8_kernel(PrefillArgs a) {
 // last token of each chain is still live after the chunk, so only it is written.
 // One block per kv head; slot of each row and chain parents in LDS (chunks up to
 // 4096 rows; else in the inv and pcnt scratch); the slots end in inv.
+// t0 is the head record's position (authoritative: calls replayed from a
+// captured graph advance it without the host); a chunk that would run past
+// max_positions is dropped and sets the pool's sticky position flag.
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ bool ext_marked(const PrefillArgs& a, int r, int h) {
     return eviction_logit(a.pool, a.logits, a.k, r, h) > 0.f;
@@ -1275,7 +1323,7 @@ __global__ __launch_bounds__(1024) void extend_update_kernel(PrefillArgs a) {
     const int gh = (a.seq * P.n_layers + a.layer) * P.n_kv_heads + h;
     int32_t* hs = P.hstate + (size_t)gh * kHS;
     const int n_old = hs[kHsLive], np_old = hs[kHsPages];
-    const int T = a.n_tokens, t0 = a.t0, w = P.window;
+    const int T = a.n_tokens, t0 = hs[kHsPos], w = P.window;
     const bool in_lds = T <= kLdsRows;
     int32_t* const gval = P.inv + (size_t)h * P.max_positions;
     int32_t* val = in_lds ? s_val : gval;                                    // slot of row r (roots: final)
@@ -1286,6 +1334,11 @@ __global__ __launch_bounds__(1024) void extend_update_kernel(PrefillArgs a) {
             for (int r = tid; r < T; r += 1024) gval[r] = s_val[r];
         }
     };
+    if ((int64_t)t0 + T > P.max_positions) {  // nothing is stored: every row's slot is -1
+        if (tid == 0) atomicOr(&P.ctl[kCtlPosError], 1);
+        for (int r = tid; r < T; r += 1024) gval[r] = -1;
+        return;
+    }
     const bool evict = P.ring_len > 0;
     const int per = (T + 1023) / 1024;
     const int r0 = min(tid * per, T), r1 = min(r0 + per, T);
@@ -1369,6 +1422,25 @@ __global__ __launch_bounds__(1024) void extend_update_kernel(PrefillArgs a) {
     }
     for (int j = tid; j < need; j += 1024)
         P.ptable[(size_t)gh * P.pages_per_head + np_old + j] = P.stack[s_base - 1 - j];
+    // Pages fresh from the shared pool may hold rows of a released sequence.
+    // Every new page but the last is filled by the chunk's fresh slots; the last
+    // one is cleared here whole (the write kernel, which runs after this one,
+    // fills its slots below n_new), so slots past the live count hold zeros.
+    if (need > 0) {
+        const size_t pg = (size_t)P.stack[s_base - need];
+        const int D = P.head_dim;
+        const int pbytes = kPage * D * (P.fp8 ? 1 : 2);
+        uint4* kz = reinterpret_cast<uint4*>(reinterpret_cast<uint8_t*>(P.kpages) + pg * pbytes);
+        uint4* vz = reinterpret_cast<uint4*>(reinterpret_cast<uint8_t*>(P.vpages) + pg * pbytes);
+        for (int u = tid; u < pbytes / 16; u += 1024) {
+            kz[u] = make_uint4(0, 0, 0, 0);
+            vz[u] = make_uint4(0, 0, 0, 0);
+        }
+        if (P.fp8 && tid < kPage) {
+            P.kscale[pg * kPage + tid] = 0.f;
+            P.vscale[pg * kPage + tid] = 0.f;
+        }
+    }
     // ring entries of the last w positions that are new
     if (evict)
         for (int r = max(0, T - w) + tid; r < T; r += 1024)
@@ -1454,7 +1526,8 @@ __global__ __launch_bounds__(256) void extend_write_kernel(PrefillArgs a) {
     if (tid < 64 && s_slot[tid] >= 0) {
         const int slot = s_slot[tid];
         const size_t sl = (size_t)s_page[tid] * kPage + slot % kPage;
-        P.slot_pos[sl] = a.t0 + rb + tid;
+        // the update kernel advanced the record's position past the chunk
+        P.slot_pos[sl] = P.hstate[(size_t)gh * kHS + kHsPos] - T + rb + tid;
         if constexpr (F8) {
             const size_t row = (size_t)(rb + tid) * hkv + h;
             P.kscale[sl] = P.q8_scales(0)[row];

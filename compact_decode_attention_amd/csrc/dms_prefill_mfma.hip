@@ -600,20 +600,23 @@ void prefill_attend_kernel(PrefillArgs a) {
 // marked (its mark is in the window ring while it is within w of t0), else
 // INT_MAX.  Written to the inv scratch ([kv head][slot]), which the attention
 // reads per far-field tile and the chain resolution overwrites afterwards.
-__device__ __forceinline__ void expiry_block(const PrefillArgs& a, int bx, int h) {
+// n_old and t0 come from the head record (the device's counters decide); the
+// nb blocks of a kv head stride over its slots.
+__device__ __forceinline__ void expiry_block(const PrefillArgs& a, int bx, int nb, int h) {
     const PoolDev& P = a.pool;
     const int w = P.window;
     const int gh = (a.seq * P.n_layers + a.layer) * P.n_kv_heads + h;
-    const int j = bx * 256 + threadIdx.x;
-    if (j >= P.hstate[(size_t)gh * kHS + kHsLive]) return;
-    const int page = P.ptable[(size_t)gh * P.pages_per_head + j / kPage];
-    const int pos = P.slot_pos[(size_t)page * kPage + j % kPage];
-    int mk = 0;
-    if (P.ring_len > 0 && pos >= a.t0 - w) {
-        const int e = P.ring[(size_t)gh * P.ring_len + pos % w];
-        mk = e >= 0 && (e & 1);
+    const int n_old = P.hstate[(size_t)gh * kHS + kHsLive], t0 = P.hstate[(size_t)gh * kHS + kHsPos];
+    for (int j = bx * 256 + threadIdx.x; j < n_old; j += nb * 256) {
+        const int page = P.ptable[(size_t)gh * P.pages_per_head + j / kPage];
+        const int pos = P.slot_pos[(size_t)page * kPage + j % kPage];
+        int mk = 0;
+        if (P.ring_len > 0 && pos >= t0 - w) {
+            const int e = P.ring[(size_t)gh * P.ring_len + pos % w];
+            mk = e >= 0 && (e & 1);
+        }
+        P.inv[(size_t)h * P.max_positions + j] = mk ? pos + w - t0 : INT_MAX;
     }
-    P.inv[(size_t)h * P.max_positions + j] = mk ? pos + w - a.t0 : INT_MAX;
 }
 
 // Extend calls with output: the chunk's unmarked rows (never evicted, so every
@@ -721,11 +724,11 @@ __device__ __forceinline__ void compact_block(const PrefillArgs& a, int bx, int 
 // expiry rows of the stored slots (next NE), the gathered unmarked rows (rest).
 template <int D, bool F8>
 __global__ __launch_bounds__(256) void extend_prep_kernel(PrefillArgs a) {
-    const int nv = (a.n_tokens + 63) / 64, ne = max(1, (a.t0 + 255) / 256);
+    const int nv = (a.n_tokens + 63) / 64, ne = max(1, (a.t0 + 255) / 256);  // t0: the host's count (a size hint)
     __shared__ uint16_t s_v[64][D + 8];
     const int bx = blockIdx.x, h = blockIdx.y;
     if (bx < nv) vt_rows<D, F8>(a, bx * 64, h, s_v);
-    else if (bx < nv + ne) expiry_block(a, bx - nv, h);
+    else if (bx < nv + ne) expiry_block(a, bx - nv, ne, h);
     else compact_block<D, F8>(a, bx - nv - ne, h);
 }
 

@@ -26,13 +26,28 @@
  *  - All tensor arguments are device pointers owned by the caller; they must
  *    stay valid until the work enqueued on `stream` has finished.  bf16 values
  *    are passed as their 16-bit patterns.  Rows are contiguous, 16-byte aligned.
+ *    K and V values must be finite (bf16 and FP8 pools alike): a query whose
+ *    key tile holds a non-finite value it does not see can still come out
+ *    non-finite (a zero weight times an infinite value).
  *  - `stream` is a hipStream_t (NULL = the legacy default stream).  Calls
  *    enqueue kernels and return without waiting, except dms_pool_create,
- *    dms_pool_destroy, dms_query_stats, dms_export_live and dms_export_kv, which
- *    synchronise.
+ *    dms_pool_destroy, dms_query_stats, dms_export_live, dms_export_kv and
+ *    dms_timing_read, which first wait for the streams the pool's calls were
+ *    enqueued on (not for the whole device).
  *  - Errors found on the host are returned at once and nothing is enqueued.
- *    A device-side failure (the shared page pool running out) sets a sticky
- *    flag that the next synchronising call returns as DMS_E_CAPACITY.
+ *    Device-side failures set sticky flags that the next synchronising call
+ *    returns: DMS_E_CAPACITY when the shared page pool ran out (the token or
+ *    chunk that needed a page is dropped), DMS_E_STATE when a decode or extend
+ *    call ran past max_positions (the tokens past it are dropped).
+ *  - HIP graph capture: dms_decode_step, dms_extend, dms_prefill and
+ *    dms_seq_release may be captured.  The positions live in the device's
+ *    per-head records, which every replay advances and every kernel reads; the
+ *    host keeps a copy for its argument checks, which replays do not advance
+ *    and which dms_query_stats refreshes from the device.  So a check the host
+ *    makes at call time may pass on a stale copy; the kernels check again
+ *    (the sticky DMS_E_STATE above).  Work replayed on a stream the pool's
+ *    calls never used must be finished by the caller before a synchronising
+ *    call.
  *  - Error text for the last failing call on the calling thread:
  *    dms_last_error().  No C++ exception crosses this interface.
  *  - A pool is not thread-safe; use it from one host thread and order all of
@@ -90,7 +105,12 @@ enum {
  *                        Details und Implementierung"; stiva.ai "Nvidia DMS ...",
  *                        section on the model managing its own memory).  The
  *                        channel keeps its value in attention; the logits
- *                        argument of the calls is ignored and may be NULL. */
+ *                        argument of the calls is ignored and may be NULL.
+ *                        K arrives after positional encoding, so a model with
+ *                        rotary embeddings must carry the logit in a channel
+ *                        the rotation leaves alone (past its rotary dims, or
+ *                        written after the rotation): a rotated channel mixes
+ *                        with its partner and would vary with position. */
 #define DMS_LOGITS_INPUT 0
 #define DMS_LOGITS_K_CHANNEL 1
 
@@ -121,17 +141,24 @@ typedef struct {
  * max_pages shared pages it holds the head records, page tables, window rings,
  * split-K partials and the prefill / extend scratch, which includes
  * ceil(max_positions / 64) scratch pages per kv head (max_pages plus these must
- * stay below 2^31). */
+ * stay below 2^31).  (The store is paged per (layer, kv head) with variable
+ * token counts and pages handed back one by one: the FastDMS announcement on
+ * molayo1419.me, "What's the catch?" table, PagedAttention row.) */
 size_t dms_pool_bytes(const dms_pool_config* cfg);
 
 /* Create a pool inside the caller's arena (device memory, >= dms_pool_bytes()
  * bytes, 256-byte aligned).  Clears the arena and fills the page free list on
  * `stream`, then synchronises.  The arena stays owned by the caller and must
- * outlive the pool. */
+ * outlive the pool.  (A compact store whose evicted slots are reclaimed, one
+ * shared page allocator for all sequences: the FastDMS announcement on
+ * molayo1419.me, release paragraph and "What's the catch?" table, PagedAttention
+ * row.)  Errors: DMS_E_INVAL (configuration, NULL or misaligned arena),
+ * DMS_E_NOMEM (arena too small), DMS_E_HIP. */
 dms_status dms_pool_create(const dms_pool_config* cfg, void* arena, size_t arena_bytes,
                            void* stream, dms_pool** out);
 
-/* Synchronise the device and free the host-side handle (not the arena). */
+/* Wait for the pool's streams and free the host-side handle (not the arena,
+ * which the caller owns). */
 dms_status dms_pool_destroy(dms_pool* pool);
 
 /* Prefill: the first n_tokens tokens (positions 0 .. n_tokens-1) of one
@@ -147,7 +174,12 @@ dms_status dms_pool_destroy(dms_pool* pool);
  *          DMS_LOGITS_K_CHANNEL)
  *   out    bf16 [n_tokens][n_q_heads][head_dim] or NULL
  * q and k arrive after any positional encoding.  Returns DMS_E_STATE if this
- * (seq, layer) already holds tokens (release the sequence first).
+ * (seq, layer) already holds tokens (release the sequence first), DMS_E_INVAL
+ * for out-of-range arguments or NULL inputs.  (Masks from delayed eviction:
+ * "NVIDIA veroeffentlicht Qwen3-8B-DMS-8x ..." news page, section "Dynamic
+ * Memory Sparsification (DMS): Eine innovative Loesung"; prefill throughput is
+ * one of the two columns of the FastDMS announcement's speed table, on
+ * molayo1419.me.)
  * Precision: fp32 accumulation; each output is within 2e-3 + 1e-2 |ref| of the
  * masked attention over the inputs (FP8 pools: over value(code) * scale).  A
  * bf16 pool that has seen a V value of magnitude 2^16 or more (in any prompt,
@@ -173,7 +205,15 @@ dms_status dms_prefill(dms_pool* pool, int32_t seq, int32_t layer, int32_t n_tok
  *   out     bf16 [n_layers][n_seqs][n_q_heads][head_dim]
  * Each (seq, layer) keeps its own position counter; the new token's position
  * is that counter.  A model calls this once per layer (n_layers = 1); a caller
- * whose layers have independent inputs may step several layers in one call. */
+ * whose layers have independent inputs may step several layers in one call.
+ * Errors: DMS_E_INVAL (arguments), DMS_E_STATE (a (seq, layer) not prefilled or
+ * at max_positions by the host's count), DMS_E_HIP; a page-pool exhaustion or a
+ * position past max_positions found on the device is reported by the next
+ * synchronising call.  (The step order is the delayed eviction of "NVIDIA
+ * veroeffentlicht Qwen3-8B-DMS-8x ..." news page, section "Dynamic Memory
+ * Sparsification (DMS): Eine innovative Loesung", and of stiva.ai "Nvidia DMS
+ * ...", section "Klyuchevoe izobretenie: delayed eviction": a marked token
+ * stays readable for w steps, its own included, then its slot is reclaimed.) */
 dms_status dms_decode_step(dms_pool* pool, int32_t n_seqs, const int32_t* seq_ids,
                            int32_t layer0, int32_t n_layers, const void* q, const void* k,
                            const void* v, const float* logits, void* out, void* stream);
@@ -216,21 +256,31 @@ typedef struct {
     int32_t device_error;         /* sticky device status: DMS_OK or DMS_E_CAPACITY */
 } dms_stats;
 
-/* Synchronise and report the store's size for one sequence (seq >= 0) or for
- * all sequences (seq = -1).  live_per_layer_head, when not NULL, is a host
- * array [n_layers][n_kv_heads] (seq >= 0 only) that receives the live counts.
- * Returns DMS_E_CAPACITY (after filling *out) if the sticky device flag is set. */
+/* Wait for the pool's streams and report the store's size for one sequence
+ * (seq >= 0) or for all sequences (seq = -1).  live_per_layer_head, when not
+ * NULL, is a host array [n_layers][n_kv_heads] (seq >= 0 only) that receives the
+ * live counts.  The byte figures are the memory the store really holds, as the
+ * FastDMS announcement's memory table reports KV memory (molayo1419.me):
+ * live bytes follow the live tokens, allocated bytes the whole pages behind
+ * them.  Also refreshes the host's copy of the positions from the device.
+ * Returns DMS_E_CAPACITY or DMS_E_STATE (after filling *out) if a sticky
+ * device flag is set. */
 dms_status dms_query_stats(dms_pool* pool, int32_t seq, dms_stats* out,
                            int32_t* live_per_layer_head);
 
-/* Synchronise and list the positions of the tokens one (seq, layer, kv_head)
- * holds, ascending, into the host array positions[cap]; *n receives the count
- * (DMS_E_INVAL if it exceeds cap). */
+/* Wait for the pool's streams and list the positions of the tokens one (seq,
+ * layer, kv_head) holds, ascending, into the host array positions[cap]; *n
+ * receives the count (DMS_E_INVAL if it exceeds cap).  The list is what a
+ * comparison with the eviction-disabled reference needs (the FastDMS
+ * announcement's quality-method paragraph, molayo1419.me: the same engine with
+ * a 1M-token window keeps every token). */
 dms_status dms_export_live(dms_pool* pool, int32_t seq, int32_t layer, int32_t kv_head,
                            int32_t* positions, int32_t cap, int32_t* n);
 
-/* Synchronise and copy what one (seq, layer, kv_head) stores, row by row in
- * ascending position order, to host arrays:
+/* Wait for the pool's streams and copy what one (seq, layer, kv_head) stores,
+ * row by row in ascending position order, to host arrays (eviction decides
+ * first and FP8 quantisation applies to what stays: the FastDMS announcement's
+ * quality-method paragraph, molayo1419.me):
  *   positions int32 [cap]
  *   k, v      [cap][head_dim]: bf16 bits (bf16 pools) or E4M3 codes (FP8 pools)
  *   k_scale, v_scale fp32 [cap]: the row scales (FP8 pools), 1 (bf16 pools)
@@ -240,15 +290,20 @@ dms_status dms_export_kv(dms_pool* pool, int32_t seq, int32_t layer, int32_t kv_
                          int32_t* positions, void* k, void* v, float* k_scale, float* v_scale, int32_t* n);
 
 /* Return every page of a sequence to the shared pool and forget its tokens on
- * all layers (enqueued on `stream`).  The sequence may then be prefilled again. */
+ * all layers (enqueued on `stream`).  The sequence may then be prefilled again.
+ * Another sequence may get these pages next; their old rows are never read as
+ * live tokens (slots past a head's live count are cleared when a page is
+ * taken).  (Pages handed back one by one: the FastDMS announcement,
+ * "What's the catch?" table, PagedAttention row.) */
 dms_status dms_seq_release(dms_pool* pool, int32_t seq, void* stream);
 
 /* Kernel timing for measurement.  While enabled, the kernels of every decode
  * launch and of every prefill that produces an output are dispatched with HIP
  * start/stop events that the dispatches themselves record, so the times cover
- * kernel execution only.  dms_timing_read synchronises, adds up the times of
- * everything recorded since the last read (milliseconds), counts the calls, and
- * releases the events.  Disabled by default. */
+ * kernel execution only.  dms_timing_read waits for the pool's streams, adds up
+ * the times of everything recorded since the last read (milliseconds), counts
+ * the calls, and releases the events.  Disabled by default.  (Decode and
+ * prefill throughput are what the FastDMS announcement's speed table reports.) */
 typedef struct {
     double decode_attend_ms;   /* split-K attention kernels */
     double decode_merge_ms;    /* merge + evict/append kernels */
