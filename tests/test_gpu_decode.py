@@ -20,7 +20,7 @@ def run_case(case, check_live_every=1, layer_batched=True):
                 out = r.decode(i)
             else:
                 out = np.concatenate([r.decode(i, layer0=l, n_layers=1) for l in range(case.n_layers)])
-            e = r.check_outputs(out, i)
+            e = r.check_outputs(out, i, record="decode (fp8 pool)" if case.kv_format else "decode")
             worst = (max(worst[0], e[0]), max(worst[1], e[1]))
             if check_live_every and (i % check_live_every == 0 or i == case.steps - 1):
                 r.check_live([case.ctx_lens[s] + i for s in range(case.n_seqs)])
@@ -42,6 +42,20 @@ def test_tiny_d64_ctx1024_end_to_end():
     assert st.device_error == 0
     r.close()
     print("worst abs %.3g rel %.3g" % worst)
+
+
+@pytest.mark.parametrize("kv_format", [0, 1])
+@pytest.mark.parametrize("scale", [0.02, 0.3])
+@pytest.mark.parametrize("D", [64, 128])
+def test_decode_softmax_scale(scale, D, kv_format):
+    """A softmax scale other than 1/sqrt(head_dim) from the pool config: every
+    step's outputs (layer-batched and per-layer calls), bf16 and FP8 pools."""
+    case = Case(n_layers=2, n_q_heads=16, n_kv_heads=4, head_dim=D, window=30, ctx_lens=[333, 129], steps=12,
+                seed=int(scale * 1000) + D, kv_format=kv_format, softmax_scale=scale)
+    r, _ = run_case(case, check_live_every=6)
+    r.close()
+    r, _ = run_case(case, check_live_every=0, layer_batched=False)
+    r.close()
 
 
 def test_page_order_does_not_change_results():

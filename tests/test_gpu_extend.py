@@ -37,7 +37,7 @@ def make_inputs(T, Hq, Hkv, D, seed, marks):
 
 
 def run_extend(ctx, chunks, w, marks="random", G=4, D=128, Hkv=2, seed=5, kv_format=0, with_out=True,
-               decode_steps=6, max_pages=None):
+               decode_steps=6, max_pages=None, softmax_scale=0.0):
     import torch
     import compact_decode_attention_amd as dms
     Hq = G * Hkv
@@ -52,8 +52,9 @@ def run_extend(ctx, chunks, w, marks="random", G=4, D=128, Hkv=2, seed=5, kv_for
     def ref_out(t0, n):
         if fp8:
             return oracle.attend_fp8(q[t0:t0 + n], np.arange(t0, t0 + n), k8[:t0 + n], ks[:t0 + n], v8[:t0 + n],
-                                     vs[:t0 + n], mk[:t0 + n], w)
-        return oracle.attend(q[t0:t0 + n], np.arange(t0, t0 + n), k[:t0 + n], v[:t0 + n], mk[:t0 + n], w)
+                                     vs[:t0 + n], mk[:t0 + n], w, softmax_scale)
+        return oracle.attend(q[t0:t0 + n], np.arange(t0, t0 + n), k[:t0 + n], v[:t0 + n], mk[:t0 + n], w,
+                             softmax_scale)
 
     def check_store(t):
         for h in range(Hkv):
@@ -66,7 +67,8 @@ def run_extend(ctx, chunks, w, marks="random", G=4, D=128, Hkv=2, seed=5, kv_for
                 assert np.array_equal(kc, k[pos, h]) and np.array_equal(vc, v[pos, h]), ("stored rows", t, h)
 
     pool = dms.Pool(n_layers=1, n_q_heads=Hq, n_kv_heads=Hkv, head_dim=D, window=w, max_seqs=1,
-                    max_positions=total, max_pages=max_pages or Hkv * ((total + 63) // 64), kv_format=kv_format)
+                    max_positions=total, max_pages=max_pages or Hkv * ((total + 63) // 64), kv_format=kv_format,
+                    softmax_scale=softmax_scale)
     dev = "cuda"
     try:
         pool.prefill(0, 0, bf(k[:ctx], torch).to(dev), bf(v[:ctx], torch).to(dev), torch.from_numpy(lg[:ctx]).to(dev))
@@ -78,7 +80,8 @@ def run_extend(ctx, chunks, w, marks="random", G=4, D=128, Hkv=2, seed=5, kv_for
                         out=out)
             if with_out:
                 got = out.view(torch.int16).cpu().numpy().view(np.uint16)
-                assert_close(got, ref_out(t, n), "extend t0=%d n=%d w=%d marks=%s" % (t, n, w, marks))
+                assert_close(got, ref_out(t, n), "extend t0=%d n=%d w=%d marks=%s" % (t, n, w, marks),
+                             record="extend (fp8 pool)" if fp8 else "extend")
             t += n
             check_store(t - 1)
         for i in range(decode_steps):
@@ -100,6 +103,14 @@ def run_extend(ctx, chunks, w, marks="random", G=4, D=128, Hkv=2, seed=5, kv_for
 @pytest.mark.parametrize("chunks", [[1], [2, 3], [15, 16, 17], [100], [200, 1, 64]])
 def test_extend_chunks(chunks, w, marks):
     run_extend(150, chunks, w, marks, seed=len(chunks) * 7 + w)
+
+
+@pytest.mark.parametrize("kv_format", [0, 1])
+@pytest.mark.parametrize("scale", [0.02, 0.3])
+def test_extend_softmax_scale(scale, kv_format):
+    """A softmax scale other than 1/sqrt(head_dim) from the pool config, in the
+    chunks' attention and the decode steps after them, on bf16 and FP8 pools."""
+    run_extend(130, [40, 97], 24, seed=int(scale * 100) + 3, kv_format=kv_format, softmax_scale=scale)
 
 
 def test_extend_eviction_disabled():

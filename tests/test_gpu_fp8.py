@@ -194,7 +194,9 @@ def test_fp8_pool_stats_count_fp8_bytes():
         for i in range(case.steps):
             r.decode(i)
         st, _ = r.pool.stats(0)
-        assert st.kv_bytes_live == st.live_slots * 2 * (128 + 4)
-        assert st.kv_bytes_allocated == st.pages_used * 64 * 2 * (128 + 4)
+        t = case.ctx_lens[0] + case.steps - 1
+        ref = oracle.kv_bytes(t, case.window, case.marks(0, 0), 128, fp8=True)
+        assert (st.kv_bytes_live, st.kv_bytes_allocated, st.kv_bytes_dense_equiv) == ref
+        assert st.kv_bytes_allocated == st.pages_used * 64 * 2 * oracle.row_bytes(128, fp8=True)
     finally:
         r.close()

@@ -30,7 +30,8 @@ def make_inputs(T, Hq, Hkv, D, seed, marks):
     return q, k, v, lg
 
 
-def run_prefill(T, w, marks, G=4, D=128, Hkv=2, seed=5, extra_positions=0, decode_steps=0):
+def run_prefill(T, w, marks, G=4, D=128, Hkv=2, seed=5, extra_positions=0, decode_steps=0, softmax_scale=0.0,
+                kv_format=0):
     import torch
     import compact_decode_attention_amd as dms
     Hq = G * Hkv
@@ -38,15 +39,27 @@ def run_prefill(T, w, marks, G=4, D=128, Hkv=2, seed=5, extra_positions=0, decod
     q, k, v, lg = make_inputs(total, Hq, Hkv, D, seed, marks)
     maxpos = total + extra_positions
     pool = dms.Pool(n_layers=1, n_q_heads=Hq, n_kv_heads=Hkv, head_dim=D, window=w, max_seqs=1,
-                    max_positions=maxpos, max_pages=Hkv * ((maxpos + 63) // 64))
+                    max_positions=maxpos, max_pages=Hkv * ((maxpos + 63) // 64), softmax_scale=softmax_scale,
+                    kv_format=kv_format)
+    mk = oracle.marks(lg)
+    if kv_format:
+        k8, ks = oracle.quantize_rows(k)
+        v8, vs = oracle.quantize_rows(v)
+
+    def ref_out(t0, n):
+        if kv_format:
+            return oracle.attend_fp8(q[t0:t0 + n], np.arange(t0, t0 + n), k8[:t0 + n], ks[:t0 + n], v8[:t0 + n],
+                                     vs[:t0 + n], mk[:t0 + n], w, softmax_scale)
+        return oracle.attend(q[t0:t0 + n], np.arange(t0, t0 + n), k[:t0 + n], v[:t0 + n], mk[:t0 + n], w,
+                             softmax_scale)
+
     dev = "cuda"
     out = torch.empty((T, Hq, D), dtype=torch.bfloat16, device=dev)
     pool.prefill(0, 0, bf(k[:T], torch).to(dev), bf(v[:T], torch).to(dev), torch.from_numpy(lg[:T]).to(dev),
                  q=bf(q[:T], torch).to(dev), out=out)
     got = out.view(torch.int16).cpu().numpy().view(np.uint16)
-    mk = oracle.marks(lg)
-    ref = oracle.attend(q[:T], np.arange(T), k[:T], v[:T], mk[:T], w)
-    assert_close(got, ref, "prefill T=%d w=%d marks=%s G=%d D=%d" % (T, w, marks, G, D))
+    assert_close(got, ref_out(0, T), "prefill T=%d w=%d marks=%s G=%d D=%d" % (T, w, marks, G, D),
+                 record="prefill (fp8 pool)" if kv_format else "prefill")
     for h in range(Hkv):
         assert np.array_equal(pool.export_live(0, 0, h), oracle.live_positions(T - 1, w, mk[:T, h]))
     for i in range(decode_steps):
@@ -54,8 +67,8 @@ def run_prefill(T, w, marks, G=4, D=128, Hkv=2, seed=5, extra_positions=0, decod
         o = torch.empty((1, 1, Hq, D), dtype=torch.bfloat16, device=dev)
         pool.decode_step([0], 0, bf(q[t], torch).to(dev).view(1, 1, Hq, D), bf(k[t], torch).to(dev).view(1, 1, Hkv, D),
                          bf(v[t], torch).to(dev).view(1, 1, Hkv, D), torch.from_numpy(lg[t]).to(dev).view(1, 1, Hkv), o)
-        r = oracle.attend(q[t:t + 1], [t], k[:t + 1], v[:t + 1], mk[:t + 1], w)[0]
-        assert_close(o.view(torch.int16).cpu().numpy().view(np.uint16)[0, 0], r, "decode after prefill t=%d" % t)
+        assert_close(o.view(torch.int16).cpu().numpy().view(np.uint16)[0, 0], ref_out(t, 1)[0],
+                     "decode after prefill t=%d" % t)
     pool.close()
 
 
@@ -82,6 +95,16 @@ def test_prefill_then_decode():
     run_prefill(257, 32, "random", decode_steps=40, seed=9)
 
 
+@pytest.mark.parametrize("kv_format", [0, 1])
+@pytest.mark.parametrize("scale", [0.02, 0.3])
+@pytest.mark.parametrize("D", [64, 128])
+def test_prefill_softmax_scale(scale, D, kv_format):
+    """A softmax scale other than 1/sqrt(head_dim) from the pool config, in the
+    prefill and in the decode steps after it, on bf16 and FP8 pools."""
+    run_prefill(300, 48, "random", D=D, seed=int(scale * 100) + D, decode_steps=5, softmax_scale=scale,
+                kv_format=kv_format)
+
+
 def test_prefill_32k_sampled_rows():
     """Qwen3-8B-shaped prefill of one layer: 32768 tokens, 32 q / 8 kv heads,
     D=128, w=512, keep score N(-1.2, 1); sampled query rows vs the oracle."""
@@ -102,7 +125,7 @@ def test_prefill_32k_sampled_rows():
                       rng.integers(0, T, 24).tolist()))
     mk = oracle.marks(lg)
     ref = oracle.attend(q[rows], np.array(rows), k, v, mk, w)
-    assert_close(got[rows], ref, "prefill 32k rows")
+    assert_close(got[rows], ref, "prefill 32k rows", record="qwen3-8b_prefill32k (sampled rows)")
     for h in range(Hkv):
         assert np.array_equal(pool.export_live(0, 0, h), oracle.live_positions(T - 1, w, mk[:, h]))
     pool.close()

@@ -7,7 +7,7 @@ import pytest
 
 import oracle
 import synth
-from dms_case import assert_close
+from dms_case import ATOL, assert_close
 
 pytestmark = pytest.mark.gpu
 
@@ -54,7 +54,7 @@ def run_workload(name, steps, check_steps, per_layer_steps=()):
             got = out.view(torch.int16).cpu().numpy().view(np.uint16)
             for l in range(L):
                 ref = oracle.attend(Q[i, l][None], [t], K[l][:t + 1], V[l][:t + 1], marks[l][:t + 1], w)[0]
-                e = assert_close(got[l, 0], ref, "%s step %d layer %d" % (name, i, l))
+                e = assert_close(got[l, 0], ref, "%s step %d layer %d" % (name, i, l), record=name, max_abs=ATOL)
                 worst = max(worst, e[0])
     st, live = pool.stats(0, per_head=True)
     assert st.position == total and st.device_error == 0
@@ -65,7 +65,8 @@ def run_workload(name, steps, check_steps, per_layer_steps=()):
             assert np.array_equal(pool.export_live(0, l, h), ref), (l, h)
     assert st.live_slots == sum(len(oracle.live_positions(total - 1, w, marks[l][:, h]))
                                 for l in range(L) for h in range(H))
-    assert st.kv_bytes_live == st.live_slots * 2 * D * 2
+    ref = np.sum([oracle.kv_bytes(total - 1, w, marks[l], D) for l in range(L)], axis=0)
+    assert (st.kv_bytes_live, st.kv_bytes_allocated, st.kv_bytes_dense_equiv) == tuple(ref)
     pool.close()
     return worst
 
@@ -149,7 +150,8 @@ def test_qwen3_8b_batch32_ragged_full_size():
                 K, V, Q = host[(s, l)]
                 t = ctx[s] + i
                 ref = oracle.attend(Q[i][None], [t], K[:t + 1], V[:t + 1], marks[(s, l)][:t + 1], w)[0]
-                assert_close(got[l, s], ref, "ragged step %d seq %d layer %d" % (i, s, l))
+                assert_close(got[l, s], ref, "ragged step %d seq %d layer %d" % (i, s, l),
+                             record="qwen3-8b_batch32_ragged (sampled)", max_abs=ATOL)
     st_all, _ = pool.stats()
     assert st_all.device_error == 0
     total_live = 0
@@ -162,6 +164,8 @@ def test_qwen3_8b_batch32_ragged_full_size():
             assert np.array_equal(live[l], ref), (s, l)
             total_live += sum(ref)
     assert st_all.live_slots == total_live
+    ref = np.sum([oracle.kv_bytes(ctx[s] + S - 1, w, marks[(s, l)], D) for s in range(B) for l in range(L)], axis=0)
+    assert (st_all.kv_bytes_live, st_all.kv_bytes_allocated, st_all.kv_bytes_dense_equiv) == tuple(ref)
     rng = np.random.default_rng(3)
     heads = [(s, l, h) for (s, l) in sampled for h in range(H)]
     heads += [(int(rng.integers(B)), int(rng.integers(L)), int(rng.integers(H))) for _ in range(16)]
