@@ -116,6 +116,7 @@ def lib() -> ctypes.CDLL:
             L.dms_pool_destroy.argtypes = [vp]
             L.dms_prefill.argtypes = [vp, i32, i32, i32, vp, vp, vp, vp, vp, vp]
             L.dms_decode_step.argtypes = [vp, i32, P(i32), i32, i32, vp, vp, vp, vp, vp, vp]
+            L.dms_decode_step_static.argtypes = [vp, i32, P(i32), i32, i32, vp, vp, vp, vp, vp, vp]
             L.dms_extend.argtypes = [vp, i32, i32, i32, vp, vp, vp, vp, vp, vp]
             L.dms_query_stats.argtypes = [vp, i32, P(dms_stats), P(i32)]
             L.dms_export_live.argtypes = [vp, i32, i32, i32, P(i32), i32, P(i32)]
@@ -124,7 +125,8 @@ def lib() -> ctypes.CDLL:
             L.dms_seq_release.argtypes = [vp, i32, vp]
             L.dms_timing_enable.argtypes = [vp, i32]
             L.dms_timing_read.argtypes = [vp, P(dms_timing)]
-            for f in (L.dms_pool_create, L.dms_pool_destroy, L.dms_prefill, L.dms_decode_step, L.dms_extend,
+            for f in (L.dms_pool_create, L.dms_pool_destroy, L.dms_prefill, L.dms_decode_step,
+                      L.dms_decode_step_static, L.dms_extend,
                       L.dms_query_stats, L.dms_export_live, L.dms_export_kv, L.dms_seq_release,
                       L.dms_timing_enable, L.dms_timing_read):
                 f.restype = ctypes.c_int32
@@ -200,6 +202,14 @@ def dms_decode_step(pool: int, seq_ids: Sequence[int], layer0: int, n_layers: in
     vp = ctypes.c_void_p
     _check(lib().dms_decode_step(vp(pool), len(seq_ids), ids, layer0, n_layers, vp(q), vp(k), vp(v),
                                  vp(logits), vp(out), vp(stream)))
+
+
+def dms_decode_step_static(pool: int, seq_ids: Sequence[int], layer0: int, n_layers: int, q: int, k: int,
+                           v: int, logits: int, out: int, stream: int):
+    ids = (ctypes.c_int32 * len(seq_ids))(*[int(s) for s in seq_ids])
+    vp = ctypes.c_void_p
+    _check(lib().dms_decode_step_static(vp(pool), len(seq_ids), ids, layer0, n_layers, vp(q), vp(k), vp(v),
+                                        vp(logits), vp(out), vp(stream)))
 
 
 def dms_query_stats(pool: int, seq: int, n_layers: int = 0, n_kv_heads: int = 0, raise_on_error=True):
@@ -333,7 +343,9 @@ class Pool:
         op = self._check_tensor(out, (T, Hq, D), torch.bfloat16, "out") if out is not None else 0
         dms_extend(self.handle, seq, layer, T, qp, kp, vpp, lp, op, self._stream())
 
-    def decode_step(self, seq_ids, layer0, q, k, v, logits, out):
+    def decode_step(self, seq_ids, layer0, q, k, v, logits, out, static_scratch=False):
+        """static_scratch: through dms_decode_step_static (split-K scratch in the
+        library's per-GPU device array; the call allocates nothing)."""
         torch = self.torch
         n = len(seq_ids)
         L = q.shape[0]
@@ -344,7 +356,8 @@ class Pool:
         lp = 0 if (logits is None and self.logits_from_k) else self._check_tensor(logits, (L, n, H), torch.float32,
                                                                                    "logits")
         op = self._check_tensor(out, (L, n, Hq, D), torch.bfloat16, "out")
-        dms_decode_step(self.handle, list(seq_ids), layer0, L, qp, kp, vpp, lp, op, self._stream())
+        fn = dms_decode_step_static if static_scratch else dms_decode_step
+        fn(self.handle, list(seq_ids), layer0, L, qp, kp, vpp, lp, op, self._stream())
 
     def stats(self, seq=-1, per_head=False, raise_on_error=True):
         if per_head and seq >= 0:

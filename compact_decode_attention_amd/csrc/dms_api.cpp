@@ -146,6 +146,7 @@ struct dms_pool {
     std::vector<int32_t> pos;  // [max_seqs][n_layers]: next position, -1 = empty
     std::vector<uint32_t> seen;  // [max_seqs]: call stamp of the last decode call naming the sequence
     uint32_t call_stamp = 0;
+    void* scratch = nullptr;     // device address of the static decode scratch on the pool's device
     int cu_count;
     int attend_per_cu;  // attention blocks per compute unit (checked once, for the largest call)
     int32_t& position(int seq, int layer) { return pos[(size_t)seq * cfg.n_layers + layer]; }
@@ -239,6 +240,7 @@ dms_status dms_pool_create(const dms_pool_config* cfg, void* arena, size_t arena
     if (e == hipSuccess) e = hipMemcpyAsync(d.hstate, rec.data(), rec.size() * 4, hipMemcpyHostToDevice, s);
     if (e == hipSuccess) e = hipMemcpyAsync(d.ctl, ctl, sizeof(ctl), hipMemcpyHostToDevice, s);
     if (e == hipSuccess) e = hipStreamSynchronize(s);
+    if (e == hipSuccess) e = dms::static_scratch_address(&p->scratch);  // once per device, here
     if (e != hipSuccess) {
         delete p;
         return hip_fail(e, "pool initialisation");
@@ -467,6 +469,15 @@ dms_status dms_decode_step(dms_pool* pool, int32_t n_seqs, const int32_t* seq_id
                            const void* q, const void* k, const void* v, const float* logits, void* out,
                            void* stream) {
     return decode_step(pool, n_seqs, seq_ids, layer0, n_layers, q, k, v, logits, out, stream, nullptr, 0);
+}
+
+dms_status dms_decode_step_static(dms_pool* pool, int32_t n_seqs, const int32_t* seq_ids, int32_t layer0,
+                                  int32_t n_layers, const void* q, const void* k, const void* v, const float* logits,
+                                  void* out, void* stream) {
+    if (!pool) return fail(DMS_E_INVAL, "pool is NULL");
+    if (!pool->scratch) return fail(DMS_E_STATE, "no static scratch on this pool's device");
+    return decode_step(pool, n_seqs, seq_ids, layer0, n_layers, q, k, v, logits, out, stream,
+                       static_cast<char*>(pool->scratch), dms::kStaticScratchBytes);
 }
 
 dms_status dms_query_stats(dms_pool* pool, int32_t seq, dms_stats* out, int32_t* live_per_layer_head) {

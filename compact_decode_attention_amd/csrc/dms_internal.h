@@ -66,6 +66,10 @@ constexpr int part_stride(int g, int d) { return part_acc_off(g) + g * d; }  // 
 constexpr int kMaxCallSeqs = 256;  // sequences per kernel launch (larger calls are split)
 constexpr int kMaxCallHeads = 4032;  // heads per launch (4 ints of plan per head in LDS, < 64 KB)
 
+// Size of the file-scope device array that holds the split-K partials and the
+// page-axis prefix of dms_decode_step_static (per GPU, for the process's life).
+constexpr size_t kStaticScratchBytes = (size_t)16 << 20;
+
 // ctl words
 constexpr int kCtlTop = 0;    // free pages on the stack
 constexpr int kCtlError = 1;  // sticky: nonzero once the page pool ran out
@@ -319,5 +323,8 @@ hipError_t launch_extend(const PrefillArgs& a, bool with_out, hipStream_t s, hip
 hipError_t launch_extend_attend(const PrefillArgs& a, hipStream_t s, hipEvent_t* ev);
 hipError_t launch_seq_release(const PoolDev& p, int32_t seq, hipStream_t s);
 int device_cu_count();
+// Device address of the static decode scratch (kStaticScratchBytes) on the
+// current device, looked up once per device.
+hipError_t static_scratch_address(void** out);
 
 }  // namespace dms

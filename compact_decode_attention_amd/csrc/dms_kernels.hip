@@ -32,7 +32,37 @@
 #include <hip/hip_ext.h>
 #include <math.h>
 
+#include <mutex>
+
 namespace dms {
+
+// Scratch of the decode entry point that allocates nothing: the split-K
+// partials and the page-axis prefix of one launch, in a file-scope device array
+// (each GPU the library runs on holds its own copy until the process ends).
+// Host code never passes the array's name to a kernel: in host code the name
+// stands for a host-side stand-in, not for the device memory.  It uses the
+// address hipGetSymbolAddress gives for the current device instead.
+static __device__ __align__(256) unsigned char scratch[kStaticScratchBytes];
+
+hipError_t static_scratch_address(void** out) {
+    constexpr int kMaxDevices = 64;
+    static std::mutex mu;
+    static void* addr[kMaxDevices] = {};
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(mu);
+    if (!addr[dev]) {  // once per device, with that device current
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        addr[dev] = p;
+    }
+    *out = addr[dev];
+    return hipSuccess;
+}
+
 namespace {
 
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));

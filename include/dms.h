@@ -218,6 +218,23 @@ dms_status dms_decode_step(dms_pool* pool, int32_t n_seqs, const int32_t* seq_id
                            int32_t layer0, int32_t n_layers, const void* q, const void* k,
                            const void* v, const float* logits, void* out, void* stream);
 
+/* dms_decode_step for callers that cannot allocate: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation.  Same
+ * arguments, same kernels and results bit for bit; the call allocates nothing
+ * (no device memory, no host containers, no timing events even when timing is
+ * enabled).  Its split-K partials and page-axis prefix live in one file-scope
+ * device array of 16 MiB per GPU (held until the process ends), not in the
+ * pool's arena.  A call whose largest launch needs more returns DMS_E_INVAL
+ * (that is (attention waves + call heads) x (8 + G x head_dim) x 4 bytes, G =
+ * n_q_heads / n_kv_heads: about 2.8 MB for 36 layers x 8 kv heads at G = 4,
+ * D = 128; up to 256 sequences x n_layers x n_kv_heads heads per launch).
+ * Nothing in the array needs clearing: each launch writes what it reads.
+ * Every call on one GPU shares that GPU's array, across all pools: calls that
+ * overlap on one GPU (other streams, other pools, other threads) race. */
+dms_status dms_decode_step_static(dms_pool* pool, int32_t n_seqs, const int32_t* seq_ids,
+                                  int32_t layer0, int32_t n_layers, const void* q, const void* k,
+                                  const void* v, const float* logits, void* out, void* stream);
+
 /* Append n_tokens new tokens to one (sequence, layer) that already holds
  * tokens, at positions t .. t+n_tokens-1 (t = its position counter): the same
  * result as n_tokens decode steps of that (seq, layer), in position order (for
