@@ -23,6 +23,7 @@ Prints one JSON line.  --gpus N with N > 1 exits: this build runs on one GPU.
 from __future__ import annotations
 
 import argparse
+import ctypes
 import hashlib
 import json
 import os
@@ -119,15 +120,23 @@ def bf16_tensor(a, torch):
 # ---------------------------------------------------------------------------
 # decode
 # ---------------------------------------------------------------------------
-def bench_decode(args, torch, dms, kv_format=0, modes=None, cpu_steps=None, logit_channel=None):
+KEEP_LAW = {"normal": "keep score N(-1.2,1) (about 1 in 8 kept)",
+            "uniform_mu": "keep-score mean U(-2,0) per head",
+            "beta": "keep rate Beta(2,14) per head"}
+
+
+def bench_decode(args, torch, dms, kv_format=0, modes=None, cpu_steps=None, logit_channel=None, workload=None,
+                 marks="keep_score"):
     """The decode leg; kv_format 1 runs it on an FP8 (E4M3) pool; logit_channel c
     carries each token's eviction logit (as bf16) in channel c of its K row and
-    the pool reads it from there (no logits input; the same marks)."""
+    the pool reads it from there (no logits input; the same marks); marks
+    "literal" hands the keep scores over as logits unchanged (mark iff s > 0:
+    about 11.5% marked instead of about 88.5%)."""
     fp8 = kv_format == 1
-    wl = synth.WORKLOADS[args.workload]
+    wl = synth.WORKLOADS[workload or args.workload]
     if wl.prefill_only or wl.n_seqs != 1:
         raise SystemExit("decode workload must be a single-sequence decode workload")
-    inp = synth.SynthInputs(wl)
+    inp = synth.SynthInputs(wl, marks=marks)
     L, Hq, H, D, w = wl.n_layers, wl.n_q_heads, wl.n_kv_heads, wl.head_dim, wl.window
     ctx = int(inp.ctx_lens()[0])
     K, W = args.steps, args.warmup
@@ -162,6 +171,7 @@ def bench_decode(args, torch, dms, kv_format=0, modes=None, cpu_steps=None, logi
     pool = dms.Pool(n_layers=L, n_q_heads=Hq, n_kv_heads=H, head_dim=D, window=w, max_seqs=1,
                     max_positions=total, max_pages=L * H * ((total + 63) // 64), kv_format=kv_format,
                     logit_channel=logit_channel, device=dev)
+    arena_bytes = pool.nbytes
     from_k = logit_channel is not None  # the pool reads the logits from K
     stream = torch.cuda.current_stream(dev)
     row_bytes = D + 4 if fp8 else 2 * D  # one stored K (or V) row
@@ -172,13 +182,25 @@ def bench_decode(args, torch, dms, kv_format=0, modes=None, cpu_steps=None, logi
             pool.prefill(0, l, pk[l], pv[l], None if from_k else plg[l])
         torch.cuda.synchronize()
 
+    # The timed loops call the C entry point through the binding with device
+    # pointers computed beforehand (the Pool wrapper's per-call tensor checks
+    # would otherwise cost the GPU idle time between steps).
+    lib, vp = dms.lib(), ctypes.c_void_p
+    seq0 = (ctypes.c_int32 * 1)(0)
+    sp = vp(stream.cuda_stream)
+    row = lambda t, i, l=None: vp(t[i].data_ptr() if l is None else t[i, l].data_ptr())
+    lgp = (lambda i, l=None: vp(None)) if from_k else (lambda i, l=None: row(dl, i, l))
+    batched_args = [(vp(pool.handle), 1, seq0, 0, L, row(dq, i), row(dk, i), row(dv, i), lgp(i), row(dout, i), sp)
+                    for i in range(S_all)]
+    layer_args = [[(vp(pool.handle), 1, seq0, l, 1, row(dq, i, l), row(dk, i, l), row(dv, i, l), lgp(i, l),
+                    row(dout, i, l), sp) for l in range(L)] for i in range(S_all)]
+
     def run_batched(i):
-        pool.decode_step([0], 0, dq[i], dk[i], dv[i], None if from_k else dl[i], dout[i])
+        dms._check(lib.dms_decode_step(*batched_args[i]))
 
     def run_per_layer(i):
-        for l in range(L):
-            pool.decode_step([0], l, dq[i, l:l + 1], dk[i, l:l + 1], dv[i, l:l + 1], dl[i, l:l + 1],
-                             dout[i, l:l + 1])
+        for args_l in layer_args[i]:
+            dms._check(lib.dms_decode_step(*args_l))
 
     # graph mode: static buffers, 36 captured per-layer calls, inputs copied in per step
     sq, sk, sv = torch.empty_like(dq[0]), torch.empty_like(dk[0]), torch.empty_like(dv[0])
@@ -253,8 +275,10 @@ def bench_decode(args, torch, dms, kv_format=0, modes=None, cpu_steps=None, logi
         achieved = attend_bytes / (avg_att / 1e3) / 1e9
         roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                     "frac": round(achieved / HBM_PEAK_GBPS, 4),
-                    "traffic": measured_traffic(TRAFFIC_SUMMARY_FP8 if fp8 else TRAFFIC_SUMMARY),
-                    "kernel": "decode_attend_kernel<128,4,%s>" % ("fp8" if fp8 else "bf16"),
+                    # the counter summaries were taken on the headline workload only
+                    "traffic": measured_traffic(TRAFFIC_SUMMARY_FP8 if fp8 else TRAFFIC_SUMMARY)
+                    if wl.name == "qwen3-8b_ctx8192" and marks == "keep_score" else None,
+                    "kernel": "decode_attend_kernel<%d,%d,%s>" % (D, Hq // H, "fp8" if fp8 else "bf16"),
                     "avg_launch_us": round(avg_att * 1e3, 2),
                     "bytes_per_launch": int(attend_bytes), "launches": int(n),
                     "merge_kernel_avg_launch_us": round(avg_mer * 1e3, 2)}
@@ -266,12 +290,12 @@ def bench_decode(args, torch, dms, kv_format=0, modes=None, cpu_steps=None, logi
     if S > 0:
         import oracle  # the CPU baseline is the oracle, timed as it stands
         cores = int(os.environ.get("OMP_NUM_THREADS", len(os.sched_getaffinity(0))))
-        marks = [oracle.marks(host_lg[l]) for l in range(L)]
+        mk = [oracle.marks(host_lg[l]) for l in range(L)]
         tc = time.perf_counter()
         for i in range(S):
             t = ctx + i
             for l in range(L):
-                oracle.attend(q_host[i, l][None], [t], host_k[l][:t + 1], host_v[l][:t + 1], marks[l][:t + 1], w)
+                oracle.attend(q_host[i, l][None], [t], host_k[l][:t + 1], host_v[l][:t + 1], mk[l][:t + 1], w)
         cpu_s = time.perf_counter() - tc
         cpu = {"value": round(S / cpu_s, 3), "unit": "tok/s", "cores": cores, "kind": "oracle",
                "sample": "%s: the first %d of the %d decode steps, all %d layers x %d q heads, masked "
@@ -279,18 +303,27 @@ def bench_decode(args, torch, dms, kv_format=0, modes=None, cpu_steps=None, logi
         log("cpu oracle: %.2f tok/s on %d threads" % (S / cpu_s, cores))
 
     main = "batched" if "batched" in results else modes[0]
+    step_gbps = step_bytes / (results[main]["ms_per_step"] * K / 1e3) / 1e9
     out = {
         "value": results[main]["tok_per_s"], "ms_per_step": results[main]["ms_per_step"],
-        "achieved_step_GBps": round(step_bytes / (results[main]["ms_per_step"] * K / 1e3) / 1e9, 1),
+        "achieved_step_GBps": round(step_gbps, 1),
+        # the whole step, beside the attention kernel alone (roofline): algorithmic
+        # bytes of a step over the step's time (both kernels and the gaps between)
+        "step_roofline": {"bound": "hbm", "achieved": round(step_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                          "frac": round(step_gbps / HBM_PEAK_GBPS, 4),
+                          "scope": "whole decode step (attention + merge/append kernels + launch gaps), "
+                                   "%s mode" % main, "bytes_per_step": int(step_bytes / K)},
         "roofline": roofline, "cpu_baseline": cpu,
         "modes": {m: {k: round(v, 5) if isinstance(v, float) else v for k, v in r.items()}
                   for m, r in results.items()},
         "modes_max_abs_diff": diff,
         "kv_gib": {"live": round(st.kv_bytes_live / 2**30, 4), "allocated": round(st.kv_bytes_allocated / 2**30, 4),
-                   "dense_equivalent": round(st.kv_bytes_dense_equiv / 2**30, 4)},
+                   "dense_equivalent": round(st.kv_bytes_dense_equiv / 2**30, 4),
+                   "arena": round(arena_bytes / 2**30, 4)},
         "config": {"workload": "%s decode: %d layers, %d q / %d kv heads, head_dim %d, batch 1, ctx %d, "
-                               "%d decode steps, w %d, keep-score mean U(-2,0) per head"
-                               % (wl.name, L, Hq, H, D, ctx, K, w),
+                               "%d decode steps, w %d, %s%s"
+                               % (wl.name, L, Hq, H, D, ctx, K, w, KEEP_LAW[wl.keep_law],
+                                  ", literal marks (logit = +keep score)" if marks == "literal" else ""),
                    "call": "one dms_decode_step per token over all %d layers" % L,
                    "parallelism": "single GPU"},
     }
@@ -527,6 +560,7 @@ def main():
     ap.add_argument("--no-fp8", action="store_true", help="skip the FP8-pool decode leg")
     ap.add_argument("--no-logit-channel", action="store_true", help="skip the K-channel-logits decode leg")
     ap.add_argument("--no-extend", action="store_true", help="skip the chunked-prefill (dms_extend) leg")
+    ap.add_argument("--no-llama", action="store_true", help="skip the Llama-3.2-1B-shaped decode leg")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="first run a plain copy of this many MiB (for counter scaling)")
     args = ap.parse_args()
@@ -556,6 +590,29 @@ def main():
               "merge_avg_launch_us": dk_["roofline"]["merge_kernel_avg_launch_us"] if dk_["roofline"] else None,
               "workload": "the decode workload above with each token's eviction logit carried (bf16) in "
                           "channel 0 of its K rows and read by the pool from there (no logits input)"}
+    llama = None
+    if not args.no_llama:
+        l2 = bench_decode(args, torch, dms, modes=["batched", "per_layer"], cpu_steps=0,
+                          workload="llama3.2-1b_ctx8192")
+        l2lit = bench_decode(args, torch, dms, modes=["batched"], cpu_steps=0, workload="llama3.2-1b_ctx8192",
+                             marks="literal")
+        llama = {"workload": l2["config"]["workload"], "call": l2["config"]["call"],
+                 "tok_per_s": round(l2["value"], 2), "ms_per_step": round(l2["ms_per_step"], 5),
+                 "modes": l2["modes"], "step_roofline": l2["step_roofline"],
+                 "kv_gib": l2["kv_gib"],
+                 "cache_note": "the live compact cache (%.0f MB) fits the GPU's 256 MB last-level cache, so "
+                               "the GB/s figures are effective bandwidth, not HBM bandwidth"
+                               % (l2["kv_gib"]["live"] * 2**30 / 1e6),
+                 "literal_marks": {"tok_per_s": round(l2lit["value"], 2), "ms_per_step": round(l2lit["ms_per_step"], 5),
+                                   "kv_gib": l2lit["kv_gib"], "step_roofline": l2lit["step_roofline"],
+                                   "cache_note": "%.0f MB live against the 256 MB last-level cache: at most partly "
+                                                 "resident" % (l2lit["kv_gib"]["live"] * 2**30 / 1e6),
+                                   "workload": l2lit["config"]["workload"]},
+                 "pages_context": {"note": "the FastDMS announcement's tables for Llama-3.2-1B at ctx 8192 / gen "
+                                           "128, c = 1, end-to-end model inference on unstated hardware: context, "
+                                           "not a target",
+                                   "kv_gib_vllm_bf16": 0.312, "kv_gib_fastdms": 0.056,
+                                   "decode_tok_per_s_vllm_bf16": 459.4}}
     pre = None if args.no_prefill else bench_prefill(args, torch, dms)
     ext = None if args.no_extend else bench_extend(args, torch, dms)
     rag = None if args.no_ragged else bench_ragged(args, torch, dms)
@@ -575,11 +632,13 @@ def main():
         "config": dec["config"],
         "achieved_step_GBps": dec["achieved_step_GBps"],
         "roofline": dec["roofline"],
+        "step_roofline": dec["step_roofline"],
         "cpu_baseline": dec["cpu_baseline"],
         "modes": dec["modes"],
         "modes_max_abs_diff": dec["modes_max_abs_diff"],
         "kv_gib": dec["kv_gib"],
         "fp8_kv": f8,
+        "llama3.2-1b_ctx8192": llama,
         "logits_from_k_channel": lk,
         "prefill": pre,
         "chunked_extend": ext,
