@@ -158,6 +158,17 @@ __device__ __forceinline__ uint4 buffer_load16(__amdgpu_buffer_rsrc_t r, int vof
     return make_uint4(v[0], v[1], v[2], v[3]);
 }
 
+// Streaming loads of K/V pages: the non-temporal cache policy (nt, bit 1 of the
+// buffer instruction's cache-policy operand on gfx950), which a read-once
+// stream of pages larger than the caches wants.
+#ifndef DMS_KV_AUX
+#define DMS_KV_AUX 2
+#endif
+__device__ __forceinline__ uint4 buffer_load16_stream(__amdgpu_buffer_rsrc_t r, int voff, int soff) {
+    const auto v = __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, DMS_KV_AUX);
+    return make_uint4(v[0], v[1], v[2], v[3]);
+}
+
 __device__ __forceinline__ uint2 buffer_load8(__amdgpu_buffer_rsrc_t r, int voff, int soff) {
     const auto v = __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, 0);
     return make_uint2(v[0], v[1]);

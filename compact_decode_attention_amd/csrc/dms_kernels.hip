@@ -229,7 +229,7 @@ template <int D>
 __device__ __forceinline__ void issue_k(const PoolDev& P, int page, bool live, int lane, uint4 (&kc)[D / 8]) {
     const __amdgpu_buffer_rsrc_t r = buffer_rsrc(P.kpages + (size_t)page * (kPage * D), live ? kPage * D * 2 : 0);
 #pragma unroll
-    for (int cc = 0; cc < D / 8; ++cc) kc[cc] = buffer_load16(r, lane * 16, cc * kPage * 16);
+    for (int cc = 0; cc < D / 8; ++cc) kc[cc] = buffer_load16_stream(r, lane * 16, cc * kPage * 16);
 }
 
 // V units of one page (lane = dim: unit (b, j) holds slots 8b .. 8b+7 of dim j*64 + lane).
@@ -239,7 +239,7 @@ __device__ __forceinline__ void issue_v(const PoolDev& P, int page, bool live, i
 #pragma unroll
     for (int b = 0; b < 8; ++b)
 #pragma unroll
-        for (int j = 0; j < D / 64; ++j) vc[b][j] = buffer_load16(r, lane * 16, (b * D + j * 64) * 16);
+        for (int j = 0; j < D / 64; ++j) vc[b][j] = buffer_load16_stream(r, lane * 16, (b * D + j * 64) * 16);
 }
 
 // QK^T of one page, lane = slot.  q comes from LDS (every lane reads the same
@@ -384,7 +384,7 @@ __device__ __forceinline__ void issue_k8(const PoolDev& P, int page, bool live, 
                                          float& ks, float& vs) {
     const __amdgpu_buffer_rsrc_t r = buffer_rsrc(P.kp8() + (size_t)page * (kPage * D), live ? kPage * D : 0);
 #pragma unroll
-    for (int cc = 0; cc < D / 16; ++cc) kc[cc] = buffer_load16(r, lane * 16, cc * kPage * 16);
+    for (int cc = 0; cc < D / 16; ++cc) kc[cc] = buffer_load16_stream(r, lane * 16, cc * kPage * 16);
     ks = buffer_load4f(buffer_rsrc(P.kscale + (size_t)page * kPage, live ? kPage * 4 : 0), lane * 4);
     vs = buffer_load4f(buffer_rsrc(P.vscale + (size_t)page * kPage, live ? kPage * 4 : 0), lane * 4);
 }
@@ -397,7 +397,7 @@ __device__ __forceinline__ void issue_v8(const PoolDev& P, int page, bool live, 
 #pragma unroll
     for (int b = 0; b < 4; ++b)
 #pragma unroll
-        for (int j = 0; j < D / 64; ++j) vc[b][j] = buffer_load16(r, lane * 16, (b * D + j * 64) * 16);
+        for (int j = 0; j < D / 64; ++j) vc[b][j] = buffer_load16_stream(r, lane * 16, (b * D + j * 64) * 16);
 }
 
 // QK^T of one FP8 page, lane = slot: chunk cc (dims 16cc .. 16cc+15) against q
