@@ -91,11 +91,12 @@ def test_qwen3_8b_batch32_ragged_full_size():
     """32 sequences with prompts U{4096..32768} in one shared page pool, 36 layers,
     64 decode steps, every step one call over all sequences and layers (split
     into several launches).  Eviction logits of every head come from the
-    counter-based generator; K/V/q of four sampled (sequence, layer) pairs (the
-    shortest and longest prompt, first and last layer) too, and their outputs are
-    checked against the oracle; the other pairs take K/V/q from torch's seeded
-    device generator.  Live counts of every head checked exactly, live sets on a
-    sample."""
+    counter-based generator; K/V/q of 36 sampled (sequence, layer) pairs too
+    (the shortest and longest prompt at the first and last layer, and one pair
+    of every sequence at a layer spread over the stack), and their outputs are
+    checked against the oracle at four steps; the other pairs take K/V/q
+    from torch's seeded device generator.  Live counts of every head checked
+    exactly, live sets on a sample."""
     import torch
     import compact_decode_attention_amd as dms
     wl = synth.WORKLOADS["qwen3-8b_batch32_ragged"]
@@ -105,6 +106,7 @@ def test_qwen3_8b_batch32_ragged_full_size():
     ctx = [int(c) for c in inp.ctx_lens()]
     s_short, s_long = int(np.argmin(ctx)), int(np.argmax(ctx))
     sampled = [(s_short, 0), (s_short, L - 1), (s_long, 0), (s_long, L - 1)]
+    sampled += [(s, (7 * s + 3) % L) for s in range(B) if (s, (7 * s + 3) % L) not in sampled]
     dev = torch.device("cuda:0")
     marks, pages = {}, 0
     for s in range(B):
@@ -129,7 +131,7 @@ def test_qwen3_8b_batch32_ragged_full_size():
                 v = torch.randn((T, H, D), generator=gen, device=dev).to(torch.bfloat16)
             pool.prefill(s, l, k, v, torch.from_numpy(inp.logits(s, l, 0, T)).to(dev))
     seqs = list(range(B))
-    check_steps = {0, S // 2, S - 1}
+    check_steps = {0, S // 3, 2 * S // 3, S - 1}
     for i in range(S):
         q = torch.randn((L, B, Hq, D), generator=gen, device=dev).to(torch.bfloat16)
         k = torch.randn((L, B, H, D), generator=gen, device=dev).to(torch.bfloat16)
