@@ -18,7 +18,7 @@ Prefill leg ("prefill"): Qwen3-8B-shaped DMS prefill of one 32768-token prompt
 (32 q / 8 kv heads, D=128, w=512, keep score N(-1.2,1)), one layer's inputs
 prefilled into 36 layer slots: masked causal attention on MFMA plus compaction.
 
-Prints one JSON line.  --gpus N with N > 1 exits: this build runs on one GPU.
+Prints one JSON line.  --gpus N with N > 1 exits: the library runs on one GPU.
 """
 from __future__ import annotations
 
@@ -565,7 +565,7 @@ def main():
                     help="first run a plain copy of this many MiB (for counter scaling)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print("bench.py runs on one GPU only (this build has no multi-GPU path); got --gpus %d" % args.gpus,
+        print("bench.py runs on one GPU only (the library has no multi-GPU path); got --gpus %d" % args.gpus,
               file=sys.stderr)
         sys.exit(2)
 
