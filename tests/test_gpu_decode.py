@@ -144,6 +144,29 @@ def test_subset_of_sequences_per_call():
     r.close()
 
 
+@pytest.mark.parametrize("kv_format", [0, 1])
+def test_more_sequences_than_one_launch_takes(kv_format):
+    """300 sequences in one call: more than the 256 a launch takes, so the call
+    runs as two launches (256 + 44) that reuse the partials in stream order.
+    Sequence ids in natural, reversed and shuffled order; every output, live set
+    and stored row checked."""
+    n = 300
+    case = Case(n_layers=1, n_q_heads=4, n_kv_heads=1, head_dim=64, window=8,
+                ctx_lens=[20 + (7 * s) % 53 for s in range(n)], steps=3, seed=41, kv_format=kv_format)
+    case.gen()
+    r = Runner(case)
+    try:
+        r.prefill_all()
+        orders = [list(range(n)), list(range(n))[::-1], [int(x) for x in np.random.default_rng(5).permutation(n)]]
+        for i, seqs in enumerate(orders):
+            out = r.decode(i, seqs=seqs)
+            r.check_outputs(out, i, seqs=seqs, record="decode (fp8 pool)" if kv_format else "decode")
+        r.check_live([case.ctx_lens[s] + case.steps - 1 for s in range(n)])
+        r.check_kv([case.ctx_lens[s] + case.steps - 1 for s in range(n)])
+    finally:
+        r.close()
+
+
 def test_zero_query_gives_mean_of_live_values():
     case = Case(n_layers=1, n_q_heads=4, n_kv_heads=1, head_dim=128, window=10,
                 ctx_lens=[150], steps=20, seed=9, zero_q=True)
