@@ -279,6 +279,8 @@ def bench_decode(args, torch, dms, kv_format=0, modes=None, cpu_steps=None, logi
                     "traffic": measured_traffic(TRAFFIC_SUMMARY_FP8 if fp8 else TRAFFIC_SUMMARY)
                     if wl.name == "qwen3-8b_ctx8192" and marks == "keep_score" else None,
                     "kernel": "decode_attend_kernel<%d,%d,%s>" % (D, Hq // H, "fp8" if fp8 else "bf16"),
+                    "cache": "K/V pages read with the non-temporal policy: they are not kept in the 256 MB "
+                             "last-level cache between steps, so the bytes come from HBM",
                     "avg_launch_us": round(avg_att * 1e3, 2),
                     "bytes_per_launch": int(attend_bytes), "launches": int(n),
                     "merge_kernel_avg_launch_us": round(avg_mer * 1e3, 2)}
