@@ -45,24 +45,12 @@ typedef float f32x16_t __attribute__((ext_vector_type(16)));
 __device__ __forceinline__ bf16x8_t as_bf16x8(uint4 u) { return __builtin_bit_cast(bf16x8_t, u); }
 __device__ __forceinline__ f16x8_t as_f16x8(uint4 u) { return __builtin_bit_cast(f16x8_t, u); }
 
-
-__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-    auto rne = [](float f) -> uint32_t {
-        uint32_t u = __float_as_uint(f);
-        u += 0x7fffu + ((u >> 16) & 1u);
-        return u >> 16;
-    };
-    return rne(lo) | (rne(hi) << 16);
-}
-
 __device__ __forceinline__ uint16_t bf16_bits(float f) {
     uint32_t u = __float_as_uint(f);
     if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);
     u += 0x7fffu + ((u >> 16) & 1u);
     return (uint16_t)(u >> 16);
 }
-
-__device__ __forceinline__ float bf16_f(uint32_t bits16) { return __uint_as_float(bits16 << 16); }
 
 // max and sum of x over lanes l and l ^ 32 (v_permlane32_swap exchanges the two
 // halves of the wave in one VALU instruction; either result pair holds x of both)
