@@ -116,6 +116,20 @@ __device__ __forceinline__ float wave_sum(float x) {
     return readlane_f(x, 63);
 }
 
+// The kernel arguments sit in memory the command processor wrote just before
+// the dispatch, so the first read of each 64-byte line of them misses the
+// caches; read lazily under branches, those misses come one after another.
+// Touching every line the kernel reads at entry puts them in flight together.
+template <int BYTES>
+__device__ __forceinline__ void touch_args(const void* args) {
+    typedef const int __attribute__((address_space(4))) cint_t;
+    cint_t* p = (cint_t*)args;
+    int acc = 0;
+#pragma unroll
+    for (int o = 0; o < BYTES / 4; o += 16) acc ^= p[o];
+    asm volatile("" ::"s"(acc));
+}
+
 // x where c holds, zeros elsewhere, component by component (a select of the
 // whole vector struct is lowered through private memory)
 __device__ __forceinline__ uint4 keep_if(bool c, uint4 x) {
@@ -491,6 +505,7 @@ template <int D, int G, bool F8>
 __global__ __attribute__((amdgpu_flat_work_group_size(64 * kAttendWaves, 64 * kAttendWaves),
                           amdgpu_waves_per_eu(2, 2)))
 void decode_attend_kernel(DecodeArgs a) {
+    touch_args<offsetof(DecodeArgs, seq_ids) + 64>(&a);  // the fixed part and the first sequence ids
     constexpr int NT = 64 * kAttendWaves;
     constexpr int VJ = D / 64;
     constexpr int QV = G * D / 8;  // 16-byte pieces of one head group's q
@@ -1036,6 +1051,7 @@ __device__ void append_head(const DecodeArgs& a, int ch) {
 
 template <int D, int G, bool F8>
 __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeArgs a) {
+    touch_args<offsetof(DecodeArgs, seq_ids) + 64>(&a);
     const int H = a.n_call_heads;
     if ((int)blockIdx.x < H) {
         merge_head<D, G, F8>(a, blockIdx.x);
