@@ -712,19 +712,22 @@ void decode_attend_kernel(DecodeArgs a) {
 // ---------------------------------------------------------------------------
 
 // Log-sum-exp merge of a head's partials with the new token; bf16 output of the
-// head's G q heads.  256 threads.  Once the head's partial range is known the
-// loads go out together, 16 bytes per lane: thread t owns output float4 f = t % NF
-// for the partials u = t / NF, t / NF + NPH, ... (a round of RU of them in
-// registers), and the maxima and sums (thread t: q head t % G of partials t / G,
-// t / G + 256 / G, ...).  The NPH phases are summed through LDS.
+// head's G q heads, or of its part ds of DS equal parts (calls with many partials
+// per head spread a head over DS blocks, so that fewer loads queue per thread and
+// one round holds DS times as many partials).  256 threads.  Once the head's
+// partial range is known the loads go out together, 16 bytes per lane: thread t
+// owns output float4 ds * NF + t % NF for the partials u = t / NF, t / NF + NPH,
+// ... (a round of RU of them in registers), and the maxima and sums (thread t:
+// q head t % G of partials t / G, t / G + 256 / G, ...).  The NPH phases are
+// summed through LDS.
 // (FP8 pools: the new token enters as its quantised K and V rows, value(code) *
 // row scale, like every stored token.)
-template <int D, int G, bool F8>
-__device__ void merge_head(const DecodeArgs& a, int ch) {
+template <int D, int G, bool F8, int DS>
+__device__ void merge_head(const DecodeArgs& a, int ch, int ds) {
     const PoolDev& P = a.pool;
     constexpr int PSTR = part_stride(G, D);  // floats per partial
     constexpr int ACC = part_acc_off(G);
-    constexpr int NF = G * D / 4;            // float4 outputs of the head
+    constexpr int NF = G * D / 4 / DS;       // float4 outputs of the block
     constexpr int NPH = 256 / NF;            // partial phases (NF divides 256)
     constexpr int RU = 16;                   // accumulators per thread per round
     constexpr int STEP = 256 / G;
@@ -753,8 +756,9 @@ __device__ void merge_head(const DecodeArgs& a, int ch) {
     const uint16_t* qg = a.q + ((size_t)c.row * P.n_q_heads + c.h * G) * D;
     const uint16_t* kn = a.k + ((size_t)c.row * P.n_kv_heads + c.h) * D;
     const uint16_t* vn = a.v + ((size_t)c.row * P.n_kv_heads + c.h) * D;
-    const int f = tid % NF, ph = tid / NF;
-    const int gf = (4 * f) / D;  // q head of this thread's outputs
+    const int ph = tid / NF;
+    const int f = ds * NF + tid % NF;  // this thread's output float4 within the head
+    const int gf = (4 * f) / D;        // q head of this thread's outputs
 
     // first round of accumulators, and every maximum and sum
     float4 xv[RU];
@@ -855,12 +859,12 @@ __device__ void merge_head(const DecodeArgs& a, int ch) {
         }
     }
     if (NPH > 1) {
-        if (ph > 0) s_o[ph - 1][f] = o;
+        if (ph > 0) s_o[ph - 1][tid % NF] = o;
         __syncthreads();
         if (ph > 0) return;
 #pragma unroll
         for (int q = 0; q < NPH - 1; ++q) {
-            const float4 t = s_o[q][f];
+            const float4 t = s_o[q][tid % NF];
             o.x += t.x;
             o.y += t.y;
             o.z += t.z;
@@ -1049,14 +1053,16 @@ __device__ void append_head(const DecodeArgs& a, int ch) {
     }
 }
 
-template <int D, int G, bool F8>
+// Blocks 0 .. DS*H-1 merge (head b / DS, part b % DS), the next H append.
+template <int D, int G, bool F8, int DS>
 __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeArgs a) {
     touch_args<offsetof(DecodeArgs, seq_ids) + 64>(&a);
     const int H = a.n_call_heads;
-    if ((int)blockIdx.x < H) {
-        merge_head<D, G, F8>(a, blockIdx.x);
+    const int b = blockIdx.x;
+    if (b < DS * H) {
+        merge_head<D, G, F8, DS>(a, b / DS, b % DS);
     } else if (threadIdx.x < 64) {
-        append_head<D, F8>(a, blockIdx.x - H);
+        append_head<D, F8>(a, b - DS * H);
     }
 }
 
@@ -1604,8 +1610,17 @@ hipError_t launch_decode_f(const DecodeArgs& a, int grid, hipStream_t s, hipEven
                           ev ? ev[0] : nullptr, ev ? ev[1] : nullptr, 0, a);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
-    hipExtLaunchKernelGGL((decode_merge_kernel<D, G, F8>), dim3(2 * a.n_call_heads), dim3(256), 0, s,
-                          ev ? ev[2] : nullptr, ev ? ev[3] : nullptr, 0, a);
+    // A head whose outputs fill 128 or more threads' float4s holds at most 32
+    // partials per round.  In a call with many partials per head (few heads, e.g.
+    // one layer of one sequence) its merge is spread over 4 blocks.  (The
+    // attention grid never exceeds the call's page bound by a block, so
+    // n_waves / H bounds the partials of an average head.)
+    if (G * D / 4 >= 128 && a.n_waves > 8 * a.n_call_heads)
+        hipExtLaunchKernelGGL((decode_merge_kernel<D, G, F8, 4>), dim3(5 * a.n_call_heads), dim3(256), 0, s,
+                              ev ? ev[2] : nullptr, ev ? ev[3] : nullptr, 0, a);
+    else
+        hipExtLaunchKernelGGL((decode_merge_kernel<D, G, F8, 1>), dim3(2 * a.n_call_heads), dim3(256), 0, s,
+                              ev ? ev[2] : nullptr, ev ? ev[3] : nullptr, 0, a);
     return hipGetLastError();
 }
 

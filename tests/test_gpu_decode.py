@@ -259,6 +259,19 @@ def test_many_items_per_head_across_blocks():
     r.close()
 
 
+@pytest.mark.parametrize("kv_format", [0, 1])
+@pytest.mark.parametrize("group", [4, 8])
+def test_merge_spread_over_blocks(group, kv_format):
+    """Calls of few heads with tens of pages each (a single layer of a single
+    sequence): every head's merge is spread over several blocks, each writing its
+    share of the head's outputs.  Checked against the oracle at every step, on
+    bf16 and FP8 pools."""
+    case = Case(n_layers=2, n_q_heads=2 * group, n_kv_heads=2, head_dim=128, window=48,
+                ctx_lens=[6000], steps=4, seed=500 + group + kv_format, keep_mu=2.0, kv_format=kv_format)
+    r, _ = run_case(case, check_live_every=2, layer_batched=False)
+    r.close()
+
+
 def test_hundreds_of_partials_for_one_head():
     """One kv head whose pages outnumber the partials the merge keeps in
     registers and LDS (every page its own wave): the merge's overflow paths."""
