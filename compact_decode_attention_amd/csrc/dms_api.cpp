@@ -29,7 +29,7 @@ constexpr size_t kAlign = 256;
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
 enum Section { S_K, S_V, S_KS, S_VS, S_POS, S_STACK, S_HSTATE, S_PTABLE, S_RING, S_PART, S_PREFIX, S_INV, S_PCNT,
-               S_VT, S_Q8, S_CTL, S_N };
+               S_VT, S_VT16, S_MBITS, S_Q8, S_CTL, S_N };
 
 struct Layout {
     size_t off[S_N + 1];
@@ -92,6 +92,8 @@ bool make_layout(const dms_pool_config* c, Layout* L, std::string* why) {
     sz[S_INV] = (size_t)c->n_kv_heads * c->max_positions * 4;
     sz[S_PCNT] = sz[S_INV];
     sz[S_VT] = (size_t)c->n_kv_heads * ((c->max_positions + 31) / 32 * 32) * D * 2;
+    sz[S_VT16] = fp8 ? 0 : sz[S_VT];
+    sz[S_MBITS] = (size_t)c->n_kv_heads * ((c->max_positions + 63) / 64) * 2 * 4;
     sz[S_Q8] = fp8 ? (size_t)2 * c->max_positions * c->n_kv_heads * (D + 4) : 0;
     sz[S_CTL] = 64 * 4;
     size_t o = 0;
@@ -205,6 +207,8 @@ dms_status dms_pool_create(const dms_pool_config* cfg, void* arena, size_t arena
     d.inv = reinterpret_cast<int32_t*>(a + L.off[S_INV]);
     d.pcnt = reinterpret_cast<int32_t*>(a + L.off[S_PCNT]);
     d.vt = reinterpret_cast<uint16_t*>(a + L.off[S_VT]);
+    d.vt16 = reinterpret_cast<uint16_t*>(a + L.off[S_VT16]);
+    d.mbits = reinterpret_cast<uint32_t*>(a + L.off[S_MBITS]);
     d.ctl = reinterpret_cast<int32_t*>(a + L.off[S_CTL]);
     d.max_pages = cfg->max_pages;
     d.n_layers = cfg->n_layers;

@@ -34,6 +34,13 @@
 //                                                  its codes as bf16) with 8 consecutive tokens
 //                                                  per 16 bytes (max_pos32 = max_positions
 //                                                  rounded up to 32)
+//   vt16     fp16 [n_kv_heads][max_pos32/8][head_dim][8]
+//                                                  bf16 pools: the same copy as fp16 values
+//                                                  (read by the prefill attention while no V
+//                                                  value is wide; FP8 pools: empty)
+//   mbits    u32  [n_kv_heads][2 * ceil(max_positions / 64)]
+//                                                  prefill scratch: bit j of word k is the
+//                                                  mark of prompt position 32k + j
 //   ctl      int32 [64]                            pool counters (kCtl* below)
 // heads = max_seqs * n_layers * n_kv_heads, head id = (seq * n_layers + layer) * n_kv_heads + h.
 #pragma once
@@ -124,6 +131,8 @@ struct PoolDev {
     int32_t* inv;
     int32_t* pcnt;
     uint16_t* vt;
+    uint16_t* vt16;    // bf16 pools only
+    uint32_t* mbits;
     int32_t* ctl;
     int64_t max_pages;
     int32_t n_layers, n_q_heads, n_kv_heads, head_dim;
@@ -141,6 +150,10 @@ struct PoolDev {
     __host__ __device__ float* q8_scales(int x) const {
         return reinterpret_cast<float*>(q8 + (size_t)2 * max_positions * n_kv_heads * head_dim) +
                (size_t)x * max_positions * n_kv_heads;
+    }
+    // mark bits of kv head h's prompt positions (prefill scratch)
+    __host__ __device__ uint32_t* mbits_of(int h) const {
+        return mbits + (size_t)h * ((max_positions + 63) / 64) * 2;
     }
     // first scratch page of kv head h (extend calls: the chunk's unmarked rows, in order)
     __host__ __device__ int xpage(int h) const { return (int)max_pages + h * pages_per_head; }
@@ -273,8 +286,9 @@ struct PrefillArgs {
 // kCtlVWide flag, which keeps the attention on its bf16 path.
 // ---------------------------------------------------------------------------
 // Rows s0 .. s0+63 of kv head h, by the 256 threads of a block (all of them
-// call it together: it synchronises the block once), staged in s_v.
-template <int D, bool F8>
+// call it together: it synchronises the block once), staged in s_v.  With
+// V16 (bf16 pools, prefill) the copy is also written as fp16 values to vt16.
+template <int D, bool F8, bool V16 = false>
 __device__ __forceinline__ void vt_rows(const PrefillArgs& a, int s0, int h, uint16_t (*s_v)[D + 8]) {
     const PoolDev& P = a.pool;
     const int tid = threadIdx.x;
@@ -306,7 +320,11 @@ __device__ __forceinline__ void vt_rows(const PrefillArgs& a, int s0, int h, uin
 #pragma unroll
         for (int i = 0; i < 4; ++i)
             w4[i] = (uint32_t)s_v[8 * b + 2 * i][d] | ((uint32_t)s_v[8 * b + 2 * i + 1][d] << 16);
-        *reinterpret_cast<uint4*>(vt + ((size_t)blk * D + d) * 8) = make_uint4(w4[0], w4[1], w4[2], w4[3]);
+        const uint4 unit = make_uint4(w4[0], w4[1], w4[2], w4[3]);
+        *reinterpret_cast<uint4*>(vt + ((size_t)blk * D + d) * 8) = unit;
+        if constexpr (V16 && !F8)
+            *reinterpret_cast<uint4*>(P.vt16 + (size_t)h * (P.max_pos32 / 8) * D * 8 + ((size_t)blk * D + d) * 8) =
+                bf16x8_to_f16x8(unit);
     }
 }
 

@@ -1100,6 +1100,14 @@ __global__ __launch_bounds__(1024) void prefill_scan_kernel(PrefillArgs a) {
             const int s = seg0 + 64 * k;
             bal[k] = __ballot(s < T && (s >= T - w || !(lg[k] > 0.f)));
             wcount += __popcll(bal[k]);
+            // the marks of these 64 positions, for the attention's band tiles
+            const uint64_t mk = __ballot(s < T && lg[k] > 0.f);
+            const int s64 = s - lane;
+            if (lane == 0 && s64 < T) {
+                uint32_t* mb = P.mbits_of(h) + s64 / 32;
+                mb[0] = (uint32_t)mk;
+                mb[1] = (uint32_t)(mk >> 32);
+            }
         }
         if (lane == 0) s_scan[wave] = wcount;
         __syncthreads();
@@ -1179,7 +1187,7 @@ __global__ __launch_bounds__(256) void prefill_compact_kernel(PrefillArgs a) {
     __shared__ uint16_t s_v[kPage][D + 8];
     const int ncomp = (a.n_tokens + kPage - 1) / kPage;  // blocks past these copy the prompt V
     if ((int)blockIdx.x >= ncomp) {
-        vt_rows<D, false>(a, ((int)blockIdx.x - ncomp) * 64, blockIdx.y, s_v);
+        vt_rows<D, false, true>(a, ((int)blockIdx.x - ncomp) * 64, blockIdx.y, s_v);
         return;
     }
     const int tid = threadIdx.x;

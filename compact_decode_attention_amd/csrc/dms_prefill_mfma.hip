@@ -63,6 +63,15 @@ __device__ __forceinline__ float sum_xor32(float x) {
     return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
+// Wait until at most N vector memory operations of this wave are in flight
+// (for loads the compiler does not see: those with an LDS destination).
+template <int N>
+__device__ __forceinline__ void wait_older_loads() {
+    static_assert(N == 2 || N == 4, "one or two units per thread and operand");
+    if constexpr (N == 2) asm volatile("s_waitcnt vmcnt(2)" ::: "memory");
+    else asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+}
+
 // row index of the S^T tile -> key index within the 32-key tile: bits 2 and 3 swapped
 __device__ __forceinline__ int swap23(int i) { return (i & ~12) | ((i & 4) << 1) | ((i & 8) >> 1); }
 
@@ -108,7 +117,15 @@ constexpr int prefill_waves(int g) { return kPrefillWaves > g ? kPrefillWaves : 
 // the factor keeps small weights out of the fp16 subnormals and cancels in
 // O / l).  Otherwise (FP8 pools, or a bf16 pool that has held a V value of
 // magnitude 2^16 or more) P enters as two bf16 parts.
-template <int D, int G, bool F8, bool EXT, bool H16>
+//
+// DIR (prompt prefill on a bf16 pool with fp16 weights, four-wave blocks): the
+// tiles go from memory straight to LDS (buffer loads with the LDS destination),
+// so no register set stages them; three LDS buffers per operand, because a tile
+// lands while the two before it are read; the band's V comes from the fp16 copy
+// and its marks from the scan's bit mask (a scalar load).  Its kernel runs
+// three waves per SIMD.  The loads are counted by hand: every step issues the
+// same 2 UPT of them, and waits at its end until only its own are in flight.
+template <int D, int G, bool F8, bool EXT, bool H16, bool DIR = false>
 __device__ __forceinline__ void prefill_attend_body(const PrefillArgs& a) {
     constexpr int NWV = prefill_waves(G);
     constexpr int NT = 64 * NWV;
@@ -118,9 +135,11 @@ __device__ __forceinline__ void prefill_attend_body(const PrefillArgs& a) {
     constexpr int DT = D / 32;             // 32-row tiles of O^T
     constexpr int UNITS = 4 * D;           // 16-byte units of a K (or V) tile of 32 keys
     constexpr int UPT = (UNITS + NT - 1) / NT;  // units per thread
-    __shared__ uint4 s_k[2][D / 8][32];
-    __shared__ uint4 s_v[2][4][D];
-    __shared__ uint32_t s_marks[2];
+    static_assert(!DIR || (!F8 && !EXT && H16 && UNITS % NT == 0), "direct staging: prompt prefill, fp16 weights");
+    constexpr int NB = DIR ? 3 : 2;  // LDS buffers per operand
+    __shared__ uint4 s_k[NB][D / 8][32];
+    __shared__ uint4 s_v[NB][4][D];
+    __shared__ uint32_t s_marks[NB];
     __shared__ float4 s_ks[2][8], s_vs[2][8];  // FP8: K and V scales of the tile's 32 keys
     __shared__ int4 s_x[2][8];                  // EXT: expiry rows of the tile's 32 stored keys
     const PoolDev& P = a.pool;
@@ -166,7 +185,7 @@ __device__ __forceinline__ void prefill_attend_body(const PrefillArgs& a) {
     const int kend = min(T, t0b + 32 * QT);
     const int ntiles = nfar + (kend > band0 ? (kend - band0 + 31) / 32 : 0);
     const int32_t* ptab = P.ptable + (size_t)gh * P.pages_per_head;
-    const uint16_t* vt = P.vt + (size_t)h * (P.max_pos32 / 8) * D * 8;
+    const uint16_t* vt = (DIR ? P.vt16 : P.vt) + (size_t)h * (P.max_pos32 / 8) * D * 8;
     const size_t rowk = (size_t)hkv * D;  // elements from one prompt row of K to the next
 
     // Staging, thread t: K units u = t, t + NT, ... (chunk u / 32, key u % 32) and the
@@ -235,6 +254,15 @@ __device__ __forceinline__ void prefill_attend_body(const PrefillArgs& a) {
     // md (compile time): 1 if tile i is a full tile of the first far-field
     // segment (the compacted prompt; extend: the stored slots), 2 if it is a full
     // band tile (32 prompt rows), 0 if any kind may hold
+    // DIR: 16 bytes per lane from r at voff into LDS at lds + 16 lane (lds:
+    // this wave's 1 KB of the buffer, passed in M0; a lane past the resource
+    // reads 0 and touches no memory, as with the register loads)
+    // (LDS byte addresses: the low half of a shared variable's generic address)
+    const uint32_t lds_k = (uint32_t)(uintptr_t)&s_k[0][0][0], lds_v = (uint32_t)(uintptr_t)&s_v[0][0][0];
+    auto dma16 = [&](__amdgpu_buffer_rsrc_t r, int voff, uint32_t lds) {
+        const uint32_t la = __builtin_amdgcn_readfirstlane((int)lds);
+        asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds" : : "s"(la), "v"(voff), "s"(r) : "memory");
+    };
     auto load_k = [&](int i, int X, int pg, auto md) {
         constexpr bool FP = decltype(md)::value == 1, BP = decltype(md)::value == 2;
         const int kb = FP ? 32 * i : BP ? band0 + 32 * (i - nfar) : tile_kb(i);
@@ -243,6 +271,13 @@ __device__ __forceinline__ void prefill_attend_body(const PrefillArgs& a) {
         const int bytes = !live ? 0 : far ? kPage * D * EB : (BP ? 32 : rows_left(kb)) * rowb;
         const __amdgpu_buffer_rsrc_t r = rsrc(base, bytes);
         const int slot16 = (kb % kPage) * 16;  // far: the tile's first slot within the page
+        if constexpr (DIR) {  // unit u = 64 wave + lane + NT x: chunk u / 32, key u % 32
+#pragma unroll
+            for (int x = 0; x < UPT; ++x)
+                dma16(r, far ? koff_far[x] + slot16 : koff_band[x],
+                      lds_k + (uint32_t)(((i % NB) * UNITS + 64 * wave + NT * x) * 16));
+            return;
+        }
 #pragma unroll
         for (int x = 0; x < UPT; ++x) {
             const int off = far ? koff_far[x] + slot16 : koff_band[x];
@@ -275,13 +310,22 @@ __device__ __forceinline__ void prefill_attend_body(const PrefillArgs& a) {
                                                    (size_t)(kb % kPage / 8) * D * 16
                                              : vfar0 + upage(pg) * (kPage * D * 2) + (size_t)(kb % kPage / 8) * D * 16;
             const __amdgpu_buffer_rsrc_t r = rsrc(base, live ? UNITS * 16 : 0);
+            if constexpr (DIR) {  // unit u = 64 wave + lane + NT x: key block u / D, dim u % D
 #pragma unroll
-            for (int x = 0; x < UPT; ++x) rv[X][x] = buffer_load16(r, F8 ? (tid + x * NT >= UNITS ? kFar : (tid + x * NT) * 16)
-                                                                    : voff[x], 0);
+                for (int x = 0; x < UPT; ++x)
+                    dma16(r, voff[x], lds_v + (uint32_t)(((i % NB) * UNITS + 64 * wave + NT * x) * 16));
+            } else {
+#pragma unroll
+                for (int x = 0; x < UPT; ++x)
+                    rv[X][x] = buffer_load16(r, F8 ? (tid + x * NT >= UNITS ? kFar : (tid + x * NT) * 16) : voff[x], 0);
+            }
         }
         // per-key data of the tile (lanes l and l + 32 read the same key)
         const bool band = live && !far;
         if (FP) {
+        } else if (DIR) {  // marks of keys kb .. kb+31 (bits past the prompt are 0)
+            typedef const uint32_t __attribute__((address_space(4))) cu32_t;
+            rlg[X] = band ? ((cu32_t*)P.mbits_of(h))[kb / 32] : 0u;
         } else if (P.logit_ch >= 0) {
             const __amdgpu_buffer_rsrc_t r =
                 rsrc(a.k + (size_t)kb * rowk + h * D + P.logit_ch, band ? rows * (int)rowk * 2 : 0);
@@ -304,28 +348,33 @@ __device__ __forceinline__ void prefill_attend_body(const PrefillArgs& a) {
         }
     };
     auto store_k = [&](int i, int X) {
+        if constexpr (DIR) return;  // already in LDS
 #pragma unroll
         for (int x = 0; x < UPT; ++x) {
             const int u = tid + x * NT;
             if (UNITS % NT == 0 || u < UNITS)
-                s_k[i & 1][u >> 5][u & 31] = F8 ? fp8x8_bf16(make_uint2(rk[X][x].x, rk[X][x].y)) : rk[X][x];
+                s_k[i % NB][u >> 5][u & 31] = F8 ? fp8x8_bf16(make_uint2(rk[X][x].x, rk[X][x].y)) : rk[X][x];
         }
     };
     auto store_v = [&](int i, int X, auto md) {
         constexpr int MD = decltype(md)::value;
         const bool far = MD == 1 || (MD != 2 && i < nfar);
+        if constexpr (DIR) {  // V is already in LDS; the tile's marks
+            if (!far && tid == 0) s_marks[i % NB] = rlg[X];
+            return;
+        }
 #pragma unroll
         for (int x = 0; x < UPT; ++x) {
             const int u = tid + x * NT;
             if (UNITS % NT == 0 || u < UNITS)
-                s_v[i & 1][u / D][u % D] = (F8 && far)           ? fp8x8_bf16(make_uint2(rv[X][x].x, rv[X][x].y))
+                s_v[i % NB][u / D][u % D] = (F8 && far)           ? fp8x8_bf16(make_uint2(rv[X][x].x, rv[X][x].y))
                                            : H16 && (EXT || !far) ? bf16x8_to_f16x8(rv[X][x])
                                                                   : rv[X][x];
         }
         if (!far && wave == 0) {  // keys past the prompt read logit 0: unmarked
             const float lg = __uint_as_float(P.logit_ch >= 0 ? rlg[X] << 16 : rlg[X]);
             const uint32_t mk = (uint32_t)__ballot(lg > 0.f);
-            if (lane == 0) s_marks[i & 1] = mk;
+            if (lane == 0) s_marks[i % NB] = mk;
         }
         if constexpr (EXT) {
             if (tid < 32 && (MD == 1 || (MD != 2 && i < nfar1)))
@@ -342,7 +391,7 @@ __device__ __forceinline__ void prefill_attend_body(const PrefillArgs& a) {
     auto scores = [&](int i) {
         uint4 ka[KS];  // every K operand of the tile first: one wait for LDS
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) ka[ks] = s_k[i & 1][2 * ks + half][krow];
+        for (int ks = 0; ks < KS; ++ks) ka[ks] = s_k[i % NB][2 * ks + half][krow];
         f32x16_t sc = f32x16_t{};
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks)
@@ -371,6 +420,7 @@ __device__ __forceinline__ void prefill_attend_body(const PrefillArgs& a) {
         load_k(2, 1, pg2, gen);
         load_v(1, 1, pg1, gen);
     }
+    if constexpr (DIR) wait_older_loads<2 * UPT>();  // K_0, V_0 and K_1 are in LDS
     __syncthreads();
     // one tile: fold S_i (in cur) while S_{i+1} (into nxt) and the next loads run.
     // md (compile time): 1 if tiles i .. i+3 are full tiles of the first
@@ -418,7 +468,7 @@ __device__ __forceinline__ void prefill_attend_body(const PrefillArgs& a) {
             if (!BP && i < nfar) {
                 vis = (1u << (Ufar - kb)) - 1u;  // Ufar - kb in [1, 31]
             } else {
-                const uint32_t marks = s_marks[i & 1];
+                const uint32_t marks = s_marks[i % NB];
                 auto above = [](int c) -> uint32_t {  // bits kr > c
                     return c < 0 ? 0xffffffffu : (c >= 31 ? 0u : (0xffffffffu << (c + 1)));
                 };
@@ -466,9 +516,12 @@ __device__ __forceinline__ void prefill_attend_body(const PrefillArgs& a) {
         // prefill.  The prompt prefill, whose blocks start staggered, gains
         // nothing from it.)
         if constexpr (EXT) __builtin_amdgcn_s_setprio(1);
+        // (DIR: each K operand read where its product is issued, to keep the
+        // register count within three waves per SIMD)
         uint4 ka[KS];
+        if constexpr (!DIR)
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) ka[ks] = s_k[(i + 1) & 1][2 * ks + half][krow];
+            for (int ks = 0; ks < KS; ++ks) ka[ks] = s_k[(i + 1) % NB][2 * ks + half][krow];
         f32x16_t sc = f32x16_t{};
         uint32_t ph[8], pl[8];
         float ps = 0.f;
@@ -477,9 +530,11 @@ __device__ __forceinline__ void prefill_attend_body(const PrefillArgs& a) {
         const float nm = (m == -INFINITY ? 0.f : -m) + (H16 ? 7.f : 0.f);
 #pragma unroll
         for (int i2 = 0; i2 < 8; ++i2) {
-            if (i2 % (8 / KS) == 0)
+            if (i2 % (8 / KS) == 0) {
+                if constexpr (DIR) ka[i2 / (8 / KS)] = s_k[(i + 1) % NB][2 * (i2 / (8 / KS)) + half][krow];
                 sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(ka[i2 / (8 / KS)]), as_bf16x8(qb[i2 / (8 / KS)]),
                                                              sc, 0, 0, 0);
+            }
             const float p0 = __builtin_amdgcn_exp2f(fmaf(z[2 * i2], sl, nm));
             const float p1 = __builtin_amdgcn_exp2f(fmaf(z[2 * i2 + 1], sl, nm));
             if constexpr (H16) {
@@ -502,12 +557,16 @@ __device__ __forceinline__ void prefill_attend_body(const PrefillArgs& a) {
         nxt = sc;
         lsum += ps;
         uint4 va[DT][2];
+        if constexpr (!DIR)
 #pragma unroll
-        for (int dt = 0; dt < DT; ++dt)
+            for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
-            for (int kk = 0; kk < 2; ++kk) va[dt][kk] = s_v[i & 1][2 * kk + half][dt * 32 + col];
+                for (int kk = 0; kk < 2; ++kk) va[dt][kk] = s_v[i % NB][2 * kk + half][dt * 32 + col];
 #pragma unroll
         for (int kk = 0; kk < 2; ++kk) {
+            if constexpr (DIR)  // (DIR: half the V operands at a time)
+#pragma unroll
+                for (int dt = 0; dt < DT; ++dt) va[dt][kk] = s_v[i % NB][2 * kk + half][dt * 32 + col];
             const uint4 hb = make_uint4(ph[4 * kk], ph[4 * kk + 1], ph[4 * kk + 2], ph[4 * kk + 3]);
             if constexpr (H16) {
 #pragma unroll
@@ -532,6 +591,7 @@ __device__ __forceinline__ void prefill_attend_body(const PrefillArgs& a) {
         if (FP || BP || i + 1 < ntiles) store_v(i + 1, X ^ 1, md);
         pg2 = pg3;
         pg3 = pg4;
+        if constexpr (DIR) wait_older_loads<2 * UPT>();  // K_{i+2} and V_{i+1} are in LDS
         __syncthreads();
     };
     // S and the in-flight loads alternate between two register sets (no copies
@@ -561,6 +621,10 @@ __device__ __forceinline__ void prefill_attend_body(const PrefillArgs& a) {
         if (i + 1 < ntiles) step(i + 1, sb, sa, 1, gen);
     }
 
+    // (DIR: the last steps' loads, of tiles past the end, land before the block
+    // can leave and its LDS be handed to another)
+    if constexpr (DIR) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+
     // ---- normalise and store: lane holds dims dt*32 + 8*(r/4) + 4*half + r%4 of query tq
     const float ltot = sum_xor32(lsum);
     if (tq < T) {
@@ -578,6 +642,11 @@ __device__ __forceinline__ void prefill_attend_body(const PrefillArgs& a) {
     }
 }
 
+// Prompt prefill on bf16 pools with four-wave blocks: the fp16-weights case runs
+// in prefill_attend3_kernel (below), this kernel only when a V value is wide.
+template <int D, int G, bool EXT>
+constexpr bool prefill_direct() { return !EXT && prefill_waves(G) == 4; }
+
 template <int D, int G, bool F8, bool EXT>
 __global__ __attribute__((amdgpu_flat_work_group_size(64 * prefill_waves(G), 64 * prefill_waves(G)),
                           amdgpu_waves_per_eu(2, 2)))
@@ -586,9 +655,21 @@ void prefill_attend_kernel(PrefillArgs a) {
         prefill_attend_body<D, G, true, EXT, false>(a);
     } else {
         typedef const int32_t __attribute__((address_space(4))) cint32_t;  // a scalar load
-        if (((cint32_t*)a.pool.ctl)[kCtlVWide] == 0) prefill_attend_body<D, G, false, EXT, true>(a);
-        else prefill_attend_body<D, G, false, EXT, false>(a);
+        if (((cint32_t*)a.pool.ctl)[kCtlVWide] == 0) {
+            if constexpr (!prefill_direct<D, G, EXT>()) prefill_attend_body<D, G, false, EXT, true>(a);
+        } else {
+            prefill_attend_body<D, G, false, EXT, false>(a);
+        }
     }
+}
+
+// The same for the fp16-weights case of a prompt prefill with direct staging:
+// three waves per SIMD (at most 168 registers), 49 KB of LDS per block.
+template <int D, int G>
+__global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(3, 3)))
+void prefill_attend3_kernel(PrefillArgs a) {
+    typedef const int32_t __attribute__((address_space(4))) cint32_t;
+    if (((cint32_t*)a.pool.ctl)[kCtlVWide] == 0) prefill_attend_body<D, G, false, false, true, true>(a);
 }
 
 // Extend calls: expiry row of every stored slot j < n_old of the (seq, layer),
@@ -734,12 +815,22 @@ hipError_t launch_attend_t(const PrefillArgs& a, hipStream_t s, hipEvent_t* ev) 
     const int nqb = (a.n_tokens + 32 * QT - 1) / (32 * QT);
     const int total = a.pool.n_kv_heads * nqb;
     const int grid = 8 * ((total + 7) / 8);
-    if (a.pool.fp8)
+    if (a.pool.fp8) {
         hipExtLaunchKernelGGL((prefill_attend_kernel<D, G, true, EXT>), dim3(grid), dim3(64 * prefill_waves(G)), 0,
                               s, ev ? ev[0] : nullptr, ev ? ev[1] : nullptr, 0, a);
-    else
+    } else if constexpr (prefill_direct<D, G, EXT>()) {
+        // whether a V value is wide is known on the device only: both kernels
+        // are launched, and the one that does not apply returns at once
+        hipExtLaunchKernelGGL((prefill_attend3_kernel<D, G>), dim3(grid), dim3(256), 0, s, ev ? ev[0] : nullptr,
+                              nullptr, 0, a);
+        const hipError_t err = hipGetLastError();
+        if (err != hipSuccess) return err;
+        hipExtLaunchKernelGGL((prefill_attend_kernel<D, G, false, EXT>), dim3(grid), dim3(64 * prefill_waves(G)), 0,
+                              s, nullptr, ev ? ev[1] : nullptr, 0, a);
+    } else {
         hipExtLaunchKernelGGL((prefill_attend_kernel<D, G, false, EXT>), dim3(grid), dim3(64 * prefill_waves(G)), 0,
                               s, ev ? ev[0] : nullptr, ev ? ev[1] : nullptr, 0, a);
+    }
     return hipGetLastError();
 }
 

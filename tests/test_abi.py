@@ -115,13 +115,15 @@ def test_fp8_pool_holds_codes_and_scales():
     """An FP8 pool's pages take head_dim + 4 bytes per row (codes and an fp32
     scale) instead of 2 * head_dim, plus the prompt scratch for its codes.  The
     page arrays hold the shared pool and ceil(max_positions / 64) scratch pages
-    per kv head."""
+    per kv head.  A bf16 pool also holds the prompt's V as fp16 values, 2 bytes
+    per (position, kv head, dim), for its prefill attention."""
     pages = 36 * 8 * 131 + 8 * 130
     b16 = dms.dms_pool_bytes(qwen_cfg())
     f8 = dms.dms_pool_bytes(qwen_cfg(kv_format=dms.DMS_KV_FP8_E4M3))
     saved = 2 * pages * 64 * (2 * 128 - (128 + 4))
     scratch = 2 * 8320 * 8 * (128 + 4)
-    assert b16 - f8 == saved - scratch
+    vt16 = 8320 * 8 * 128 * 2
+    assert b16 - f8 == saved - scratch + vt16
 
 
 def test_window_beyond_positions_needs_no_ring():
