@@ -473,7 +473,8 @@ def bench_prefill(args, torch, dms):
            "tok_per_s": round(T / (ms / 1e3), 1), "ms_all_layers": round(ms, 4),
            "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
                         "unit": "TFLOP/s", "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4),
-                        "kernel": "prefill_attend_kernel<128,4>", "avg_launch_us": round(avg_att * 1e3, 2),
+                        "kernel": "prefill_attend3_kernel<128,4> (fp16 weights; its bf16-weights fallback, "
+                                  "launched beside it, returns at once)", "avg_launch_us": round(avg_att * 1e3, 2),
                         "flops_per_launch": flops, "dense_causal_flops": dense},
            "compaction_avg_us": round(avg_cmp * 1e3, 2),
            "kv_gib": {"live": round(st.kv_bytes_live / 2**30, 4),
