@@ -603,6 +603,9 @@ __device__ __forceinline__ void prefill_attend_body(const PrefillArgs& a) {
     const std::integral_constant<int, 1> farc;
     const std::integral_constant<int, 2> bandc;
     f32x16_t sa = scores(0), sb;
+    // (DIR: step 0 loads K_3 into K_0's buffer, which every wave has just read
+    // for S_0; with staging through registers that write came two barriers later)
+    if constexpr (DIR) __syncthreads();
     int i = 0;
     for (; i + 6 <= nfar1; i += 2) {
         step(i, sa, sb, 0, farc);
