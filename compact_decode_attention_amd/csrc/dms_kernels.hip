@@ -1069,12 +1069,20 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeArgs a) {
 // ---------------------------------------------------------------------------
 // prefill: marks, live set of the last position, page allocation, ring
 // ---------------------------------------------------------------------------
+constexpr int kScanChunk = 16 * 64 * 8;  // prompt positions per scan block
+
+// Block (c, h): positions [c kScanChunk, (c+1) kScanChunk) of kv head h.  The
+// live positions before the chunk are counted first (all their logits requested
+// at once), so the chunks of a long prompt run side by side; the block of the
+// last chunk, which then knows the head's live count, pops its pages and writes
+// its record and window ring.
 __global__ __launch_bounds__(1024) void prefill_scan_kernel(PrefillArgs a) {
     const PoolDev& P = a.pool;
     __shared__ int s_scan[2 * 16 + 1];
     __shared__ int s_base;
     const int tid = threadIdx.x;
-    const int h = blockIdx.x;
+    const int h = blockIdx.y;
+    const int chunk = blockIdx.x;
     const int hkv = P.n_kv_heads;
     const int gh = (a.seq * P.n_layers + a.layer) * hkv + h;
     const int T = a.n_tokens, w = P.window;
@@ -1088,7 +1096,25 @@ __global__ __launch_bounds__(1024) void prefill_scan_kernel(PrefillArgs a) {
     constexpr int KW = 8;
     const int lane = tid & 63, wave = tid >> 6;
     int n = 0;  // live positions before the current chunk
-    for (int c0 = 0; c0 < T; c0 += 16 * 64 * KW) {
+    if (chunk > 0) {
+        // live(s) = s >= T - w or s unmarked; thread t reads positions t, t + 1024, ...
+        // (all below chunk * kScanChunk <= T - 1)
+        int cnt = 0;  // live positions of this wave's share
+        const int end = chunk * kScanChunk;
+        for (int s0 = 0; s0 < end; s0 += 1024 * KW) {
+            float lg[KW];
+#pragma unroll
+            for (int k = 0; k < KW; ++k) lg[k] = eviction_logit(P, a.logits, a.k, s0 + 1024 * k + tid, h);
+#pragma unroll
+            for (int k = 0; k < KW; ++k) cnt += __popcll(__ballot(s0 + 1024 * k + tid >= T - w || !(lg[k] > 0.f)));
+        }
+        if (lane == 0) s_scan[wave] = cnt;
+        __syncthreads();
+#pragma unroll
+        for (int v = 0; v < 16; ++v) n += s_scan[v];
+        __syncthreads();  // s_scan is rewritten below
+    }
+    for (int c0 = chunk * kScanChunk; c0 < min(T, (chunk + 1) * kScanChunk); c0 += 16 * 64 * KW) {
         const int seg0 = c0 + wave * 64 * KW + lane;
         float lg[KW];
 #pragma unroll
@@ -1132,6 +1158,7 @@ __global__ __launch_bounds__(1024) void prefill_scan_kernel(PrefillArgs a) {
         }
         n += tot;
     }
+    if (chunk != (T - 1) / kScanChunk) return;  // the head's last chunk finishes it
     const int np = (n + kPage - 1) / kPage;
     if (tid == 0) {
         const int old = atomicSub(&P.ctl[kCtlTop], np);
@@ -1694,7 +1721,8 @@ hipError_t launch_prefill_compact(const PrefillArgs& a, bool with_vt, hipStream_
         if (err != hipSuccess) return err;
         start = nullptr;
     }
-    hipExtLaunchKernelGGL(prefill_scan_kernel, dim3(a.pool.n_kv_heads), dim3(1024), 0, s, start, nullptr, 0, a);
+    hipExtLaunchKernelGGL(prefill_scan_kernel, dim3((a.n_tokens + kScanChunk - 1) / kScanChunk, a.pool.n_kv_heads),
+                          dim3(1024), 0, s, start, nullptr, 0, a);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
     // one block per page of live slots (those past the head's count return at
