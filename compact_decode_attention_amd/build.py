@@ -12,9 +12,13 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libdms.so")
 SOURCES = ["dms_api.cpp", "dms_kernels.hip", "dms_prefill_mfma.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
-# -packed-fp32-ops: no v_pk_{add,mul,fma}_f32 in device code
+# -packed-fp32-ops: no v_pk_{add,mul,fma}_f32 in device code.
+# -amdgpu-kernarg-preload-count: the dispatch places the first 8 dwords of the
+# kernel arguments in registers (the decode kernels' leading arguments are what
+# their first loads need).
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+         "-mllvm", "-amdgpu-kernarg-preload-count=8",
          "-I", os.path.join(ROOT, "include"), "-I", CSRC]
 
 

@@ -120,11 +120,13 @@ __device__ __forceinline__ float wave_sum(float x) {
 // the dispatch, so the first read of each 64-byte line of them misses the
 // caches; read lazily under branches, those misses come one after another.
 // Touching every line the kernel reads at entry puts them in flight together.
+// (with: uniform values loaded just before, which are waited for together with
+// the lines)
 template <int BYTES>
-__device__ __forceinline__ void touch_args(const void* args) {
+__device__ __forceinline__ void touch_args(const void* args, int with = 0) {
     typedef const int __attribute__((address_space(4))) cint_t;
     cint_t* p = (cint_t*)args;
-    int acc = 0;
+    int acc = with;
 #pragma unroll
     for (int o = 0; o < BYTES / 4; o += 16) acc ^= p[o];
     asm volatile("" ::"s"(acc));
@@ -504,15 +506,15 @@ __device__ __forceinline__ const uint16_t* q_group(const DecodeArgs& a, int ch) 
 template <int D, int G, bool F8>
 __global__ __attribute__((amdgpu_flat_work_group_size(64 * kAttendWaves, 64 * kAttendWaves),
                           amdgpu_waves_per_eu(2, 2)))
-void decode_attend_kernel(DecodeArgs a) {
-    touch_args<offsetof(DecodeArgs, seq_ids) + 64>(&a);  // the fixed part and the first sequence ids
+void decode_attend_kernel(const int32_t* __restrict__ hs_plan, int32_t gh0, int32_t n_heads, int32_t n_kv,
+                          int32_t n_seqs, int32_t pool_layers, int32_t layer0, DecodeArgs a) {
     constexpr int NT = 64 * kAttendWaves;
     constexpr int VJ = D / 64;
     constexpr int QV = G * D / 8;  // 16-byte pieces of one head group's q
     constexpr int QR = (QV + 63) / 64;
     constexpr int PSTR = part_stride(G, D);
     constexpr int ACC = part_acc_off(G);
-    const int H = a.n_call_heads;
+    const int H = n_heads;
     extern __shared__ int32_t s_dyn[];
     int32_t* s_pp = s_dyn;            // [H + 1] first page of each head on the call's page axis
     int32_t* s_nold = s_pp + H + 1;   // [H] live count before this step
@@ -537,10 +539,16 @@ void decode_attend_kernel(DecodeArgs a) {
 #pragma unroll
         for (int i = 0; i < MAXPER; ++i) {
             if (h0 + i < h1) {
-                ghs[i] = call_head(a, h0 + i).gh;
-                rec[i] = *reinterpret_cast<const int4*>(P.hstate + (size_t)ghs[i] * kHS);
+                // (the global head id as call_head computes it, from the leading
+                // arguments; a call of one sequence needs no sequence id)
+                const int ch = h0 + i, li = ch / (n_seqs * n_kv), si = (ch - li * n_seqs * n_kv) / n_kv;
+                ghs[i] = gh0 >= 0 ? gh0 + ch : (a.seq_ids[si] * pool_layers + layer0 + li) * n_kv + ch % n_kv;
+                rec[i] = *reinterpret_cast<const int4*>(hs_plan + (size_t)ghs[i] * kHS);
             }
         }
+        // (after the head records are requested: the fixed part of the
+        // arguments and the first sequence ids, one word of every line)
+        touch_args<offsetof(DecodeArgs, seq_ids) + 64>(&a);
         int local = 0;
 #pragma unroll
         for (int i = 0; i < MAXPER; ++i) {
@@ -723,7 +731,7 @@ void decode_attend_kernel(DecodeArgs a) {
 // (FP8 pools: the new token enters as its quantised K and V rows, value(code) *
 // row scale, like every stored token.)
 template <int D, int G, bool F8, int DS>
-__device__ void merge_head(const DecodeArgs& a, int ch, int ds) {
+__device__ void merge_head(const DecodeArgs& a, const int32_t* __restrict__ prefix, int H, int ch, int ds) {
     const PoolDev& P = a.pool;
     constexpr int PSTR = part_stride(G, D);  // floats per partial
     constexpr int ACC = part_acc_off(G);
@@ -738,12 +746,15 @@ __device__ void merge_head(const DecodeArgs& a, int ch, int ds) {
     __shared__ float s_red[2][4][G];  // per wave: max, then sum
     __shared__ float s_w[NW_MAX][G];  // weights
     __shared__ float4 s_o[NPH > 1 ? NPH - 1 : 1][NF];
+    // partial slots of this head: w + ch for the waves w whose runs of the page
+    // axis meet the head's pages [pf, pl); wave of page p: ((p + 1) * W - 1) / total
+    const int pf = prefix[ch], pl = prefix[ch + 1], total = prefix[H];
+    // the argument lines requested beside the prefix (whose pointer and
+    // count are leading arguments), one wait for both
+    touch_args<offsetof(DecodeArgs, seq_ids) + 64>(&a, pf ^ pl ^ total);
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const CallHead c = call_head(a, ch);
-    // partial slots of this head: w + ch for the waves w whose runs of the page
-    // axis meet the head's pages [pf, pl); wave of page p: ((p + 1) * W - 1) / total
-    const int pf = P.prefix[ch], pl = P.prefix[ch + 1], total = P.prefix[a.n_call_heads];
     int i0 = 0, n = 0;
     if (pl > pf) {
         const int64_t W = min(a.n_waves, total);
@@ -1055,13 +1066,14 @@ __device__ void append_head(const DecodeArgs& a, int ch) {
 
 // Blocks 0 .. DS*H-1 merge (head b / DS, part b % DS), the next H append.
 template <int D, int G, bool F8, int DS>
-__global__ __launch_bounds__(256) void decode_merge_kernel(DecodeArgs a) {
-    touch_args<offsetof(DecodeArgs, seq_ids) + 64>(&a);
-    const int H = a.n_call_heads;
+__global__ __launch_bounds__(256) void decode_merge_kernel(const int32_t* __restrict__ prefix, int32_t n_heads,
+                                                          DecodeArgs a) {
+    const int H = n_heads;
     const int b = blockIdx.x;
     if (b < DS * H) {
-        merge_head<D, G, F8, DS>(a, b / DS, b % DS);
+        merge_head<D, G, F8, DS>(a, prefix, H, b / DS, b % DS);
     } else if (threadIdx.x < 64) {
+        touch_args<offsetof(DecodeArgs, seq_ids) + 64>(&a);
         append_head<D, F8>(a, b - DS * H);
     }
 }
@@ -1641,8 +1653,14 @@ size_t decode_shm(const DecodeArgs& a) { return (size_t)(4 * a.n_call_heads + 1)
 // taken by the dispatches themselves (kernel execution only)
 template <int D, int G, bool F8>
 hipError_t launch_decode_f(const DecodeArgs& a, int grid, hipStream_t s, hipEvent_t* ev) {
+    // the plan's first loads need the head records, the call's head count and
+    // what the global head ids are made of (for a call of one sequence, the id
+    // of its first head: the others follow it): leading arguments, which the
+    // dispatch places in registers (kernel-argument preloading)
+    const int32_t gh0 = a.n_seqs == 1 ? (a.seq_ids[0] * a.pool.n_layers + a.layer0) * a.pool.n_kv_heads : -1;
     hipExtLaunchKernelGGL((decode_attend_kernel<D, G, F8>), dim3(grid), dim3(64 * kAttendWaves), decode_shm(a), s,
-                          ev ? ev[0] : nullptr, ev ? ev[1] : nullptr, 0, a);
+                          ev ? ev[0] : nullptr, ev ? ev[1] : nullptr, 0, (const int32_t*)a.pool.hstate, gh0,
+                          a.n_call_heads, a.pool.n_kv_heads, a.n_seqs, a.pool.n_layers, a.layer0, a);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
     // A head whose outputs fill 128 or more threads' float4s holds at most 32
@@ -1652,10 +1670,12 @@ hipError_t launch_decode_f(const DecodeArgs& a, int grid, hipStream_t s, hipEven
     // n_waves / H bounds the partials of an average head.)
     if (G * D / 4 >= 128 && a.n_waves > 8 * a.n_call_heads)
         hipExtLaunchKernelGGL((decode_merge_kernel<D, G, F8, 4>), dim3(5 * a.n_call_heads), dim3(256), 0, s,
-                              ev ? ev[2] : nullptr, ev ? ev[3] : nullptr, 0, a);
+                              ev ? ev[2] : nullptr, ev ? ev[3] : nullptr, 0, (const int32_t*)a.pool.prefix,
+                              a.n_call_heads, a);
     else
         hipExtLaunchKernelGGL((decode_merge_kernel<D, G, F8, 1>), dim3(2 * a.n_call_heads), dim3(256), 0, s,
-                              ev ? ev[2] : nullptr, ev ? ev[3] : nullptr, 0, a);
+                              ev ? ev[2] : nullptr, ev ? ev[3] : nullptr, 0, (const int32_t*)a.pool.prefix,
+                              a.n_call_heads, a);
     return hipGetLastError();
 }
 
