@@ -119,7 +119,9 @@ __device__ __forceinline__ float wave_sum(float x) {
 // The kernel arguments sit in memory the command processor wrote just before
 // the dispatch, so the first read of each 64-byte line of them misses the
 // caches; read lazily under branches, those misses come one after another.
-// Touching every line the kernel reads at entry puts them in flight together.
+// Touching every line the kernel reads puts them in flight together (the
+// decode kernels do it right after their first loads, whose addresses come in
+// the preloaded leading arguments).
 // (with: uniform values loaded just before, which are waited for together with
 // the lines)
 template <int BYTES>
