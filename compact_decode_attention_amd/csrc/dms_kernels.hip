@@ -979,23 +979,12 @@ __device__ void append_head(const DecodeArgs& a, int ch) {
         const float ks = e4m3_row_scale(wave_max(ka)), vs = e4m3_row_scale(wave_max(va));
         uint8_t* kp = P.kp8() + (size_t)page * (kPage * D);
         uint8_t* vp = P.vp8() + (size_t)page * (kPage * D);
-        if (lane < D / 16) {  // 16 dims per lane: one 16-byte chunk
-            const uint4 x0 = *reinterpret_cast<const uint4*>(kn + lane * 16);
-            const uint4 x1 = *reinterpret_cast<const uint4*>(kn + lane * 16 + 8);
-            const uint32_t xw[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
-            uint32_t cw[4];
+        // every lane encodes its dims d = lane + 64 jj (the values it read for the
+        // maximum) and stores each code as the byte d % 16 of chunk d / 16
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                uint32_t c = 0;
-#pragma unroll
-                for (int h2 = 0; h2 < 2; ++h2) {
-                    const uint32_t wbits = xw[2 * q + h2];
-                    c |= e4m3_encode(bf16_to_f32((uint16_t)(wbits & 0xffffu)) / ks) << (16 * h2);
-                    c |= e4m3_encode(bf16_to_f32((uint16_t)(wbits >> 16)) / ks) << (16 * h2 + 8);
-                }
-                cw[q] = c;
-            }
-            *reinterpret_cast<uint4*>(kp + ((size_t)lane * kPage + j) * 16) = make_uint4(cw[0], cw[1], cw[2], cw[3]);
+        for (int jj = 0; jj < VJ; ++jj) {
+            const int d = jj * 64 + lane;
+            kp[((size_t)(d / 16) * kPage + j) * 16 + d % 16] = (uint8_t)e4m3_encode(bf16_to_f32(kn[d]) / ks);
         }
         if (fresh) {  // j = 0: slots 1..63 cleared (codes and scales), V units written whole
             if (lane > 0) {
