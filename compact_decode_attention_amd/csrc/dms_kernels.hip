@@ -579,8 +579,13 @@ void decode_attend_kernel(const int32_t* __restrict__ hs_plan, int32_t gh0, int3
     }
     // ---- this wave's run of pages (no block-wide synchronisation below)
     const int total = __builtin_amdgcn_readfirstlane(s_pp[H]);
-    const int W = min((int)gridDim.x * kAttendWaves, total);
-    const int w = blockIdx.x * kAttendWaves + wave;
+    const int NW = (int)gridDim.x * kAttendWaves;
+    const int W = min(NW, total);
+    // Run w of W.  A call with fewer pages than waves (one page per run, e.g.
+    // one layer of one sequence) hands its runs to wave 0 of every block first,
+    // so that each run has a compute unit's load path to itself; otherwise the
+    // waves of a block take consecutive runs.
+    const int w = W < NW ? wave * (int)gridDim.x + (int)blockIdx.x : (int)blockIdx.x * kAttendWaves + wave;
     if (w >= W) return;
     const int p0 = (int)(((int64_t)w * total) / W);
     const int p1 = (int)(((int64_t)(w + 1) * total) / W);
