@@ -207,6 +207,47 @@ def test_release_and_reprefill_conserves_pages():
     r.close()
 
 
+def test_reprefill_onto_other_pages_after_one_layer_calls():
+    """Sequence 0 is stepped by one-layer calls, released, its freed pages are
+    taken by sequence 1's prefill, and sequence 0 is prefilled again with the
+    same prompt: the same page counts, so the calls' runs cover the same (head,
+    page index) pairs as before the release, but on other pages.  Its next
+    one-layer calls must read the new pages; sequence 1 must read its own."""
+    case = Case(n_layers=2, n_q_heads=8, n_kv_heads=2, head_dim=64, window=8,
+                ctx_lens=[600, 600], steps=3, seed=23)
+    case.gen()
+    r = Runner(case)
+    try:
+        t = r.torch
+        from dms_case import to_dev
+
+        def prefill(s):
+            T = case.ctx_lens[s]
+            for l in range(case.n_layers):
+                d = case.data[(s, l)]
+                r.pool.prefill(s, l, to_dev(d.k[:T], t, t.bfloat16), to_dev(d.v[:T], t, t.bfloat16),
+                               to_dev(d.logits[:T], t, t.float32))
+
+        def one_layer_steps():
+            for i in range(case.steps):
+                for l in range(case.n_layers):
+                    out = r.decode(i, seqs=[0], layer0=l, n_layers=1)
+                    r.check_outputs(out, i, seqs=[0], layer0=l)
+
+        prefill(0)
+        one_layer_steps()
+        r.pool.release(0)
+        prefill(1)
+        prefill(0)
+        one_layer_steps()
+        for i in range(case.steps):
+            out = r.decode(i, seqs=[1])
+            r.check_outputs(out, i, seqs=[1])
+        r.check_live([case.ctx_lens[s] + case.steps - 1 for s in range(2)])
+    finally:
+        r.close()
+
+
 def test_capacity_exhaustion_is_reported():
     import compact_decode_attention_amd as dms
     case = Case(n_layers=1, n_q_heads=4, n_kv_heads=1, head_dim=64, window=4,
