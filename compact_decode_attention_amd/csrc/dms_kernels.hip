@@ -579,6 +579,78 @@ void decode_attend_kernel(const int32_t* __restrict__ hs_plan, int32_t gh0, int3
     }
     // ---- this wave's run of pages (no block-wide synchronisation below)
     const int total = __builtin_amdgcn_readfirstlane(s_pp[H]);
+    if (total <= (int)gridDim.x) {
+        // A call with at most one page per block (e.g. one layer of one
+        // sequence): block b takes page b (run b of W = total), and its waves
+        // split the page's G q heads, GW each, every wave with its own copy of
+        // the page.  Each head's arithmetic is the general path's, so the
+        // partial holds the same bits; the page's dot products are spread over
+        // the block's SIMDs.  A 32 KB page (D = 128) goes to at most two waves:
+        // four copies of it load one compute unit's memory path more than the
+        // shorter dot products save.
+        constexpr int NAX = D == 128 ? 2 : kAttendWaves;
+        constexpr int NA = G < NAX ? G : NAX;  // waves with heads
+        constexpr int GW = G / NA;                               // q heads per wave
+        constexpr int QW = GW * D / 8;                           // 16-byte pieces of their q
+        const int pg = blockIdx.x;
+        if (pg >= total || wave >= NA) return;
+        int lo = 0, hi = H;  // s_pp[lo] <= pg < s_pp[hi]
+        while (hi - lo > 1) {
+            const int mid = (lo + hi) >> 1;
+            if (s_pp[mid] <= pg) lo = mid; else hi = mid;
+        }
+        const int hd = __builtin_amdgcn_readfirstlane(lo);
+        const int j = pg - __builtin_amdgcn_readfirstlane(s_pp[hd]);
+        const int gh = __builtin_amdgcn_readfirstlane(s_gh[hd]);
+        const int pid = __builtin_amdgcn_readfirstlane(P.ptable[(size_t)gh * P.pages_per_head + j]);
+        const uint4 qv = buffer_load16(buffer_rsrc(q_group(a, hd) + wave * GW * D, QW * 16), lane * 16, 0);
+        uint4 kc[F8 ? D / 16 : D / 8], vc[F8 ? 4 : 8][VJ];
+        float ksn = 1.f, vsn = 1.f;
+        if constexpr (F8) {
+            issue_k8<D>(P, pid, true, lane, kc, ksn, vsn);
+            issue_v8<D>(P, pid, true, lane, vc);
+        } else {
+            issue_k<D>(P, pid, true, lane, kc);
+            issue_v<D>(P, pid, true, lane, vc);
+        }
+        if (lane < QW) s_q[wave][lane] = qv;
+        wave_lds_sync();
+        float z[GW], m[GW], l[GW], acc[GW][VJ], vmax = 1.f, vsc = 1.f;
+#pragma unroll
+        for (int g = 0; g < GW; ++g) {
+            m[g] = -INFINITY;
+            l[g] = 0.f;
+#pragma unroll
+            for (int jj = 0; jj < VJ; ++jj) acc[g][jj] = 0.f;
+        }
+        if constexpr (F8) {
+            qk_page8<D, GW>(kc, s_q[wave], z);
+#pragma unroll
+            for (int g = 0; g < GW; ++g) z[g] *= ksn;
+            vsc = vsn;
+        } else {
+            qk_page<D, GW>(kc, s_q[wave], z);
+        }
+        uint16_t(*sp)[GW][kPage] = reinterpret_cast<uint16_t(*)[GW][kPage]>(&s_p[wave][0][0][0]);
+        softmax_page<D, GW, F8>(z, P.scale_log2, j * kPage, __builtin_amdgcn_readfirstlane(s_nold[hd]),
+                                __builtin_amdgcn_readfirstlane(s_exp[hd]), lane, vsc, sp, m, l, acc, vmax);
+        wave_lds_sync();
+        if constexpr (F8) pv_page8<D, GW>(vc, sp, vmax, acc);
+        else pv_page<D, GW>(vc, sp, acc);
+        float* part = P.partials + (size_t)(pg + hd) * PSTR;
+        if (lane == 0) {
+#pragma unroll
+            for (int g = 0; g < GW; ++g) {
+                part[wave * GW + g] = m[g];
+                part[G + wave * GW + g] = l[g];
+            }
+        }
+#pragma unroll
+        for (int g = 0; g < GW; ++g)
+#pragma unroll
+            for (int jj = 0; jj < VJ; ++jj) part[ACC + (wave * GW + g) * D + jj * 64 + lane] = acc[g][jj];
+        return;
+    }
     const int NW = (int)gridDim.x * kAttendWaves;
     const int W = min(NW, total);
     // Run w of W.  A call with fewer pages than waves (one page per run, e.g.
