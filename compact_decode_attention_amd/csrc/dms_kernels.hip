@@ -234,7 +234,10 @@ __device__ __forceinline__ CallHead call_head(const DecodeArgs& a, int ch) {
 // runs; wave w takes pages [w*P/W, (w+1)*P/W) and folds them into a running
 // softmax, writing one partial per head its run touches, at partial slot w + ch
 // (distinct for all (w, ch) pairs that occur, and contiguous per head).  Waves
-// never wait for each other after the plan is built.
+// never wait for each other after the plan is built.  Small calls: with fewer
+// pages than waves, run w (one page) goes to wave w / grid of block w % grid;
+// with at most one page per block, block b takes page b and its waves share
+// out the page's q heads.
 //
 // Pipeline of one wave: K and V of page k+1 are requested while page k is being
 // computed (K right after QK^T has consumed the K registers, V right after P.V
