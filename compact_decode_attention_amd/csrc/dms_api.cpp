@@ -28,8 +28,8 @@ dms_status hip_fail(hipError_t e, const char* what) {
 constexpr size_t kAlign = 256;
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
-enum Section { S_K, S_V, S_KS, S_VS, S_POS, S_STACK, S_HSTATE, S_PTABLE, S_RING, S_PART, S_PREFIX, S_INV, S_PCNT,
-               S_VT, S_VT16, S_MBITS, S_Q8, S_CTL, S_N };
+enum Section { S_K, S_V, S_KS, S_VS, S_POS, S_STACK, S_RCACHE, S_HSTATE, S_PTABLE, S_RING, S_PART, S_PREFIX,
+               S_INV, S_PCNT, S_VT, S_VT16, S_MBITS, S_Q8, S_CTL, S_N };
 
 struct Layout {
     size_t off[S_N + 1];
@@ -95,6 +95,7 @@ bool make_layout(const dms_pool_config* c, Layout* L, std::string* why) {
     sz[S_VT16] = fp8 ? 0 : sz[S_VT];
     sz[S_MBITS] = (size_t)c->n_kv_heads * ((c->max_positions + 63) / 64) * 2 * 4;
     sz[S_Q8] = fp8 ? (size_t)2 * c->max_positions * c->n_kv_heads * (D + 4) : 0;
+    sz[S_RCACHE] = dms::kRunCacheBytes;
     sz[S_CTL] = 64 * 4;
     size_t o = 0;
     for (int i = 0; i < S_N; ++i) {
@@ -102,6 +103,8 @@ bool make_layout(const dms_pool_config* c, Layout* L, std::string* why) {
         o = align_up(o + sz[i]);
     }
     L->off[S_N] = o;
+    // the decode attention finds the page cache from the head-record pointer
+    if (L->off[S_HSTATE] != L->off[S_RCACHE] + dms::kRunCacheBytes) return bad("arena layout: cache placement");
     return true;
 }
 
@@ -209,6 +212,7 @@ dms_status dms_pool_create(const dms_pool_config* cfg, void* arena, size_t arena
     d.vt = reinterpret_cast<uint16_t*>(a + L.off[S_VT]);
     d.vt16 = reinterpret_cast<uint16_t*>(a + L.off[S_VT16]);
     d.mbits = reinterpret_cast<uint32_t*>(a + L.off[S_MBITS]);
+    d.rcache = reinterpret_cast<int32_t*>(a + L.off[S_RCACHE]);
     d.ctl = reinterpret_cast<int32_t*>(a + L.off[S_CTL]);
     d.max_pages = cfg->max_pages;
     d.n_layers = cfg->n_layers;
@@ -243,6 +247,8 @@ dms_status dms_pool_create(const dms_pool_config* cfg, void* arena, size_t arena
     if (e == hipSuccess) e = hipMemcpyAsync(d.stack, order.data(), order.size() * 4, hipMemcpyHostToDevice, s);
     if (e == hipSuccess) e = hipMemcpyAsync(d.hstate, rec.data(), rec.size() * 4, hipMemcpyHostToDevice, s);
     if (e == hipSuccess) e = hipMemcpyAsync(d.ctl, ctl, sizeof(ctl), hipMemcpyHostToDevice, s);
+    const int32_t epoch = 1;  // the zeroed page-cache entries carry epoch 0: none is valid
+    if (e == hipSuccess) e = hipMemcpyAsync(d.rcache, &epoch, sizeof(epoch), hipMemcpyHostToDevice, s);
     if (e == hipSuccess) e = hipStreamSynchronize(s);
     if (e == hipSuccess) e = dms::static_scratch_address(&p->scratch);  // once per device, here
     if (e != hipSuccess) {

@@ -18,6 +18,10 @@
 //            [n_kv_heads][head_dim] (K, V) then scales f32 [2][max_positions][n_kv_heads]
 //   slot_pos int32 [max_pages][64]                 position held by each slot
 //   stack    int32 [max_pages]                     free pages, stack[0 .. top)
+//   rcache   int32 [kRunCacheHeader + kRunCacheRows * kRunCacheRuns * 4]
+//                                                  decode attention: the pool's epoch, then the
+//                                                  pages of earlier small calls' blocks (directly
+//                                                  before hstate; kRunCache* below)
 //   hstate   int32 [heads][8]                      per-head record (kHs* below)
 //   ptable   int32 [heads][pages_per_head]         page of slots 64j .. 64j+63
 //   ring     int32 [heads][ring_len]               entry of position s at s % w:
@@ -84,6 +88,20 @@ constexpr int kCtlVWide = 2;  // sticky: nonzero once a bf16 V value of magnitud
 constexpr int kCtlPosError = 3;  // sticky: nonzero once a decode or extend call ran past max_positions (the
                                  // device's position counters decide; tokens past the limit are dropped)
 
+// Page cache of the decode attention's calls with at most one page per block:
+// a header of kRunCacheHeader ints, whose first is the pool's epoch (advanced by
+// every release and prefill: a head's page-table entries below its page count
+// change only when a release frees them), then kRunCacheRows rows (the first
+// head of a call of one sequence picks the row) of kRunCacheRuns entries {page
+// id, global head, page index, epoch}, one per block.  The arena places it
+// directly before the head records, so the attention finds it from the
+// head-record pointer it gets in registers.
+constexpr int kRunCacheRows = 64;
+constexpr int kRunCacheRuns = 1024;
+constexpr int kRunCacheHeader = 64;
+constexpr size_t kRunCacheBytes = ((size_t)kRunCacheHeader + (size_t)kRunCacheRows * kRunCacheRuns * 4) * 4;
+static_assert(kRunCacheBytes % 256 == 0, "the head records follow the cache without padding");
+
 // Nonzero if one of the two bf16 values in w has magnitude >= 2^16, is inf or
 // is NaN (exponent field >= 143): such a value has no fp16 counterpart.
 __device__ __forceinline__ uint32_t bf16x2_wide(uint32_t w) {
@@ -133,6 +151,7 @@ struct PoolDev {
     uint16_t* vt;
     uint16_t* vt16;    // bf16 pools only
     uint32_t* mbits;
+    int32_t* rcache;
     int32_t* ctl;
     int64_t max_pages;
     int32_t n_layers, n_q_heads, n_kv_heads, head_dim;

@@ -508,7 +508,7 @@ __device__ __forceinline__ const uint16_t* q_group(const DecodeArgs& a, int ch) 
     return a.q + ((size_t)c.row * a.pool.n_q_heads + c.h * (a.pool.n_q_heads / a.pool.n_kv_heads)) * a.pool.head_dim;
 }
 
-template <int D, int G, bool F8>
+template <int D, int G, bool F8, bool RC>
 __global__ __attribute__((amdgpu_flat_work_group_size(64 * kAttendWaves, 64 * kAttendWaves),
                           amdgpu_waves_per_eu(2, 2)))
 void decode_attend_kernel(const int32_t* __restrict__ hs_plan, int32_t gh0, int32_t n_heads, int32_t n_kv,
@@ -533,6 +533,29 @@ void decode_attend_kernel(const int32_t* __restrict__ hs_plan, int32_t gh0, int3
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
 
+    // Calls with at most one page per block (below): NA waves of a block take
+    // its page, GW q heads each.  A 32 KB page (D = 128) goes to at most two
+    // waves: four copies of it load one compute unit's memory path more than
+    // the shorter dot products save.
+    constexpr int NAX = D == 128 ? 2 : kAttendWaves;
+    constexpr int NA = G < NAX ? G : NAX;  // waves with q heads
+    constexpr int GW = G / NA;             // q heads per such wave
+    constexpr int QW = GW * D / 8;         // 16-byte pieces of their q
+    // Their page, K/V and q registers, which the block may fill before the plan
+    // is done: from the page cache entry of this block in the row of the call's
+    // head group, when it is of the pool's current epoch.  Only calls of one
+    // layer of one sequence (the calls a model makes at batch 1) use the cache
+    // (RC, chosen at launch): other calls run the kernel without its code.  The
+    // cache sits directly before the head records.
+    const int32_t* const rc0 = hs_plan - kRunCacheBytes / 4;
+    const bool rc_on = RC && gh0 >= 0 && n_heads == n_kv && (int)blockIdx.x < kRunCacheRuns;
+    int32_t* const rce_at = const_cast<int32_t*>(rc0) + kRunCacheHeader +
+                            ((size_t)(rc_on ? gh0 / n_kv % kRunCacheRows : 0) * kRunCacheRuns + blockIdx.x) * 4;
+    uint4 kc[F8 ? D / 16 : D / 8], vc[F8 ? 4 : 8][VJ];
+    float ksn = 1.f, vsn = 1.f;
+    uint4 qv = make_uint4(0u, 0u, 0u, 0u);
+    int rpid = -1, rgh = -1, rj = -1, epoch = 0;
+
     // ---- plan: pages per head and their prefix (every block builds its own);
     // a thread's head records (16 bytes each) are all requested before any is used
     {
@@ -551,9 +574,39 @@ void decode_attend_kernel(const int32_t* __restrict__ hs_plan, int32_t gh0, int3
                 rec[i] = *reinterpret_cast<const int4*>(hs_plan + (size_t)ghs[i] * kHS);
             }
         }
+        // the page cache entry and the epoch, behind the head records (blocks
+        // past the cache read through empty resources: no memory access)
+        uint4 e = make_uint4(~0u, ~0u, ~0u, ~0u);
+        int ep = 0;
+        if constexpr (RC) {
+            e = buffer_load16(buffer_rsrc(rce_at, rc_on ? 16 : 0), 0, 0);
+            ep = buffer_load4i(buffer_rsrc(rc0, rc_on ? 4 : 0), 0);
+        }
         // (after the head records are requested: the fixed part of the
         // arguments and the first sequence ids, one word of every line)
         touch_args<offsetof(DecodeArgs, seq_ids) + 64>(&a);
+        if constexpr (RC) {
+            rpid = __builtin_amdgcn_readfirstlane((int)e.x);
+            rgh = __builtin_amdgcn_readfirstlane((int)e.y);
+            rj = __builtin_amdgcn_readfirstlane((int)e.z);
+            epoch = __builtin_amdgcn_readfirstlane(ep);
+            if (__builtin_amdgcn_readfirstlane((int)e.w) != epoch) rgh = -1;
+            // the cached page, if this call covers its head: its K, V and this
+            // wave's q go out now, while the plan is being built
+            const int64_t all_pages = P.max_pages + (int64_t)P.n_kv_heads * P.pages_per_head;
+            if (rc_on && wave < NA && rgh >= gh0 && rgh - gh0 < H && rpid >= 0 && rpid < all_pages) {
+                if constexpr (F8) {
+                    issue_k8<D>(P, rpid, true, lane, kc, ksn, vsn);
+                    issue_v8<D>(P, rpid, true, lane, vc);
+                } else {
+                    issue_k<D>(P, rpid, true, lane, kc);
+                    issue_v<D>(P, rpid, true, lane, vc);
+                }
+                qv = buffer_load16(buffer_rsrc(q_group(a, rgh - gh0) + wave * GW * D, QW * 16), lane * 16, 0);
+            } else {
+                rgh = -1;
+            }
+        }
         int local = 0;
 #pragma unroll
         for (int i = 0; i < MAXPER; ++i) {
@@ -584,17 +637,15 @@ void decode_attend_kernel(const int32_t* __restrict__ hs_plan, int32_t gh0, int3
     const int total = __builtin_amdgcn_readfirstlane(s_pp[H]);
     if (total <= (int)gridDim.x) {
         // A call with at most one page per block (e.g. one layer of one
-        // sequence): block b takes page b (run b of W = total), and its waves
-        // split the page's G q heads, GW each, every wave with its own copy of
-        // the page.  Each head's arithmetic is the general path's, so the
-        // partial holds the same bits; the page's dot products are spread over
-        // the block's SIMDs.  A 32 KB page (D = 128) goes to at most two waves:
-        // four copies of it load one compute unit's memory path more than the
-        // shorter dot products save.
-        constexpr int NAX = D == 128 ? 2 : kAttendWaves;
-        constexpr int NA = G < NAX ? G : NAX;  // waves with heads
-        constexpr int GW = G / NA;                               // q heads per wave
-        constexpr int QW = GW * D / 8;                           // 16-byte pieces of their q
+        // sequence): block b takes page b (run b of W = total), and NA of its
+        // waves split the page's G q heads, GW each, every wave with its own
+        // copy of the page.  Each head's arithmetic is the general path's, so
+        // the partial holds the same bits; the page's dot products are spread
+        // over the block's SIMDs.  The page is the cached one if the block's
+        // cache entry names the same (head, page index) in the current epoch (a
+        // head's page-table entries below its page count change only after a
+        // release, which advances the epoch); else it is read from the page
+        // table and the entry rewritten.
         const int pg = blockIdx.x;
         if (pg >= total || wave >= NA) return;
         int lo = 0, hi = H;  // s_pp[lo] <= pg < s_pp[hi]
@@ -605,16 +656,19 @@ void decode_attend_kernel(const int32_t* __restrict__ hs_plan, int32_t gh0, int3
         const int hd = __builtin_amdgcn_readfirstlane(lo);
         const int j = pg - __builtin_amdgcn_readfirstlane(s_pp[hd]);
         const int gh = __builtin_amdgcn_readfirstlane(s_gh[hd]);
-        const int pid = __builtin_amdgcn_readfirstlane(P.ptable[(size_t)gh * P.pages_per_head + j]);
-        const uint4 qv = buffer_load16(buffer_rsrc(q_group(a, hd) + wave * GW * D, QW * 16), lane * 16, 0);
-        uint4 kc[F8 ? D / 16 : D / 8], vc[F8 ? 4 : 8][VJ];
-        float ksn = 1.f, vsn = 1.f;
-        if constexpr (F8) {
-            issue_k8<D>(P, pid, true, lane, kc, ksn, vsn);
-            issue_v8<D>(P, pid, true, lane, vc);
-        } else {
-            issue_k<D>(P, pid, true, lane, kc);
-            issue_v<D>(P, pid, true, lane, vc);
+        if (!RC || rgh != gh || rj != j) {
+            // (registers still awaiting the cached page are refilled after it:
+            // loads return in order)
+            const int pid = __builtin_amdgcn_readfirstlane(P.ptable[(size_t)gh * P.pages_per_head + j]);
+            if constexpr (F8) {
+                issue_k8<D>(P, pid, true, lane, kc, ksn, vsn);
+                issue_v8<D>(P, pid, true, lane, vc);
+            } else {
+                issue_k<D>(P, pid, true, lane, kc);
+                issue_v<D>(P, pid, true, lane, vc);
+            }
+            qv = buffer_load16(buffer_rsrc(q_group(a, hd) + wave * GW * D, QW * 16), lane * 16, 0);
+            if (RC && rc_on && wave == 0 && lane == 0) *reinterpret_cast<int4*>(rce_at) = make_int4(pid, gh, j, epoch);
         }
         if (lane < QW) s_q[wave][lane] = qv;
         wave_lds_sync();
@@ -708,11 +762,9 @@ void decode_attend_kernel(const int32_t* __restrict__ hs_plan, int32_t gh0, int3
     int hd = __builtin_amdgcn_readfirstlane(chd);
     uint4 qr[QR];
     load_q(hd, true, qr);
-    // K and V registers of one page (FP8 pages: half as many, plus the slot's
-    // scales, loaded with K into ksn / vsn and taken over at the top of the
-    // page); once consumed they are refilled with the next page.
-    uint4 kc[F8 ? D / 16 : D / 8], vc[F8 ? 4 : 8][VJ];
-    float ksn = 1.f, vsn = 1.f;
+    // kc, vc: K and V registers of one page (FP8 pages: half as many, plus the
+    // slot's scales, loaded with K into ksn / vsn and taken over at the top of
+    // the page); once consumed they are refilled with the next page.
     auto ik = [&](int page, bool live) {
         if constexpr (F8) issue_k8<D>(P, page, live, lane, kc, ksn, vsn);
         else issue_k<D>(P, page, live, lane, kc);
@@ -1272,6 +1324,7 @@ __global__ __launch_bounds__(1024) void prefill_scan_kernel(PrefillArgs a) {
         hs[kHsPages] = np;
         hs[kHsPos] = T;
         hs[kHsExp] = e;
+        if (h == 0) atomicAdd(P.rcache, 1);  // epoch: a page table written afresh
     }
     // ring entry idx holds the newest position s < T with s % w == idx (all of
     // them lie in the window, so their slots are the last ones: n - T + s)
@@ -1714,8 +1767,10 @@ __global__ __launch_bounds__(64) void seq_release_kernel(PoolDev P, int seq) {
     if (threadIdx.x == 0 && np > 0) base = atomicAdd(&P.ctl[kCtlTop], np);
     base = __shfl(base, 0, 64);
     for (int j = threadIdx.x; j < np; j += 64) P.stack[base + j] = P.ptable[(size_t)gh * P.pages_per_head + j];
-    if (threadIdx.x == 0)
+    if (threadIdx.x == 0) {
         for (int i = 0; i < kHS; ++i) hs[i] = i == kHsExp ? -1 : 0;
+        if (blockIdx.x == 0) atomicAdd(P.rcache, 1);  // epoch: the freed pages' table entries are stale
+    }
 }
 
 size_t decode_shm(const DecodeArgs& a) { return (size_t)(4 * a.n_call_heads + 1) * sizeof(int32_t); }
@@ -1729,9 +1784,17 @@ hipError_t launch_decode_f(const DecodeArgs& a, int grid, hipStream_t s, hipEven
     // of its first head: the others follow it): leading arguments, which the
     // dispatch places in registers (kernel-argument preloading)
     const int32_t gh0 = a.n_seqs == 1 ? (a.seq_ids[0] * a.pool.n_layers + a.layer0) * a.pool.n_kv_heads : -1;
-    hipExtLaunchKernelGGL((decode_attend_kernel<D, G, F8>), dim3(grid), dim3(64 * kAttendWaves), decode_shm(a), s,
-                          ev ? ev[0] : nullptr, ev ? ev[1] : nullptr, 0, (const int32_t*)a.pool.hstate, gh0,
-                          a.n_call_heads, a.pool.n_kv_heads, a.n_seqs, a.pool.n_layers, a.layer0, a);
+    // calls of one layer of one sequence: the kernel with the page cache
+    if (a.n_seqs == 1 && a.n_layers == 1)
+        hipExtLaunchKernelGGL((decode_attend_kernel<D, G, F8, true>), dim3(grid), dim3(64 * kAttendWaves),
+                              decode_shm(a), s, ev ? ev[0] : nullptr, ev ? ev[1] : nullptr, 0,
+                              (const int32_t*)a.pool.hstate, gh0, a.n_call_heads, a.pool.n_kv_heads, a.n_seqs,
+                              a.pool.n_layers, a.layer0, a);
+    else
+        hipExtLaunchKernelGGL((decode_attend_kernel<D, G, F8, false>), dim3(grid), dim3(64 * kAttendWaves),
+                              decode_shm(a), s, ev ? ev[0] : nullptr, ev ? ev[1] : nullptr, 0,
+                              (const int32_t*)a.pool.hstate, gh0, a.n_call_heads, a.pool.n_kv_heads, a.n_seqs,
+                              a.pool.n_layers, a.layer0, a);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
     // A head whose outputs fill 128 or more threads' float4s holds at most 32
@@ -1757,13 +1820,21 @@ hipError_t launch_decode_t(const DecodeArgs& a, int grid, hipStream_t s, hipEven
 
 template <int D, int G>
 int blocks_per_cu_t(const DecodeArgs& a) {
-    int n = 0;
-    const hipError_t e =
-        a.pool.fp8 ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_attend_kernel<D, G, true>,
-                                                                  64 * kAttendWaves, decode_shm(a))
-                   : hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_attend_kernel<D, G, false>,
-                                                                  64 * kAttendWaves, decode_shm(a));
-    return e == hipSuccess ? n : 0;
+    // (the smaller count of the kernel's two forms, with and without the page cache)
+    int n = 0, m = 0;
+    hipError_t e, f;
+    if (a.pool.fp8) {
+        e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_attend_kernel<D, G, true, false>,
+                                                         64 * kAttendWaves, decode_shm(a));
+        f = hipOccupancyMaxActiveBlocksPerMultiprocessor(&m, decode_attend_kernel<D, G, true, true>,
+                                                         64 * kAttendWaves, decode_shm(a));
+    } else {
+        e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_attend_kernel<D, G, false, false>,
+                                                         64 * kAttendWaves, decode_shm(a));
+        f = hipOccupancyMaxActiveBlocksPerMultiprocessor(&m, decode_attend_kernel<D, G, false, true>,
+                                                         64 * kAttendWaves, decode_shm(a));
+    }
+    return e == hipSuccess && f == hipSuccess ? std::min(n, m) : 0;
 }
 
 template <int D>

@@ -248,6 +248,31 @@ def test_reprefill_onto_other_pages_after_one_layer_calls():
         r.close()
 
 
+@pytest.mark.parametrize("head_dim", [64, 128])
+@pytest.mark.parametrize("kv_format", [0, 1])
+def test_one_layer_calls_over_many_steps(head_dim, kv_format):
+    """One sequence stepped by one-layer calls for 100 steps, every output
+    checked.  About half the tokens are kept, so the heads keep growing into
+    new pages: the page axis of later calls shifts, and a block's page from
+    the call before it (which such calls read ahead of their plan) is often no
+    longer its page."""
+    case = Case(n_layers=2, n_q_heads=16, n_kv_heads=4, head_dim=head_dim, window=16,
+                ctx_lens=[1500], steps=100, seed=31 + head_dim, keep_mu=0.0, kv_format=kv_format)
+    case.gen()
+    r = Runner(case)
+    try:
+        r.prefill_all()
+        for i in range(case.steps):
+            for l in range(case.n_layers):
+                out = r.decode(i, seqs=[0], layer0=l, n_layers=1)
+                r.check_outputs(out, i, seqs=[0], layer0=l,
+                                record="decode (fp8 pool)" if kv_format else "decode")
+        r.check_live([case.ctx_lens[0] + case.steps - 1])
+        r.check_kv([case.ctx_lens[0] + case.steps - 1])
+    finally:
+        r.close()
+
+
 def test_capacity_exhaustion_is_reported():
     import compact_decode_attention_amd as dms
     case = Case(n_layers=1, n_q_heads=4, n_kv_heads=1, head_dim=64, window=4,
