@@ -533,14 +533,18 @@ void decode_attend_kernel(const int32_t* __restrict__ hs_plan, int32_t gh0, int3
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
 
-    // Calls with at most one page per block (below): NA waves of a block take
-    // its page, GW q heads each.  A 32 KB page (D = 128) goes to at most two
-    // waves: four copies of it load one compute unit's memory path more than
-    // the shorter dot products save.
+    // Calls with at most NG pages per block (below): each group of NA waves of
+    // a block takes a page, GW q heads per wave (group k of block b: page
+    // b + k * grid).  A 32 KB page (D = 128) goes to at most two waves: four
+    // copies of it load one compute unit's memory path more than the shorter
+    // dot products save.
     constexpr int NAX = D == 128 ? 2 : kAttendWaves;
-    constexpr int NA = G < NAX ? G : NAX;  // waves with q heads
-    constexpr int GW = G / NA;             // q heads per such wave
+    constexpr int NA = G < NAX ? G : NAX;  // waves per page
+    constexpr int NG = kAttendWaves / NA;  // pages per block
+    constexpr int GW = G / NA;             // q heads per wave
     constexpr int QW = GW * D / 8;         // 16-byte pieces of their q
+    const int grp = NG == 1 ? 0 : wave / NA, role = NG == 1 ? wave : wave % NA;
+    const int ei = (int)blockIdx.x + grp * (int)gridDim.x;  // this group's page (and cache entry)
     // Their page, K/V and q registers, which the block may fill before the plan
     // is done: from the page cache entry of this block in the row of the call's
     // head group, when it is of the pool's current epoch.  Only calls of one
@@ -548,9 +552,9 @@ void decode_attend_kernel(const int32_t* __restrict__ hs_plan, int32_t gh0, int3
     // (RC, chosen at launch): other calls run the kernel without its code.  The
     // cache sits directly before the head records.
     const int32_t* const rc0 = hs_plan - kRunCacheBytes / 4;
-    const bool rc_on = RC && gh0 >= 0 && n_heads == n_kv && (int)blockIdx.x < kRunCacheRuns;
+    const bool rc_on = RC && gh0 >= 0 && n_heads == n_kv && ei < kRunCacheRuns;
     int32_t* const rce_at = const_cast<int32_t*>(rc0) + kRunCacheHeader +
-                            ((size_t)(rc_on ? gh0 / n_kv % kRunCacheRows : 0) * kRunCacheRuns + blockIdx.x) * 4;
+                            ((size_t)(rc_on ? gh0 / n_kv % kRunCacheRows : 0) * kRunCacheRuns + (rc_on ? ei : 0)) * 4;
     uint4 kc[F8 ? D / 16 : D / 8], vc[F8 ? 4 : 8][VJ];
     float ksn = 1.f, vsn = 1.f;
     uint4 qv = make_uint4(0u, 0u, 0u, 0u);
@@ -594,7 +598,7 @@ void decode_attend_kernel(const int32_t* __restrict__ hs_plan, int32_t gh0, int3
             // the cached page, if this call covers its head: its K, V and this
             // wave's q go out now, while the plan is being built
             const int64_t all_pages = P.max_pages + (int64_t)P.n_kv_heads * P.pages_per_head;
-            if (rc_on && wave < NA && rgh >= gh0 && rgh - gh0 < H && rpid >= 0 && rpid < all_pages) {
+            if (rc_on && rgh >= gh0 && rgh - gh0 < H && rpid >= 0 && rpid < all_pages) {
                 if constexpr (F8) {
                     issue_k8<D>(P, rpid, true, lane, kc, ksn, vsn);
                     issue_v8<D>(P, rpid, true, lane, vc);
@@ -602,7 +606,7 @@ void decode_attend_kernel(const int32_t* __restrict__ hs_plan, int32_t gh0, int3
                     issue_k<D>(P, rpid, true, lane, kc);
                     issue_v<D>(P, rpid, true, lane, vc);
                 }
-                qv = buffer_load16(buffer_rsrc(q_group(a, rgh - gh0) + wave * GW * D, QW * 16), lane * 16, 0);
+                qv = buffer_load16(buffer_rsrc(q_group(a, rgh - gh0) + role * GW * D, QW * 16), lane * 16, 0);
             } else {
                 rgh = -1;
             }
@@ -635,19 +639,19 @@ void decode_attend_kernel(const int32_t* __restrict__ hs_plan, int32_t gh0, int3
     }
     // ---- this wave's run of pages (no block-wide synchronisation below)
     const int total = __builtin_amdgcn_readfirstlane(s_pp[H]);
-    if (total <= (int)gridDim.x) {
-        // A call with at most one page per block (e.g. one layer of one
-        // sequence): block b takes page b (run b of W = total), and NA of its
-        // waves split the page's G q heads, GW each, every wave with its own
-        // copy of the page.  Each head's arithmetic is the general path's, so
-        // the partial holds the same bits; the page's dot products are spread
-        // over the block's SIMDs.  The page is the cached one if the block's
-        // cache entry names the same (head, page index) in the current epoch (a
-        // head's page-table entries below its page count change only after a
-        // release, which advances the epoch); else it is read from the page
-        // table and the entry rewritten.
-        const int pg = blockIdx.x;
-        if (pg >= total || wave >= NA) return;
+    if (total <= (int)gridDim.x * NG) {
+        // A call with at most NG pages per block (e.g. one layer of one
+        // sequence): group k of block b takes page b + k * grid (run pg of W =
+        // total), and its NA waves split the page's G q heads, GW each, every
+        // wave with its own copy of the page.  Each head's arithmetic is the
+        // general path's, so the partial holds the same bits; the page's dot
+        // products are spread over the block's SIMDs.  The page is the cached
+        // one if the group's cache entry names the same (head, page index) in
+        // the current epoch (a head's page-table entries below its page count
+        // change only after a release, which advances the epoch); else it is
+        // read from the page table and the entry rewritten.
+        const int pg = ei;
+        if (pg >= total) return;
         int lo = 0, hi = H;  // s_pp[lo] <= pg < s_pp[hi]
         while (hi - lo > 1) {
             const int mid = (lo + hi) >> 1;
@@ -667,8 +671,8 @@ void decode_attend_kernel(const int32_t* __restrict__ hs_plan, int32_t gh0, int3
                 issue_k<D>(P, pid, true, lane, kc);
                 issue_v<D>(P, pid, true, lane, vc);
             }
-            qv = buffer_load16(buffer_rsrc(q_group(a, hd) + wave * GW * D, QW * 16), lane * 16, 0);
-            if (RC && rc_on && wave == 0 && lane == 0) *reinterpret_cast<int4*>(rce_at) = make_int4(pid, gh, j, epoch);
+            qv = buffer_load16(buffer_rsrc(q_group(a, hd) + role * GW * D, QW * 16), lane * 16, 0);
+            if (RC && rc_on && role == 0 && lane == 0) *reinterpret_cast<int4*>(rce_at) = make_int4(pid, gh, j, epoch);
         }
         if (lane < QW) s_q[wave][lane] = qv;
         wave_lds_sync();
@@ -698,14 +702,14 @@ void decode_attend_kernel(const int32_t* __restrict__ hs_plan, int32_t gh0, int3
         if (lane == 0) {
 #pragma unroll
             for (int g = 0; g < GW; ++g) {
-                part[wave * GW + g] = m[g];
-                part[G + wave * GW + g] = l[g];
+                part[role * GW + g] = m[g];
+                part[G + role * GW + g] = l[g];
             }
         }
 #pragma unroll
         for (int g = 0; g < GW; ++g)
 #pragma unroll
-            for (int jj = 0; jj < VJ; ++jj) part[ACC + (wave * GW + g) * D + jj * 64 + lane] = acc[g][jj];
+            for (int jj = 0; jj < VJ; ++jj) part[ACC + (role * GW + g) * D + jj * 64 + lane] = acc[g][jj];
         return;
     }
     const int NW = (int)gridDim.x * kAttendWaves;
