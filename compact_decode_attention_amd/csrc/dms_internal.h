@@ -88,12 +88,13 @@ constexpr int kCtlVWide = 2;  // sticky: nonzero once a bf16 V value of magnitud
 constexpr int kCtlPosError = 3;  // sticky: nonzero once a decode or extend call ran past max_positions (the
                                  // device's position counters decide; tokens past the limit are dropped)
 
-// Page cache of the decode attention's calls with at most one page per block:
+// Page cache of the decode attention's calls of one layer of one sequence:
 // a header of kRunCacheHeader ints, whose first is the pool's epoch (advanced by
 // every release and prefill: a head's page-table entries below its page count
 // change only when a release frees them), then kRunCacheRows rows (the first
 // head of a call of one sequence picks the row) of kRunCacheRuns entries {page
-// id, global head, page index, epoch}, one per block.  The arena places it
+// id, global head, page index, epoch}, one per wave group's page (block b's
+// first group: entry b; its second: entry b + grid).  The arena places it
 // directly before the head records, so the attention finds it from the
 // head-record pointer it gets in registers.
 constexpr int kRunCacheRows = 64;
