@@ -580,11 +580,13 @@ def main():
     dec = bench_decode(args, torch, dms)
     f8 = None
     if not args.no_fp8:
-        d8 = bench_decode(args, torch, dms, kv_format=1, modes=["batched"], cpu_steps=0)
+        d8 = bench_decode(args, torch, dms, kv_format=1, modes=["batched", "per_layer"], cpu_steps=0)
         f8 = {"tok_per_s": round(d8["value"], 2), "ms_per_step": round(d8["ms_per_step"], 5),
               "achieved_step_GBps": d8["achieved_step_GBps"], "roofline": d8["roofline"], "kv_gib": d8["kv_gib"],
+              "modes": d8["modes"], "modes_max_abs_diff": d8["modes_max_abs_diff"],
               "workload": "the decode workload above on an FP8 (OCP E4M3) pool: K/V rows stored as codes "
-                          "with one fp32 scale each, one dms_decode_step per token over all layers"}
+                          "with one fp32 scale each, one dms_decode_step per token over all layers "
+                          "(modes.per_layer: one call per layer, 36 per token)"}
     lk = None
     if not args.no_logit_channel:
         dk_ = bench_decode(args, torch, dms, modes=["batched"], cpu_steps=0, logit_channel=0)
