@@ -151,6 +151,7 @@ struct dms_pool {
     std::vector<int32_t> pos;  // [max_seqs][n_layers]: next position, -1 = empty
     std::vector<uint32_t> seen;  // [max_seqs]: call stamp of the last decode call naming the sequence
     uint32_t call_stamp = 0;
+    uint64_t rewrites = 0;       // releases and prefills (each advances the device's page-cache epoch once at most)
     void* scratch = nullptr;     // device address of the static decode scratch on the pool's device
     int cu_count;
     int attend_per_cu;  // attention blocks per compute unit (checked once, for the largest call)
@@ -247,8 +248,9 @@ dms_status dms_pool_create(const dms_pool_config* cfg, void* arena, size_t arena
     if (e == hipSuccess) e = hipMemcpyAsync(d.stack, order.data(), order.size() * 4, hipMemcpyHostToDevice, s);
     if (e == hipSuccess) e = hipMemcpyAsync(d.hstate, rec.data(), rec.size() * 4, hipMemcpyHostToDevice, s);
     if (e == hipSuccess) e = hipMemcpyAsync(d.ctl, ctl, sizeof(ctl), hipMemcpyHostToDevice, s);
-    const int32_t epoch = 1;  // the zeroed page-cache entries carry epoch 0: none is valid
+    const int32_t epoch = 1;
     if (e == hipSuccess) e = hipMemcpyAsync(d.rcache, &epoch, sizeof(epoch), hipMemcpyHostToDevice, s);
+    if (e == hipSuccess) e = dms::launch_page_cache_clear(d, s);
     if (e == hipSuccess) e = hipStreamSynchronize(s);
     if (e == hipSuccess) e = dms::static_scratch_address(&p->scratch);  // once per device, here
     if (e != hipSuccess) {
@@ -333,6 +335,10 @@ dms_status dms_prefill(dms_pool* pool, int32_t seq, int32_t layer, int32_t n_tok
         if (e != hipSuccess) return hip_fail(e, "prefill attention launch");
     }
     pool->position(seq, layer) = n_tokens;
+    if (++pool->rewrites % dms::kRunCacheRefill == 0) {
+        e = dms::launch_page_cache_clear(pool->dev, s);
+        if (e != hipSuccess) return hip_fail(e, "page cache clear launch");
+    }
     g_err.clear();
     return DMS_OK;
 }
@@ -655,6 +661,10 @@ dms_status dms_seq_release(dms_pool* pool, int32_t seq, void* stream) {
     pool->note(static_cast<hipStream_t>(stream));
     hipError_t e = dms::launch_seq_release(pool->dev, seq, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return hip_fail(e, "release launch");
+    if (++pool->rewrites % dms::kRunCacheRefill == 0) {
+        e = dms::launch_page_cache_clear(pool->dev, static_cast<hipStream_t>(stream));
+        if (e != hipSuccess) return hip_fail(e, "page cache clear launch");
+    }
     for (int l = 0; l < pool->cfg.n_layers; ++l) pool->position(seq, l) = -1;
     g_err.clear();
     return DMS_OK;

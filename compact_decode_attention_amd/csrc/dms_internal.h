@@ -371,6 +371,11 @@ hipError_t launch_extend(const PrefillArgs& a, bool with_out, hipStream_t s, hip
 // ev (optional, 4 events): start/stop of the preparation kernel, then of the attention kernel
 hipError_t launch_extend_attend(const PrefillArgs& a, hipStream_t s, hipEvent_t* ev);
 hipError_t launch_seq_release(const PoolDev& p, int32_t seq, hipStream_t s);
+// Every entry of the decode attention's page cache set to -1 (its global head
+// then matches no head): at pool creation, and every kRunCacheRefill releases
+// and prefills, so that no entry outlives 2^30 advances of the 32-bit epoch.
+hipError_t launch_page_cache_clear(const PoolDev& p, hipStream_t s);
+constexpr uint64_t kRunCacheRefill = (uint64_t)1 << 30;
 int device_cu_count();
 // Device address of the static decode scratch (kStaticScratchBytes) on the
 // current device, looked up once per device.

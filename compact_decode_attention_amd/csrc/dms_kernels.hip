@@ -1929,6 +1929,16 @@ hipError_t launch_extend(const PrefillArgs& a, bool with_out, hipStream_t s, hip
     return hipGetLastError();
 }
 
+__global__ __launch_bounds__(256) void page_cache_clear_kernel(int32_t* e, int32_t n) {
+    for (int i = blockIdx.x * 256 + threadIdx.x; i < n; i += gridDim.x * 256) e[i] = -1;
+}
+
+hipError_t launch_page_cache_clear(const PoolDev& p, hipStream_t s) {
+    constexpr int n = kRunCacheRows * kRunCacheRuns * 4;
+    hipLaunchKernelGGL(page_cache_clear_kernel, dim3(256), dim3(256), 0, s, p.rcache + kRunCacheHeader, n);
+    return hipGetLastError();
+}
+
 hipError_t launch_seq_release(const PoolDev& p, int32_t seq, hipStream_t s) {
     hipLaunchKernelGGL(seq_release_kernel, dim3(p.n_layers * p.n_kv_heads), dim3(64), 0, s, p, seq);
     return hipGetLastError();
