@@ -273,6 +273,34 @@ def test_one_layer_calls_over_many_steps(head_dim, kv_format):
         r.close()
 
 
+def test_one_layer_calls_with_more_pages_than_blocks():
+    """One-layer calls of about 260 pages (head_dim 128): more pages than the
+    attention grid has blocks on a 256-CU part, so the second pair of waves of
+    a block takes page b + grid; the layer-batched call of the same step (about
+    520 pages) takes the general path.  Every output checked against the
+    oracle."""
+    case = Case(n_layers=2, n_q_heads=16, n_kv_heads=4, head_dim=128, window=32,
+                ctx_lens=[6000], steps=4, seed=57, keep_mu=0.5)
+    case.gen()
+    r = Runner(case)
+    try:
+        r.prefill_all()
+        _, live = r.pool.stats(0, per_head=True)
+        pages = [int(sum((int(n) + 63) // 64 for n in live[l])) for l in range(case.n_layers)]
+        assert all(256 < p <= 512 for p in pages), pages
+        for i in range(case.steps):
+            if i % 2:
+                out = r.decode(i)
+                r.check_outputs(out, i)
+            else:
+                for l in range(case.n_layers):
+                    out = r.decode(i, seqs=[0], layer0=l, n_layers=1)
+                    r.check_outputs(out, i, seqs=[0], layer0=l)
+        r.check_live([case.ctx_lens[0] + case.steps - 1])
+    finally:
+        r.close()
+
+
 def test_capacity_exhaustion_is_reported():
     import compact_decode_attention_amd as dms
     case = Case(n_layers=1, n_q_heads=4, n_kv_heads=1, head_dim=64, window=4,
